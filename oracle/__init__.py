@@ -1,0 +1,152 @@
+"""ctypes front end of the fp64 CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library and
+its Python binding) never does. Arrays are numpy: bf16 tensors travel as their
+raw ``uint16`` bit patterns, everything the oracle computes comes back in fp64.
+
+Functions mirror the definitions in ``oracle.c``; see the comments there for the
+passages of the pages each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# Status bits, as the public header documents them for the library.
+BAD_PAGE, BAD_POS, BAD_ROWS, BAD_TOKEN = 1, 2, 4, 8
+PAGE = 16
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (fp64, IEEE semantics: no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+                        "-ffp-contract=off", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16, ties to even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def validate(page_table, max_pages, n_pages, pos, k, kmax, B, R):
+    off = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    pt = None if page_table is None else _i32(page_table)
+    lib().oracle_validate(_p(pt), ctypes.c_int32(max_pages), ctypes.c_int64(n_pages), _p(_i32(pos)),
+                          _p(_i32(k)), ctypes.c_int32(kmax), ctypes.c_int32(B), ctypes.c_int32(R),
+                          _p(off), _p(st))
+    return off, st
+
+
+def append_kv(k_new, v_new, k_pool, v_pool, page_table, max_pages, pos, k, off, st, B, Hkv, D):
+    """In place on k_pool / v_pool (uint16 arrays)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    lib().oracle_append_kv(_p(_u16(k_new)), _p(_u16(v_new)), _p(k_pool), _p(v_pool),
+                           _p(_i32(page_table)), ctypes.c_int32(max_pages), _p(_i32(pos)),
+                           _p(_i32(k)), _p(_i32(off)), _p(_i32(st)), ctypes.c_int32(B),
+                           ctypes.c_int32(Hkv), ctypes.c_int32(D))
+
+
+def verify_attn(q, k_pool, v_pool, page_table, max_pages, pos, k, off, st, B, R, Hq, Hkv, D, scale,
+                out=None):
+    """Returns fp64 [R, Hq, D]; rows of bad sequences keep ``out``'s values (NaN if new)."""
+    if out is None:
+        out = np.full((R, Hq, D), np.nan, np.float64)
+    lib().oracle_verify_attn(_p(_u16(q)), _p(_u16(k_pool)), _p(_u16(v_pool)), _p(_i32(page_table)),
+                             ctypes.c_int32(max_pages), _p(_i32(pos)), _p(_i32(k)), _p(_i32(off)),
+                             _p(_i32(st)), ctypes.c_int32(B), ctypes.c_int32(R), ctypes.c_int32(Hq),
+                             ctypes.c_int32(Hkv), ctypes.c_int32(D), ctypes.c_double(scale), _p(out))
+    return out
+
+
+def lm_head_argmax(hidden, w, R, H, V, want_logits=False):
+    """Returns (g int32 [R], top1 f64 [R], top2 f64 [R], logits f64 [R,V] or None)."""
+    g = np.zeros(R, np.int32)
+    t1 = np.zeros(R, np.float64)
+    t2 = np.zeros(R, np.float64)
+    lg = np.zeros((R, V), np.float64) if want_logits else None
+    lib().oracle_lm_head_argmax(_p(_u16(hidden)), _p(_u16(w)), ctypes.c_int32(R), ctypes.c_int32(H),
+                                ctypes.c_int32(V), _p(g), _p(t1), _p(t2), _p(lg))
+    return g, t1, t2, lg
+
+
+def greedy_accept(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in):
+    """Returns dict with pos_out, accept_len, n_emit, emit [B, kmax+1], next_tok, status."""
+    pos_out = np.zeros(B, np.int32)
+    acc = np.zeros(B, np.int32)
+    ne = np.zeros(B, np.int32)
+    emit = np.zeros((B, kmax + 1), np.int32)
+    nt = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    dr = _i32(drafts).reshape(B, max(kmax, 0)) if kmax > 0 else np.zeros((B, 1), np.int32)
+    d2 = None if d2t is None else _i32(d2t)
+    lib().oracle_greedy_accept(_p(_i32(g)), _p(dr), ctypes.c_int32(kmax), _p(_i32(k)), _p(d2),
+                               ctypes.c_int32(n_draft_vocab), ctypes.c_int32(V), ctypes.c_int32(B),
+                               ctypes.c_int32(R), _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne),
+                               _p(emit), _p(nt), _p(st))
+    return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st)
+
+
+def delta_verify(q, k, v, a, b, q_scale, state, B, T, Hd, dk, dv):
+    """Returns (rec f64 [B,T,Hd,dv,dk], o f64 [B,T,Hd,dv])."""
+    rec = np.zeros((B, T, Hd, dv, dk), np.float64)
+    o = np.zeros((B, T, Hd, dv), np.float64)
+    lib().oracle_delta_verify(_p(_u16(q)), _p(_u16(k)), _p(_u16(v)),
+                              _p(np.ascontiguousarray(a, np.float32)),
+                              _p(np.ascontiguousarray(b, np.float32)), ctypes.c_double(q_scale),
+                              _p(np.ascontiguousarray(state, np.float32)), ctypes.c_int32(B),
+                              ctypes.c_int32(T), ctypes.c_int32(Hd), ctypes.c_int32(dk),
+                              ctypes.c_int32(dv), _p(rec), _p(o))
+    return rec, o
+
+
+def delta_rollback(rec, L, state, B, T, Hd, dk, dv):
+    """state: fp64 [B,Hd,dv,dk], updated in place and returned."""
+    state = np.ascontiguousarray(state, np.float64)
+    lib().oracle_delta_rollback(_p(np.ascontiguousarray(rec, np.float64)), _p(_i32(L)),
+                                ctypes.c_int32(B), ctypes.c_int32(T), ctypes.c_int32(Hd),
+                                ctypes.c_int32(dk), ctypes.c_int32(dv), _p(state))
+    return state

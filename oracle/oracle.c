@@ -1,0 +1,362 @@
+/*
+ * Plain fp64 CPU oracle for the greedy draft/verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this file: only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it. It shares no code, header or table with the HIP
+ * library; the only things both sides agree on are the buffer formats that the
+ * public C header documents (bf16 bit patterns, the paged KV layout, the
+ * per-sequence status bits).
+ *
+ * Every function is the definition written out, in fp64, with bf16 inputs
+ * widened exactly. Loops run in the order of the definitions; OpenMP only
+ * spreads independent units (rows, heads, vocabulary entries) over cores.
+ *
+ * Sources (the web pages this build follows):
+ *  - "span-02 engine/crates/model/src/spec.rs", module doc: one verify forward
+ *    of B(k+1) rows, KV appended in place at pos..pos+k, greedy acceptance,
+ *    rollback = pos advances by the accepted tokens, kv_hi = position;
+ *    SpecReq doc: the KV slot of position p is page pages[p / 16].
+ *  - "DSSD-dev/dssd/fast.py", _attention: per-row softmax attention over keys
+ *    [0, p+1) with grouped query heads; the greedy chain acceptance loop in
+ *    generate_spec (first miss stops, then target[len(committed)] is appended).
+ *  - "memra-engine src/spec.rs", full_attn_verify: query row r attends to keys
+ *    [0 .. base_len + r + 1); attention scale 1/sqrt(head_dim).
+ *  - "oxinfer src/qwen_mtp.rs", module doc: Gated DeltaNet states recorded per
+ *    token and restored exactly on partial acceptance; DraftHead: draft index i
+ *    stands for target token d2t[i]; speculative_accept in the greedy case.
+ *  - "flashrt-structures whole_step.py", _gstep / generate_speculative: argmax on
+ *    fp32 logits, device prefix match, pos += j + 1.
+ *  - The Gated DeltaNet per-token update S_t = a_t S_{t-1} (I - b_t k_t k_t^T)
+ *    + b_t v_t k_t^T, o_t = S_t q_t, as the problem statement gives it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_PAGE 16
+
+/* Per-sequence status bits (same meaning as the library's documented bits). */
+#define ORC_BAD_PAGE 1  /* a page id the sequence needs is outside [0, n_pages) */
+#define ORC_BAD_POS 2   /* pos < 0, or (pos + k) / 16 >= max_pages              */
+#define ORC_BAD_ROWS 4  /* k < 0, k > kmax, or sum(k + 1) != R                   */
+#define ORC_BAD_TOKEN 8 /* draft id or d2t entry out of range                    */
+
+static double bf(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_version(void) { return 1; }
+
+/* ---------------------------------------------------------------------------
+ * Row bookkeeping (spec.rs spec_build_verify; fast.py _set_pos): sequence s
+ * owns rows off_s .. off_s + k_s, row j of it feeds position pos_s + j.
+ * Returns per-sequence status bits in st[B]; fills off[B] (row offsets).
+ * ------------------------------------------------------------------------- */
+void oracle_validate(const int32_t* page_table, int32_t max_pages, int64_t n_pages,
+                     const int32_t* pos, const int32_t* k, int32_t kmax, int32_t B, int32_t R,
+                     int32_t* off, int32_t* st) {
+    int64_t total = 0;
+    for (int s = 0; s < B; ++s) {
+        off[s] = (int32_t)total;
+        total += (int64_t)k[s] + 1;
+    }
+    for (int s = 0; s < B; ++s) {
+        int bits = 0;
+        if (k[s] < 0 || (kmax >= 0 && k[s] > kmax) || total != R) bits |= ORC_BAD_ROWS;
+        if (pos[s] < 0) {
+            bits |= ORC_BAD_POS;
+        } else if (k[s] >= 0) {
+            int64_t last = (int64_t)pos[s] + k[s];
+            if (last / ORC_PAGE >= max_pages) {
+                bits |= ORC_BAD_POS;
+            } else if (page_table) {
+                for (int64_t pg = 0; pg <= last / ORC_PAGE; ++pg) {
+                    int32_t id = page_table[(int64_t)s * max_pages + pg];
+                    if (id < 0 || id >= n_pages) bits |= ORC_BAD_PAGE;
+                }
+            }
+        }
+        st[s] = bits;
+    }
+}
+
+/* Offsets of the paged pool format: K pages are [n_pages][Hkv][16][D] (a token's
+ * D values contiguous), V pages are [n_pages][Hkv][D][16] (a channel's 16 tokens
+ * contiguous). */
+static int64_t k_index(int64_t page, int hk, int t, int d, int Hkv, int D) {
+    return ((page * Hkv + hk) * ORC_PAGE + t) * D + d;
+}
+static int64_t v_index(int64_t page, int hk, int t, int d, int Hkv, int D) {
+    return ((page * Hkv + hk) * (int64_t)D + d) * ORC_PAGE + t;
+}
+
+/* ---------------------------------------------------------------------------
+ * KV append in place (spec.rs module doc: KV appended at pos..pos+k; fast.py
+ * _layers index_copy_ into the cache at the rows' slots). Row r = off_s + j of
+ * k_new/v_new [R][Hkv][D] goes to position p = pos_s + j, i.e. page
+ * page_table[s][p / 16], in-page token p % 16. Bit-exact copy. Sequences with
+ * st[s] != 0 are skipped.
+ * ------------------------------------------------------------------------- */
+void oracle_append_kv(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                      uint16_t* v_pool, const int32_t* page_table, int32_t max_pages,
+                      const int32_t* pos, const int32_t* k, const int32_t* off, const int32_t* st,
+                      int32_t B, int32_t Hkv, int32_t D) {
+    for (int s = 0; s < B; ++s) {
+        if (st[s]) continue;
+        for (int j = 0; j <= k[s]; ++j) {
+            int64_t r = off[s] + j;
+            int64_t p = (int64_t)pos[s] + j;
+            int64_t page = page_table[(int64_t)s * max_pages + p / ORC_PAGE];
+            int t = (int)(p % ORC_PAGE);
+            for (int hk = 0; hk < Hkv; ++hk)
+                for (int d = 0; d < D; ++d) {
+                    int64_t src = (r * Hkv + hk) * D + d;
+                    k_pool[k_index(page, hk, t, d, Hkv, D)] = k_new[src];
+                    v_pool[v_index(page, hk, t, d, Hkv, D)] = v_new[src];
+                }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Verify attention (fast.py _attention reference path; memra full_attn_verify:
+ * row r attends to keys [0 .. base_len + r + 1); span-02: kv_hi = position).
+ * For row r = (s, j) at position p = pos_s + j and query head h, with kv head
+ * hk = h / (Hq / Hkv) (contiguous groups, as grouped-query SDPA does):
+ *   z_t = scale * sum_d q[r,h,d] K_t[hk,d]            t = 0..p
+ *   w_t = exp(z_t - max z) / sum_u exp(z_u - max z)
+ *   o[r,h,:] = sum_t w_t V_t[hk,:]
+ * K_t / V_t are read through the page table (after the append). out is fp64
+ * [R][Hq][D]; rows of sequences with st[s] != 0 are left untouched.
+ * ------------------------------------------------------------------------- */
+void oracle_verify_attn(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                        const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                        const int32_t* k, const int32_t* off, const int32_t* st, int32_t B,
+                        int32_t R, int32_t Hq, int32_t Hkv, int32_t D, double scale, double* out) {
+    int G = Hq / Hkv;
+    (void)R;
+    for (int s = 0; s < B; ++s) {
+        if (st[s]) continue;
+        int T = k[s] + 1;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+        for (int j = 0; j < T; ++j) {
+            for (int h = 0; h < Hq; ++h) {
+                int64_t r = off[s] + j;
+                int64_t p = (int64_t)pos[s] + j;
+                int hk = h / G;
+                const uint16_t* qr = q + (r * Hq + h) * D;
+                double* z = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+                double zmax = -INFINITY;
+                for (int64_t t = 0; t <= p; ++t) {
+                    int64_t page = page_table[(int64_t)s * max_pages + t / ORC_PAGE];
+                    int tt = (int)(t % ORC_PAGE);
+                    double acc = 0.0;
+                    for (int d = 0; d < D; ++d) acc += bf(qr[d]) * bf(k_pool[k_index(page, hk, tt, d, Hkv, D)]);
+                    z[t] = scale * acc;
+                    if (z[t] > zmax) zmax = z[t];
+                }
+                double denom = 0.0;
+                for (int64_t t = 0; t <= p; ++t) {
+                    z[t] = exp(z[t] - zmax);
+                    denom += z[t];
+                }
+                double* o = out + (r * Hq + h) * D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t t = 0; t <= p; ++t) {
+                    int64_t page = page_table[(int64_t)s * max_pages + t / ORC_PAGE];
+                    int tt = (int)(t % ORC_PAGE);
+                    double w = z[t] / denom;
+                    for (int d = 0; d < D; ++d) o[d] += w * bf(v_pool[v_index(page, hk, tt, d, Hkv, D)]);
+                }
+                free(z);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * lm_head contraction + greedy argmax (span-02 lm_head_argmax; greedy_logprob:
+ * the FIRST maximum wins; flashrt: argmax taken on full-precision logits).
+ *   logit[r,v] = sum_i W[v,i] h[r,i]      (fp64, i ascending)
+ *   g[r]       = lowest v with logit[r,v] == max_v logit[r,v]
+ *   top1[r]    = that maximum, top2[r] = the largest logit at any other index
+ * (top2 == top1 when the maximum is tied). logits_out (nullable) receives the
+ * full [R][V] fp64 matrix.
+ * ------------------------------------------------------------------------- */
+void oracle_lm_head_argmax(const uint16_t* hidden, const uint16_t* w, int32_t R, int32_t H,
+                           int32_t V, int32_t* g, double* top1, double* top2, double* logits_out) {
+    double* hd = (double*)malloc(sizeof(double) * (size_t)R * H);
+    for (int64_t i = 0; i < (int64_t)R * H; ++i) hd[i] = bf(hidden[i]);
+    double* logit = logits_out ? logits_out : (double*)malloc(sizeof(double) * (size_t)R * V);
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)R);
+        double* wrow = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+        for (int v = 0; v < V; ++v) {
+            for (int i = 0; i < H; ++i) wrow[i] = bf(w[(int64_t)v * H + i]);
+            for (int r = 0; r < R; ++r) acc[r] = 0.0;
+            /* each acc[r] is one dot product summed over i in ascending order */
+            for (int i = 0; i < H; ++i)
+                for (int r = 0; r < R; ++r) acc[r] += wrow[i] * hd[(int64_t)r * H + i];
+            for (int r = 0; r < R; ++r) logit[(int64_t)r * V + v] = acc[r];
+        }
+        free(acc);
+        free(wrow);
+    }
+    for (int r = 0; r < R; ++r) {
+        const double* z = logit + (int64_t)r * V;
+        int best = 0;
+        for (int v = 1; v < V; ++v)
+            if (z[v] > z[best]) best = v;
+        double second = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if (v != best && z[v] > second) second = z[v];
+        g[r] = best;
+        if (top1) top1[r] = z[best];
+        if (top2) top2[r] = second;
+    }
+    if (!logits_out) free(logit);
+    free(hd);
+}
+
+/* ---------------------------------------------------------------------------
+ * Greedy acceptance and rollback bookkeeping (fast.py generate_spec accept loop;
+ * oxinfer MtpDecoder::step; flashrt device prefix match; span-02 step_chunk:
+ * pos <- pos + a + 1, next token <- last emitted).
+ *   map(x) = d2t ? d2t[x] : x
+ *   a      = number of leading j < k_s with map(draft[s][j]) == g[off_s + j]
+ *   emit   = map(draft[s][0..a)) ++ [g[off_s + a]]        (n_emit = a + 1)
+ *   pos_out = pos_in + a + 1, next_tok = g[off_s + a]
+ * emit is [B][kmax + 1], unused entries are -1. A sequence with a bad status
+ * (from oracle_validate, plus draft ids / d2t entries out of range) gets
+ * accept_len = -1, n_emit = 0, next_tok = -1, pos_out = pos_in, emit row -1.
+ * ------------------------------------------------------------------------- */
+void oracle_greedy_accept(const int32_t* g, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                          const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B,
+                          int32_t R, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
+                          int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* st) {
+    int64_t total = 0;
+    for (int s = 0; s < B; ++s) total += (int64_t)k[s] + 1;
+    int64_t off = 0;
+    for (int s = 0; s < B; ++s) {
+        int bits = 0;
+        int ks = k[s];
+        if (ks < 0 || ks > kmax || total != R) bits |= ORC_BAD_ROWS;
+        if (pos_in[s] < 0) bits |= ORC_BAD_POS;
+        if (!bits) {
+            for (int j = 0; j < ks; ++j) {
+                int32_t x = drafts[(int64_t)s * kmax + j];
+                if (d2t) {
+                    if (x < 0 || x >= n_draft_vocab || d2t[x] < 0 || d2t[x] >= V) bits |= ORC_BAD_TOKEN;
+                } else if (x < 0 || x >= V) {
+                    bits |= ORC_BAD_TOKEN;
+                }
+            }
+        }
+        int32_t* e = emit + (int64_t)s * (kmax + 1);
+        for (int j = 0; j <= kmax; ++j) e[j] = -1;
+        if (bits) {
+            st[s] = bits;
+            accept_len[s] = -1;
+            n_emit[s] = 0;
+            next_tok[s] = -1;
+            pos_out[s] = pos_in[s];
+            off += (ks >= 0 ? ks : 0) + 1;
+            continue;
+        }
+        st[s] = 0;
+        int a = 0;
+        while (a < ks) {
+            int32_t x = drafts[(int64_t)s * kmax + a];
+            int32_t mapped = d2t ? d2t[x] : x;
+            if (mapped != g[off + a]) break;
+            e[a] = mapped;
+            ++a;
+        }
+        e[a] = g[off + a];
+        accept_len[s] = a;
+        n_emit[s] = a + 1;
+        next_tok[s] = g[off + a];
+        pos_out[s] = pos_in[s] + a + 1;
+        off += ks + 1;
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Gated DeltaNet verify with per-token state recording (oxinfer qwen_mtp.rs:
+ * states recorded per token during the verify forward; memra: per-column state
+ * clones). For each sequence s and head h, starting from S_0 = state[s,h]
+ * (dv x dk, row = value channel, column = key channel), for t = 1..T:
+ *   M   = I - b_t k_t k_t^T                       (dk x dk)
+ *   S_t = a_t S_{t-1} M + b_t v_t k_t^T          (matrix products, fp64)
+ *   o_t = S_t (q_scale q_t)
+ *   rec[s,t-1,h] = S_t
+ * q, k, v: bf16 [B][T][Hd][dk|dv]; a, b: fp32 [B][T][Hd]; state: fp32
+ * [B][Hd][dv][dk]; rec: fp64 [B][T][Hd][dv][dk]; o: fp64 [B][T][Hd][dv].
+ * ------------------------------------------------------------------------- */
+void oracle_delta_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* a,
+                         const float* b, double q_scale, const float* state, int32_t B, int32_t T,
+                         int32_t Hd, int32_t dk, int32_t dv, double* rec, double* o) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int s = 0; s < B; ++s) {
+        for (int h = 0; h < Hd; ++h) {
+            double* S = (double*)malloc(sizeof(double) * (size_t)dv * dk);
+            double* Sn = (double*)malloc(sizeof(double) * (size_t)dv * dk);
+            double* M = (double*)malloc(sizeof(double) * (size_t)dk * dk);
+            double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+            double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+            double* vt = (double*)malloc(sizeof(double) * (size_t)dv);
+            const float* S0 = state + ((int64_t)s * Hd + h) * dv * dk;
+            for (int64_t i = 0; i < (int64_t)dv * dk; ++i) S[i] = (double)S0[i];
+            for (int t = 0; t < T; ++t) {
+                int64_t th = ((int64_t)s * T + t) * Hd + h;
+                double at = (double)a[th], bt = (double)b[th];
+                for (int i = 0; i < dk; ++i) kt[i] = bf(k[th * dk + i]);
+                for (int i = 0; i < dk; ++i) qt[i] = q_scale * bf(q[th * dk + i]);
+                for (int i = 0; i < dv; ++i) vt[i] = bf(v[th * dv + i]);
+                for (int i = 0; i < dk; ++i)
+                    for (int jj = 0; jj < dk; ++jj)
+                        M[i * dk + jj] = (i == jj ? 1.0 : 0.0) - bt * kt[i] * kt[jj];
+                for (int i = 0; i < dv; ++i)
+                    for (int jj = 0; jj < dk; ++jj) {
+                        double acc = 0.0;
+                        for (int l = 0; l < dk; ++l) acc += S[i * dk + l] * M[l * dk + jj];
+                        Sn[i * dk + jj] = at * acc + bt * vt[i] * kt[jj];
+                    }
+                memcpy(S, Sn, sizeof(double) * (size_t)dv * dk);
+                double* ot = o + th * dv;
+                for (int i = 0; i < dv; ++i) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < dk; ++jj) acc += S[i * dk + jj] * qt[jj];
+                    ot[i] = acc;
+                }
+                memcpy(rec + th * dv * dk, S, sizeof(double) * (size_t)dv * dk);
+            }
+            free(S); free(Sn); free(M); free(kt); free(qt); free(vt);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * DeltaNet rollback (oxinfer: restore the recorded state of the last committed
+ * token; flashrt: roll the gated-delta states back). L[s] = committed tokens in
+ * 0..T: the state becomes S_L = rec[s, L-1], or stays S_0 when L = 0.
+ * rec and state are fp64 here: [B][T][Hd][dv][dk] and [B][Hd][dv][dk].
+ * ------------------------------------------------------------------------- */
+void oracle_delta_rollback(const double* rec, const int32_t* L, int32_t B, int32_t T, int32_t Hd,
+                           int32_t dk, int32_t dv, double* state) {
+    int64_t n = (int64_t)dv * dk;
+    for (int s = 0; s < B; ++s) {
+        if (L[s] <= 0) continue;
+        int t = L[s] - 1;
+        for (int h = 0; h < Hd; ++h)
+            memcpy(state + ((int64_t)s * Hd + h) * n, rec + (((int64_t)s * T + t) * Hd + h) * n,
+                   sizeof(double) * (size_t)n);
+    }
+}

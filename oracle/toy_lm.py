@@ -1,0 +1,114 @@
+"""A toy one-layer language model driven through the oracle, for the lossless invariant.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The span-02 spec.rs module doc states the invariant the whole verify step exists
+for: a token is emitted only if it equals the target's greedy token at the verify
+row before it, and rows are computed exactly as one-row decoding computes them, so
+the emitted stream equals one-row greedy decoding. The DSSD fast.py page measures
+against its one-row ``generate_ar`` stream the same way.
+
+The toy model (sizes of the tiny workload): token x at position p
+    e = E[x]                                      bf16 embedding, H = 256
+    q = bf16(Wq e), k = bf16(Wk e), v = bf16(Wv e) 4 query heads / 1 kv head, D = 64
+    k, v appended into the paged pool at p; attention over positions 0..p
+    h = bf16(e + Wo bf16(attn))
+    greedy token = argmax(Wlm h)                  vocabulary 1024
+Projections are fp64 matrix-vector products of bf16 values, one row at a time, so a
+row's arithmetic never depends on how many rows share a call.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+
+PAGE = 16
+
+
+class ToyLM:
+    def __init__(self, seed=0, V=1024, H=256, Hq=4, Hkv=1, D=64, max_len=1024):
+        rng = np.random.default_rng(seed)
+        bfr = lambda shape, std: oracle.f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+        self.V, self.H, self.Hq, self.Hkv, self.D = V, H, Hq, Hkv, D
+        self.E = bfr((V, H), 1.0)
+        self.Wq = bfr((Hq * D, H), 1 / math.sqrt(H))
+        self.Wk = bfr((Hkv * D, H), 1 / math.sqrt(H))
+        self.Wv = bfr((Hkv * D, H), 1 / math.sqrt(H))
+        self.Wo = bfr((H, Hq * D), 1 / math.sqrt(Hq * D))
+        self.Wlm = bfr((V, H), 1 / math.sqrt(H))
+        self.f = {n: oracle.bf16_bits_to_f64(getattr(self, n)) for n in ("E", "Wq", "Wk", "Wv", "Wo")}
+        self.max_pages = max_len // PAGE
+        # pages of the single sequence, scattered over a larger pool
+        self.n_pages = self.max_pages * 2
+        self.page_table = rng.permutation(self.n_pages)[: self.max_pages].astype(np.int32)[None, :]
+        self.reset()
+
+    def reset(self):
+        self.k_pool = np.zeros((self.n_pages, self.Hkv, PAGE, self.D), np.uint16)
+        self.v_pool = np.zeros((self.n_pages, self.Hkv, self.D, PAGE), np.uint16)
+
+    def _proj(self, W, x):
+        return oracle.f32_to_bf16_bits(np.array([W[i] @ x for i in range(W.shape[0])], np.float64).astype(np.float32))
+
+    def forward_rows(self, tokens, pos):
+        """Rows tokens[j] at positions pos + j (one sequence). Returns greedy tokens [T]."""
+        T = len(tokens)
+        q = np.empty((T, self.Hq, self.D), np.uint16)
+        kn = np.empty((T, self.Hkv, self.D), np.uint16)
+        vn = np.empty((T, self.Hkv, self.D), np.uint16)
+        for j, x in enumerate(tokens):
+            e = self.f["E"][x]
+            q[j] = self._proj(self.f["Wq"], e).reshape(self.Hq, self.D)
+            kn[j] = self._proj(self.f["Wk"], e).reshape(self.Hkv, self.D)
+            vn[j] = self._proj(self.f["Wv"], e).reshape(self.Hkv, self.D)
+        posa = np.array([pos], np.int32)
+        ka = np.array([T - 1], np.int32)
+        off, st = oracle.validate(self.page_table, self.max_pages, self.n_pages, posa, ka, 64, 1, T)
+        assert st[0] == 0
+        oracle.append_kv(kn, vn, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa, ka, off,
+                         st, 1, self.Hkv, self.D)
+        att = oracle.verify_attn(q, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa, ka, off,
+                                 st, 1, T, self.Hq, self.Hkv, self.D, 1 / math.sqrt(self.D))
+        att_bf = oracle.bf16_bits_to_f64(oracle.f32_to_bf16_bits(att.astype(np.float32)))
+        h = np.empty((T, self.H), np.uint16)
+        for j, x in enumerate(tokens):
+            hv = self.f["E"][x] + np.array([self.f["Wo"][i] @ att_bf[j].reshape(-1) for i in range(self.H)])
+            h[j] = oracle.f32_to_bf16_bits(hv.astype(np.float32))
+        g, _, _, _ = oracle.lm_head_argmax(h, self.Wlm, T, self.H, self.V)
+        return g
+
+    def generate_ar(self, prompt, n_new):
+        """One-row greedy decoding (DSSD fast.py generate_ar)."""
+        self.reset()
+        out = []
+        g = None
+        for i, x in enumerate(prompt):
+            g = int(self.forward_rows([x], i)[0])
+        pos = len(prompt)
+        while len(out) < n_new:
+            out.append(g)
+            g = int(self.forward_rows([g], pos)[0])
+            pos += 1
+        return out
+
+    def generate_spec(self, prompt, n_new, drafter, k):
+        """Draft -> one verify of k+1 rows -> greedy accept -> pos += a + 1."""
+        self.reset()
+        for i, x in enumerate(prompt[:-1]):
+            self.forward_rows([x], i)
+        x0, pos = prompt[-1], len(prompt) - 1
+        out, accepted_hist = [], []
+        while len(out) < n_new:
+            drafts = [int(d) for d in drafter(out, k)]
+            g = self.forward_rows([x0] + drafts, pos)
+            res = oracle.greedy_accept(g, np.array([drafts], np.int32), k, np.array([k], np.int32), None, 0,
+                                       self.V, 1, k + 1, np.array([pos], np.int32))
+            n = int(res["n_emit"][0])
+            out.extend(int(t) for t in res["emit"][0, :n])
+            accepted_hist.append(int(res["accept_len"][0]))
+            pos = int(res["pos_out"][0])
+            x0 = int(res["next_tok"][0])
+        return out[:n_new], accepted_hist
