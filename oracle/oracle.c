@@ -40,7 +40,8 @@
 /* Per-sequence status bits (same meaning as the library's documented bits). */
 #define ORC_BAD_PAGE 1  /* a page id the sequence needs is outside [0, n_pages) */
 #define ORC_BAD_POS 2   /* pos < 0, or (pos + k) / 16 >= max_pages              */
-#define ORC_BAD_ROWS 4  /* k < 0, k > kmax, or sum(k + 1) != R                   */
+#define ORC_BAD_ROWS 4  /* packing undefined (some k < 0 or sum(k + 1) != R: all  */
+                        /* sequences), or this k > kmax                          */
 #define ORC_BAD_TOKEN 8 /* draft id or d2t entry out of range                    */
 
 static double bf(uint16_t b) {
@@ -60,14 +61,19 @@ int oracle_version(void) { return 1; }
 void oracle_validate(const int32_t* page_table, int32_t max_pages, int64_t n_pages,
                      const int32_t* pos, const int32_t* k, int32_t kmax, int32_t B, int32_t R,
                      int32_t* off, int32_t* st) {
+    /* The packing r = off_s + j exists only if every k_s >= 0 and the counts add
+     * up to R; otherwise no row can be attributed and every sequence is flagged. */
     int64_t total = 0;
+    int packing_ok = 1;
     for (int s = 0; s < B; ++s) {
         off[s] = (int32_t)total;
         total += (int64_t)k[s] + 1;
+        if (k[s] < 0) packing_ok = 0;
     }
+    if (total != R) packing_ok = 0;
     for (int s = 0; s < B; ++s) {
         int bits = 0;
-        if (k[s] < 0 || (kmax >= 0 && k[s] > kmax) || total != R) bits |= ORC_BAD_ROWS;
+        if (!packing_ok || (kmax >= 0 && k[s] > kmax)) bits |= ORC_BAD_ROWS;
         if (pos[s] < 0) {
             bits |= ORC_BAD_POS;
         } else if (k[s] >= 0) {
@@ -242,12 +248,17 @@ void oracle_greedy_accept(const int32_t* g, const int32_t* drafts, int32_t kmax,
                           int32_t R, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
                           int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* st) {
     int64_t total = 0;
-    for (int s = 0; s < B; ++s) total += (int64_t)k[s] + 1;
+    int packing_ok = 1;
+    for (int s = 0; s < B; ++s) {
+        total += (int64_t)k[s] + 1;
+        if (k[s] < 0) packing_ok = 0;
+    }
+    if (total != R) packing_ok = 0;
     int64_t off = 0;
     for (int s = 0; s < B; ++s) {
         int bits = 0;
         int ks = k[s];
-        if (ks < 0 || ks > kmax || total != R) bits |= ORC_BAD_ROWS;
+        if (!packing_ok || ks > kmax) bits |= ORC_BAD_ROWS;
         if (pos_in[s] < 0) bits |= ORC_BAD_POS;
         if (!bits) {
             for (int j = 0; j < ks; ++j) {
@@ -267,7 +278,7 @@ void oracle_greedy_accept(const int32_t* g, const int32_t* drafts, int32_t kmax,
             n_emit[s] = 0;
             next_tok[s] = -1;
             pos_out[s] = pos_in[s];
-            off += (ks >= 0 ? ks : 0) + 1;
+            off += (int64_t)ks + 1;
             continue;
         }
         st[s] = 0;
@@ -346,15 +357,17 @@ void oracle_delta_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v
 /* ---------------------------------------------------------------------------
  * DeltaNet rollback (oxinfer: restore the recorded state of the last committed
  * token; flashrt: roll the gated-delta states back). L[s] = committed tokens in
- * 0..T: the state becomes S_L = rec[s, L-1], or stays S_0 when L = 0.
+ * 0..T (clamped into that range): the state becomes S_L = rec[s, L-1], or
+ * stays S_0 when L = 0.
  * rec and state are fp64 here: [B][T][Hd][dv][dk] and [B][Hd][dv][dk].
  * ------------------------------------------------------------------------- */
 void oracle_delta_rollback(const double* rec, const int32_t* L, int32_t B, int32_t T, int32_t Hd,
                            int32_t dk, int32_t dv, double* state) {
     int64_t n = (int64_t)dv * dk;
     for (int s = 0; s < B; ++s) {
-        if (L[s] <= 0) continue;
-        int t = L[s] - 1;
+        int Ls = L[s] < 0 ? 0 : (L[s] > T ? T : L[s]); /* clamped to 0..T */
+        if (Ls == 0) continue;
+        int t = Ls - 1;
         for (int h = 0; h < Hd; ++h)
             memcpy(state + ((int64_t)s * Hd + h) * n, rec + (((int64_t)s * T + t) * Hd + h) * n,
                    sizeof(double) * (size_t)n);

@@ -440,3 +440,27 @@ def test_make_drafts_corruption_always_mismatches():
     assert ((d4 >= 0) & (d4 < wl4.n_d2t)).all()
     hit = d2t[d4] == true4
     assert 0.5 < hit.mean() < 0.9
+
+
+def test_packing_errors_flag_every_sequence():
+    pt = np.zeros((3, 4), np.int32)
+    pos = np.array([1, 2, 3], np.int32)
+    _, st = oracle.validate(pt, 4, 8, pos, np.array([1, -1, 1], np.int32), 6, 3, 4)
+    assert (st & oracle.BAD_ROWS).all()
+    res = oracle.greedy_accept(np.zeros(4, np.int32), np.zeros((3, 2), np.int32), 2,
+                               np.array([1, -1, 1], np.int32), None, 0, 10, 3, 4, pos)
+    assert (res["status"] & oracle.BAD_ROWS).all() and (res["n_emit"] == 0).all()
+    # a single k beyond kmax flags that sequence only
+    res = oracle.greedy_accept(np.zeros(7, np.int32), np.zeros((3, 2), np.int32), 2,
+                               np.array([1, 3, 0], np.int32), None, 0, 10, 3, 7, pos)
+    assert list(res["status"]) == [0, oracle.BAD_ROWS, 0]
+    assert res["pos_out"][2] == 3 + 1 and res["emit"][2, 0] == 0
+
+
+def test_delta_rollback_clamps_L():
+    x = _delta(8, B=2, T=3)
+    rec, _ = _run_delta(x)
+    st = oracle.delta_rollback(rec, np.array([-2, 9], np.int32), x["S0"].astype(np.float64), 2, 3,
+                               x["Hd"], x["dk"], x["dv"])
+    np.testing.assert_array_equal(st[0], x["S0"][0].astype(np.float64))
+    np.testing.assert_array_equal(st[1], rec[1, 2])
