@@ -1,0 +1,221 @@
+/*
+ * spec_verify.h — C ABI of the greedy draft/verify step on MI355X (gfx950).
+ *
+ * One speculative cycle scores B sequences of k_s + 1 rows each against the target
+ * model: row j of sequence s feeds position pos_s + j (row 0 carries the last
+ * emitted token, rows 1..k_s the drafts). The library provides the four steps of
+ * that verify pass that dominate its cost:
+ *
+ *   spec_verify_attn           KV append in place + paged causal attention
+ *   spec_lm_head_argmax        lm_head contraction with the greedy argmax fused in
+ *   spec_greedy_accept         greedy acceptance and position rollback
+ *   spec_delta_verify_rollback Gated DeltaNet per-token state record and restore
+ *
+ * The method follows the page "span-02 engine/crates/model/src/spec.rs"
+ * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
+ * pages, KV appended in place at pos..pos+k, greedy acceptance, rollback by
+ * advancing pos only, rejected KV never attended because kv_hi = position;
+ * SpecReq: the KV slot of position p lives in page pages[p / 16]).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers are DEVICE pointers unless marked "host". The caller owns every
+ *    buffer; the library allocates nothing and keeps no state between calls.
+ *  - bf16 values travel as their raw 16-bit patterns (spec_bf16).
+ *  - Every call takes `stream` (a hipStream_t, NULL = the null stream), only
+ *    enqueues work on it and never synchronises.
+ *  - Return codes: SPEC_OK, or a negative SPEC_E* code for errors the host can see
+ *    (bad scalar, bad pointer, workspace too small, launch failure); nothing is
+ *    enqueued in that case, and spec_last_error() gives the message (thread-local).
+ *  - Conditions only the device can see (a page id out of range, a position past
+ *    the page table, row counts that do not add up, a draft id out of range) are
+ *    reported per sequence in `seq_status` [B] (written for EVERY sequence on
+ *    every call, 0 = fine, else an OR of SPEC_STATUS_* bits); such a sequence is
+ *    skipped and its outputs are as documented per call.
+ *  - Row packing: sequence s owns rows off_s .. off_s + k_s with
+ *    off_s = sum_{s' < s} (k_{s'} + 1) (the chain packing of span-02's
+ *    spec_build_verify, made ragged). The packing is defined only if every
+ *    k_s >= 0 and sum_s (k_s + 1) == R; otherwise EVERY sequence is flagged
+ *    SPEC_STATUS_BAD_ROWS.
+ *  - Row invariance: no launch parameter, tile or reduction order depends on R, B,
+ *    the k_s or on other rows, so each row's result bytes depend only on its own
+ *    inputs, its absolute position and the shape arguments. A verify row is
+ *    therefore byte-identical to a one-row decode at the same position (the
+ *    exactness rule of span-02 set_row_invariant, DSSD fast.py _layers and memra
+ *    full_attn_verify).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t spec_bf16;
+
+#define SPEC_PAGE_TOKENS 16
+
+#define SPEC_OK 0
+#define SPEC_EINVAL (-1)     /* bad scalar argument, null or misaligned pointer */
+#define SPEC_ECAPACITY (-2)  /* a host-known size exceeds a documented limit     */
+#define SPEC_EHIP (-3)       /* the HIP runtime refused a launch                 */
+#define SPEC_EWORKSPACE (-4) /* workspace pointer null or smaller than required  */
+
+#define SPEC_STATUS_BAD_PAGE 1  /* a page id the sequence needs is outside [0, n_pages)   */
+#define SPEC_STATUS_BAD_POS 2   /* pos_s < 0, or (pos_s + k_s) / 16 >= max_pages         */
+#define SPEC_STATUS_BAD_ROWS 4  /* packing undefined (see above), or k_s > kmax           */
+#define SPEC_STATUS_BAD_TOKEN 8 /* draft id outside its vocabulary, or d2t entry >= V     */
+#define SPEC_STATUS_TOO_WIDE 16 /* (Hq / Hkv) * (k_s + 1) > 128 query rows per kv head   */
+
+/* Library version (increases with any ABI or numerics change). */
+int spec_version(void);
+
+/* Message of the last error returned on the calling host thread ("" if none). */
+const char* spec_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * spec_verify_attn — KV append + paged causal verify attention (one layer).
+ *
+ * Defined by: span-02 spec.rs module doc (KV appended in place at pos..pos+k;
+ * kv_hi = position); memra-engine spec.rs full_attn_verify ("query row r attends
+ * to keys [0 .. base_len + r + 1)", scale 1/sqrt(head_dim), per-row KV append);
+ * DSSD fast.py _attention (per-row SDPA over keys [0, p+1) with grouped query
+ * heads) and _layers (index_copy_ of the rows' K/V into the cache).
+ *
+ * For every valid sequence s and row j (position p = pos[s] + j, packed row r):
+ *   1. K/V append: k_new[r, hk, :] and v_new[r, hk, :] are written to position p
+ *      of every kv head hk (page page_table[s, p / 16], in-page token p % 16).
+ *   2. Attention, for every query head h (kv head hk = h / (Hq / Hkv)):
+ *        out[r, h, :] = sum_{t <= p} softmax_t(scale * q[r,h,:] . K_t[hk,:]) V_t[hk,:]
+ *      over the sequence's positions 0..p after the append; bf16 output rounded
+ *      to nearest-even from fp32 accumulation.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q      [R][Hq][D]           bf16         k_new, v_new [R][Hkv][D] bf16
+ *   k_pool [n_pages][Hkv][16][D]  bf16: a page holds 16 tokens, token-major
+ *   v_pool [n_pages][Hkv][D][16]  bf16: a page holds 16 tokens, channel-major
+ *   page_table [B][max_pages] int32 (entries past a sequence's last page unread)
+ *   pos [B], k [B] int32         out [R][Hq][D] bf16      seq_status [B] int32
+ * Pool pages shared by two sequences, or two rows mapping to one slot, give
+ * unspecified results. Bytes of the pool other than the R x Hkv written slots
+ * are never modified.
+ *
+ * Split-KV: each sequence's positions are cut into splits of kv_split_tokens
+ * (a multiple of 64; 0 = spec_attn_split_tokens(max_pages)) at absolute
+ * positions; a row's result depends on the split size, so decode and verify
+ * calls that must agree use the same value.
+ *
+ * Limits: D in {64, 128, 256}; 1 <= Hkv <= Hq, Hq % Hkv == 0, Hq / Hkv <= 16;
+ * 1 <= B <= 4096; R >= 1; scale > 0; 16-byte aligned q, k_new, v_new, k_pool,
+ * v_pool, out, workspace. Per sequence (device): (Hq / Hkv) * (k_s + 1) <= 128.
+ * A flagged sequence writes nothing to the pool or to its out rows.
+ * workspace: at least spec_verify_attn_workspace_bytes(...) bytes; no state is
+ * carried between calls in it.
+ * ------------------------------------------------------------------------- */
+int32_t spec_attn_split_tokens(int32_t max_pages);
+size_t spec_verify_attn_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t max_pages, int32_t kv_split_tokens);
+int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
+                     spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
+                     const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                     const int32_t* k, int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                     float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
+                     size_t workspace_bytes, int32_t* seq_status, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_lm_head_argmax — lm_head contraction with the greedy argmax fused in.
+ *
+ * Defined by: span-02 spec.rs body_inner (lm_head_argmax writes the per-row
+ * token g and its maximum am_val; logits are not materialised) and
+ * greedy_logprob (the FIRST maximum wins); flashrt whole_step.py _gstep (argmax
+ * on fp32 logits, not bf16); memra-engine spec.rs decode_step_t (lm_head on the
+ * normed hidden rows).
+ *
+ *   logit[r, v] = sum_i w[v, i] * hidden[r, i]      (bf16 products, fp32 sums)
+ *   argmax[r]   = smallest v with logit[r, v] == max_v logit[r, v]
+ *   maxval[r]   = that maximum (fp32)                (maxval may be NULL)
+ *
+ * Layouts: hidden [R][H] bf16, w [V][H] bf16, argmax [R] int32, maxval [R] fp32.
+ * Limits: R >= 1, H % 256 == 0, 1 <= V < 2^31 - 1; 16-byte aligned hidden, w,
+ * workspace. NaN logits never win. workspace: at least
+ * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes.
+ * ------------------------------------------------------------------------- */
+size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V);
+int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w, int32_t R, int32_t H,
+                        int32_t V, int32_t* argmax, float* maxval, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_greedy_accept — greedy acceptance and rollback bookkeeping.
+ *
+ * Defined by: span-02 spec.rs module doc ("a token is emitted only if it equals
+ * the target's argmax at the verify row before it"; rollback = pos advances by
+ * the accepted tokens) and step_chunk (next pos = pos + a + 1, next token = last
+ * emitted); DSSD fast.py generate_spec (first miss stops; target[len(committed)]
+ * appended as correction or bonus); oxinfer qwen_mtp.rs speculative_accept
+ * (greedy case: accept iff the draft is the target argmax, else emit the
+ * argmax) and DraftHead (draft id i stands for target id d2t[i]); flashrt
+ * generate_speculative (device prefix match, pos += j + 1).
+ *
+ * With map(x) = d2t ? d2t[x] : x and g = argmax (packed rows):
+ *   a_s         = number of leading j < k_s with map(drafts[s, j]) == g[off_s + j]
+ *   emit[s, :]  = map(drafts[s, 0..a_s)) ++ [g[off_s + a_s]], then -1 up to kmax + 1
+ *   accept_len[s] = a_s, n_emit[s] = a_s + 1, next_tok[s] = g[off_s + a_s]
+ *   pos_out[s]  = pos_in[s] + a_s + 1      (pos_out may alias pos_in)
+ *
+ * Layouts: argmax [R], drafts [B][kmax] (only the first k_s of a row are read),
+ * k [B], d2t [n_draft_vocab] (NULL: drafts are target ids), pos_in, pos_out,
+ * accept_len, n_emit, next_tok, seq_status [B], emit [B][kmax + 1]; all int32.
+ * A flagged sequence gets accept_len = -1, n_emit = 0, next_tok = -1,
+ * pos_out = pos_in and an all -1 emit row. Only the d2t entries that drafts
+ * reference are checked. Limits: 1 <= B <= 8192, 0 <= kmax <= 1024, R >= 1, V >= 1.
+ * ------------------------------------------------------------------------- */
+int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kmax,
+                       const int32_t* k, const int32_t* d2t, int32_t n_draft_vocab, int32_t V,
+                       int32_t B, int32_t R, const int32_t* pos_in, int32_t* pos_out,
+                       int32_t* accept_len, int32_t* n_emit, int32_t* emit, int32_t* next_tok,
+                       int32_t* seq_status, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * spec_delta_verify_rollback — Gated DeltaNet verify with per-token state
+ * recording, and rollback to the committed prefix.
+ *
+ * Defined by: oxinfer qwen_mtp.rs module doc (the Gated DeltaNet states are
+ * recorded per token during the verify forward, so a partial acceptance
+ * restores them exactly instead of re-running the accepted tokens); memra-engine
+ * spec.rs decode_step_t_core_stream (per-column state clones) and
+ * linear_attn_verify_t (one scan over T tokens equals T chained one-token
+ * steps); flashrt whole_step.py (the gated-delta states roll back on a partial
+ * accept). The update is the gated delta rule
+ *   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t (q_scale q_t)
+ * with S [dv][dk] (row = value channel), fp32 state and arithmetic.
+ *
+ * mode 1 (RECORD):   from S_0 = state, run t = 1..T; rec[s, t-1, h] = S_t,
+ *                    o[s, t-1, h] = o_t. state is not modified.
+ * mode 2 (ROLLBACK): state[s, h] = rec[s, L[s]-1, h] when L[s] >= 1; L[s] = 0
+ *                    leaves S_0. Bit-exact copy.
+ * mode 3 (BOTH):     mode 1, then state <- S_{L[s]} in the same pass.
+ * L[s] = committed tokens in 0..T (the greedy flow commits a_s + 1); values
+ * outside 0..T are clamped.
+ *
+ * Layouts: q, k [B][T][Hd][dk] bf16; v [B][T][Hd][dv] bf16; a, b [B][T][Hd] fp32;
+ * state [B][Hd][dv][dk] fp32; rec [B][T][Hd][dv][dk] fp32; L [B] int32 (may be
+ * NULL in mode 1); o [B][T][Hd][dv] bf16 (may be NULL; unused in mode 2).
+ * Limits: dk == dv == 128, 1 <= T <= 64, B, Hd >= 1; 16-byte aligned state, rec.
+ * ------------------------------------------------------------------------- */
+#define SPEC_DELTA_RECORD 1
+#define SPEC_DELTA_ROLLBACK 2
+#define SPEC_DELTA_BOTH 3
+int spec_delta_verify_rollback(int32_t mode, const spec_bf16* q, const spec_bf16* k,
+                               const spec_bf16* v, const float* a, const float* b, float q_scale,
+                               float* state, float* rec, const int32_t* L, int32_t B, int32_t T,
+                               int32_t Hd, int32_t dk, int32_t dv, spec_bf16* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */
