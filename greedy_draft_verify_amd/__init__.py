@@ -1,0 +1,223 @@
+"""Python binding of libspecverify.so, the MI355X verify-step library.
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch
+supplies device memory (tensors are passed as raw pointers) and the stream (the
+current torch stream unless one is given). The functions keep the C names and
+argument order of ``include/spec_verify.h``; shapes are read off the tensors.
+
+The library must have been built (``python -m greedy_draft_verify_amd.build`` or
+``__graft_entry__.build()``); there is no fallback path, a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_PAGE_TOKENS = 16
+STATUS_BAD_PAGE, STATUS_BAD_POS, STATUS_BAD_ROWS, STATUS_BAD_TOKEN, STATUS_TOO_WIDE = 1, 2, 4, 8, 16
+DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH = 1, 2, 3
+
+EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
+            "spec_verify_attn_workspace_bytes", "spec_verify_attn",
+            "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_greedy_accept",
+            "spec_delta_verify_rollback"]
+
+_lib = None
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SpecError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        L.spec_version.restype = ctypes.c_int
+        L.spec_last_error.restype = ctypes.c_char_p
+        L.spec_attn_split_tokens.argtypes = [i32]
+        L.spec_attn_split_tokens.restype = i32
+        L.spec_verify_attn_workspace_bytes.argtypes = [i32] * 7
+        L.spec_verify_attn_workspace_bytes.restype = sz
+        L.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32,
+                                       i32, vp, vp, sz, vp, vp]
+        L.spec_lm_head_argmax_workspace_bytes.argtypes = [i32, i32, i32]
+        L.spec_lm_head_argmax_workspace_bytes.restype = sz
+        L.spec_lm_head_argmax.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.spec_greedy_accept.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                         vp, vp]
+        L.spec_delta_verify_rollback.argtypes = [i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
+                                                 i32, vp, vp]
+        for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
+                     "spec_delta_verify_rollback"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().spec_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        msg = lib().spec_last_error().decode(errors="replace")
+        raise SpecError(f"{name} returned {rc}: {msg}")
+
+
+def _want(t, dtype, name, ndim=None):
+    if t is None:
+        raise SpecError(f"{name} is required")
+    if t.dtype != dtype:
+        raise SpecError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise SpecError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise SpecError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise SpecError(f"{name}: {t.dim()} dims, expected {ndim}")
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise SpecError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def attn_split_tokens(max_pages: int) -> int:
+    return lib().spec_attn_split_tokens(max_pages)
+
+
+def verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens=0) -> int:
+    return lib().spec_verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens)
+
+
+def lm_head_argmax_workspace_bytes(R, H, V) -> int:
+    return lib().spec_lm_head_argmax_workspace_bytes(R, H, V)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, scale, out, seq_status,
+                     workspace_buf=None, kv_split_tokens=0, stream=None):
+    """q [R,Hq,D], k_new/v_new [R,Hkv,D], k_pool [n_pages,Hkv,16,D], v_pool [n_pages,Hkv,D,16],
+    out [R,Hq,D] (bf16); page_table [B,max_pages], pos [B], k [B], seq_status [B] (int32)."""
+    for t, n, nd in ((q, "q", 3), (k_new, "k_new", 3), (v_new, "v_new", 3), (k_pool, "k_pool", 4),
+                     (v_pool, "v_pool", 4), (out, "out", 3)):
+        _want(t, torch.bfloat16, n, nd)
+    for t, n in ((page_table, "page_table"), (pos, "pos"), (k, "k"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    R, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    _want(page_table, torch.int32, "page_table", 2)
+    B, max_pages = page_table.shape
+    n_pages = k_pool.shape[0]
+    _shape(k_new, (R, Hkv, D), "k_new")
+    _shape(v_new, (R, Hkv, D), "v_new")
+    _shape(k_pool, (n_pages, Hkv, SPEC_PAGE_TOKENS, D), "k_pool")
+    _shape(v_pool, (n_pages, Hkv, D, SPEC_PAGE_TOKENS), "v_pool")
+    _shape(out, (R, Hq, D), "out")
+    for t, n in ((pos, "pos"), (k, "k"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    if workspace_buf is None:
+        workspace_buf = workspace(verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens),
+                                  q.device)
+    rc = lib().spec_verify_attn(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), n_pages,
+                                _ptr(page_table), max_pages, _ptr(pos), _ptr(k), B, R, Hq, Hkv, D, scale,
+                                kv_split_tokens, _ptr(out), _ptr(workspace_buf), workspace_buf.numel(),
+                                _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_verify_attn")
+
+
+def spec_lm_head_argmax(hidden, w, argmax, maxval=None, workspace_buf=None, stream=None):
+    """hidden [R,H], w [V,H] (bf16) -> argmax [R] int32, maxval [R] fp32 (optional)."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w, torch.bfloat16, "w", 2)
+    _want(argmax, torch.int32, "argmax", 1)
+    if maxval is not None:
+        _want(maxval, torch.float32, "maxval", 1)
+    R, H = hidden.shape
+    V = w.shape[0]
+    _shape(w, (V, H), "w")
+    _shape(argmax, (R,), "argmax")
+    if maxval is not None:
+        _shape(maxval, (R,), "maxval")
+    if workspace_buf is None:
+        workspace_buf = workspace(lm_head_argmax_workspace_bytes(R, H, V), hidden.device)
+    rc = lib().spec_lm_head_argmax(_ptr(hidden), _ptr(w), R, H, V, _ptr(argmax), _ptr(maxval),
+                                   _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
+    _check(rc, "spec_lm_head_argmax")
+
+
+def spec_greedy_accept(argmax, drafts, k, d2t, V, pos_in, pos_out, accept_len, n_emit, emit, next_tok,
+                       seq_status, stream=None):
+    """argmax [R], drafts [B,kmax], k [B], d2t [n] or None, pos_in/pos_out/accept_len/n_emit/next_tok/
+    seq_status [B], emit [B,kmax+1] (int32)."""
+    for t, n in ((argmax, "argmax"), (drafts, "drafts"), (k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"),
+                 (accept_len, "accept_len"), (n_emit, "n_emit"), (emit, "emit"), (next_tok, "next_tok"),
+                 (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    B, kmax = drafts.shape
+    R = argmax.shape[0]
+    _shape(argmax, (R,), "argmax")
+    _shape(emit, (B, kmax + 1), "emit")
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    rc = lib().spec_greedy_accept(_ptr(argmax), _ptr(drafts), kmax, _ptr(k), _ptr(d2t),
+                                  0 if d2t is None else d2t.shape[0], V, B, R, _ptr(pos_in), _ptr(pos_out),
+                                  _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
+                                  _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_greedy_accept")
+
+
+def spec_delta_verify_rollback(mode, q, k, v, a, b, q_scale, state, rec, L, o=None, stream=None):
+    """q,k [B,T,Hd,dk], v [B,T,Hd,dv] bf16; a,b [B,T,Hd] fp32; state [B,Hd,dv,dk] fp32;
+    rec [B,T,Hd,dv,dk] fp32; L [B] int32 (None in mode 1); o [B,T,Hd,dv] bf16 or None."""
+    _want(state, torch.float32, "state", 4)
+    _want(rec, torch.float32, "rec", 5)
+    B, T, Hd, dv, dk = rec.shape
+    _shape(state, (B, Hd, dv, dk), "state")
+    if mode & DELTA_RECORD:
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _want(t, torch.bfloat16, n, 4)
+        _want(a, torch.float32, "a", 3)
+        _want(b, torch.float32, "b", 3)
+        _shape(q, (B, T, Hd, dk), "q")
+        _shape(k, (B, T, Hd, dk), "k")
+        _shape(v, (B, T, Hd, dv), "v")
+        _shape(a, (B, T, Hd), "a")
+        _shape(b, (B, T, Hd), "b")
+    if L is not None:
+        _want(L, torch.int32, "L", 1)
+        _shape(L, (B,), "L")
+    if o is not None:
+        _want(o, torch.bfloat16, "o", 4)
+        _shape(o, (B, T, Hd, dv), "o")
+    rc = lib().spec_delta_verify_rollback(mode, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), q_scale,
+                                          _ptr(state), _ptr(rec), _ptr(L), B, T, Hd, dk, dv, _ptr(o),
+                                          _stream(stream))
+    _check(rc, "spec_delta_verify_rollback")

@@ -1,0 +1,177 @@
+// spec_greedy_accept: greedy acceptance and position rollback, plus the library's
+// version and error-string entry points.
+//
+// One workgroup of 1024 threads: a block scan gives every sequence its row offset
+// (ragged packing), then each wave takes sequences in turn. Within a wave, lane j
+// compares draft j with the greedy token of row j; a ballot of the mismatches and
+// a count of trailing ones give the accepted length in one step (the device-side
+// prefix match of flashrt whole_step.py generate_speculative).
+#include "common.h"
+
+namespace sv {
+
+std::string& last_error() {
+    static thread_local std::string msg;
+    return msg;
+}
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    last_error() = buf;
+    return code;
+}
+
+constexpr int kAcceptThreads = 1024;
+constexpr int kAcceptMaxB = 8192;
+
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
+    const int32_t* __restrict__ g, const int32_t* __restrict__ drafts, int kmax,
+    const int32_t* __restrict__ k, const int32_t* __restrict__ d2t, int n_draft_vocab, int V, int B,
+    int R, const int32_t* __restrict__ pos_in, int32_t* pos_out, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ n_emit, int32_t* __restrict__ emit, int32_t* __restrict__ next_tok,
+    int32_t* __restrict__ status) {
+    __shared__ long long s_scan[kAcceptThreads];
+    __shared__ int s_off[kAcceptMaxB];
+    __shared__ int s_bad_k;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_bad_k = 0;
+    __syncthreads();
+
+    // -- row offsets: exclusive prefix sums of (k_s + 1) over a contiguous segment per thread
+    const int per = (B + kAcceptThreads - 1) / kAcceptThreads;
+    const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
+    long long local = 0;
+    for (int s = s0; s < s1; ++s) {
+        int ks = k[s];
+        if (ks < 0) s_bad_k = 1;
+        local += (long long)ks + 1;
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int d = 1; d < kAcceptThreads; d <<= 1) {
+        long long v = tid >= d ? s_scan[tid - d] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    const long long total = s_scan[kAcceptThreads - 1];
+    long long run = tid ? s_scan[tid - 1] : 0;
+    for (int s = s0; s < s1; ++s) {
+        s_off[s] = (int)run;
+        run += (long long)k[s] + 1;
+    }
+    __syncthreads();
+    const bool packing_ok = (total == (long long)R) && !s_bad_k;
+
+    // -- one wave per sequence
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int n_waves = kAcceptThreads / kWave;
+    for (int s = wave; s < B; s += n_waves) {
+        const int ks = k[s];
+        const int off = s_off[s];
+        int bits = 0;
+        if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
+        if (pos_in[s] < 0) bits |= SPEC_STATUS_BAD_POS;
+        int32_t* e = emit + (size_t)s * (kmax + 1);
+        if (bits) {
+            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
+            if (lane == 0) {
+                status[s] = bits;
+                accept_len[s] = -1;
+                n_emit[s] = 0;
+                next_tok[s] = -1;
+                pos_out[s] = pos_in[s];
+            }
+            continue;
+        }
+        // first mismatch, 64 drafts at a time; token range checks over every used draft
+        int a = ks;
+        bool bad_tok = false;
+        for (int base = 0; base < ks; base += kWave) {
+            const int j = base + lane;
+            bool miss = false;
+            if (j < ks) {
+                const int x = drafts[(size_t)s * kmax + j];
+                int mapped = x;
+                if (d2t) {
+                    if (x < 0 || x >= n_draft_vocab) {
+                        bad_tok = true;
+                    } else {
+                        mapped = d2t[x];
+                        if (mapped < 0 || mapped >= V) bad_tok = true;
+                    }
+                } else if (x < 0 || x >= V) {
+                    bad_tok = true;
+                }
+                miss = bad_tok || mapped != g[off + j];
+            }
+            const unsigned long long mm = __ballot(miss);
+            if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
+        }
+        if (__ballot(bad_tok)) {
+            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
+            if (lane == 0) {
+                status[s] = SPEC_STATUS_BAD_TOKEN;
+                accept_len[s] = -1;
+                n_emit[s] = 0;
+                next_tok[s] = -1;
+                pos_out[s] = pos_in[s];
+            }
+            continue;
+        }
+        const int bonus = g[off + a];
+        for (int j = lane; j <= kmax; j += kWave) {
+            int val = -1;
+            if (j < a) {
+                const int x = drafts[(size_t)s * kmax + j];
+                val = d2t ? d2t[x] : x;
+            } else if (j == a) {
+                val = bonus;
+            }
+            e[j] = val;
+        }
+        if (lane == 0) {
+            const int p = pos_in[s];
+            status[s] = 0;
+            accept_len[s] = a;
+            n_emit[s] = a + 1;
+            next_tok[s] = bonus;
+            pos_out[s] = p + a + 1;
+        }
+    }
+}
+
+}  // namespace sv
+
+extern "C" {
+
+int spec_version(void) { return 1; }
+
+const char* spec_last_error(void) { return sv::last_error().c_str(); }
+
+int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                       const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R,
+                       const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
+                       int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* seq_status,
+                       void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (B < 1 || B > kAcceptMaxB) return fail(SPEC_EINVAL, "spec_greedy_accept: B=%d outside 1..%d", B, kAcceptMaxB);
+    if (kmax < 0 || kmax > 1024) return fail(SPEC_EINVAL, "spec_greedy_accept: kmax=%d outside 0..1024", kmax);
+    if (R < 1) return fail(SPEC_EINVAL, "spec_greedy_accept: R=%d < 1", R);
+    if (V < 1) return fail(SPEC_EINVAL, "spec_greedy_accept: V=%d < 1", V);
+    if (d2t && n_draft_vocab < 1) return fail(SPEC_EINVAL, "spec_greedy_accept: d2t given with n_draft_vocab=%d", n_draft_vocab);
+    if (!argmax || !k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !seq_status || (kmax > 0 && !drafts))
+        return fail(SPEC_EINVAL, "spec_greedy_accept: null required pointer");
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
+                       drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
+                       n_emit, emit, next_tok, seq_status);
+    SV_LAUNCH_CHECK("spec_greedy_accept");
+    return SPEC_OK;
+}
+
+}  // extern "C"

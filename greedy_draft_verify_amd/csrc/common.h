@@ -1,0 +1,68 @@
+// Shared helpers of the verify-step HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/spec_verify.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int kWave = 64;
+constexpr int kPage = SPEC_PAGE_TOKENS;
+
+// ---- numerics -------------------------------------------------------------
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ u16 f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (u16)(u >> 16);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate (gfx950). Operand layout, lane l:
+//   A[m][k]: m = l % 16, k = 8 * (l / 16) + 0..7
+//   B[k][n]: n = l % 16, k = 8 * (l / 16) + 0..7
+//   C[m][n]: n = l % 16, m = 4 * (l / 16) + 0..3
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Packs 8 fp32 values into bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+    uint4 r;
+    r.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
+    r.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
+    r.z = (uint32_t)f2bf(x[4]) | ((uint32_t)f2bf(x[5]) << 16);
+    r.w = (uint32_t)f2bf(x[6]) | ((uint32_t)f2bf(x[7]) << 16);
+    return as_bf16x8(r);
+}
+
+// ---- host error reporting ---------------------------------------------------
+std::string& last_error();
+int fail(int code, const char* fmt, ...);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define SV_LAUNCH_CHECK(what)                                                              \
+    do {                                                                                   \
+        hipError_t e_ = hipGetLastError();                                                 \
+        if (e_ != hipSuccess) return ::sv::fail(SPEC_EHIP, "%s: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
+}  // namespace sv

@@ -141,11 +141,12 @@ class VerifyInputs:
         return 1.0 / math.sqrt(self.wl.D)
 
 
-def make_verify_inputs(name: str, seed: int = 0, device="cpu", with_lm_head: bool = True,
+def make_verify_inputs(name, seed: int = 0, device="cpu", with_lm_head: bool = True,
                        B: int | None = None, ctx: int | None = None) -> VerifyInputs:
-    """Draw one verify batch. ``B`` / ``ctx`` override the workload's batch size and
-    context (used by tests that need a smaller instance of the same shape)."""
-    wl = WORKLOADS[name]
+    """Draw one verify batch for a named workload (or a VerifyWorkload). ``B`` / ``ctx``
+    override the batch size and context (smaller instances of the same shape)."""
+    wl = WORKLOADS[name] if isinstance(name, str) else name
+    name = wl.name
     Bn = wl.B if B is None else B
     rng_pos = np_rng(seed, name, "pos")
     if ctx is not None:

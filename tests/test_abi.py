@@ -1,0 +1,91 @@
+"""The C ABI library: it loads, exports every symbol the header declares, and its
+host-side argument checks reject bad calls before anything reaches a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import greedy_draft_verify_amd as gdv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
+            "spec_delta_verify_rollback"} <= set(names)
+    lib = gdv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gdv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (spec_\w+)", out))
+    assert set(names) <= exported
+    assert set(gdv.EXPORTED) == set(names)
+
+
+def test_version_and_split_rule():
+    assert gdv.version() >= 1
+    # capacity-derived split: power of two >= 256 with <= 64 splits, capped at 2048
+    assert gdv.attn_split_tokens(32) == 256
+    assert gdv.attn_split_tokens(260) == 256
+    assert gdv.attn_split_tokens(2052) == 1024
+    assert gdv.attn_split_tokens(8196) == 2048
+
+
+def _vp(x=0x1000):
+    return ctypes.c_void_p(x)
+
+
+def test_host_argument_checks():
+    L = gdv.lib()
+    p = _vp()
+    # D outside {64,128,256}
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 100, 0.1, 0, p, p, 1 << 30, p, None)
+    assert rc == -1 and b"D=100" in L.spec_last_error()
+    # Hq % Hkv != 0
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 6, 4, 128, 0.1, 0, p, p, 1 << 30, p, None)
+    assert rc == -1
+    # split not a multiple of 64
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 100, p, p, 1 << 30, p, None)
+    assert rc == -1
+    # misaligned pointer
+    rc = L.spec_verify_attn(_vp(0x1002), p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
+    assert rc == -1 and b"aligned" in L.spec_last_error()
+    # workspace too small
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 0, p, p, 16, p, None)
+    assert rc == -4
+    need = L.spec_verify_attn_workspace_bytes(1, 4, 4, 1, 64, 4, 0)
+    assert need > 0
+    # lm_head: H not a multiple of 128, workspace
+    assert L.spec_lm_head_argmax(p, p, 4, 100, 1000, p, None, p, 1 << 30, None) == -1
+    assert L.spec_lm_head_argmax(p, p, 4, 256, 1000, p, None, p, 8, None) == -4
+    assert L.spec_lm_head_argmax_workspace_bytes(4, 256, 1000) >= 4 * 8 * 8
+    # accept: B out of range, null pointers
+    assert L.spec_greedy_accept(p, p, 3, p, None, 0, 100, 0, 4, p, p, p, p, p, p, p, None) == -1
+    assert L.spec_greedy_accept(p, None, 3, p, None, 0, 100, 1, 4, p, p, p, p, p, p, p, None) == -1
+    # delta: mode, dims, missing L
+    assert L.spec_delta_verify_rollback(4, p, p, p, p, p, 1.0, p, p, p, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(1, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 64, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(2, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_last_error() != b""
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package never imports or links the oracle."""
+    pkg = os.path.join(ROOT, "greedy_draft_verify_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|oracle\.(so|h|c)\b", src, re.M), f
+    out = subprocess.run(["ldd", gdv.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
