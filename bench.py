@@ -1,0 +1,258 @@
+"""Benchmark of one verify step on one MI355X.
+
+A step is the whole hot path over one batch: spec_verify_attn (KV append + paged
+attention, one layer) -> spec_lm_head_argmax -> spec_greedy_accept, on the
+b16k4 workload (B=16 sequences, k=4 drafts, 80 rows, context U{512..4096},
+32 q / 8 kv heads, head_dim 128, hidden 4096, vocabulary 151936). Inputs are
+seeded synthetic tensors already resident in HBM; drafts are the target's greedy
+tokens (from an untimed pass) corrupted with probability 0.3.
+
+Prints one JSON line: verify rows/s (value), emitted tokens/s, the roofline of the
+dominant kernel (lm_head, weight-stream bound at 80 rows) measured with HIP events
+on the launch stream, the attention roofline, and the CPU oracle timed on a bounded
+sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import greedy_draft_verify_amd as gdv  # noqa: E402
+from greedy_draft_verify_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+
+class VerifyStep:
+    """Device buffers and the three launches of one verify step."""
+
+    def __init__(self, x: synth.VerifyInputs, dev, stream):
+        wl = x.wl
+        self.x, self.dev, self.stream = x, dev, stream
+        self.B, self.R = len(x.pos), x.R
+        self.q, self.k_new, self.v_new = x.q, x.k_new, x.v_new
+        self.k_pool, self.v_pool = x.k_pool, x.v_pool
+        self.page_table = i32(x.page_table, dev)
+        self.pos, self.k = i32(x.pos, dev), i32(x.k, dev)
+        self.hidden, self.w = x.hidden, x.w
+        self.attn_out = torch.empty((x.R, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+        self.attn_status = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.attn_ws = gdv.workspace(gdv.verify_attn_workspace_bytes(self.B, x.R, wl.Hq, wl.Hkv, wl.D,
+                                                                     x.page_table.shape[1]), dev)
+        self.argmax = torch.empty(x.R, dtype=torch.int32, device=dev)
+        self.maxval = torch.empty(x.R, dtype=torch.float32, device=dev)
+        self.lm_ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(x.R, wl.H, wl.V), dev)
+        self.d2t = None if x.d2t is None else i32(x.d2t, dev)
+        e = lambda: torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.pos_out, self.acc_len, self.n_emit, self.next_tok, self.acc_status = e(), e(), e(), e(), e()
+        self.emit = torch.empty((self.B, wl.kmax + 1), dtype=torch.int32, device=dev)
+        self.drafts = None
+
+    def attn(self):
+        gdv.spec_verify_attn(self.q, self.k_new, self.v_new, self.k_pool, self.v_pool, self.page_table,
+                             self.pos, self.k, self.x.scale, self.attn_out, self.attn_status,
+                             workspace_buf=self.attn_ws, stream=self.stream)
+
+    def lm_head(self):
+        gdv.spec_lm_head_argmax(self.hidden, self.w, self.argmax, self.maxval, workspace_buf=self.lm_ws,
+                                stream=self.stream)
+
+    def accept(self):
+        gdv.spec_greedy_accept(self.argmax, self.drafts, self.k, self.d2t, self.x.wl.V, self.pos, self.pos_out,
+                               self.acc_len, self.n_emit, self.emit, self.next_tok, self.acc_status,
+                               stream=self.stream)
+
+
+def attn_bytes(x: synth.VerifyInputs) -> int:
+    """Algorithmic bytes of one spec_verify_attn: every cached K/V byte of the attended
+    positions once per (sequence, kv head), q read, output written, new K/V read and
+    written once."""
+    wl = x.wl
+    kv = int(((x.pos.astype(np.int64) + x.k + 1) * wl.Hkv * wl.D * 2 * 2).sum())
+    return kv + x.R * wl.Hq * wl.D * 2 * 2 + x.R * wl.Hkv * wl.D * 2 * 2 * 2
+
+
+def lm_head_bytes(R, H, V) -> int:
+    """W once + hidden once + (argmax, maxval) per row."""
+    return V * H * 2 + R * H * 2 + R * 8
+
+
+def cpu_baseline(x_host: synth.VerifyInputs, n_seq: int):
+    """The CPU oracle on the first n_seq sequences of the workload (same inputs)."""
+    import oracle
+    wl = x_host.wl
+    bits = synth.bf16_bits
+    seqs = list(range(n_seq))
+    off_all = np.concatenate([[0], np.cumsum(x_host.k + 1)]).astype(np.int64)
+    rows = np.concatenate([np.arange(off_all[s], off_all[s + 1]) for s in seqs])
+    R = len(rows)
+    pos, k, pt = x_host.pos[seqs], x_host.k[seqs], x_host.page_table[seqs]
+    kp, vp = bits(x_host.k_pool).copy(), bits(x_host.v_pool).copy()
+    qb, knb, vnb = bits(x_host.q)[rows], bits(x_host.k_new)[rows], bits(x_host.v_new)[rows]
+    hb, wb = bits(x_host.hidden)[rows], bits(x_host.w)
+    oracle.lib()
+    t0 = time.perf_counter()
+    off, st = oracle.validate(pt, pt.shape[1], x_host.n_pages, pos, k, wl.kmax, n_seq, R)
+    oracle.append_kv(knb, vnb, kp, vp, pt, pt.shape[1], pos, k, off, st, n_seq, wl.Hkv, wl.D)
+    oracle.verify_attn(qb, kp, vp, pt, pt.shape[1], pos, k, off, st, n_seq, R, wl.Hq, wl.Hkv, wl.D, x_host.scale)
+    t1 = time.perf_counter()
+    g, _, _, _ = oracle.lm_head_argmax(hb, wb, R, wl.H, wl.V)
+    t2 = time.perf_counter()
+    true_next = [g[off[s]:off[s] + k[s]] for s in range(n_seq)]
+    drafts = synth.make_drafts(wl, k, true_next, seed=0, d2t=x_host.d2t)
+    t3 = time.perf_counter()
+    oracle.greedy_accept(g, drafts, wl.kmax, k, x_host.d2t, 0 if x_host.d2t is None else len(x_host.d2t), wl.V,
+                         n_seq, R, pos)
+    t4 = time.perf_counter()
+    secs = (t1 - t0) + (t2 - t1) + (t4 - t3)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=R / secs, unit="rows/s", cores=cores, kind="oracle",
+                sample=f"first {n_seq} of {len(x_host.pos)} sequences ({R} rows): fp64 attention+append "
+                       f"{t1 - t0:.2f}s, lm_head+argmax {t2 - t1:.2f}s, accept {t4 - t3:.4f}s",
+                seconds=secs)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b16k4", choices=["b16k4", "ragged", "long", "tiny"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verify step runs on a single MI355X here "
+              "(sharding is described in the design notes, not run)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    t_gen = time.perf_counter()
+    x = synth.make_verify_inputs(args.workload, seed=args.seed, device=dev)
+    wl = x.wl
+    log(f"[bench] {wl.name}: B={len(x.pos)} R={x.R} pos {x.pos.min()}..{x.pos.max()} pool {x.n_pages} pages, "
+        f"inputs drawn in {time.perf_counter() - t_gen:.1f}s")
+    # host copies for the CPU baseline (before any append touches the pool)
+    x_host = None
+    if not args.no_cpu_baseline:
+        x_host = synth.VerifyInputs(wl, x.pos, x.k, x.R, x.page_table, x.n_pages, x.q.cpu(), x.k_new.cpu(),
+                                    x.v_new.cpu(), x.k_pool.cpu(), x.v_pool.cpu(), x.hidden.cpu(), x.w.cpu(), x.d2t)
+
+    step = VerifyStep(x, dev, stream)
+    # drafts: greedy tokens of an untimed lm_head pass, corrupted per position
+    step.lm_head()
+    torch.cuda.synchronize()
+    g0 = step.argmax.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    true_next = [g0[off[s]:off[s] + x.k[s]] for s in range(len(x.pos))]
+    step.drafts = i32(synth.make_drafts(wl, x.k, true_next, seed=args.seed, d2t=x.d2t), dev)
+
+    def run_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        step.attn()
+        if ev:
+            ev[1].record(stream)
+        step.lm_head()
+        if ev:
+            ev[2].record(stream)
+        step.accept()
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    assert (step.attn_status.cpu() == 0).all() and (step.acc_status.cpu() == 0).all()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        run_step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    lm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    acc_len = step.acc_len.cpu().numpy()
+    emitted = int((acc_len + 1).sum())
+    rows_per_s = x.R / (ms_step / 1e3)
+    lm_b = lm_head_bytes(x.R, wl.H, wl.V)
+    at_b = attn_bytes(x)
+    lm_gbs = lm_b / (lm_ms / 1e3) / 1e9
+    at_gbs = at_b / (attn_ms / 1e3) / 1e9
+    lm_tflops = 2.0 * x.R * wl.H * wl.V / (lm_ms / 1e3) / 1e12
+    hist = np.bincount(acc_len, minlength=wl.kmax + 1).tolist()
+    log(f"[bench] step {ms_step * 1e3:.1f} us: attn {attn_ms * 1e3:.1f} us ({at_gbs:.0f} GB/s), lm_head "
+        f"{lm_ms * 1e3:.1f} us ({lm_gbs:.0f} GB/s, {lm_tflops:.1f} TFLOP/s), accept {acc_ms * 1e3:.1f} us; "
+        f"accept-length histogram {hist}")
+
+    cpu = None
+    if x_host is not None:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_seqs} sequences ...")
+        cpu = cpu_baseline(x_host, args.cpu_sample_seqs)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} rows/s ({cpu['sample']})")
+        cpu.pop("seconds")
+
+    result = {
+        "metric": "verify rows/s (B=16, k=4; emitted tokens/s and roofline fractions alongside)",
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; drafts = greedy tokens corrupted with p=0.3)",
+        "config": {"workload": wl.name, "B": len(x.pos), "k": wl.kmax, "rows": x.R,
+                   "context": f"U{{{wl.ctx_lo}..{wl.ctx_hi}}}", "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "hidden": wl.H, "vocab": wl.V, "page": 16,
+                   "kv_split_tokens": gdv.attn_split_tokens(x.page_table.shape[1])},
+        "emitted_tokens_per_s": emitted / (ms_step / 1e3),
+        "emitted_per_step": emitted,
+        "accept_len_hist": hist,
+        "kernel_us": {"spec_verify_attn": attn_ms * 1e3, "spec_lm_head_argmax": lm_ms * 1e3,
+                      "spec_greedy_accept": acc_ms * 1e3},
+        "roofline": {"kernel": "spec_lm_head_argmax", "bound": "hbm", "achieved": lm_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "mfma_frac": lm_tflops / BF16_PEAK_TFLOPS, "algorithmic_bytes": lm_b},
+        "attn_roofline": {"kernel": "spec_verify_attn", "bound": "hbm", "achieved": at_gbs, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS, "algorithmic_bytes": at_b},
+        "cpu_baseline": cpu,
+        "context": "pages' own figure: 6.5 ms per 16-row whole-model verify, RTX 5090 with CUDA graphs "
+                   "(not comparable: whole model, other hardware)",
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
