@@ -54,7 +54,8 @@ class VerifyStep:
         self.k_pool, self.v_pool = x.k_pool, x.v_pool
         self.page_table = i32(x.page_table, dev)
         self.pos, self.k = i32(x.pos, dev), i32(x.k, dev)
-        self.hidden, self.w = x.hidden, x.w
+        self.hidden = x.hidden
+        self.w_packed = gdv.spec_lm_head_pack(x.w)   # one-time weight re-layout, outside the timed loop
         self.attn_out = torch.empty((x.R, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
         self.attn_status = torch.empty(self.B, dtype=torch.int32, device=dev)
         self.attn_ws = gdv.workspace(gdv.verify_attn_workspace_bytes(self.B, x.R, wl.Hq, wl.Hkv, wl.D,
@@ -74,8 +75,8 @@ class VerifyStep:
                              workspace_buf=self.attn_ws, stream=self.stream)
 
     def lm_head(self):
-        gdv.spec_lm_head_argmax(self.hidden, self.w, self.argmax, self.maxval, workspace_buf=self.lm_ws,
-                                stream=self.stream)
+        gdv.spec_lm_head_argmax(self.hidden, self.w_packed, self.x.wl.V, self.argmax, self.maxval,
+                                workspace_buf=self.lm_ws, stream=self.stream)
 
     def accept(self):
         gdv.spec_greedy_accept(self.argmax, self.drafts, self.k, self.d2t, self.x.wl.V, self.pos, self.pos_out,
@@ -161,6 +162,8 @@ def main():
                                     x.v_new.cpu(), x.k_pool.cpu(), x.v_pool.cpu(), x.hidden.cpu(), x.w.cpu(), x.d2t)
 
     step = VerifyStep(x, dev, stream)
+    x.w = None                      # the packed copy is the one the step reads
+    torch.cuda.empty_cache()
     # drafts: greedy tokens of an untimed lm_head pass, corrupted per position
     step.lm_head()
     torch.cuda.synchronize()

@@ -24,8 +24,8 @@ DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH = 1, 2, 3
 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_verify_attn_workspace_bytes", "spec_verify_attn",
-            "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_greedy_accept",
-            "spec_delta_verify_rollback"]
+            "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_packed_bytes",
+            "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback"]
 
 _lib = None
 
@@ -53,11 +53,14 @@ def lib() -> ctypes.CDLL:
         L.spec_lm_head_argmax_workspace_bytes.argtypes = [i32, i32, i32]
         L.spec_lm_head_argmax_workspace_bytes.restype = sz
         L.spec_lm_head_argmax.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.spec_lm_head_packed_bytes.argtypes = [i32, i32]
+        L.spec_lm_head_packed_bytes.restype = sz
+        L.spec_lm_head_pack.argtypes = [vp, i32, i32, vp, vp]
         L.spec_greedy_accept.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                          vp, vp]
         L.spec_delta_verify_rollback.argtypes = [i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
                                                  i32, vp, vp]
-        for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
+        for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack", "spec_greedy_accept",
                      "spec_delta_verify_rollback"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -149,22 +152,43 @@ def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, scale,
     _check(rc, "spec_verify_attn")
 
 
-def spec_lm_head_argmax(hidden, w, argmax, maxval=None, workspace_buf=None, stream=None):
-    """hidden [R,H], w [V,H] (bf16) -> argmax [R] int32, maxval [R] fp32 (optional)."""
-    _want(hidden, torch.bfloat16, "hidden", 2)
+def lm_head_packed_bytes(V, H) -> int:
+    return lib().spec_lm_head_packed_bytes(V, H)
+
+
+def spec_lm_head_pack(w, w_packed=None, stream=None):
+    """w [V,H] bf16 (row-major) -> packed weight (a flat bf16 tensor) for spec_lm_head_argmax."""
     _want(w, torch.bfloat16, "w", 2)
+    V, H = w.shape
+    nbytes = lm_head_packed_bytes(V, H)
+    if w_packed is None:
+        w_packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
+    if w_packed.numel() * 2 != nbytes:
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {nbytes}")
+    rc = lib().spec_lm_head_pack(_ptr(w), V, H, _ptr(w_packed), _stream(stream))
+    _check(rc, "spec_lm_head_pack")
+    return w_packed
+
+
+def spec_lm_head_argmax(hidden, w_packed, V, argmax, maxval=None, workspace_buf=None, stream=None):
+    """hidden [R,H] bf16, w_packed from spec_lm_head_pack (vocabulary V) -> argmax [R] int32,
+    maxval [R] fp32 (optional)."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
     _want(argmax, torch.int32, "argmax", 1)
     if maxval is not None:
         _want(maxval, torch.float32, "maxval", 1)
     R, H = hidden.shape
-    V = w.shape[0]
-    _shape(w, (V, H), "w")
+    if w_packed.numel() * 2 != lm_head_packed_bytes(V, H):
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {lm_head_packed_bytes(V, H)} "
+                        f"for V={V} H={H}")
     _shape(argmax, (R,), "argmax")
     if maxval is not None:
         _shape(maxval, (R,), "maxval")
     if workspace_buf is None:
         workspace_buf = workspace(lm_head_argmax_workspace_bytes(R, H, V), hidden.device)
-    rc = lib().spec_lm_head_argmax(_ptr(hidden), _ptr(w), R, H, V, _ptr(argmax), _ptr(maxval),
+    rc = lib().spec_lm_head_argmax(_ptr(hidden), _ptr(w_packed), R, H, V, _ptr(argmax), _ptr(maxval),
                                    _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
     _check(rc, "spec_lm_head_argmax")
 

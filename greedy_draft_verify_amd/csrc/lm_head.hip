@@ -1,18 +1,27 @@
 // spec_lm_head_argmax: bf16 MFMA lm_head with the greedy argmax fused into the
 // epilogue; the logits never leave registers.
 //
+// W is consumed in a packed form made once by spec_lm_head_pack: tiles of 16
+// vocabulary rows x 32 channels, each stored as the 64 lanes' MFMA B fragments in
+// lane order (1 KB), the K steps of a 16-row tile back to back. A row-major [V][H]
+// matrix read as MFMA fragments touches 16 rows x 64 bytes per wave instruction,
+// which caps the stream far below HBM peak; the packed form makes every wave
+// instruction one contiguous 1 KB read, and a 16-row tile a contiguous H*32-byte
+// stream. The packing is a byte permutation, so results are identical.
+//
 // lm_head_tile_kernel: one workgroup per (vocabulary tile of 128 entries, group of
-// up to 128 rows). Each wave owns 32 vocabulary rows of W and streams them straight
-// from HBM into MFMA B-operand registers (W is read exactly once per row group),
-// double-buffered one K-block (128 channels) ahead. The hidden rows are shared by
-// the four waves through LDS. After the K loop each wave reduces its logits to the
-// best (value, index) per row with the order "larger value, then smaller index"
-// (the first-maximum rule of span-02 greedy_logprob), the workgroup merges its four
-// waves, and one record per (tile, row) goes to the workspace.
+// up to 128 rows). Each wave owns two 16-row tiles of W and streams them from HBM
+// straight into MFMA B-operand registers with non-temporal loads (W is read once
+// and must not push the hidden rows out of L2), double-buffered one K-block
+// ahead. The hidden rows are shared by the four waves through LDS. After the K
+// loop each wave reduces its logits to the best (value, index) per row with the
+// order "larger value, then smaller index" (the first-maximum rule of span-02
+// greedy_logprob), the workgroup merges its four waves, and one record per
+// (tile, row) goes to the workspace.
 // lm_head_final_kernel: one workgroup per row merges the tiles' records with the
 // same order. The order is total, so the result does not depend on how the
 // reduction is grouped; each logit is one MFMA chain over K in a fixed order, so a
-// row's result does not depend on R.
+// row's result does not depend on R, the row group or the K-block size.
 #include "common.h"
 
 namespace sv {
@@ -20,9 +29,34 @@ namespace sv {
 constexpr int kLmThreads = 256;
 constexpr int kLmNT = 2;                  // 16-entry vocabulary tiles per wave
 constexpr int kLmVocabPerWg = 4 * 16 * kLmNT;
-constexpr int kLmKB = 128;                // K-block (channels) per LDS stage
-constexpr int kLmHStr = kLmKB + 8;        // LDS row stride (elements)
 constexpr int kLmMaxMT = 8;               // 16-row tiles per row group
+constexpr int kLmHAlign = 256;            // H must be a multiple of this
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load: W is touched once per call.
+__device__ __forceinline__ uint4 ld16_stream(const u16* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Packed W: fragment f = (tile * (H / 32) + kstep) * 64 + lane holds
+// W[16 * tile + lane % 16][32 * kstep + 8 * (lane / 16) .. + 8] (zero past V).
+__global__ __launch_bounds__(256) void lm_head_pack_kernel(const u16* __restrict__ w, int V, int H,
+                                                           u16* __restrict__ wp) {
+    const size_t ksteps = (size_t)(H / 32);
+    const size_t nfrag = (size_t)((V + 15) / 16) * ksteps * 64;
+    for (size_t f = (size_t)blockIdx.x * blockDim.x + threadIdx.x; f < nfrag;
+         f += (size_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(f % 64);
+        const size_t t = f / 64;
+        const int ks = (int)(t % ksteps);
+        const size_t tile = t / ksteps;
+        const size_t v = tile * 16 + lane % 16;
+        const int k = ks * 32 + (lane / 16) * 8;
+        st16(wp + f * 8, v < (size_t)V ? ld16(w + v * H + k) : make_uint4(0, 0, 0, 0));
+    }
+}
 
 struct Best {
     float v;
@@ -33,11 +67,15 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-template <int MT>
+template <int MT, int KB>
 __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
-    const u16* __restrict__ hidden, const u16* __restrict__ w, int R, int H, int V, int n_vt,
+    const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, float* __restrict__ part_v, int* __restrict__ part_i) {
-    __shared__ __attribute__((aligned(16))) u16 hs[16 * MT * kLmHStr];
+    constexpr int HSTR = KB + 8;             // LDS row stride (elements)
+    constexpr int KS = KB / 32;              // MFMA k-steps per K-block
+    constexpr int HCH = 16 * MT * KB / 8 / kLmThreads;  // hidden chunks per thread per K-block
+    static_assert(HCH * kLmThreads * 8 == 16 * MT * KB, "hidden staging must tile evenly");
+    __shared__ __attribute__((aligned(16))) u16 hs[16 * MT * HSTR];
     __shared__ Best wbest[4][16 * MT];
 
     // Logical tile: with several row groups, hardware workgroup i runs on XCD i % 8;
@@ -53,33 +91,30 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
     const int r0 = rg * 16 * MT;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
-    const int vbase = vt * kLmVocabPerWg + wave * 16 * kLmNT;
+    const int tile0 = (vt * 4 + wave) * kLmNT;       // first 16-row W tile of this wave
+    const int n_tiles = (V + 15) / 16;
+    const int ksteps = H / 32;
 
-    // W rows of this lane (clamped in range; out-of-range entries are masked later)
-    const u16* wrow[kLmNT];
+    const u16* wt[kLmNT];
 #pragma unroll
-    for (int nt = 0; nt < kLmNT; ++nt) {
-        const int v = min(vbase + nt * 16 + l16, V - 1);
-        wrow[nt] = w + (size_t)v * H + lq * 8;
-    }
-    constexpr int KS = kLmKB / 32;  // MFMA k-steps per K-block
+    for (int nt = 0; nt < kLmNT; ++nt)
+        wt[nt] = wp + ((size_t)min(tile0 + nt, n_tiles - 1) * ksteps * 64 + lane) * 8;
     uint4 wcur[kLmNT][KS], wnext[kLmNT][KS];
-    // hidden staging: MT * 256 chunks of 16 bytes per K-block, MT per thread
-    uint4 hcur[MT], hnext[MT];
+    uint4 hcur[HCH], hnext[HCH];
     auto load_h = [&](int kb, uint4* dst) {
 #pragma unroll
-        for (int it = 0; it < MT; ++it) {
+        for (int it = 0; it < HCH; ++it) {
             const int cidx = it * kLmThreads + tid;
-            const int row = cidx / (kLmKB / 8), ch = cidx % (kLmKB / 8);
+            const int row = cidx / (KB / 8), ch = cidx % (KB / 8);
             const int r = r0 + row;
-            dst[it] = r < R ? ld16(hidden + (size_t)r * H + kb * kLmKB + ch * 8) : make_uint4(0, 0, 0, 0);
+            dst[it] = r < R ? ld16(hidden + (size_t)r * H + kb * KB + ch * 8) : make_uint4(0, 0, 0, 0);
         }
     };
     auto load_w = [&](int kb, uint4 (*dst)[KS]) {
 #pragma unroll
         for (int nt = 0; nt < kLmNT; ++nt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) dst[nt][ks] = ld16(wrow[nt] + kb * kLmKB + ks * 32);
+            for (int ks = 0; ks < KS; ++ks) dst[nt][ks] = ld16_stream(wt[nt] + (size_t)(kb * KS + ks) * 512);
     };
 
     f32x4 acc[MT][kLmNT];
@@ -88,22 +123,22 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
 #pragma unroll
         for (int nt = 0; nt < kLmNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkb = H / kLmKB;
+    const int nkb = H / KB;
     load_h(0, hnext);
     load_w(0, wnext);
     for (int kb = 0; kb < nkb; ++kb) {
 #pragma unroll
-        for (int it = 0; it < MT; ++it) hcur[it] = hnext[it];
+        for (int it = 0; it < HCH; ++it) hcur[it] = hnext[it];
 #pragma unroll
         for (int nt = 0; nt < kLmNT; ++nt)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) wcur[nt][ks] = wnext[nt][ks];
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < MT; ++it) {
+        for (int it = 0; it < HCH; ++it) {
             const int cidx = it * kLmThreads + tid;
-            const int row = cidx / (kLmKB / 8), ch = cidx % (kLmKB / 8);
-            st16(hs + row * kLmHStr + ch * 8, hcur[it]);
+            const int row = cidx / (KB / 8), ch = cidx % (KB / 8);
+            st16(hs + row * HSTR + ch * 8, hcur[it]);
         }
         __syncthreads();
         if (kb + 1 < nkb) {
@@ -114,7 +149,7 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 a = as_bf16x8(ld16(hs + (mt * 16 + l16) * kLmHStr + ks * 32 + lq * 8));
+                const bf16x8 a = as_bf16x8(ld16(hs + (mt * 16 + l16) * HSTR + ks * 32 + lq * 8));
 #pragma unroll
                 for (int nt = 0; nt < kLmNT; ++nt)
                     acc[mt][nt] = mfma16x16x32(a, as_bf16x8(wcur[nt][ks]), acc[mt][nt]);
@@ -122,7 +157,7 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
         }
     }
 
-    // epilogue: C[row = 16 mt + 4 lq + i][vocab = vbase + 16 nt + l16]
+    // epilogue: C[row = 16 mt + 4 lq + i][vocab = 16 (tile0 + nt) + l16]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -131,7 +166,7 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
             int bi = 0x7fffffff;
 #pragma unroll
             for (int nt = 0; nt < kLmNT; ++nt) {
-                const int v = vbase + nt * 16 + l16;
+                const int v = (tile0 + nt) * 16 + l16;
                 const float x = acc[mt][nt][i];
                 if (v < V && better(x, v, bv, bi)) {
                     bv = x;
@@ -206,13 +241,33 @@ static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, i
                          float* pv, int* pi, hipStream_t st) {
     int grid = n_vt * n_rg;
     if (n_rg > 1) grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL(lm_head_tile_kernel<MT>, dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R, H,
-                       V, n_vt, n_rg, pv, pi);
+    // deeper K-blocks keep more of the W stream in flight; wide row groups trade
+    // depth for the registers their hidden staging needs
+    constexpr int KB = MT <= 5 ? 256 : 128;
+    hipLaunchKernelGGL((lm_head_tile_kernel<MT, KB>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
+                       H, V, n_vt, n_rg, pv, pi);
 }
 
 }  // namespace sv
 
 extern "C" {
+
+size_t spec_lm_head_packed_bytes(int32_t V, int32_t H) {
+    if (V < 1 || H < 1) return 0;
+    return (size_t)((V + 15) / 16) * 16 * (size_t)H * sizeof(spec_bf16);
+}
+
+int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_packed, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_pack: V=%d", V);
+    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "spec_lm_head_pack: H=%d not a positive multiple of %d", H, kLmHAlign);
+    if (!w || !w_packed) return fail(SPEC_EINVAL, "spec_lm_head_pack: null pointer");
+    if (!aligned16(w) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_pack: w and w_packed must be 16-byte aligned");
+    hipLaunchKernelGGL(lm_head_pack_kernel, dim3(8192), dim3(256), 0, (hipStream_t)stream, w, V, H, w_packed);
+    SV_LAUNCH_CHECK("spec_lm_head_pack");
+    return SPEC_OK;
+}
 
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
@@ -221,16 +276,17 @@ size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     return ((n * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(int);
 }
 
-int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w, int32_t R, int32_t H, int32_t V,
+int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
                         int32_t* argmax, float* maxval, void* workspace, size_t workspace_bytes,
                         void* stream) {
     using namespace sv;
     last_error().clear();
     if (R < 1) return fail(SPEC_EINVAL, "spec_lm_head_argmax: R=%d < 1", R);
-    if (H < kLmKB || H % kLmKB) return fail(SPEC_EINVAL, "spec_lm_head_argmax: H=%d not a positive multiple of %d", H, kLmKB);
+    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "spec_lm_head_argmax: H=%d not a positive multiple of %d", H, kLmHAlign);
     if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_argmax: V=%d", V);
-    if (!hidden || !w || !argmax) return fail(SPEC_EINVAL, "spec_lm_head_argmax: null required pointer");
-    if (!aligned16(hidden) || !aligned16(w)) return fail(SPEC_EINVAL, "spec_lm_head_argmax: hidden and w must be 16-byte aligned");
+    if (!hidden || !w_packed || !argmax) return fail(SPEC_EINVAL, "spec_lm_head_argmax: null required pointer");
+    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_argmax: hidden and w_packed must be 16-byte aligned");
+    const spec_bf16* w = w_packed;
     const size_t need = spec_lm_head_argmax_workspace_bytes(R, H, V);
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(SPEC_EWORKSPACE, "spec_lm_head_argmax: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, need);

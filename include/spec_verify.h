@@ -138,15 +138,28 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
  *   argmax[r]   = smallest v with logit[r, v] == max_v logit[r, v]
  *   maxval[r]   = that maximum (fp32)                (maxval may be NULL)
  *
- * Layouts: hidden [R][H] bf16, w [V][H] bf16, argmax [R] int32, maxval [R] fp32.
- * Limits: R >= 1, H % 256 == 0, 1 <= V < 2^31 - 1; 16-byte aligned hidden, w,
- * workspace. NaN logits never win. workspace: at least
+ * The weight is passed packed (see spec_lm_head_pack), the way the pages' engines
+ * keep their weights in kernel-specific block formats; packing is a byte
+ * permutation done once per weight, so every logit is the same.
+ * Layouts: hidden [R][H] bf16, w_packed spec_lm_head_packed_bytes(V, H) bytes,
+ * argmax [R] int32, maxval [R] fp32.
+ * Limits: R >= 1, H % 256 == 0, 1 <= V < 2^31 - 1; 16-byte aligned hidden,
+ * w_packed, workspace. NaN logits never win. workspace: at least
  * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes.
  * ------------------------------------------------------------------------- */
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V);
-int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w, int32_t R, int32_t H,
+int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,
                         int32_t V, int32_t* argmax, float* maxval, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* spec_lm_head_pack — one-time re-layout of a row-major lm_head weight w [V][H]
+ * (bf16) into the packed form spec_lm_head_argmax reads: tiles of 16 vocabulary
+ * rows x 32 channels, each tile stored as 64 lanes x 8 bf16 in MFMA B-fragment
+ * order (lane l holds w[16t + l % 16][32s + 8(l / 16) .. +8]), the H/32 tiles of
+ * a 16-row group consecutive, rows past V zero. w_packed holds
+ * spec_lm_head_packed_bytes(V, H) bytes and must not overlap w. Limits as above. */
+size_t spec_lm_head_packed_bytes(int32_t V, int32_t H);
+int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_packed, void* stream);
 
 /* ---------------------------------------------------------------------------
  * spec_greedy_accept — greedy acceptance and rollback bookkeeping.

@@ -83,12 +83,16 @@ def oracle_attn(x: synth.VerifyInputs, seqs=None, k_pool_bits=None, v_pool_bits=
 # ---------------------------------------------------------------------------
 # lm_head
 # ---------------------------------------------------------------------------
-def gpu_lm_head(hidden, w, dev):
+def gpu_lm_head(hidden, w, dev, w_packed=None):
+    """Packs w (unless a packed copy is given) and runs spec_lm_head_argmax."""
     import greedy_draft_verify_amd as gdv
     R = hidden.shape[0]
+    V = w.shape[0]
+    if w_packed is None:
+        w_packed = gdv.spec_lm_head_pack(w.to(dev).contiguous())
     am = torch.full((R,), -5, dtype=torch.int32, device=dev)
     mv = torch.full((R,), float("nan"), dtype=torch.float32, device=dev)
-    gdv.spec_lm_head_argmax(hidden.to(dev).contiguous(), w.to(dev).contiguous(), am, mv)
+    gdv.spec_lm_head_argmax(hidden.to(dev).contiguous(), w_packed, V, am, mv)
     torch.cuda.synchronize()
     return am.cpu().numpy(), mv.cpu().numpy()
 

@@ -136,8 +136,8 @@ def synth_status(name):
 # ---------------------------------------------------------------------------
 # lm_head + argmax
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("R,H,V", [(1, 128, 1), (4, 256, 1024), (5, 256, 1000), (17, 384, 4097),
-                                   (80, 512, 3000), (130, 256, 777), (300, 128, 2000)])
+@pytest.mark.parametrize("R,H,V", [(1, 256, 1), (4, 256, 1024), (5, 256, 1000), (17, 768, 4097),
+                                   (80, 512, 3000), (96, 256, 129), (130, 256, 777), (300, 256, 2000)])
 def test_lm_head_shapes(dev, R, H, V):
     rng = np.random.default_rng(R * 1000 + V)
     h = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(torch.bfloat16)
@@ -146,6 +146,26 @@ def test_lm_head_shapes(dev, R, H, V):
     g_ref, t1, t2, _ = oracle.lm_head_argmax(bits(h), bits(w), R, H, V)
     n_undecided = check_argmax(g, mv, g_ref, t1, t2, f"lm_head R={R} H={H} V={V}")
     assert n_undecided <= max(2, R // 3)
+
+
+def test_lm_head_pack_is_the_documented_permutation(dev):
+    """Packed fragment (t, s, lane) holds w[16t + lane % 16][32s + 8(lane // 16) .. +8], zero past V."""
+    import greedy_draft_verify_amd as gdv
+    rng = np.random.default_rng(21)
+    V, H = 37, 512
+    w = torch.from_numpy(rng.standard_normal((V, H)).astype(np.float32)).to(torch.bfloat16)
+    wp = bits(gdv.spec_lm_head_pack(w.to(dev)))
+    torch.cuda.synchronize()
+    wb = bits(w)
+    nt, ks = (V + 15) // 16, H // 32
+    exp = np.zeros((nt, ks, 64, 8), np.uint16)
+    for t in range(nt):
+        for s in range(ks):
+            for lane in range(64):
+                v = 16 * t + lane % 16
+                if v < V:
+                    exp[t, s, lane] = wb[v, 32 * s + 8 * (lane // 16): 32 * s + 8 * (lane // 16) + 8]
+    assert np.array_equal(wp.reshape(exp.shape), exp)
 
 
 def test_lm_head_tiny_workload(dev):
@@ -160,13 +180,15 @@ def test_lm_head_rows_are_batch_invariant(dev):
     with 79 or 299 other rows (row groups of 128 included)."""
     rng = np.random.default_rng(7)
     H, V = 512, 5000
+    import greedy_draft_verify_amd as gdv
     h = torch.from_numpy(rng.standard_normal((300, H)).astype(np.float32)).to(torch.bfloat16)
     w = torch.from_numpy((rng.standard_normal((V, H)) / math.sqrt(H)).astype(np.float32)).to(torch.bfloat16)
-    g300, m300 = gpu_lm_head(h, w, dev)
-    g80, m80 = gpu_lm_head(h[:80], w, dev)
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    g300, m300 = gpu_lm_head(h, w, dev, wp)
+    g80, m80 = gpu_lm_head(h[:80], w, dev, wp)
     assert np.array_equal(g80, g300[:80]) and np.array_equal(m80.view(np.uint32), m300[:80].view(np.uint32))
     for r in (0, 5, 79, 130, 299):
-        g1, m1 = gpu_lm_head(h[r:r + 1], w, dev)
+        g1, m1 = gpu_lm_head(h[r:r + 1], w, dev, wp)
         assert g1[0] == g300[r] and m1.view(np.uint32)[0] == m300.view(np.uint32)[r], r
 
 
