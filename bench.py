@@ -71,7 +71,7 @@ class VerifyStep:
 
     def attn(self):
         gdv.spec_verify_attn(self.q, self.k_new, self.v_new, self.k_pool, self.v_pool, self.page_table,
-                             self.pos, self.k, self.x.scale, self.attn_out, self.attn_status,
+                             self.pos, self.k, self.x.wl.kmax, self.x.scale, self.attn_out, self.attn_status,
                              workspace_buf=self.attn_ws, stream=self.stream)
 
     def lm_head(self):

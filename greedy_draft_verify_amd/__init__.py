@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_PAGE_TOKENS = 16
-STATUS_BAD_PAGE, STATUS_BAD_POS, STATUS_BAD_ROWS, STATUS_BAD_TOKEN, STATUS_TOO_WIDE = 1, 2, 4, 8, 16
+STATUS_BAD_PAGE, STATUS_BAD_POS, STATUS_BAD_ROWS, STATUS_BAD_TOKEN = 1, 2, 4, 8
 DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH = 1, 2, 3
 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
@@ -48,8 +48,8 @@ def lib() -> ctypes.CDLL:
         L.spec_attn_split_tokens.restype = i32
         L.spec_verify_attn_workspace_bytes.argtypes = [i32] * 7
         L.spec_verify_attn_workspace_bytes.restype = sz
-        L.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32,
-                                       i32, vp, vp, sz, vp, vp]
+        L.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       f32, i32, vp, vp, sz, vp, vp]
         L.spec_lm_head_argmax_workspace_bytes.argtypes = [i32, i32, i32]
         L.spec_lm_head_argmax_workspace_bytes.restype = sz
         L.spec_lm_head_argmax.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
@@ -121,12 +121,13 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, scale, out, seq_status,
+def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, scale, out, seq_status,
                      workspace_buf=None, kv_split_tokens=0, stream=None):
-    """q [R,Hq,D], k_new/v_new [R,Hkv,D], k_pool [n_pages,Hkv,16,D], v_pool [n_pages,Hkv,D,16],
-    out [R,Hq,D] (bf16); page_table [B,max_pages], pos [B], k [B], seq_status [B] (int32)."""
-    for t, n, nd in ((q, "q", 3), (k_new, "k_new", 3), (v_new, "v_new", 3), (k_pool, "k_pool", 4),
-                     (v_pool, "v_pool", 4), (out, "out", 3)):
+    """q [R,Hq,D], k_new/v_new [R,Hkv,D], k_pool/v_pool [n_pages,Hkv,16*D] (pool block layout),
+    out [R,Hq,D] (bf16); page_table [B,max_pages], pos [B], k [B], seq_status [B] (int32);
+    kmax = an upper bound on k."""
+    for t, n, nd in ((q, "q", 3), (k_new, "k_new", 3), (v_new, "v_new", 3), (k_pool, "k_pool", 3),
+                     (v_pool, "v_pool", 3), (out, "out", 3)):
         _want(t, torch.bfloat16, n, nd)
     for t, n in ((page_table, "page_table"), (pos, "pos"), (k, "k"), (seq_status, "seq_status")):
         _want(t, torch.int32, n)
@@ -137,8 +138,8 @@ def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, scale,
     n_pages = k_pool.shape[0]
     _shape(k_new, (R, Hkv, D), "k_new")
     _shape(v_new, (R, Hkv, D), "v_new")
-    _shape(k_pool, (n_pages, Hkv, SPEC_PAGE_TOKENS, D), "k_pool")
-    _shape(v_pool, (n_pages, Hkv, D, SPEC_PAGE_TOKENS), "v_pool")
+    _shape(k_pool, (n_pages, Hkv, SPEC_PAGE_TOKENS * D), "k_pool")
+    _shape(v_pool, (n_pages, Hkv, SPEC_PAGE_TOKENS * D), "v_pool")
     _shape(out, (R, Hq, D), "out")
     for t, n in ((pos, "pos"), (k, "k"), (seq_status, "seq_status")):
         _shape(t, (B,), n)
@@ -146,7 +147,7 @@ def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, scale,
         workspace_buf = workspace(verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens),
                                   q.device)
     rc = lib().spec_verify_attn(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), n_pages,
-                                _ptr(page_table), max_pages, _ptr(pos), _ptr(k), B, R, Hq, Hkv, D, scale,
+                                _ptr(page_table), max_pages, _ptr(pos), _ptr(k), kmax, B, R, Hq, Hkv, D, scale,
                                 kv_split_tokens, _ptr(out), _ptr(workspace_buf), workspace_buf.numel(),
                                 _ptr(seq_status), _stream(stream))
     _check(rc, "spec_verify_attn")

@@ -1,33 +1,46 @@
 // spec_verify_attn: KV append in place + paged causal split-KV verify attention.
 //
-// Three launches on the caller's stream:
+// Pool format: one 16-token x D block per (page, kv head), stored as MFMA operand
+// fragments so that every wave instruction reads contiguous memory:
+//   K block: token t, channel d at (d/32)*512 + ((d%32)/8)*128 + t*8 + d%8, i.e. for
+//            k-step ds the 64 lanes' A fragments (lane = 16*(d%32/8) + t) are 1 KB;
+//   V block: token t, channel d at (d/16)*256 + (t/4)*64 + (d%16)*4 + t%4, i.e. for
+//            output tile dt each lane's 4 tokens of one channel are 8 contiguous bytes.
+//
+// Launches on the caller's stream:
 //   1. attn_prep_kernel  grid B: validates sequence s (row packing, positions, page
-//      ids), records its row offset in the workspace, writes the rows' K/V into
+//      ids), records its row offset in the workspace and writes the rows' K/V into
 //      their pool slots (span-02 spec.rs: KV appended in place at pos..pos+k).
-//   2. attn_split_kernel grid (2 * n_splits, Hkv, B): one workgroup per (sequence,
-//      kv head, split of kv_split_tokens positions, half of the query rows). The
-//      G*T query rows of a kv head (grouped-query heads x verify rows) share every
-//      K/V page: the workgroup streams the split's pages through LDS in tiles of
-//      64 tokens (4 pages), each wave turns one 16-row query tile into scores with
-//      bf16 MFMA (S^T = K Q^T), runs the online softmax in registers, and
-//      accumulates O^T = V^T P^T with MFMA. A key t is kept for row j only if
-//      t <= pos + j (kv_hi = position, memra full_attn_verify's per-row bound).
+//   2. attn_split_kernel: one workgroup per (sequence, kv head, split of
+//      kv_split_tokens positions, group of 64 query rows). It stages 64-token tiles
+//      (4 K blocks + 4 V blocks, each a contiguous 16*D*2-byte copy) in LDS and
+//      gives each wave a 16-row query tile; per 32-token step a wave computes
+//      S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 (the G*T query
+//      rows of a kv head are the MFMA columns, so each K/V byte read from HBM serves
+//      all of them) and runs the online softmax in registers (row max/sum across
+//      the 4 lanes holding a row). A key t is kept for row j only if t <= pos + j
+//      (kv_hi = position, memra full_attn_verify's per-row bound). The split's page
+//      ids are read once per wave and taken with readlane, so tiles never wait on a
+//      page-table load.
 //   3. attn_combine_kernel one wave per (row, q head): merges the row's splits in
 //      ascending order (log-sum-exp weights) and writes bf16.
 //
-// Row invariance: splits sit at absolute multiples of kv_split_tokens, tiles at
-// absolute multiples of 64, every reduction runs in a fixed order, and a row reads
-// only splits that contain keys <= its position. Tiles past a row's position add
-// exact zeros with rescale factor exactly 1, so a row's bytes are the same whatever
-// other rows share the launch.
+// Row invariance: splits sit at absolute multiples of kv_split_tokens and steps at
+// absolute multiples of 32; every row's operations run in the same order whichever
+// wave, row group or launch serves it; reductions run in a fixed order; a row reads
+// only splits that contain keys <= its position; steps past a row's position add
+// exact zeros with rescale factor exactly 1. So a row's bytes are the same whatever
+// other rows share the launch (kmax only sizes the grid).
 #include "common.h"
 
 namespace sv {
 
-constexpr int kKT = 64;            // keys per LDS tile (4 pages)
+constexpr int kKT = 64;            // tokens per LDS tile of attn_split_kernel (4 pages)
+constexpr int kStep = 32;          // tokens per online-softmax step (2 pages)
 constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kMaxRowsPerKvHead = 128;
-constexpr int kRowsPerGroup = 64;  // query rows one workgroup handles (4 waves x 16)
+constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup handles
+constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SeqInfo {
@@ -35,12 +48,20 @@ struct SeqInfo {
     int32_t valid;  // 1 if the sequence passed validation
 };
 
+// In-block offsets of token t, channel d (see the pool format above).
+__device__ __forceinline__ int k_off(int t, int d) {
+    return (d >> 5) * 512 + ((d & 31) >> 3) * 128 + t * 8 + (d & 7);
+}
+__device__ __forceinline__ int v_off(int t, int d) {
+    return (d >> 4) * 256 + (t >> 2) * 64 + (d & 15) * 4 + (t & 3);
+}
+
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, u16* __restrict__ k_pool,
     u16* __restrict__ v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int B, int R, int Hq, int Hkv,
-    int D, SeqInfo* __restrict__ info, int32_t* __restrict__ status) {
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int kmax, int B, int R, int Hq,
+    int Hkv, int D, SeqInfo* __restrict__ info, int32_t* __restrict__ status) {
     __shared__ long long s_before[256], s_total[256];
     __shared__ int s_flags;
     const int s = blockIdx.x, tid = threadIdx.x;
@@ -69,8 +90,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const int P = pos[s];
     if (tid == 0) {
         int bits = 0;
-        if (s_total[0] != (long long)R) bits |= SPEC_STATUS_BAD_ROWS;
-        if (ks >= 0 && (long long)(Hq / Hkv) * (ks + 1) > kMaxRowsPerKvHead) bits |= SPEC_STATUS_TOO_WIDE;
+        if (s_total[0] != (long long)R || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
         if (P < 0) {
             bits |= SPEC_STATUS_BAD_POS;
         } else if (ks >= 0 && ((long long)P + ks) / kPage >= max_pages) {
@@ -97,7 +117,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         info[s].valid = bits == 0;
     }
     if (bits) return;
-    // append: one 16-byte chunk (8 channels) per item
+    // append: 8 channels (one 16-byte chunk of the row) per item
     const int dch = D / 8;
     const int n = (ks + 1) * Hkv * dch;
     for (int i = tid; i < n; i += 256) {
@@ -109,43 +129,123 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         const int64_t page = page_table[(size_t)s * max_pages + p / kPage];
         const int t = p % kPage;
         const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
-        st16(k_pool + ((size_t)(page * Hkv + hk) * kPage + t) * D + dc * 8, ld16(k_new + src));
+        const size_t blk = (size_t)(page * Hkv + hk) * (kPage * D);
+        st16(k_pool + blk + k_off(t, dc * 8), ld16(k_new + src));   // 8 channels contiguous
         const uint4 vv = ld16(v_new + src);
-        u16* vdst = v_pool + ((size_t)(page * Hkv + hk) * D + dc * 8) * kPage + t;
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vdst[(2 * e) * kPage] = (u16)(w[e] & 0xffffu);
-            vdst[(2 * e + 1) * kPage] = (u16)(w[e] >> 16);
-        }
+        for (int e = 0; e < 8; ++e)
+            v_pool[blk + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
     }
 }
 
 // ---------------------------------------------------------------------------
+// One 32-token online-softmax step for one 16-row query tile.
+//   src.k(t, ds): K A-fragment of the step's page t (t = 0, 1), k-step ds
+//   src.v(t, dt): V fragment (4 tokens of channel 16 dt + l16) of page t
+//   lane l holds query row m = l % 16 of the tile; after the S^T MFMAs it holds
+//   the scores of tokens step0 + 16 t + 4 (l / 16) + i, i = 0..3.
 template <int D>
-struct AttnTile {
-    static constexpr int KSTR = D + 8;    // K tile row stride (elements): token-major
-    static constexpr int VSTR = kKT + 8;  // V tile row stride (elements): channel-major
-    static constexpr int K_ELEMS = kKT * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int CHUNKS = 16 * D;  // 16-byte chunks per tile (K + V, 4 pages)
-    static constexpr int PER_THREAD = CHUNKS / kAttnThreads;
-    static constexpr int LDS_BYTES = (K_ELEMS + V_ELEMS) * 2;
+struct StepMath {
+    static constexpr int NDS = D / 32;
+    static constexpr int NDT = D / 16;
+
+    template <class Src>
+    __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int step0, int p_m,
+                                               int lq, float scale_log2, float& m_run, float& l_lane,
+                                               f32x4 (&o)[NDT]) {
+        float sc[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) acc = mfma16x16x32(as_bf16x8(src.k(t, ds)), qf[ds], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i];
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int kp = step0 + 16 * (jj >> 2) + 4 * lq + (jj & 3);
+            const float x = (kp <= p_m) ? sc[jj] * scale_log2 : -INFINITY;
+            sc[jj] = x;
+            tmax = fmaxf(tmax, x);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            sc[jj] = exp2f(sc[jj] - m_use);
+            psum += sc[jj];
+        }
+        const bf16x8 pf = pack8(sc);   // k-slot 8 lq + jj <-> token 16 (jj/4) + 4 lq + jj%4
+        l_lane = l_lane * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const uint2 a = src.v(0, dt), b = src.v(1, dt);
+            o[dt] = mfma16x16x32(as_bf16x8(make_uint4(a.x, a.y, b.x, b.y)), pf, o[dt] * alpha);
+        }
+    }
 };
 
+// Fragments of a 32-token step read from the LDS tile (4 K blocks, then 4 V blocks).
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
+struct LdsStep {
+    const u16* kb;   // K block of the step's first page, offset by this lane's fragment
+    const u16* vb;   // V block of the step's first page, offset by this lane's fragment
+    __device__ __forceinline__ uint4 k(int t, int ds) const { return ld16(kb + t * (kPage * D) + ds * 512); }
+    __device__ __forceinline__ uint2 v(int t, int dt) const {
+        return *reinterpret_cast<const uint2*>(vb + t * (kPage * D) + dt * 256);
+    }
+};
+
+// Zeroes the V values of tokens past the sequence's last written position in one
+// 8-byte fragment (tokens tok0 .. tok0 + 3): a zero softmax weight must not meet
+// whatever those slots hold.
+__device__ __forceinline__ uint2 mask_v(uint2 v, int tok0, int last) {
+    if (tok0 + 3 <= last) return v;
+    uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (tok0 + e > last) w[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+    return make_uint2(w[0], w[1]);
+}
+
+// Writes one query tile's split partial (unnormalised O, running max, sum).
+template <int D>
+__device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_run, float l_lane, bool m_ok,
+                                              int p_m, int c0, size_t idx, int lq, float2* part_ml,
+                                              float* part_o) {
+    float l_tot = l_lane + __shfl_xor(l_lane, 16);
+    l_tot = l_tot + __shfl_xor(l_tot, 32);
+    if (!m_ok || p_m < c0) return;
+    if (lq == 0) part_ml[idx] = make_float2(m_run, l_tot);
+    float* po = part_o + idx * D + lq * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+}
+
+// ---------------------------------------------------------------------------
+// attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
+// 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
     float scale_log2, int split, int n_splits, float2* __restrict__ part_ml,
     float* __restrict__ part_o) {
-    using TL = AttnTile<D>;
-    constexpr int NDS = D / 32;  // QK^T k-steps
-    constexpr int NDT = D / 16;  // PV output tiles
-    __shared__ __attribute__((aligned(16))) u16 smem[TL::K_ELEMS + TL::V_ELEMS];
-    u16* Ks = smem;
-    u16* Vs = smem + TL::K_ELEMS;
+    using SM = StepMath<D>;
+    constexpr int NDS = SM::NDS, NDT = SM::NDT;
+    constexpr int BLK = kPage * D;               // elements per block
+    constexpr int BLK_CH = BLK / 8;              // 16-byte chunks per block
+    constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
+    __shared__ __attribute__((aligned(16))) u16 smem[8 * BLK];   // K0..K3, V0..V3
 
     const int c = blockIdx.x % n_splits;
     const int mgroup = blockIdx.x / n_splits;
@@ -153,173 +253,93 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(
     const int s = blockIdx.z;
     const SeqInfo si = info[s];
     if (!si.valid) return;
-    const int G = Hq / Hkv;
-    const int T = k[s] + 1;
-    const int M = G * T;
-    const int P0 = pos[s];
-    const int last = P0 + T - 1;
+    const int G = Hq / Hkv, T = k[s] + 1, M = G * T, P0 = pos[s], last = P0 + T - 1;
     const int c0 = c * split;
     if (c0 > last) return;
     if (mgroup * kRowsPerGroup >= M) return;
     const int c1 = min(c0 + split, last + 1);
 
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int l16 = lane % 16, lq = lane / 16;
+    const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
     const bool active = m_tile0 < M;
-
-    // this lane's query row (B operand column / output column)
     const int m = m_tile0 + l16;
     const bool m_ok = m < M;
     const int jrow = m_ok ? m / G : 0;
-    const int p_m = m_ok ? P0 + jrow : -1;  // kv_hi of this query row
+    const int h = hk * G + (m_ok ? m % G : 0);
+    const int p_m = m_ok ? P0 + jrow : -1;
     bf16x8 qf[NDS];
     if (active) {
-        const size_t qoff = ((size_t)(si.off + jrow) * Hq + hk * G + (m_ok ? m % G : 0)) * D;
+        const size_t qoff = ((size_t)(si.off + jrow) * Hq + h) * D;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            uint4 v = m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0);
-            qf[ds] = as_bf16x8(v);
-        }
+        for (int ds = 0; ds < NDS; ++ds)
+            qf[ds] = as_bf16x8(m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0));
     }
     f32x4 o[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_lane = 0.f;
-
-    const int32_t* pt = page_table + (size_t)s * max_pages;
     const int last_page = last / kPage;
+    // page ids of this split, lane i holding page c0/16 + i + 64 r (read once; taken
+    // with readlane per tile, so no tile waits on a page-table load)
+    const int pg0 = c0 / kPage;
+    const int n_pg = (c1 - 1) / kPage - pg0 + 1;
+    int pid[(kMaxSplit / kPage + kWave - 1) / kWave];
+#pragma unroll
+    for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
+        const int i = r * kWave + lane;
+        pid[r] = i < n_pg ? page_table[(size_t)s * max_pages + pg0 + i] : 0;
+    }
+    auto page_of = [&](int pg) -> int64_t {   // pg: absolute page index, wave-uniform
+        const int i = pg - pg0;
+        int id = 0;
+#pragma unroll
+        for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
+            if ((i >> 6) == r) id = __builtin_amdgcn_readlane(pid[r], i & 63);
+        return id;
+    };
 
-    // staging registers for the next tile
-    uint4 stage[TL::PER_THREAD];
+    uint4 stage[PER_THREAD];
     auto load_tile = [&](int t0) {
 #pragma unroll
-        for (int it = 0; it < TL::PER_THREAD; ++it) {
+        for (int it = 0; it < PER_THREAD; ++it) {
             const int cidx = it * kAttnThreads + tid;
+            const int b = cidx / BLK_CH, ch = cidx % BLK_CH;      // block 0..3 K, 4..7 V
+            const int pg = t0 / kPage + (b & 3);
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (cidx < 8 * D) {  // K chunk: page i, token row, 8-channel chunk
-                const int i = cidx / (2 * D), cc = cidx % (2 * D);
-                const int row = cc / (D / 8), dc = cc % (D / 8);
-                const int pg = t0 / kPage + i;
-                if (pg <= last_page) {
-                    const int64_t page = pt[pg];
-                    v = ld16(k_pool + ((size_t)(page * Hkv + hk) * kPage + row) * D + dc * 8);
-                }
-            } else {  // V chunk: page i, channel d, 8-token half
-                const int c2 = cidx - 8 * D;
-                const int i = c2 / (2 * D), cc = c2 % (2 * D);
-                const int d = cc / 2, half = cc % 2;
-                const int pg = t0 / kPage + i;
-                if (pg <= last_page) {
-                    const int64_t page = pt[pg];
-                    v = ld16(v_pool + ((size_t)(page * Hkv + hk) * D + d) * kPage + half * 8);
-                    // tokens past the sequence's last written position may hold anything:
-                    // zero them so that a zero softmax weight times V stays zero
-                    const int tok0 = pg * kPage + half * 8;
-                    if (tok0 + 7 > last) {
-                        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (tok0 + e > last) w[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                        v = make_uint4(w[0], w[1], w[2], w[3]);
-                    }
+            if (pg <= last_page) {
+                const u16* base = (b < 4 ? k_pool : v_pool) + (size_t)(page_of(pg) * Hkv + hk) * BLK;
+                v = ld16(base + ch * 8);
+                if (b >= 4) {
+                    // chunk = 8 consecutive V elements: tokens 4 g .. 4 g + 3 of two channels
+                    const int tok0 = pg * kPage + 4 * ((ch * 8 % 256) / 64);
+                    const uint2 lo = mask_v(make_uint2(v.x, v.y), tok0, last);
+                    const uint2 hi = mask_v(make_uint2(v.z, v.w), tok0, last);
+                    v = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
             }
             stage[it] = v;
         }
     };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int it = 0; it < TL::PER_THREAD; ++it) {
-            const int cidx = it * kAttnThreads + tid;
-            if (cidx < 8 * D) {
-                const int i = cidx / (2 * D), cc = cidx % (2 * D);
-                const int row = cc / (D / 8), dc = cc % (D / 8);
-                st16(Ks + (i * kPage + row) * TL::KSTR + dc * 8, stage[it]);
-            } else {
-                const int c2 = cidx - 8 * D;
-                const int i = c2 / (2 * D), cc = c2 % (2 * D);
-                const int d = cc / 2, half = cc % 2;
-                st16(Vs + d * TL::VSTR + i * kPage + half * 8, stage[it]);
-            }
-        }
-    };
-
     load_tile(c0);
     for (int t0 = c0; t0 < c1; t0 += kKT) {
         __syncthreads();  // previous tile's LDS reads are done
-        store_tile();
+#pragma unroll
+        for (int it = 0; it < PER_THREAD; ++it) st16(smem + (it * kAttnThreads + tid) * 8, stage[it]);
         __syncthreads();
         if (t0 + kKT < c1) load_tile(t0 + kKT);
         if (!active) continue;
-
-        // scores: lane holds, for query row m, keys t0 + 32*g2 + 8*lq + jj (jj = 0..7)
-        float sc[2][8];
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            // A-operand row l16 <-> key 8*(l16/4) + 4*sub + l16%4 of the 32-key group
-            const u16* k0 = Ks + (g2 * 32 + 8 * (l16 / 4) + (l16 % 4)) * TL::KSTR + lq * 8;
-            const u16* k1 = k0 + 4 * TL::KSTR;
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) {
-                s0 = mfma16x16x32(as_bf16x8(ld16(k0 + ds * 32)), qf[ds], s0);
-                s1 = mfma16x16x32(as_bf16x8(ld16(k1 + ds * 32)), qf[ds], s1);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[g2][i] = s0[i];
-                sc[g2][4 + i] = s1[i];
-            }
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int kp = t0 + g2 * 32 + lq * 8 + jj;
-                const float x = (kp <= p_m) ? sc[g2][jj] * scale_log2 : -INFINITY;
-                sc[g2][jj] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        float psum = 0.f;
-        bf16x8 pf[2];
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-            float pv[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                pv[jj] = exp2f(sc[g2][jj] - m_use);
-                psum += pv[jj];
-            }
-            pf[g2] = pack8(pv);
-        }
-        l_lane = l_lane * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            f32x4 acc = o[dt] * alpha;
-            const u16* vrow = Vs + (dt * 16 + l16) * TL::VSTR + lq * 8;
-            acc = mfma16x16x32(as_bf16x8(ld16(vrow)), pf[0], acc);
-            acc = mfma16x16x32(as_bf16x8(ld16(vrow + 32)), pf[1], acc);
-            o[dt] = acc;
+        for (int half = 0; half < 2; ++half) {
+            const int step0 = t0 + half * kStep;
+            if (step0 >= c1) break;
+            const LdsStep<D> src{smem + (2 * half) * BLK + lane * 8, smem + (4 + 2 * half) * BLK + lane * 4};
+            SM::run(qf, src, step0, p_m, lq, scale_log2, m_run, l_lane, o);
         }
     }
     if (!active) return;
-    float l_tot = l_lane + __shfl_xor(l_lane, 16);
-    l_tot = l_tot + __shfl_xor(l_tot, 32);
-    if (!m_ok || p_m < c0) return;
-    const size_t idx = ((size_t)(si.off + jrow) * Hq + hk * G + m % G) * n_splits + c;
-    if (lq == 0) part_ml[idx] = make_float2(m_run, l_tot);
-    float* po = part_o + idx * D + lq * 4;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+    const size_t idx = ((size_t)(si.off + jrow) * Hq + h) * n_splits + c;
+    store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -389,10 +409,12 @@ static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_
 
 template <int D>
 static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, const int32_t* pt,
-                        int max_pages, const int32_t* pos, const int32_t* k, const SeqInfo* info,
+                        int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
                         int B, int R, int Hq, int Hkv, float scale, int split, int n_splits,
                         float2* ml, float* po, u16* out, hipStream_t st) {
-    dim3 grid(2 * n_splits, Hkv, B);
+    const int rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
+    const int mgroups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
+    dim3 grid(mgroups * n_splits, Hkv, B);
     hipLaunchKernelGGL(attn_split_kernel<D>, grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
                        max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po);
     const long long items = (long long)R * Hq;
@@ -424,8 +446,8 @@ size_t spec_verify_attn_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_
 int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
                      spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
                      const int32_t* page_table, int32_t max_pages, const int32_t* pos,
-                     const int32_t* k, int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
-                     float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
+                     const int32_t* k, int32_t kmax, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
+                     int32_t D, float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
                      size_t workspace_bytes, int32_t* seq_status, void* stream) {
     using namespace sv;
     last_error().clear();
@@ -434,16 +456,20 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
     if (Hq / Hkv > 16) return fail(SPEC_EINVAL, "spec_verify_attn: Hq/Hkv=%d > 16", Hq / Hkv);
     if (B < 1 || B > 4096) return fail(SPEC_EINVAL, "spec_verify_attn: B=%d outside 1..4096", B);
     if (R < 1) return fail(SPEC_EINVAL, "spec_verify_attn: R=%d < 1", R);
+    if (kmax < 0 || (long long)(Hq / Hkv) * (kmax + 1) > kMaxRowsPerKvHead)
+        return fail(SPEC_EINVAL, "spec_verify_attn: kmax=%d (need 0 <= (Hq/Hkv)*(kmax+1) <= %d)", kmax, kMaxRowsPerKvHead);
     if (max_pages < 1 || n_pages < 1) return fail(SPEC_EINVAL, "spec_verify_attn: max_pages=%d n_pages=%lld", max_pages, (long long)n_pages);
     if (!(scale > 0.f)) return fail(SPEC_EINVAL, "spec_verify_attn: scale must be > 0");
-    if (kv_split_tokens < 0 || kv_split_tokens % kKT) return fail(SPEC_EINVAL, "spec_verify_attn: kv_split_tokens=%d not a multiple of 64", kv_split_tokens);
+    if (kv_split_tokens < 0 || kv_split_tokens % kKT || kv_split_tokens > kMaxSplit)
+        return fail(SPEC_EINVAL, "spec_verify_attn: kv_split_tokens=%d not a multiple of 64 in 0..%d", kv_split_tokens, kMaxSplit);
     if (!q || !k_new || !v_new || !k_pool || !v_pool || !page_table || !pos || !k || !out || !seq_status)
         return fail(SPEC_EINVAL, "spec_verify_attn: null required pointer");
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
         return fail(SPEC_EINVAL, "spec_verify_attn: q, k_new, v_new, k_pool, v_pool and out must be 16-byte aligned");
     const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
     const int64_t n_splits = split_count(max_pages, split);
-    if (n_splits * 2 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_verify_attn: too many splits");
+    if (n_splits * 2 > 0x7fffffffLL || (long long)B * Hkv * n_splits > 0x7fffffffLL)
+        return fail(SPEC_ECAPACITY, "spec_verify_attn: too many splits");
     const AttnWs lay = attn_ws_layout(B, R, Hq, D, n_splits);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace))
         return fail(SPEC_EWORKSPACE, "spec_verify_attn: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, lay.total);
@@ -453,12 +479,12 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
     float* po = reinterpret_cast<float*>(ws + lay.o_off);
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(attn_prep_kernel, dim3(B), dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       n_pages, page_table, max_pages, pos, k, B, R, Hq, Hkv, D, info, seq_status);
+                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, info, seq_status);
     SV_LAUNCH_CHECK("spec_verify_attn(prep)");
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
     }
     SV_LAUNCH_CHECK("spec_verify_attn");
     return SPEC_OK;

@@ -130,8 +130,8 @@ class VerifyInputs:
     q: torch.Tensor            # [R, Hq, D] bf16
     k_new: torch.Tensor        # [R, Hkv, D] bf16
     v_new: torch.Tensor        # [R, Hkv, D] bf16
-    k_pool: torch.Tensor       # [n_pages, Hkv, 16, D] bf16
-    v_pool: torch.Tensor       # [n_pages, Hkv, D, 16] bf16
+    k_pool: torch.Tensor       # [n_pages, Hkv, 16 * D] bf16 (pool block layout)
+    v_pool: torch.Tensor       # [n_pages, Hkv, 16 * D] bf16 (pool block layout)
     hidden: torch.Tensor       # [R, H] bf16
     w: torch.Tensor            # [V, H] bf16
     d2t: np.ndarray | None     # [n_d2t] int32
@@ -168,8 +168,8 @@ def make_verify_inputs(name, seed: int = 0, device="cpu", with_lm_head: bool = T
     for s in range(Bn):
         page_table[s, :need[s]] = perm[cur:cur + need[s]]
         cur += int(need[s])
-    k_pool = normal_bf16((n_pages, wl.Hkv, PAGE, wl.D), 1.0, seed, name, "k_pool", device)
-    v_pool = normal_bf16((n_pages, wl.Hkv, wl.D, PAGE), 1.0, seed, name, "v_pool", device)
+    k_pool = normal_bf16((n_pages, wl.Hkv, PAGE * wl.D), 1.0, seed, name, "k_pool", device)
+    v_pool = normal_bf16((n_pages, wl.Hkv, PAGE * wl.D), 1.0, seed, name, "v_pool", device)
     q = normal_bf16((R, wl.Hq, wl.D), 1.0, seed, name, "q", device)
     k_new = normal_bf16((R, wl.Hkv, wl.D), 1.0, seed, name, "k_new", device)
     v_new = normal_bf16((R, wl.Hkv, wl.D), 1.0, seed, name, "v_new", device)

@@ -68,7 +68,6 @@ typedef uint16_t spec_bf16;
 #define SPEC_STATUS_BAD_POS 2   /* pos_s < 0, or (pos_s + k_s) / 16 >= max_pages         */
 #define SPEC_STATUS_BAD_ROWS 4  /* packing undefined (see above), or k_s > kmax           */
 #define SPEC_STATUS_BAD_TOKEN 8 /* draft id outside its vocabulary, or d2t entry >= V     */
-#define SPEC_STATUS_TOO_WIDE 16 /* (Hq / Hkv) * (k_s + 1) > 128 query rows per kv head   */
 
 /* Library version (increases with any ABI or numerics change). */
 int spec_version(void);
@@ -93,12 +92,17 @@ const char* spec_last_error(void);
  *      over the sequence's positions 0..p after the append; bf16 output rounded
  *      to nearest-even from fp32 accumulation.
  *
- * Layouts (all row-major, contiguous):
+ * Layouts (row-major, contiguous):
  *   q      [R][Hq][D]           bf16         k_new, v_new [R][Hkv][D] bf16
- *   k_pool [n_pages][Hkv][16][D]  bf16: a page holds 16 tokens, token-major
- *   v_pool [n_pages][Hkv][D][16]  bf16: a page holds 16 tokens, channel-major
+ *   k_pool, v_pool [n_pages][Hkv][16 * D] bf16: one block of 16 tokens x D channels
+ *          per (page, kv head); inside a block, token t and channel d sit at
+ *            K: (d/32)*512 + ((d%32)/8)*128 + t*8 + d%8
+ *            V: (d/16)*256 + (t/4)*64 + (d%16)*4 + t%4
+ *          (MFMA operand-fragment order: every wave access is contiguous)
  *   page_table [B][max_pages] int32 (entries past a sequence's last page unread)
  *   pos [B], k [B] int32         out [R][Hq][D] bf16      seq_status [B] int32
+ * kmax: an upper bound on the k_s (a sequence with k_s > kmax is flagged
+ * BAD_ROWS); it sizes the launch and never changes a row's result.
  * Pool pages shared by two sequences, or two rows mapping to one slot, give
  * unspecified results. Bytes of the pool other than the R x Hkv written slots
  * are never modified.
@@ -109,8 +113,8 @@ const char* spec_last_error(void);
  * calls that must agree use the same value.
  *
  * Limits: D in {64, 128, 256}; 1 <= Hkv <= Hq, Hq % Hkv == 0, Hq / Hkv <= 16;
- * 1 <= B <= 4096; R >= 1; scale > 0; 16-byte aligned q, k_new, v_new, k_pool,
- * v_pool, out, workspace. Per sequence (device): (Hq / Hkv) * (k_s + 1) <= 128.
+ * 1 <= B <= 4096; R >= 1; scale > 0; (Hq / Hkv) * (kmax + 1) <= 128; 16-byte
+ * aligned q, k_new, v_new, k_pool, v_pool, out, workspace.
  * A flagged sequence writes nothing to the pool or to its out rows.
  * workspace: at least spec_verify_attn_workspace_bytes(...) bytes; no state is
  * carried between calls in it.
@@ -121,8 +125,8 @@ size_t spec_verify_attn_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_
 int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
                      spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
                      const int32_t* page_table, int32_t max_pages, const int32_t* pos,
-                     const int32_t* k, int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
-                     float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
+                     const int32_t* k, int32_t kmax, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
+                     int32_t D, float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
                      size_t workspace_bytes, int32_t* seq_status, void* stream);
 
 /* ---------------------------------------------------------------------------

@@ -91,14 +91,18 @@ void oracle_validate(const int32_t* page_table, int32_t max_pages, int64_t n_pag
     }
 }
 
-/* Offsets of the paged pool format: K pages are [n_pages][Hkv][16][D] (a token's
- * D values contiguous), V pages are [n_pages][Hkv][D][16] (a channel's 16 tokens
- * contiguous). */
+/* Offsets of the paged pool format. Both pools hold one 16 * D block per (page,
+ * kv head) at ((page * Hkv + hk) * 16 * D); inside a block, token t / channel d
+ * sits at
+ *   K: (d / 32) * 512 + ((d % 32) / 8) * 128 + t * 8 + d % 8
+ *   V: (d / 16) * 256 + (t / 4) * 64 + (d % 16) * 4 + t % 4
+ * (the library's documented layout; any permutation inside a block would do for
+ * the oracle, which only reads through these two functions). */
 static int64_t k_index(int64_t page, int hk, int t, int d, int Hkv, int D) {
-    return ((page * Hkv + hk) * ORC_PAGE + t) * D + d;
+    return (page * Hkv + hk) * (int64_t)(ORC_PAGE * D) + (d / 32) * 512 + ((d % 32) / 8) * 128 + t * 8 + d % 8;
 }
 static int64_t v_index(int64_t page, int hk, int t, int d, int Hkv, int D) {
-    return ((page * Hkv + hk) * (int64_t)D + d) * ORC_PAGE + t;
+    return (page * Hkv + hk) * (int64_t)(ORC_PAGE * D) + (d / 16) * 256 + (t / 4) * 64 + (d % 16) * 4 + t % 4;
 }
 
 /* ---------------------------------------------------------------------------

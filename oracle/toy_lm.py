@@ -47,8 +47,8 @@ class ToyLM:
         self.reset()
 
     def reset(self):
-        self.k_pool = np.zeros((self.n_pages, self.Hkv, PAGE, self.D), np.uint16)
-        self.v_pool = np.zeros((self.n_pages, self.Hkv, self.D, PAGE), np.uint16)
+        self.k_pool = np.zeros((self.n_pages, self.Hkv, PAGE * self.D), np.uint16)
+        self.v_pool = np.zeros((self.n_pages, self.Hkv, PAGE * self.D), np.uint16)
 
     def _proj(self, W, x):
         return oracle.f32_to_bf16_bits(np.array([W[i] @ x for i in range(W.shape[0])], np.float64).astype(np.float32))

@@ -38,7 +38,7 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
 # attention
 # ---------------------------------------------------------------------------
 def gpu_attn(x: synth.VerifyInputs, dev, kv_split_tokens=0, pos=None, k=None, page_table=None,
-             k_pool=None, v_pool=None, q=None, k_new=None, v_new=None):
+             k_pool=None, v_pool=None, q=None, k_new=None, v_new=None, kmax=None):
     """Runs spec_verify_attn; returns (out bf16 [R,Hq,D] device, k_pool, v_pool, status np)."""
     pos = x.pos if pos is None else pos
     k = x.k if k is None else k
@@ -52,8 +52,10 @@ def gpu_attn(x: synth.VerifyInputs, dev, kv_split_tokens=0, pos=None, k=None, pa
     out = torch.full((R, x.wl.Hq, x.wl.D), float("nan"), dtype=torch.bfloat16, device=dev)
     status = torch.full((len(pos),), -7, dtype=torch.int32, device=dev)
     import greedy_draft_verify_amd as gdv
+    if kmax is None:
+        kmax = max(int(np.max(k)), 0)
     gdv.spec_verify_attn(q.to(dev).contiguous(), k_new.to(dev).contiguous(), v_new.to(dev).contiguous(), kp,
-                         vp, i32(pt, dev), i32(pos, dev), i32(k, dev), x.scale, out, status,
+                         vp, i32(pt, dev), i32(pos, dev), i32(k, dev), kmax, x.scale, out, status,
                          kv_split_tokens=kv_split_tokens)
     torch.cuda.synchronize()
     return out, kp, vp, status.cpu().numpy()

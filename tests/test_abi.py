@@ -49,19 +49,22 @@ def test_host_argument_checks():
     L = gdv.lib()
     p = _vp()
     # D outside {64,128,256}
-    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 100, 0.1, 0, p, p, 1 << 30, p, None)
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 100, 0.1, 0, p, p, 1 << 30, p, None)
     assert rc == -1 and b"D=100" in L.spec_last_error()
     # Hq % Hkv != 0
-    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 6, 4, 128, 0.1, 0, p, p, 1 << 30, p, None)
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 6, 4, 128, 0.1, 0, p, p, 1 << 30, p, None)
     assert rc == -1
     # split not a multiple of 64
-    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 100, p, p, 1 << 30, p, None)
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 64, 0.1, 100, p, p, 1 << 30, p, None)
     assert rc == -1
     # misaligned pointer
-    rc = L.spec_verify_attn(_vp(0x1002), p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
+    rc = L.spec_verify_attn(_vp(0x1002), p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
     assert rc == -1 and b"aligned" in L.spec_last_error()
+    # kmax too large for the query-row limit
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 40, 1, 4, 16, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
+    assert rc == -1 and b"kmax" in L.spec_last_error()
     # workspace too small
-    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 1, 4, 4, 1, 64, 0.1, 0, p, p, 16, p, None)
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 64, 0.1, 0, p, p, 16, p, None)
     assert rc == -4
     need = L.spec_verify_attn_workspace_bytes(1, 4, 4, 1, 64, 4, 0)
     assert need > 0

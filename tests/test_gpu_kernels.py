@@ -86,6 +86,19 @@ def test_attention_rows_equal_one_row_decode(dev):
             assert torch.equal(o1[0].view(torch.int16), out[r].view(torch.int16)), f"row {r} (seq {s}, j {j})"
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_attention_kmax_does_not_change_results(dev, D):
+    """kmax only sizes the launch (one or two 64-row groups): results are byte-identical."""
+    wl = _wl(f"both{D}", 4, 0, 3, 10, 1500, 4, 1, D, 128)
+    x = synth.make_verify_inputs(wl, seed=9, with_lm_head=False)
+    small, _, _, st1 = gpu_attn(x, dev, kmax=3)       # 16 rows per kv head: one row group
+    large, _, _, st2 = gpu_attn(x, dev, kmax=31)      # 128 rows: two row groups
+    assert (st1 == 0).all() and (st2 == 0).all()
+    assert torch.equal(small.view(torch.int16), large.view(torch.int16))
+    _, ref, *_ = oracle_attn(x)
+    assert_close(small.float().cpu().numpy(), ref, "both kernels")
+
+
 def test_attention_split_sizes_agree(dev):
     wl = _wl("spl", 3, 2, 5, 1000, 2000, 8, 2, 128, 160)
     x = synth.make_verify_inputs(wl, seed=4, with_lm_head=False)
@@ -121,11 +134,23 @@ def test_attention_error_paths(dev):
     assert np.isnan(out.float().cpu().numpy()).all()
 
 
-def test_attention_too_many_rows_flagged(dev):
-    wl = _wl("wide", 2, 8, 8, 100, 200, 16, 1, 64, 32)   # G*T = 144 > 128
+def test_attention_rows_beyond_kmax(dev):
+    """kmax bounds the launch: a sequence with k_s > kmax is flagged BAD_ROWS (and untouched);
+    a kmax whose query rows exceed 128 per kv head is refused on the host."""
+    import greedy_draft_verify_amd as gdv
+    wl = _wl("wide", 3, 2, 5, 100, 200, 16, 1, 64, 32)
     x = synth.make_verify_inputs(wl, seed=6, with_lm_head=False)
-    out, _, _, st = gpu_attn(x, dev)
-    assert (st == synth_status("TOO_WIDE")).all()
+    kmax = int(x.k.max()) - 1
+    out, _, _, st = gpu_attn(x, dev, kmax=kmax)
+    over = x.k > kmax
+    assert over.any()
+    assert (st[over] == synth_status("BAD_ROWS")).all() and (st[~over] == 0).all()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    o = out.float().cpu().numpy()
+    for s in np.nonzero(over)[0]:
+        assert np.isnan(o[off[s]:off[s + 1]]).all()
+    with pytest.raises(gdv.SpecError):
+        gpu_attn(x, dev, kmax=8)      # 16 * 9 = 144 query rows > 128
 
 
 def synth_status(name):

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from greedy_draft_verify_amd import synth
+from tests import pool_layout as PL
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -139,7 +140,7 @@ def _small_inputs(seed=0, B=3, ctx=(5, 70), k=(0, 4), Hq=4, Hkv=2, D=16, extra_p
     f = lambda *shape: oracle.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
     return dict(pos=pos, k=kk, pt=pt, n_pages=n_pages, max_pages=max_pages, R=R, B=B, Hq=Hq, Hkv=Hkv,
                 D=D, q=f(R, Hq, D), k_new=f(R, Hkv, D), v_new=f(R, Hkv, D),
-                k_pool=f(n_pages, Hkv, 16, D), v_pool=f(n_pages, Hkv, D, 16))
+                k_pool=f(n_pages, Hkv, 16 * D), v_pool=f(n_pages, Hkv, 16 * D))
 
 
 def _run_attn(x, k_pool=None, v_pool=None, q=None):
@@ -158,23 +159,25 @@ def test_append_changes_exactly_the_row_slots():
     x = _small_inputs(1)
     out, kp, vp, off, st = _run_attn(x)
     assert (st == 0).all()
-    k_exp, v_exp = x["k_pool"].copy(), x["v_pool"].copy()
+    ko, vo = PL.k_offsets(x["D"]), PL.v_offsets(x["D"])
+    k_exp, v_exp = PL.unpack(x["k_pool"], ko), PL.unpack(x["v_pool"], vo)
     for s in range(x["B"]):
         for j in range(x["k"][s] + 1):
             p = x["pos"][s] + j
             page = x["pt"][s, p // 16]
             r = off[s] + j
             k_exp[page, :, p % 16, :] = x["k_new"][r]
-            v_exp[page, :, :, p % 16] = x["v_new"][r]
-    assert np.array_equal(kp, k_exp) and np.array_equal(vp, v_exp)
+            v_exp[page, :, p % 16, :] = x["v_new"][r]
+    assert np.array_equal(kp, PL.pack(k_exp, ko)) and np.array_equal(vp, PL.pack(v_exp, vo))
 
 
 def _gather(x, kp, vp, s, upto):
     """K/V of sequence s at positions 0..upto as float64 [Hkv, n, D] (independent indexing)."""
     idx = np.arange(upto + 1)
     pages = x["pt"][s, idx // 16]
-    K = oracle.bf16_bits_to_f64(kp[pages, :, idx % 16, :])          # [n, Hkv, D]
-    V = oracle.bf16_bits_to_f64(vp[pages, :, :, idx % 16])          # [n, Hkv, D]
+    Kl, Vl = PL.unpack(kp, PL.k_offsets(x["D"])), PL.unpack(vp, PL.v_offsets(x["D"]))
+    K = oracle.bf16_bits_to_f64(Kl[pages, :, idx % 16, :])          # [n, Hkv, D]
+    V = oracle.bf16_bits_to_f64(Vl[pages, :, idx % 16, :])          # [n, Hkv, D]
     return np.transpose(K, (1, 0, 2)), np.transpose(V, (1, 0, 2))
 
 
@@ -196,9 +199,9 @@ def test_attention_matches_torch_sdpa():
 def test_attention_closed_forms():
     x = _small_inputs(3, B=2, Hq=4, Hkv=1, D=16)
     # (a) every key equal -> uniform weights -> mean of V over t <= p
-    kp = x["k_pool"].copy()
-    kp[...] = x["k_pool"][0, 0, 0, :]
-    kn = np.broadcast_to(x["k_pool"][0, 0, 0, :], x["k_new"].shape).copy()
+    key = x["k_pool"][0, 0, :16]
+    kp = PL.pack(np.broadcast_to(key, x["k_pool"].shape[:2] + (16, 16)).copy(), PL.k_offsets(16))
+    kn = np.broadcast_to(key, x["k_new"].shape).copy()
     y = dict(x, k_new=kn)
     out, kp2, vp2, off, st = _run_attn(y, k_pool=kp)
     for s in range(x["B"]):
@@ -209,8 +212,7 @@ def test_attention_closed_forms():
                                        rtol=1e-12, atol=1e-12)
     # (b) every V equal to one vector c -> output c exactly (weights sum to one)
     c = oracle.f32_to_bf16_bits(np.linspace(-2, 2, 16).astype(np.float32))
-    vp = np.empty_like(x["v_pool"])
-    vp[...] = c[None, None, :, None]
+    vp = PL.pack(np.broadcast_to(c, x["v_pool"].shape[:2] + (16, 16)).copy(), PL.v_offsets(16))
     vn = np.broadcast_to(c, x["v_new"].shape).copy()
     out, *_ = _run_attn(dict(x, v_new=vn), v_pool=vp)
     np.testing.assert_allclose(out, np.broadcast_to(oracle.bf16_bits_to_f64(c), out.shape), atol=1e-12)
