@@ -102,8 +102,37 @@ def verify_attn(q, k_pool, v_pool, page_table, max_pages, pos, k, off, st, B, R,
     return out
 
 
+def lm_head_logits(hidden, w, R, H, V, chunk=16384):
+    """logit[r, v] = sum_i w[v, i] hidden[r, i] in fp64 (numpy's matmul as the contraction
+    step, one vocabulary chunk at a time; inputs widened exactly from bf16)."""
+    h = bf16_bits_to_f64(np.asarray(hidden).reshape(R, H))
+    wv = np.asarray(w).reshape(V, H)
+    out = np.empty((R, V), np.float64)
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = h @ bf16_bits_to_f64(wv[v0:v0 + chunk]).T
+    return out
+
+
+def argmax_rows(logits):
+    """First maximum, its value and the runner-up value per row (plain C scan)."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    R, V = logits.shape
+    g = np.zeros(R, np.int32)
+    t1 = np.zeros(R, np.float64)
+    t2 = np.zeros(R, np.float64)
+    lib().oracle_argmax_rows(_p(logits), ctypes.c_int32(R), ctypes.c_int32(V), _p(g), _p(t1), _p(t2))
+    return g, t1, t2
+
+
 def lm_head_argmax(hidden, w, R, H, V, want_logits=False):
     """Returns (g int32 [R], top1 f64 [R], top2 f64 [R], logits f64 [R,V] or None)."""
+    lg = lm_head_logits(hidden, w, R, H, V)
+    g, t1, t2 = argmax_rows(lg)
+    return g, t1, t2, (lg if want_logits else None)
+
+
+def lm_head_argmax_loops(hidden, w, R, H, V, want_logits=False):
+    """The same definition as plain C loops (an independent implementation, for pins)."""
     g = np.zeros(R, np.int32)
     t1 = np.zeros(R, np.float64)
     t2 = np.zeros(R, np.float64)

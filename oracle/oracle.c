@@ -235,6 +235,25 @@ void oracle_lm_head_argmax(const uint16_t* hidden, const uint16_t* w, int32_t R,
     free(hd);
 }
 
+/* First maximum and runner-up of each row of an fp64 logit matrix [R][V]
+ * (span-02 greedy_logprob: strict '>' scan from index 0, so the lowest index of
+ * the maximum wins). top2 is the largest value at any other index. */
+void oracle_argmax_rows(const double* logit, int32_t R, int32_t V, int32_t* g, double* top1,
+                        double* top2) {
+    for (int r = 0; r < R; ++r) {
+        const double* z = logit + (int64_t)r * V;
+        int best = 0;
+        for (int v = 1; v < V; ++v)
+            if (z[v] > z[best]) best = v;
+        double second = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if (v != best && z[v] > second) second = z[v];
+        g[r] = best;
+        if (top1) top1[r] = z[best];
+        if (top2) top2[r] = second;
+    }
+}
+
 /* ---------------------------------------------------------------------------
  * Greedy acceptance and rollback bookkeeping (fast.py generate_spec accept loop;
  * oxinfer MtpDecoder::step; flashrt device prefix match; span-02 step_chunk:

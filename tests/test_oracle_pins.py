@@ -278,12 +278,26 @@ def test_attention_bad_sequence_untouched():
 # ----------------------------------------------------------------------------
 # lm_head + argmax
 # ----------------------------------------------------------------------------
+def test_lm_head_two_implementations_agree():
+    """The matmul-based oracle and the plain C loops give the same logits and picks."""
+    rng = np.random.default_rng(10)
+    R, H, V = 9, 96, 40000
+    h = oracle.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    w = oracle.f32_to_bf16_bits((rng.standard_normal((V, H)) / 10).astype(np.float32))
+    g1, a1, b1, l1 = oracle.lm_head_argmax(h, w, R, H, V, want_logits=True)
+    g2, a2, b2, l2 = oracle.lm_head_argmax_loops(h, w, R, H, V, want_logits=True)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+    assert list(g1) == list(g2)
+    np.testing.assert_allclose(a1, a2, rtol=1e-12)
+    np.testing.assert_allclose(b1, b2, rtol=1e-12)
+
+
 def test_lm_head_matches_numpy():
     rng = np.random.default_rng(11)
     R, H, V = 7, 64, 333
     h = oracle.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
     w = oracle.f32_to_bf16_bits((rng.standard_normal((V, H)) / 8).astype(np.float32))
-    g, t1, t2, lg = oracle.lm_head_argmax(h, w, R, H, V, want_logits=True)
+    g, t1, t2, lg = oracle.lm_head_argmax_loops(h, w, R, H, V, want_logits=True)
     ref = oracle.bf16_bits_to_f64(h) @ oracle.bf16_bits_to_f64(w).T
     np.testing.assert_allclose(lg, ref, rtol=1e-12, atol=1e-12)
     assert list(g) == list(np.argmax(ref, axis=1))
