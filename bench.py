@@ -98,6 +98,27 @@ def lm_head_bytes(R, H, V) -> int:
     return V * H * 2 + R * H * 2 + R * 8
 
 
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of a kernel
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_b16k4_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if " = " in line:
+            a, b = line.split(" = ", 1)
+            kv[a.strip()] = b.split()[0]
+    src = os.path.join(ROOT, kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("source_sha256_16"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(x_host: synth.VerifyInputs, n_seq: int):
     """The CPU oracle on the first n_seq sequences of the workload (same inputs)."""
     import oracle
@@ -142,6 +163,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed loop, copy this many MiB 3 times (a plain copy kernel of known "
+                         "size, used to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify step runs on a single MI355X here "
@@ -216,6 +240,15 @@ def main():
         f"{lm_ms * 1e3:.1f} us ({lm_gbs:.0f} GB/s, {lm_tflops:.1f} TFLOP/s), accept {acc_ms * 1e3:.1f} us; "
         f"accept-length histogram {hist}")
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if x_host is not None:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_seqs} sequences ...")
@@ -246,10 +279,12 @@ def main():
         "kernel_us": {"spec_verify_attn": attn_ms * 1e3, "spec_lm_head_argmax": lm_ms * 1e3,
                       "spec_greedy_accept": acc_ms * 1e3},
         "roofline": {"kernel": "spec_lm_head_argmax", "bound": "hbm", "achieved": lm_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("lm_head_tile") if wl.name == "b16k4" else None,
                      "mfma_frac": lm_tflops / BF16_PEAK_TFLOPS, "algorithmic_bytes": lm_b},
         "attn_roofline": {"kernel": "spec_verify_attn", "bound": "hbm", "achieved": at_gbs, "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS, "algorithmic_bytes": at_b},
+                          "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS, "algorithmic_bytes": at_b,
+                          "traffic_split_kernel": measured_traffic("attn_split") if wl.name == "b16k4" else None},
         "cpu_baseline": cpu,
         "context": "pages' own figure: 6.5 ms per 16-row whole-model verify, RTX 5090 with CUDA graphs "
                    "(not comparable: whole model, other hardware)",
