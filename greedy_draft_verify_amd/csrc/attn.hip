@@ -36,7 +36,6 @@
 namespace sv {
 
 constexpr int kKT = 64;            // tokens per LDS tile of attn_split_kernel (4 pages)
-constexpr int kStep = 32;          // tokens per online-softmax step (2 pages)
 constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kMaxRowsPerKvHead = 128;
 constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup handles
@@ -140,67 +139,86 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// One 32-token online-softmax step for one 16-row query tile.
-//   src.k(t, ds): K A-fragment of the step's page t (t = 0, 1), k-step ds
-//   src.v(t, dt): V fragment (4 tokens of channel 16 dt + l16) of page t
+// Online softmax over one 64-token tile (4 pages) for one 16-row query tile.
+//   src.k(p, ds): K A-fragment of the tile's page p (0..3), k-step ds
+//   src.v(p, dt): V fragment (4 tokens of channel 16 dt + l16) of page p
 //   lane l holds query row m = l % 16 of the tile; after the S^T MFMAs it holds
-//   the scores of tokens step0 + 16 t + 4 (l / 16) + i, i = 0..3.
+//   the scores of tokens t0 + 16 p + 4 (l / 16) + i, i = 0..3.
+// The running maximum is raised only when a row's tile maximum exceeds it by more
+// than kRescaleLog2 (a bound on exp2 of the lag); then that row's accumulators
+// are scaled by exp2(old - new). The branch is taken by the whole wave, rows that
+// do not need it are scaled by exactly 1.0, so a row's arithmetic depends on its
+// own scores only.
+constexpr float kRescaleLog2 = 8.f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int D>
-struct StepMath {
+struct TileMath {
     static constexpr int NDS = D / 32;
     static constexpr int NDT = D / 16;
 
     template <class Src>
-    __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int step0, int p_m,
-                                               int lq, float scale_log2, float& m_run, float& l_lane,
-                                               f32x4 (&o)[NDT]) {
-        float sc[8];
+    __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int t0, int p_m,
+                                               bool full, int lq, float scale_log2, float& m_run,
+                                               float& l_lane, f32x4 (&o)[NDT]) {
+        float sc[16];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int p = 0; p < 4; ++p) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) acc = mfma16x16x32(as_bf16x8(src.k(t, ds)), qf[ds], acc);
+            for (int ds = 0; ds < NDS; ++ds) acc = mfma16x16x32(as_bf16x8(src.k(p, ds)), qf[ds], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i];
+            for (int i = 0; i < 4; ++i) sc[4 * p + i] = acc[i] * scale_log2;
         }
-        float tmax = -INFINITY;
+        if (!full) {   // some token of the tile lies past some row's position
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int kp = step0 + 16 * (jj >> 2) + 4 * lq + (jj & 3);
-            const float x = (kp <= p_m) ? sc[jj] * scale_log2 : -INFINITY;
-            sc[jj] = x;
-            tmax = fmaxf(tmax, x);
+            for (int jj = 0; jj < 16; ++jj) {
+                const int kp = t0 + 16 * (jj >> 2) + 4 * lq + (jj & 3);
+                if (kp > p_m) sc[jj] = -INFINITY;
+            }
         }
+        float tmax = sc[0];
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) tmax = fmaxf(tmax, sc[jj]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const bool raise = tmax > m_run + kRescaleLog2;       // also true on a row's first tile
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? tmax : m_run;
+            const float alpha = raise ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new)) : 1.f;
+            l_lane *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[dt] = o[dt] * alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            sc[jj] = exp2f(sc[jj] - m_use);
+        for (int jj = 0; jj < 16; ++jj) {
+            sc[jj] = fast_exp2(sc[jj] - m_use);
             psum += sc[jj];
         }
-        const bf16x8 pf = pack8(sc);   // k-slot 8 lq + jj <-> token 16 (jj/4) + 4 lq + jj%4
-        l_lane = l_lane * alpha + psum;
-        m_run = m_new;
+        l_lane += psum;
+        // 32-token halves h: k-slot 8 lq + jj <-> token 32 h + 16 (jj/4) + 4 lq + jj%4
+        const bf16x8 pf0 = pack8(sc), pf1 = pack8(sc + 8);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const uint2 a = src.v(0, dt), b = src.v(1, dt);
-            o[dt] = mfma16x16x32(as_bf16x8(make_uint4(a.x, a.y, b.x, b.y)), pf, o[dt] * alpha);
+            const uint2 a0 = src.v(0, dt), b0 = src.v(1, dt), a1 = src.v(2, dt), b1 = src.v(3, dt);
+            f32x4 acc = mfma16x16x32(as_bf16x8(make_uint4(a0.x, a0.y, b0.x, b0.y)), pf0, o[dt]);
+            o[dt] = mfma16x16x32(as_bf16x8(make_uint4(a1.x, a1.y, b1.x, b1.y)), pf1, acc);
         }
     }
 };
 
-// Fragments of a 32-token step read from the LDS tile (4 K blocks, then 4 V blocks).
+// Fragments of a 64-token tile read from LDS (4 K blocks, then 4 V blocks).
 template <int D>
-struct LdsStep {
-    const u16* kb;   // K block of the step's first page, offset by this lane's fragment
-    const u16* vb;   // V block of the step's first page, offset by this lane's fragment
-    __device__ __forceinline__ uint4 k(int t, int ds) const { return ld16(kb + t * (kPage * D) + ds * 512); }
-    __device__ __forceinline__ uint2 v(int t, int dt) const {
-        return *reinterpret_cast<const uint2*>(vb + t * (kPage * D) + dt * 256);
+struct LdsTile {
+    const u16* kb;   // first K block, offset by this lane's fragment
+    const u16* vb;   // first V block, offset by this lane's fragment
+    __device__ __forceinline__ uint4 k(int p, int ds) const { return ld16(kb + p * (kPage * D) + ds * 512); }
+    __device__ __forceinline__ uint2 v(int p, int dt) const {
+        return *reinterpret_cast<const uint2*>(vb + p * (kPage * D) + dt * 256);
     }
 };
 
@@ -234,14 +252,14 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 1) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
     float scale_log2, int split, int n_splits, float2* __restrict__ part_ml,
     float* __restrict__ part_o) {
-    using SM = StepMath<D>;
-    constexpr int NDS = SM::NDS, NDT = SM::NDT;
+    using TM = TileMath<D>;
+    constexpr int NDS = TM::NDS, NDT = TM::NDT;
     constexpr int BLK = kPage * D;               // elements per block
     constexpr int BLK_CH = BLK / 8;              // 16-byte chunks per block
     constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
@@ -329,13 +347,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
         __syncthreads();
         if (t0 + kKT < c1) load_tile(t0 + kKT);
         if (!active) continue;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int step0 = t0 + half * kStep;
-            if (step0 >= c1) break;
-            const LdsStep<D> src{smem + (2 * half) * BLK + lane * 8, smem + (4 + 2 * half) * BLK + lane * 4};
-            SM::run(qf, src, step0, p_m, lq, scale_log2, m_run, l_lane, o);
-        }
+        const bool full = t0 + kKT - 1 <= P0 + m_tile0 / G;    // every token <= every row's position
+        const LdsTile<D> src{smem + lane * 8, smem + 4 * BLK + lane * 4};
+        TM::run(qf, src, t0, p_m, full, lq, scale_log2, m_run, l_lane, o);
     }
     if (!active) return;
     const size_t idx = ((size_t)(si.off + jrow) * Hq + h) * n_splits + c;

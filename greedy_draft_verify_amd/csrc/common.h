@@ -43,14 +43,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// Packs 8 fp32 values into bf16x8 (round to nearest even).
+// Packs 8 fp32 values into bf16x8 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
-    uint4 r;
-    r.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
-    r.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
-    r.z = (uint32_t)f2bf(x[4]) | ((uint32_t)f2bf(x[5]) << 16);
-    r.w = (uint32_t)f2bf(x[6]) | ((uint32_t)f2bf(x[7]) << 16);
-    return as_bf16x8(r);
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+    return r;
 }
 
 // ---- host error reporting ---------------------------------------------------
