@@ -60,61 +60,55 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, u16* __restrict__ k_pool,
     u16* __restrict__ v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int kmax, int B, int R, int Hq,
-    int Hkv, int D, SeqInfo* __restrict__ info, int32_t* __restrict__ status) {
-    __shared__ long long s_before[256], s_total[256];
-    __shared__ int s_flags;
-    const int s = blockIdx.x, tid = threadIdx.x;
-    if (tid == 0) s_flags = 0;
-    __syncthreads();
+    int Hkv, int D, SeqInfo* __restrict__ info, int32_t* __restrict__ row_seq, int32_t* __restrict__ status) {
+    __shared__ long long s_before[4], s_total[4];
+    __shared__ int s_flags[4];
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // one round of independent loads: this sequence's (pos, k), every k for the row
+    // packing, and the page ids the sequence needs
+    const int ks = k[s];
+    const int P = pos[s];
     long long before = 0, total = 0;
-    int neg = 0;
+    int flags = 0;
     for (int i = tid; i < B; i += 256) {
         const long long kk = k[i];
         total += kk + 1;
         if (i < s) before += kk + 1;
-        if (kk < 0) neg = 1;
+        if (kk < 0) flags |= SPEC_STATUS_BAD_ROWS;
     }
-    if (neg) atomicOr(&s_flags, SPEC_STATUS_BAD_ROWS);
-    s_before[tid] = before;
-    s_total[tid] = total;
-    __syncthreads();
-    for (int d = 128; d > 0; d >>= 1) {
-        if (tid < d) {
-            s_before[tid] += s_before[tid + d];
-            s_total[tid] += s_total[tid + d];
-        }
-        __syncthreads();
-    }
-    const int ks = k[s];
-    const int P = pos[s];
-    if (tid == 0) {
-        int bits = 0;
-        if (s_total[0] != (long long)R || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
-        if (P < 0) {
-            bits |= SPEC_STATUS_BAD_POS;
-        } else if (ks >= 0 && ((long long)P + ks) / kPage >= max_pages) {
-            bits |= SPEC_STATUS_BAD_POS;
-        }
-        atomicOr(&s_flags, bits);
-    }
-    __syncthreads();
-    if (!(s_flags & SPEC_STATUS_BAD_POS) && ks >= 0) {
+    const bool pos_ok = P >= 0 && (ks < 0 || ((long long)P + ks) / kPage < max_pages);
+    if (!pos_ok) flags |= SPEC_STATUS_BAD_POS;
+    if (pos_ok && ks >= 0) {
         const int last_page = (int)(((long long)P + ks) / kPage);
-        int bad = 0;
         for (int pg = tid; pg <= last_page; pg += 256) {
             const int id = page_table[(size_t)s * max_pages + pg];
-            if (id < 0 || id >= n_pages) bad = 1;
+            if (id < 0 || id >= n_pages) flags |= SPEC_STATUS_BAD_PAGE;
         }
-        if (bad) atomicOr(&s_flags, SPEC_STATUS_BAD_PAGE);
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        before += __shfl_xor(before, d);
+        total += __shfl_xor(total, d);
+        flags |= __shfl_xor(flags, d);
+    }
+    if (lane == 0) {
+        s_before[wave] = before;
+        s_total[wave] = total;
+        s_flags[wave] = flags;
     }
     __syncthreads();
-    const int bits = s_flags;
-    const int off = (int)s_before[0];
+    int bits = s_flags[0] | s_flags[1] | s_flags[2] | s_flags[3];
+    if (s_total[0] + s_total[1] + s_total[2] + s_total[3] != (long long)R || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
+    const int off = (int)(s_before[0] + s_before[1] + s_before[2] + s_before[3]);
     if (tid == 0) {
         status[s] = bits;
         info[s].off = off;
         info[s].valid = bits == 0;
     }
+    // row -> sequence map for the combine (only when the packing is defined; otherwise
+    // every sequence is invalid and the combine writes nothing)
+    if (!(bits & SPEC_STATUS_BAD_ROWS))
+        for (int j = tid; j <= ks; j += 256) row_seq[off + j] = s;
     if (bits) return;
     // append: 8 channels (one 16-byte chunk of the row) per item
     const int dch = D / 8;
@@ -360,24 +354,20 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 1) void attn_split_ker
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int32_t* __restrict__ pos, const int32_t* __restrict__ k, const SeqInfo* __restrict__ info,
-    int B, int R, int Hq, int split, int n_splits, const float2* __restrict__ part_ml,
-    const float* __restrict__ part_o, u16* __restrict__ out) {
+    const int32_t* __restrict__ row_seq, int B, int R, int Hq, int split, int n_splits,
+    const float2* __restrict__ part_ml, const float* __restrict__ part_o, u16* __restrict__ out) {
     constexpr int PER = D / kWave;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const long long item = (long long)blockIdx.x * 4 + wave;
     if (item >= (long long)R * Hq) return;
     const int r = (int)(item / Hq), h = (int)(item % Hq);
-    // sequence of row r: last s with off_s <= r (offsets are monotone when valid)
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (info[mid].off <= r) lo = mid; else hi = mid - 1;
-    }
-    const SeqInfo si = info[lo];
+    const int sq = row_seq[r];
+    if (sq < 0 || sq >= B) return;               // packing undefined: every sequence is invalid
+    const SeqInfo si = info[sq];
     if (!si.valid) return;
     const int j = r - si.off;
-    if (j < 0 || j > k[lo]) return;
-    const int p = pos[lo] + j;
+    if (j < 0 || j > k[sq]) return;
+    const int p = pos[sq] + j;
     const int nc = p / split + 1;
     const size_t base = ((size_t)r * Hq + h) * n_splits;
     float mx = -INFINITY;
@@ -388,13 +378,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float L = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float2 ml = part_ml[base + c];
-        const float wgt = exp2f(ml.x - mx);
-        L += wgt * ml.y;
-        const float* po = part_o + (base + c) * D;
+    // splits merged in ascending order; each group of 8 is loaded at once first
+    constexpr int kGroup = 8;
+    for (int c0 = 0; c0 < nc; c0 += kGroup) {
+        float2 ml[kGroup];
+        float po[kGroup][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += wgt * po[e * kWave + lane];
+        for (int u = 0; u < kGroup; ++u) {
+            const int c = c0 + u < nc ? c0 + u : nc - 1;
+            ml[u] = part_ml[base + c];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) po[u][e] = part_o[(base + c) * D + e * kWave + lane];
+        }
+        // consume every loaded value here so that the group's loads are all issued first
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            asm volatile("" : "+v"(ml[u].x), "+v"(ml[u].y));
+#pragma unroll
+            for (int e = 0; e < PER; ++e) asm volatile("" : "+v"(po[u][e]));
+        }
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            if (c0 + u >= nc) break;
+            const float wgt = exp2f(ml[u].x - mx);
+            L += wgt * ml[u].y;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wgt * po[u][e];
+        }
     }
     const float inv = 1.f / L;
     u16* dst = out + ((size_t)r * Hq + h) * D;
@@ -408,14 +418,15 @@ static int64_t split_count(int32_t max_pages, int32_t split) {
 }
 
 struct AttnWs {
-    size_t info_off, ml_off, o_off, total;
+    size_t info_off, rows_off, ml_off, o_off, total;
 };
 
 static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_t n_splits) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     AttnWs w;
     w.info_off = 0;
-    w.ml_off = up(sizeof(SeqInfo) * (size_t)B);
+    w.rows_off = up(sizeof(SeqInfo) * (size_t)B);
+    w.ml_off = w.rows_off + up(sizeof(int32_t) * (size_t)R);
     w.o_off = w.ml_off + up(sizeof(float2) * (size_t)R * Hq * n_splits);
     w.total = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
     return w;
@@ -424,7 +435,7 @@ static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_
 template <int D>
 static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, const int32_t* pt,
                         int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
-                        int B, int R, int Hq, int Hkv, float scale, int split, int n_splits,
+                        const int32_t* row_seq, int B, int R, int Hq, int Hkv, float scale, int split, int n_splits,
                         float2* ml, float* po, u16* out, hipStream_t st) {
     const int rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
@@ -433,7 +444,7 @@ static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, cons
                        max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po);
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
-                       pos, k, info, B, R, Hq, split, n_splits, ml, po, out);
+                       pos, k, info, row_seq, B, R, Hq, split, n_splits, ml, po, out);
 }
 
 }  // namespace sv
@@ -489,16 +500,17 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
         return fail(SPEC_EWORKSPACE, "spec_verify_attn: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, lay.total);
     char* ws = static_cast<char*>(workspace);
     SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + lay.info_off);
+    int32_t* row_seq = reinterpret_cast<int32_t*>(ws + lay.rows_off);
     float2* ml = reinterpret_cast<float2*>(ws + lay.ml_off);
     float* po = reinterpret_cast<float*>(ws + lay.o_off);
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(attn_prep_kernel, dim3(B), dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, info, seq_status);
+                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, info, row_seq, seq_status);
     SV_LAUNCH_CHECK("spec_verify_attn(prep)");
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
     }
     SV_LAUNCH_CHECK("spec_verify_attn");
     return SPEC_OK;

@@ -12,8 +12,8 @@
 // lm_head_tile_kernel: one workgroup per (vocabulary tile of 128 entries, group of
 // up to 128 rows). Each wave owns two 16-row tiles of W and streams them from HBM
 // straight into MFMA B-operand registers with non-temporal loads (W is read once
-// and must not push the hidden rows out of L2), double-buffered one K-block
-// ahead. The hidden rows are shared by the four waves through LDS. After the K
+// and must not push the hidden rows out of L2), double-buffered one 128-channel
+// K-block ahead. The hidden rows are shared by the four waves through LDS. After the K
 // loop each wave reduces its logits to the best (value, index) per row with the
 // order "larger value, then smaller index" (the first-maximum rule of span-02
 // greedy_logprob), the workgroup merges its four waves, and one record per
@@ -68,7 +68,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 }
 
 template <int MT, int KB>
-__global__ __launch_bounds__(kLmThreads) void lm_head_tile_kernel(
+__global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, float* __restrict__ part_v, int* __restrict__ part_i) {
     constexpr int HSTR = KB + 8;             // LDS row stride (elements)
@@ -241,9 +241,9 @@ static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, i
                          float* pv, int* pi, hipStream_t st) {
     int grid = n_vt * n_rg;
     if (n_rg > 1) grid = (grid + 7) / 8 * 8;
-    // deeper K-blocks keep more of the W stream in flight; wide row groups trade
-    // depth for the registers their hidden staging needs
-    constexpr int KB = MT <= 5 ? 256 : 128;
+    // 128-channel K-blocks keep the wave at <= 256 registers (two waves per SIMD):
+    // more waves in flight per CU beat deeper per-wave prefetch for the W stream
+    constexpr int KB = 128;
     hipLaunchKernelGGL((lm_head_tile_kernel<MT, KB>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
                        H, V, n_vt, n_rg, pv, pi);
 }
