@@ -1,34 +1,43 @@
 // spec_lm_head_argmax: bf16 MFMA lm_head with the greedy argmax fused into the
 // epilogue; the logits never leave registers.
 //
-// W is consumed in a packed form made once by spec_lm_head_pack: tiles of 16
-// vocabulary rows x 32 channels, each stored as the 64 lanes' MFMA B fragments in
-// lane order (1 KB), the K steps of a 16-row tile back to back. A row-major [V][H]
-// matrix read as MFMA fragments touches 16 rows x 64 bytes per wave instruction,
-// which caps the stream far below HBM peak; the packed form makes every wave
-// instruction one contiguous 1 KB read, and a 16-row tile a contiguous H*32-byte
-// stream. The packing is a byte permutation, so results are identical.
+// W is consumed in a packed form made once by spec_lm_head_pack. A row-major
+// [V][H] matrix read as MFMA fragments touches 16 rows x 64 bytes per wave
+// instruction, which caps the stream far below HBM peak. The packed form is
+// group-major: a group is 128 vocabulary rows (one workgroup's share), a K-block
+// is 128 channels, and the group's 8 tiles of 16 rows store, K-block by K-block,
+// their 4 k-steps as the 64 lanes' MFMA B fragments in lane order (1 KB each).
+// A workgroup therefore streams one contiguous region, 32 KB per K-block, and
+// every wave instruction is one contiguous 1 KB read. The packing is a byte
+// permutation, so results are identical.
 //
-// lm_head_tile_kernel: one workgroup per (vocabulary tile of 128 entries, group of
-// up to 128 rows). Each wave owns two 16-row tiles of W and streams them from HBM
-// straight into MFMA B-operand registers with non-temporal loads (W is read once
-// and must not push the hidden rows out of L2), double-buffered one 128-channel
-// K-block ahead. The hidden rows are shared by the four waves through LDS. After the K
-// loop each wave reduces its logits to the best (value, index) per row with the
-// order "larger value, then smaller index" (the first-maximum rule of span-02
-// greedy_logprob), the workgroup merges its four waves, and one record per
-// (tile, row) goes to the workspace.
-// lm_head_final_kernel: one workgroup per row merges the tiles' records with the
+// lm_head_tile_kernel: one workgroup per (group of 128 vocabulary entries, group
+// of up to 128 rows). Each wave owns two 16-row tiles of W and streams them from
+// HBM straight into MFMA B-operand registers with non-temporal loads (W is read
+// once and must not push the hidden rows out of L2) through a ring of one
+// K-block: a k-step's fragments are re-requested for the next K-block as soon as
+// its MFMAs are issued, and every load is unconditional so the in-order load
+// counter never has to drain. The hidden rows are shared by the four waves through
+// LDS, one K-block ahead. After the K loop each wave reduces its logits to the best
+// (value, index) per row with the order "larger value, then smaller index" (the
+// first-maximum rule of span-02 greedy_logprob), the workgroup merges its four
+// waves, and one record per (row, group) goes to the workspace.
+// lm_head_final_kernel: one workgroup per row merges that row's records with the
 // same order. The order is total, so the result does not depend on how the
 // reduction is grouped; each logit is one MFMA chain over K in a fixed order, so a
-// row's result does not depend on R, the row group or the K-block size.
+// row's result does not depend on R or the row group.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sv {
 
 constexpr int kLmThreads = 256;
 constexpr int kLmNT = 2;                  // 16-entry vocabulary tiles per wave
-constexpr int kLmVocabPerWg = 4 * 16 * kLmNT;
+constexpr int kLmTiles = 4 * kLmNT;       // tiles per group (one workgroup)
+constexpr int kLmVocabPerWg = 16 * kLmTiles;
+constexpr int kLmKB = 128;                // channels per K-block
+constexpr int kLmKS = kLmKB / 32;         // MFMA k-steps per K-block
 constexpr int kLmMaxMT = 8;               // 16-row tiles per row group
 constexpr int kLmHAlign = 256;            // H must be a multiple of this
 
@@ -40,20 +49,23 @@ __device__ __forceinline__ uint4 ld16_stream(const u16* p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Packed W: fragment f = (tile * (H / 32) + kstep) * 64 + lane holds
-// W[16 * tile + lane % 16][32 * kstep + 8 * (lane / 16) .. + 8] (zero past V).
+// Packed W: fragment f = (((g * H/128 + kb) * 8 + t) * 4 + s) * 64 + lane holds
+// W[128 g + 16 t + lane % 16][128 kb + 32 s + 8 (lane / 16) .. + 8] (zero past V).
 __global__ __launch_bounds__(256) void lm_head_pack_kernel(const u16* __restrict__ w, int V, int H,
                                                            u16* __restrict__ wp) {
-    const size_t ksteps = (size_t)(H / 32);
-    const size_t nfrag = (size_t)((V + 15) / 16) * ksteps * 64;
+    const size_t nkb = (size_t)(H / kLmKB);
+    const size_t nfrag = (size_t)((V + kLmVocabPerWg - 1) / kLmVocabPerWg) * nkb * kLmTiles * kLmKS * 64;
     for (size_t f = (size_t)blockIdx.x * blockDim.x + threadIdx.x; f < nfrag;
          f += (size_t)gridDim.x * blockDim.x) {
         const int lane = (int)(f % 64);
-        const size_t t = f / 64;
-        const int ks = (int)(t % ksteps);
-        const size_t tile = t / ksteps;
-        const size_t v = tile * 16 + lane % 16;
-        const int k = ks * 32 + (lane / 16) * 8;
+        size_t t = f / 64;
+        const int s = (int)(t % kLmKS);
+        t /= kLmKS;
+        const int tile = (int)(t % kLmTiles);
+        t /= kLmTiles;
+        const size_t kb = t % nkb, g = t / nkb;
+        const size_t v = g * kLmVocabPerWg + (size_t)tile * 16 + lane % 16;
+        const size_t k = kb * kLmKB + (size_t)s * 32 + (lane / 16) * 8;
         st16(wp + f * 8, v < (size_t)V ? ld16(w + v * H + k) : make_uint4(0, 0, 0, 0));
     }
 }
@@ -67,20 +79,19 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-template <int MT, int KB>
+template <int MT>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, float* __restrict__ part_v, int* __restrict__ part_i) {
-    constexpr int HSTR = KB + 8;             // LDS row stride (elements)
-    constexpr int KS = KB / 32;              // MFMA k-steps per K-block
-    constexpr int HCH = 16 * MT * KB / 8 / kLmThreads;  // hidden chunks per thread per K-block
-    static_assert(HCH * kLmThreads * 8 == 16 * MT * KB, "hidden staging must tile evenly");
+    constexpr int HSTR = kLmKB + 8;                            // LDS row stride (elements)
+    constexpr int HCH = 16 * MT * kLmKB / 8 / kLmThreads;     // hidden chunks per thread per K-block
+    static_assert(HCH * kLmThreads * 8 == 16 * MT * kLmKB, "hidden staging must tile evenly");
     __shared__ __attribute__((aligned(16))) u16 hs[16 * MT * HSTR];
     __shared__ Best wbest[4][16 * MT];
 
     // Logical tile: with several row groups, hardware workgroup i runs on XCD i % 8;
-    // give the row groups of one vocabulary tile consecutive slots of one XCD so that
-    // W is fetched from HBM once and re-read from that XCD's L2.
+    // give the row groups of one vocabulary group consecutive slots of one XCD so
+    // that W is fetched from HBM once and re-read from that XCD's L2.
     int lid = blockIdx.x;
     if (n_rg > 1) {
         const int per_xcd = (int)((gridDim.x + 7) / 8);
@@ -92,29 +103,25 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
     const int tile0 = (vt * 4 + wave) * kLmNT;       // first 16-row W tile of this wave
-    const int n_tiles = (V + 15) / 16;
-    const int ksteps = H / 32;
+    const int nkb = H / kLmKB;
 
-    const u16* wt[kLmNT];
-#pragma unroll
-    for (int nt = 0; nt < kLmNT; ++nt)
-        wt[nt] = wp + ((size_t)min(tile0 + nt, n_tiles - 1) * ksteps * 64 + lane) * 8;
-    uint4 wcur[kLmNT][KS], wnext[kLmNT][KS];
-    uint4 hcur[HCH], hnext[HCH];
-    auto load_h = [&](int kb, uint4* dst) {
+    const u16* wt = wp + (((size_t)vt * nkb * kLmTiles + wave * kLmNT) * kLmKS * 64 + lane) * 8;
+    const size_t kb_stride = (size_t)kLmTiles * kLmKS * 512;   // elements per K-block of a group
+    uint4 ring[kLmKS][kLmNT], hnext[HCH];
+    // Rows past R re-read row R - 1: a row's logits depend on its own hidden row
+    // only, and those rows' results are never written.
+    auto load_h = [&](int kb) {
 #pragma unroll
         for (int it = 0; it < HCH; ++it) {
             const int cidx = it * kLmThreads + tid;
-            const int row = cidx / (KB / 8), ch = cidx % (KB / 8);
-            const int r = r0 + row;
-            dst[it] = r < R ? ld16(hidden + (size_t)r * H + kb * KB + ch * 8) : make_uint4(0, 0, 0, 0);
+            const int row = cidx / (kLmKB / 8), ch = cidx % (kLmKB / 8);
+            hnext[it] = ld16(hidden + (size_t)min(r0 + row, R - 1) * H + kb * kLmKB + ch * 8);
         }
     };
-    auto load_w = [&](int kb, uint4 (*dst)[KS]) {
+    auto load_slot = [&](int kb, int s, uint4* dst) {
+        const u16* p = wt + (size_t)kb * kb_stride + s * 512;
 #pragma unroll
-        for (int nt = 0; nt < kLmNT; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) dst[nt][ks] = ld16_stream(wt[nt] + (size_t)(kb * KS + ks) * 512);
+        for (int nt = 0; nt < kLmNT; ++nt) dst[nt] = ld16_stream(p + nt * kLmKS * 512);
     };
 
     f32x4 acc[MT][kLmNT];
@@ -123,39 +130,37 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 #pragma unroll
         for (int nt = 0; nt < kLmNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkb = H / KB;
-    load_h(0, hnext);
-    load_w(0, wnext);
-    for (int kb = 0; kb < nkb; ++kb) {
-#pragma unroll
-        for (int it = 0; it < HCH; ++it) hcur[it] = hnext[it];
-#pragma unroll
-        for (int nt = 0; nt < kLmNT; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) wcur[nt][ks] = wnext[nt][ks];
+    // One K-block: publish its hidden rows in LDS, request the next block's hidden
+    // rows, then per k-step: MFMAs, and re-request that ring slot for the next block.
+    auto block = [&](int kb, auto more_c) {
+        constexpr bool more = decltype(more_c)::value;
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < HCH; ++it) {
             const int cidx = it * kLmThreads + tid;
-            const int row = cidx / (KB / 8), ch = cidx % (KB / 8);
-            st16(hs + row * HSTR + ch * 8, hcur[it]);
+            const int row = cidx / (kLmKB / 8), ch = cidx % (kLmKB / 8);
+            st16(hs + row * HSTR + ch * 8, hnext[it]);
         }
+        if constexpr (more) load_h(kb + 1);
         __syncthreads();
-        if (kb + 1 < nkb) {
-            load_h(kb + 1, hnext);
-            load_w(kb + 1, wnext);
-        }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int s = 0; s < kLmKS; ++s) {
+            bf16x8 a[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 a = as_bf16x8(ld16(hs + (mt * 16 + l16) * HSTR + ks * 32 + lq * 8));
+            for (int mt = 0; mt < MT; ++mt) a[mt] = as_bf16x8(ld16(hs + (mt * 16 + l16) * HSTR + s * 32 + lq * 8));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < kLmNT; ++nt)
-                    acc[mt][nt] = mfma16x16x32(a, as_bf16x8(wcur[nt][ks]), acc[mt][nt]);
-            }
+                    acc[mt][nt] = mfma16x16x32(a[mt], as_bf16x8(ring[s][nt]), acc[mt][nt]);
+            if constexpr (more) load_slot(kb + 1, s, ring[s]);
         }
-    }
+    };
+    load_h(0);
+#pragma unroll
+    for (int s = 0; s < kLmKS; ++s) load_slot(0, s, ring[s]);
+    for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, std::true_type{});
+    block(nkb - 1, std::false_type{});
 
     // epilogue: C[row = 16 mt + 4 lq + i][vocab = 16 (tile0 + nt) + l16]
 #pragma unroll
@@ -193,8 +198,8 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
             const Best o = wbest[wv][tid];
             if (better(o.v, o.i, b.v, b.i)) b = o;
         }
-        part_v[(size_t)vt * R + r0 + tid] = b.v;
-        part_i[(size_t)vt * R + r0 + tid] = b.i;
+        part_v[(size_t)(r0 + tid) * n_vt + vt] = b.v;
+        part_i[(size_t)(r0 + tid) * n_vt + vt] = b.i;
     }
 }
 
@@ -206,9 +211,11 @@ __global__ __launch_bounds__(256) void lm_head_final_kernel(const float* __restr
     const int r = blockIdx.x, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
+    const float* rv = part_v + (size_t)r * n_vt;
+    const int* ri = part_i + (size_t)r * n_vt;
     for (int t = tid; t < n_vt; t += 256) {
-        const float v = part_v[(size_t)t * R + r];
-        const int i = part_i[(size_t)t * R + r];
+        const float v = rv[t];
+        const int i = ri[t];
         if (better(v, i, bv, bi)) {
             bv = v;
             bi = i;
@@ -241,10 +248,7 @@ static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, i
                          float* pv, int* pi, hipStream_t st) {
     int grid = n_vt * n_rg;
     if (n_rg > 1) grid = (grid + 7) / 8 * 8;
-    // 128-channel K-blocks keep the wave at <= 256 registers (two waves per SIMD):
-    // more waves in flight per CU beat deeper per-wave prefetch for the W stream
-    constexpr int KB = 128;
-    hipLaunchKernelGGL((lm_head_tile_kernel<MT, KB>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
+    hipLaunchKernelGGL((lm_head_tile_kernel<MT>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
                        H, V, n_vt, n_rg, pv, pi);
 }
 
@@ -254,7 +258,7 @@ extern "C" {
 
 size_t spec_lm_head_packed_bytes(int32_t V, int32_t H) {
     if (V < 1 || H < 1) return 0;
-    return (size_t)((V + 15) / 16) * 16 * (size_t)H * sizeof(spec_bf16);
+    return (size_t)((V + sv::kLmVocabPerWg - 1) / sv::kLmVocabPerWg) * sv::kLmVocabPerWg * (size_t)H * sizeof(spec_bf16);
 }
 
 int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_packed, void* stream) {

@@ -157,11 +157,14 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
                         size_t workspace_bytes, void* stream);
 
 /* spec_lm_head_pack — one-time re-layout of a row-major lm_head weight w [V][H]
- * (bf16) into the packed form spec_lm_head_argmax reads: tiles of 16 vocabulary
- * rows x 32 channels, each tile stored as 64 lanes x 8 bf16 in MFMA B-fragment
- * order (lane l holds w[16t + l % 16][32s + 8(l / 16) .. +8]), the H/32 tiles of
- * a 16-row group consecutive, rows past V zero. w_packed holds
- * spec_lm_head_packed_bytes(V, H) bytes and must not overlap w. Limits as above. */
+ * (bf16) into the packed form spec_lm_head_argmax reads. Vocabulary rows are
+ * taken in groups of 128 and channels in K-blocks of 128; a group stores its
+ * K-blocks in order, each K-block its 8 tiles of 16 rows, each tile its 4 k-steps
+ * of 32 channels as 64 lanes x 8 bf16 in MFMA B-fragment order. Fragment
+ *   f = (((g * H/128 + b) * 8 + t) * 4 + s) * 64 + lane
+ * holds w[128g + 16t + lane % 16][128b + 32s + 8(lane / 16) .. +8]; rows past V
+ * are zero. w_packed holds spec_lm_head_packed_bytes(V, H) = ceil(V/128) * 128 *
+ * H * 2 bytes and must not overlap w. Limits as above. */
 size_t spec_lm_head_packed_bytes(int32_t V, int32_t H);
 int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_packed, void* stream);
 

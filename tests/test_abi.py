@@ -73,7 +73,7 @@ def test_host_argument_checks():
     assert L.spec_lm_head_argmax(p, p, 4, 256, 1000, p, None, p, 8, None) == -4
     assert L.spec_lm_head_argmax_workspace_bytes(4, 256, 1000) >= 4 * 8 * 8
     assert L.spec_lm_head_pack(p, 1000, 128, p, None) == -1
-    assert L.spec_lm_head_packed_bytes(1000, 256) == 1008 * 256 * 2
+    assert L.spec_lm_head_packed_bytes(1000, 256) == 1024 * 256 * 2
     # accept: B out of range, null pointers
     assert L.spec_greedy_accept(p, p, 3, p, None, 0, 100, 0, 4, p, p, p, p, p, p, p, None) == -1
     assert L.spec_greedy_accept(p, None, 3, p, None, 0, 100, 1, 4, p, p, p, p, p, p, p, None) == -1

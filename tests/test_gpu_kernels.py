@@ -174,22 +174,27 @@ def test_lm_head_shapes(dev, R, H, V):
 
 
 def test_lm_head_pack_is_the_documented_permutation(dev):
-    """Packed fragment (t, s, lane) holds w[16t + lane % 16][32s + 8(lane // 16) .. +8], zero past V."""
+    """Packed fragment (g, b, t, s, lane) holds w[128g + 16t + lane % 16][128b + 32s + 8(lane // 16) .. +8],
+    zero past V (groups of 128 rows, K-blocks of 128 channels)."""
     import greedy_draft_verify_amd as gdv
     rng = np.random.default_rng(21)
-    V, H = 37, 512
+    V, H = 150, 512
     w = torch.from_numpy(rng.standard_normal((V, H)).astype(np.float32)).to(torch.bfloat16)
     wp = bits(gdv.spec_lm_head_pack(w.to(dev)))
     torch.cuda.synchronize()
     wb = bits(w)
-    nt, ks = (V + 15) // 16, H // 32
-    exp = np.zeros((nt, ks, 64, 8), np.uint16)
-    for t in range(nt):
-        for s in range(ks):
-            for lane in range(64):
-                v = 16 * t + lane % 16
-                if v < V:
-                    exp[t, s, lane] = wb[v, 32 * s + 8 * (lane // 16): 32 * s + 8 * (lane // 16) + 8]
+    ng, nb = (V + 127) // 128, H // 128
+    exp = np.zeros((ng, nb, 8, 4, 64, 8), np.uint16)
+    for g in range(ng):
+        for b in range(nb):
+            for t in range(8):
+                for s in range(4):
+                    for lane in range(64):
+                        v = 128 * g + 16 * t + lane % 16
+                        k = 128 * b + 32 * s + 8 * (lane // 16)
+                        if v < V:
+                            exp[g, b, t, s, lane] = wb[v, k:k + 8]
+    assert wp.size == exp.size
     assert np.array_equal(wp.reshape(exp.shape), exp)
 
 
