@@ -246,7 +246,7 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 1) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 1) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
@@ -263,15 +263,25 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 1) void attn_split_ker
     const int mgroup = blockIdx.x / n_splits;
     const int hk = blockIdx.y;
     const int s = blockIdx.z;
-    const SeqInfo si = info[s];
-    if (!si.valid) return;
-    const int G = Hq / Hkv, T = k[s] + 1, M = G * T, P0 = pos[s], last = P0 + T - 1;
+    const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
     const int c0 = c * split;
+    // Page ids of this split (lane i holds page c0/16 + i + 64 r), requested together
+    // with the sequence's metadata: the index depends on the launch coordinates only
+    // (clamped to the page-table row; entries past the sequence's last page are never
+    // used), so the first tile waits on one round trip, not two.
+    const int pg0 = c0 / kPage;
+    int pid[(kMaxSplit / kPage + kWave - 1) / kWave];
+#pragma unroll
+    for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
+        pid[r] = page_table[(size_t)s * max_pages + min(pg0 + r * kWave + lane, max_pages - 1)];
+    const SeqInfo si = info[s];
+    const int ks = k[s], P0 = pos[s];
+    if (!si.valid) return;
+    const int G = Hq / Hkv, T = ks + 1, M = G * T, last = P0 + T - 1;
     if (c0 > last) return;
     if (mgroup * kRowsPerGroup >= M) return;
     const int c1 = min(c0 + split, last + 1);
 
-    const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
     const bool active = m_tile0 < M;
@@ -292,16 +302,6 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 1) void attn_split_ker
     for (int i = 0; i < NDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_lane = 0.f;
     const int last_page = last / kPage;
-    // page ids of this split, lane i holding page c0/16 + i + 64 r (read once; taken
-    // with readlane per tile, so no tile waits on a page-table load)
-    const int pg0 = c0 / kPage;
-    const int n_pg = (c1 - 1) / kPage - pg0 + 1;
-    int pid[(kMaxSplit / kPage + kWave - 1) / kWave];
-#pragma unroll
-    for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
-        const int i = r * kWave + lane;
-        pid[r] = i < n_pg ? page_table[(size_t)s * max_pages + pg0 + i] : 0;
-    }
     auto page_of = [&](int pg) -> int64_t {   // pg: absolute page index, wave-uniform
         const int i = pg - pg0;
         int id = 0;
