@@ -7,7 +7,10 @@ b16k4 workload (B=16 sequences, k=4 drafts, 80 rows, context U{512..4096},
 seeded synthetic tensors already resident in HBM; drafts are the target's greedy
 tokens (from an untimed pass) corrupted with probability 0.3.
 
-Prints one JSON line: verify rows/s (value), emitted tokens/s, the roofline of the
+The timed step is a HIP graph replay of the three calls (captured once after an
+eager timed loop of the same calls; the replay must reproduce the eager outputs
+byte for byte). Prints one JSON line: verify rows/s (value), emitted tokens/s, the
+eager per-call times, the roofline of the
 dominant kernel (lm_head, weight-stream bound at 80 rows) measured with HIP events
 on the launch stream, the attention roofline, and the CPU oracle timed on a bounded
 sample of the same workload (cpu_baseline).
@@ -44,11 +47,12 @@ def i32(a, dev):
 
 
 class VerifyStep:
-    """Device buffers and the three launches of one verify step."""
+    """Device buffers and the three launches of one verify step (on the current
+    stream, so that the same calls run eagerly or under HIP graph capture)."""
 
-    def __init__(self, x: synth.VerifyInputs, dev, stream):
+    def __init__(self, x: synth.VerifyInputs, dev):
         wl = x.wl
-        self.x, self.dev, self.stream = x, dev, stream
+        self.x, self.dev = x, dev
         self.B, self.R = len(x.pos), x.R
         self.q, self.k_new, self.v_new = x.q, x.k_new, x.v_new
         self.k_pool, self.v_pool = x.k_pool, x.v_pool
@@ -72,16 +76,20 @@ class VerifyStep:
     def attn(self):
         gdv.spec_verify_attn(self.q, self.k_new, self.v_new, self.k_pool, self.v_pool, self.page_table,
                              self.pos, self.k, self.x.wl.kmax, self.x.scale, self.attn_out, self.attn_status,
-                             workspace_buf=self.attn_ws, stream=self.stream)
+                             workspace_buf=self.attn_ws)
 
     def lm_head(self):
         gdv.spec_lm_head_argmax(self.hidden, self.w_packed, self.x.wl.V, self.argmax, self.maxval,
-                                workspace_buf=self.lm_ws, stream=self.stream)
+                                workspace_buf=self.lm_ws)
 
     def accept(self):
         gdv.spec_greedy_accept(self.argmax, self.drafts, self.k, self.d2t, self.x.wl.V, self.pos, self.pos_out,
-                               self.acc_len, self.n_emit, self.emit, self.next_tok, self.acc_status,
-                               stream=self.stream)
+                               self.acc_len, self.n_emit, self.emit, self.next_tok, self.acc_status)
+
+    def outputs(self):
+        """Copies of everything the step writes."""
+        return [t.clone() for t in (self.attn_out, self.attn_status, self.argmax, self.maxval, self.pos_out,
+                                    self.acc_len, self.n_emit, self.emit, self.next_tok, self.acc_status)]
 
 
 def attn_bytes(x: synth.VerifyInputs) -> int:
@@ -117,6 +125,66 @@ def measured_traffic(kernel_key: str):
     if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("source_sha256_16"):
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def time_call(f, reps: int, warmup: int = 3) -> float:
+    """Mean seconds per call of f over reps back-to-back calls (HIP events on the current stream)."""
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps / 1e3
+
+
+def delta_leg(dev, reps: int):
+    """Gated DeltaNet verify with per-token record and fused rollback (mode BOTH) on the
+    hybrid workload: B=32, T=5, 32 heads, 128x128 fp32 state. Algorithmic bytes: S_0
+    read, every S_t recorded, q/k/v/a/b read, o written, S_L written for L > 0."""
+    d = synth.make_delta_inputs(seed=0, device=dev)
+    st_bytes = d.dv * d.dk * 4
+    rec = torch.empty((d.B, d.T, d.Hd, d.dv, d.dk), dtype=torch.float32, device=dev)
+    o = torch.empty((d.B, d.T, d.Hd, d.dv), dtype=torch.bfloat16, device=dev)
+    L = i32(d.L, dev)
+    state = d.state.clone()
+    f = lambda: gdv.spec_delta_verify_rollback(gdv.DELTA_BOTH, d.q, d.k, d.v, d.a, d.b, 1.0, state, rec, L, o)
+    sec = time_call(f, reps)
+    n_sh = d.B * d.Hd
+    byts = (n_sh * st_bytes * (1 + d.T) + d.B * d.T * d.Hd * (2 * d.dk + d.dv) * 2 + d.B * d.T * d.Hd * 8
+            + d.B * d.T * d.Hd * d.dv * 2 + int((d.L > 0).sum()) * d.Hd * st_bytes)
+    gbs = byts / sec / 1e9
+    restore = lambda: gdv.spec_delta_verify_rollback(gdv.DELTA_ROLLBACK, None, None, None, None, None, 1.0, state,
+                                                     rec, L, None)
+    sec_r = time_call(restore, reps)
+    byts_r = 2 * int((d.L > 0).sum()) * d.Hd * st_bytes
+    return {"workload": f"B={d.B} T={d.T} heads={d.Hd} state {d.dv}x{d.dk} fp32, L ~ U{{0..{d.T}}}",
+            "verify_record_rollback_us": sec * 1e6, "algorithmic_bytes": byts, "achieved": gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "bound": "hbm",
+            "rollback_only_us": sec_r * 1e6, "rollback_only_bytes": byts_r,
+            "rollback_only_frac": byts_r / sec_r / 1e9 / HBM_PEAK_GBS}
+
+
+def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
+    """spec_lm_head_argmax alone at growing row counts with the workload's W: where the
+    weight stream stops bounding it and the MFMA work starts to."""
+    wl = x.wl
+    out = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    for R in (80, 160, 288, 512, 1024):
+        h = torch.randn((R, wl.H), generator=g, device=dev).to(torch.bfloat16)
+        am = torch.empty(R, dtype=torch.int32, device=dev)
+        ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, wl.H, wl.V), dev)
+        sec = time_call(lambda: gdv.spec_lm_head_argmax(h, w_packed, wl.V, am, None, workspace_buf=ws), reps)
+        tf = 2.0 * R * wl.H * wl.V / sec / 1e12
+        gbs = lm_head_bytes(R, wl.H, wl.V) / sec / 1e9
+        out.append({"rows": R, "us": sec * 1e6, "GB/s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "TFLOP/s": tf,
+                    "mfma_frac": tf / BF16_PEAK_TFLOPS})
+    return out
 
 
 def cpu_baseline(x_host: synth.VerifyInputs, n_seq: int):
@@ -163,6 +231,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the DeltaNet leg and the lm_head row sweep (reported beside the step)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed loop, copy this many MiB 3 times (a plain copy kernel of known "
                          "size, used to scale hardware byte counters)")
@@ -185,7 +255,7 @@ def main():
         x_host = synth.VerifyInputs(wl, x.pos, x.k, x.R, x.page_table, x.n_pages, x.q.cpu(), x.k_new.cpu(),
                                     x.v_new.cpu(), x.k_pool.cpu(), x.v_pool.cpu(), x.hidden.cpu(), x.w.cpu(), x.d2t)
 
-    step = VerifyStep(x, dev, stream)
+    step = VerifyStep(x, dev)
     x.w = None                      # the packed copy is the one the step reads
     torch.cuda.empty_cache()
     # drafts: greedy tokens of an untimed lm_head pass, corrupted per position
@@ -222,8 +292,31 @@ def main():
         run_step(evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
+    eager_ms_step = start.elapsed_time(stop) / args.steps
+    eager_out = step.outputs()
+
+    # The same step captured once as a HIP graph and replayed: the launches' host
+    # overhead and gaps leave the step. Every replay must reproduce the eager bytes.
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run_step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run_step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    for a, b in zip(eager_out, step.outputs()):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "graph replay differs from the eager step"
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     lm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -236,9 +329,20 @@ def main():
     at_gbs = at_b / (attn_ms / 1e3) / 1e9
     lm_tflops = 2.0 * x.R * wl.H * wl.V / (lm_ms / 1e3) / 1e12
     hist = np.bincount(acc_len, minlength=wl.kmax + 1).tolist()
-    log(f"[bench] step {ms_step * 1e3:.1f} us: attn {attn_ms * 1e3:.1f} us ({at_gbs:.0f} GB/s), lm_head "
+    log(f"[bench] step {ms_step * 1e3:.1f} us (graph replay; eager {eager_ms_step * 1e3:.1f} us): attn {attn_ms * 1e3:.1f} us ({at_gbs:.0f} GB/s), lm_head "
         f"{lm_ms * 1e3:.1f} us ({lm_gbs:.0f} GB/s, {lm_tflops:.1f} TFLOP/s), accept {acc_ms * 1e3:.1f} us; "
         f"accept-length histogram {hist}")
+
+    extras = {}
+    if not args.no_extras:
+        extras["lm_head_row_sweep"] = lm_head_sweep(x, step.w_packed, dev, reps=10)
+        extras["delta_roofline"] = delta_leg(dev, reps=20)
+        sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
+        dl = extras["delta_roofline"]
+        log(f"[bench] lm_head sweep: {sw}")
+        log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
+            f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
+            f"{dl['rollback_only_us']:.1f} us")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -264,6 +368,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "eager_ms_per_step": eager_ms_step,
+        "step_launch": "HIP graph replay of the three entry points (per-entry times and rooflines from the eager loop)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -286,6 +392,7 @@ def main():
                           "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS, "algorithmic_bytes": at_b,
                           "traffic_split_kernel": measured_traffic("attn_split") if wl.name == "b16k4" else None},
         "cpu_baseline": cpu,
+        **extras,
         "context": "pages' own figure: 6.5 ms per 16-row whole-model verify, RTX 5090 with CUDA graphs "
                    "(not comparable: whole model, other hardware)",
     }
