@@ -12,7 +12,9 @@
 //      ids), records its row offset in the workspace and writes the rows' K/V into
 //      their pool slots (span-02 spec.rs: KV appended in place at pos..pos+k).
 //   2. attn_split_kernel: one workgroup per (sequence, kv head, split of
-//      kv_split_tokens positions, group of 64 query rows). It stages 64-token tiles
+//      kv_split_tokens positions, group of 64 query rows), kv head fastest in the
+//      launch order so that the Hkv blocks of a page (adjacent in the pool) are
+//      fetched at about the same time. It stages 64-token tiles
 //      (4 K blocks + 4 V blocks, each a contiguous 16*D*2-byte copy) in LDS and
 //      gives each wave a 16-row query tile; per 32-token step a wave computes
 //      S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 (the G*T query
@@ -20,8 +22,8 @@
 //      all of them) and runs the online softmax in registers (row max/sum across
 //      the 4 lanes holding a row). A key t is kept for row j only if t <= pos + j
 //      (kv_hi = position, memra full_attn_verify's per-row bound). The split's page
-//      ids are read once per wave and taken with readlane, so tiles never wait on a
-//      page-table load.
+//      ids are requested with the sequence metadata, once per wave, and taken with
+//      readlane, so tiles never wait on a page-table load.
 //   3. attn_combine_kernel one wave per (row, q head): merges the row's splits in
 //      ascending order (log-sum-exp weights) and writes bf16.
 //
@@ -245,8 +247,10 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // ---------------------------------------------------------------------------
 // attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
+// Register budget: four workgroups per CU at D <= 128 (32 KB of LDS each), two at
+// D = 256 (64 KB each), so that enough tiles are in flight per CU.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 1) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
@@ -259,9 +263,11 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 1) void attn_split_ker
     constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
     __shared__ __attribute__((aligned(16))) u16 smem[8 * BLK];   // K0..K3, V0..V3
 
-    const int c = blockIdx.x % n_splits;
-    const int mgroup = blockIdx.x / n_splits;
-    const int hk = blockIdx.y;
+    // kv head fastest: the workgroups of one (sequence, split) start together and
+    // fetch the Hkv blocks of each page (adjacent in the pool) at about the same time
+    const int hk = blockIdx.x % Hkv;
+    const int c = (blockIdx.x / Hkv) % n_splits;
+    const int mgroup = blockIdx.x / Hkv / n_splits;
     const int s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
     const int c0 = c * split;
@@ -311,6 +317,8 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 1) void attn_split_ker
         return id;
     };
 
+    // The next tile is requested into registers while the current one is used from
+    // LDS; V slots past the last written position are zeroed as they arrive.
     uint4 stage[PER_THREAD];
     auto load_tile = [&](int t0) {
 #pragma unroll
@@ -439,7 +447,7 @@ static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, cons
                         float2* ml, float* po, u16* out, hipStream_t st) {
     const int rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
-    dim3 grid(mgroups * n_splits, Hkv, B);
+    dim3 grid(mgroups * n_splits * Hkv, 1, B);
     hipLaunchKernelGGL(attn_split_kernel<D>, grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
                        max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po);
     const long long items = (long long)R * Hq;
@@ -493,7 +501,7 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
         return fail(SPEC_EINVAL, "spec_verify_attn: q, k_new, v_new, k_pool, v_pool and out must be 16-byte aligned");
     const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
     const int64_t n_splits = split_count(max_pages, split);
-    if (n_splits * 2 > 0x7fffffffLL || (long long)B * Hkv * n_splits > 0x7fffffffLL)
+    if (n_splits * 2 * Hkv > 0x7fffffffLL || (long long)B * Hkv * n_splits > 0x7fffffffLL)
         return fail(SPEC_ECAPACITY, "spec_verify_attn: too many splits");
     const AttnWs lay = attn_ws_layout(B, R, Hq, D, n_splits);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace))
