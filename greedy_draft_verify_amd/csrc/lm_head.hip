@@ -79,7 +79,9 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-template <int MT>
+// SHARED: other row groups re-read this vocabulary group's W through the XCD's L2,
+// so W is loaded with the default cache policy instead of as a stream.
+template <int MT, bool SHARED>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, float* __restrict__ part_v, int* __restrict__ part_i) {
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     auto load_slot = [&](int kb, int s, uint4* dst) {
         const u16* p = wt + (size_t)kb * kb_stride + s * 512;
 #pragma unroll
-        for (int nt = 0; nt < kLmNT; ++nt) dst[nt] = ld16_stream(p + nt * kLmKS * 512);
+        for (int nt = 0; nt < kLmNT; ++nt)
+            dst[nt] = SHARED ? ld16(p + nt * kLmKS * 512) : ld16_stream(p + nt * kLmKS * 512);
     };
 
     f32x4 acc[MT][kLmNT];
@@ -246,10 +249,14 @@ static int n_vtiles(int V) { return (V + kLmVocabPerWg - 1) / kLmVocabPerWg; }
 template <int MT>
 static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
                          float* pv, int* pi, hipStream_t st) {
-    int grid = n_vt * n_rg;
-    if (n_rg > 1) grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((lm_head_tile_kernel<MT>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
-                       H, V, n_vt, n_rg, pv, pi);
+    if (n_rg == 1) {
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, false>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden, w, R,
+                           H, V, n_vt, n_rg, pv, pi);
+    } else if constexpr (MT >= 5) {   // several row groups always have >= 5 tiles each
+        const int grid = (n_vt * n_rg + 7) / 8 * 8;
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, true>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
+                           H, V, n_vt, n_rg, pv, pi);
+    }
 }
 
 }  // namespace sv
@@ -298,9 +305,10 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
     const size_t n = (size_t)n_vt * R;
     float* pv = static_cast<float*>(workspace);
     int* pi = reinterpret_cast<int*>(static_cast<char*>(workspace) + ((n * sizeof(float) + 255) & ~(size_t)255));
+    // row groups of at most kLmMaxMT 16-row tiles, balanced (160 rows: 2 x 80)
     const int mtiles = (R + 15) / 16;
-    const int MT = mtiles < kLmMaxMT ? mtiles : kLmMaxMT;
-    const int n_rg = (mtiles + MT - 1) / MT;
+    const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
+    const int MT = (mtiles + n_rg - 1) / n_rg;
     if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_argmax: grid too large");
     hipStream_t st = (hipStream_t)stream;
     switch (MT) {
