@@ -6,9 +6,9 @@
 // key columns 4*(t % 32) .. +3 of the sixteen value rows (t / 32) + 8*i, so every
 // row of S is spread over 32 lanes of one half-wave and each store instruction of
 // a wave writes two whole rows (1 KB contiguous). Per token:
-//   u  = S k_t                     (half-wave reduction)
+//   u  = S k_t                     (half-wave reduce-scatter, then a broadcast per row)
 //   S <- a_t S + (b_t v_t - a_t b_t u) k_t^T     (= a_t S (I - b_t k k^T) + b_t v k^T)
-//   o_t = S (q_scale q_t)          (half-wave reduction)
+//   o_t = S (q_scale q_t)          (half-wave reduce-scatter)
 // and S_t is written to the record (mode 1/3) and, at t = L, to the state (mode 3).
 // Iteration t does the same arithmetic whatever T is, so S_L of a T-token scan
 // equals the final state of an L-token scan bit for bit (memra linear_attn_verify_t:
@@ -20,20 +20,49 @@ namespace sv {
 
 constexpr int kDk = 128, kDv = 128;
 
-__device__ __forceinline__ float half_wave_sum(float x) {
+// Reduce-scatter of 16 per-row partial sums over the 32 lanes of a half-wave:
+// at distances 16, 8, 4, 2 each lane keeps half of its remaining rows and adds the
+// partner's partials of those rows; a final exchange at distance 1 completes the
+// sum. Lane l of the half-wave ends with the full sum of row (l / 2); 16 shuffles
+// instead of 5 per row. The order of the additions is fixed.
+__device__ __forceinline__ float reduce_scatter16(const float (&p)[16], int c32) {
+    float a8[8], a4[4], a2[2];
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) x += __shfl_xor(x, d);
-    return x;
+    for (int i = 0; i < 8; ++i) {
+        const bool hi = c32 & 16;
+        a8[i] = (hi ? p[8 + i] : p[i]) + __shfl_xor(hi ? p[i] : p[8 + i], 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool hi = c32 & 8;
+        a4[i] = (hi ? a8[4 + i] : a8[i]) + __shfl_xor(hi ? a8[i] : a8[4 + i], 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const bool hi = c32 & 4;
+        a2[i] = (hi ? a4[2 + i] : a4[i]) + __shfl_xor(hi ? a4[i] : a4[2 + i], 4);
+    }
+    const bool hi = c32 & 2;
+    const float a1 = (hi ? a2[1] : a2[0]) + __shfl_xor(hi ? a2[0] : a2[1], 2);
+    return a1 + __shfl_xor(a1, 1);
 }
 
-__global__ __launch_bounds__(256) void delta_scan_kernel(
+// Tokens whose q/k/v/a/b are staged in LDS per round (fp32, 24.6 KB), so the scan
+// runs without waiting on global loads between tokens.
+constexpr int kTokChunk = 16;
+
+// At most 128 VGPRs: four workgroups per CU, so a launch of B*Hd <= 4 * CUs
+// workgroups (the 32 x 32 hybrid workload on 256 CUs) is resident at once.
+__global__ __launch_bounds__(256, 3) void delta_scan_kernel(
     int mode, const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, float q_scale, float* state,
     float* __restrict__ rec, const int32_t* __restrict__ L, int T, int Hd, u16* __restrict__ o) {
-    __shared__ float sk[kDk], sq[kDk], sv[kDv];
+    __shared__ __attribute__((aligned(16))) float sk[kTokChunk][kDk], sq[kTokChunk][kDk], sv[kTokChunk][kDv];
+    __shared__ float sa[kTokChunk], sb[kTokChunk];
     const int sh = blockIdx.x;
     const int s = sh / Hd, h = sh % Hd;
     const int tid = threadIdx.x, c32 = tid % 32, rg = tid / 32;
+    const int lane_base = tid % kWave - c32;     // first lane of this half-wave
     const int j0 = 4 * c32;
     constexpr int NR = kDv / 8;  // rows per thread
     float S[NR][4];
@@ -51,52 +80,76 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(
         Ls = L[s];
         Ls = Ls < 0 ? 0 : (Ls > T ? T : Ls);
     }
-    for (int t = 0; t < T; ++t) {
-        const size_t th = ((size_t)s * T + t) * Hd + h;
-        __syncthreads();
-        if (tid < kDk) {
-            sk[tid] = bf2f(k[th * kDk + tid]);
-            sq[tid] = q_scale * bf2f(q[th * kDk + tid]);
-        } else if (tid - kDk < kDv) {
-            sv[tid - kDk] = bf2f(v[th * kDv + tid - kDk]);
+    for (int tc = 0; tc < T; tc += kTokChunk) {
+        const int nt = min(kTokChunk, T - tc);
+        __syncthreads();   // the previous round's values are no longer read
+        // stage: per token 3 x 16 chunks of 8 bf16 (k, q, v), and a_t, b_t
+        for (int c = tid; c < nt * 48; c += 256) {
+            const int tok = c / 48, part = c % 48, which = part / 16, off = (part % 16) * 8;
+            const size_t th = ((size_t)s * T + tc + tok) * Hd + h;
+            const u16* src = (which == 0 ? k : which == 1 ? q : v) + th * kDk + off;
+            const uint4 x = ld16(src);
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = bf2f((u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu)));
+            float* dst = which == 0 ? &sk[tok][off] : which == 1 ? &sq[tok][off] : &sv[tok][off];
+            const float sc = which == 1 ? q_scale : 1.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = which == 1 ? sc * f[e] : f[e];
+        }
+        if (tid < nt) {
+            const size_t th = ((size_t)s * T + tc + tid) * Hd + h;
+            sa[tid] = a[th];
+            sb[tid] = b[th];
         }
         __syncthreads();
-        const float at = a[th], bt = b[th];
-        float kj[4], qj[4];
+        for (int tt = 0; tt < nt; ++tt) {
+            const int t = tc + tt;
+            const size_t th = ((size_t)s * T + t) * Hd + h;
+            const float at = sa[tt], bt = sb[tt];
+            float kj[4], qj[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kj[e] = sk[j0 + e];
-            qj[e] = sq[j0 + e];
-        }
-        float orow = 0.f;
+            for (int e = 0; e < 4; ++e) {
+                kj[e] = sk[tt][j0 + e];
+                qj[e] = sq[tt][j0 + e];
+            }
+            // u = S k (row i of this half-wave: value row rg + 8 i)
+            float part[NR];
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            float u = S[i][0] * kj[0];
-            u = fmaf(S[i][1], kj[1], u);
-            u = fmaf(S[i][2], kj[2], u);
-            u = fmaf(S[i][3], kj[3], u);
-            u = half_wave_sum(u);
-            const float wv = bt * (sv[rg + 8 * i] - at * u);
+            for (int i = 0; i < NR; ++i) {
+                float u = S[i][0] * kj[0];
+                u = fmaf(S[i][1], kj[1], u);
+                u = fmaf(S[i][2], kj[2], u);
+                part[i] = fmaf(S[i][3], kj[3], u);
+            }
+            const float u_mine = reduce_scatter16(part, c32);   // row c32 / 2
+            // S <- a S + (b v - a b u) k^T, then the partials of o = S q
+            const int hbase = lane_base;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[i][e] = fmaf(wv, kj[e], at * S[i][e]);
-            float ov = S[i][0] * qj[0];
-            ov = fmaf(S[i][1], qj[1], ov);
-            ov = fmaf(S[i][2], qj[2], ov);
-            ov = fmaf(S[i][3], qj[3], ov);
-            ov = half_wave_sum(ov);
-            if (c32 == i) orow = ov;
-        }
-        if (o && c32 < NR) o[th * kDv + rg + 8 * c32] = f2bf(orow);
-        if (mode & SPEC_DELTA_RECORD) {
-            float* dst = rec + th * kDv * kDk;
+            for (int i = 0; i < NR; ++i) {
+                const float u = __shfl(u_mine, hbase + 2 * i);
+                const float wv = bt * (sv[tt][rg + 8 * i] - at * u);
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                *reinterpret_cast<f32x4*>(dst + (rg + 8 * i) * kDk + j0) = f32x4{S[i][0], S[i][1], S[i][2], S[i][3]};
-        }
-        if (Ls == t + 1) {
+                for (int e = 0; e < 4; ++e) S[i][e] = fmaf(wv, kj[e], at * S[i][e]);
+                float ov = S[i][0] * qj[0];
+                ov = fmaf(S[i][1], qj[1], ov);
+                ov = fmaf(S[i][2], qj[2], ov);
+                part[i] = fmaf(S[i][3], qj[3], ov);
+            }
+            const float o_mine = reduce_scatter16(part, c32);   // row c32 / 2
+            if (o && (c32 & 1) == 0) o[th * kDv + rg + 8 * (c32 >> 1)] = f2bf(o_mine);
+            if (mode & SPEC_DELTA_RECORD) {
+                float* dst = rec + th * kDv * kDk;
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                *reinterpret_cast<f32x4*>(st + (rg + 8 * i) * kDk + j0) = f32x4{S[i][0], S[i][1], S[i][2], S[i][3]};
+                for (int i = 0; i < NR; ++i)
+                    *reinterpret_cast<f32x4*>(dst + (rg + 8 * i) * kDk + j0) = f32x4{S[i][0], S[i][1], S[i][2], S[i][3]};
+            }
+            if (Ls == t + 1) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i)
+                    *reinterpret_cast<f32x4*>(st + (rg + 8 * i) * kDk + j0) = f32x4{S[i][0], S[i][1], S[i][2], S[i][3]};
+            }
         }
     }
 }
