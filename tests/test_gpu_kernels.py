@@ -256,7 +256,8 @@ def test_accept_golden_cases(dev):
 
 
 @pytest.mark.parametrize("B,kmax,use_d2t", [(1, 3, False), (16, 4, False), (64, 6, False), (8, 6, True),
-                                            (300, 9, True), (5, 70, False), (2000, 3, False)])
+                                            (300, 9, True), (5, 70, False), (2000, 3, False),
+                                            (8192, 2, False), (3, 1024, True)])
 def test_accept_random_vs_oracle(dev, B, kmax, use_d2t):
     rng = np.random.default_rng(B * 7 + kmax)
     V = 5000
@@ -339,7 +340,7 @@ def _delta_gpu(d, dev, mode, L=None, state=None):
     return st, rec, o
 
 
-@pytest.mark.parametrize("B,T,Hd", [(1, 1, 1), (2, 5, 3), (3, 7, 2)])
+@pytest.mark.parametrize("B,T,Hd", [(1, 1, 1), (2, 5, 3), (3, 7, 2), (2, 37, 2), (1, 64, 1)])
 def test_delta_record_vs_oracle(dev, B, T, Hd):
     d = synth.make_delta_inputs(seed=B + T, B=B, T=T, Hd=Hd)
     st, rec, o = _delta_gpu(d, dev, 1)
@@ -367,11 +368,13 @@ def test_delta_rollback_modes(dev):
         assert torch.equal(st3[s].cpu(), want), s
 
 
-def test_delta_record_is_prefix_invariant(dev):
-    """S_L of a T-token scan equals the last state of an L-token scan, bit for bit."""
-    d = synth.make_delta_inputs(seed=12, B=2, T=5, Hd=2)
+@pytest.mark.parametrize("T,Ls", [(5, (1, 2, 3, 4)), (20, (1, 15, 16, 17))])
+def test_delta_record_is_prefix_invariant(dev, T, Ls):
+    """S_L of a T-token scan equals the last state of an L-token scan, bit for bit (also
+    across the 16-token rounds in which the scan stages its inputs)."""
+    d = synth.make_delta_inputs(seed=12, B=2, T=T, Hd=2)
     _, rec, o = _delta_gpu(d, dev, 1)
-    for L in range(1, 5):
+    for L in Ls:
         e = synth.DeltaInputs(d.B, L, d.Hd, d.dk, d.dv, d.q[:, :L].contiguous(), d.k[:, :L].contiguous(),
                               d.v[:, :L].contiguous(), d.a[:, :L].contiguous(), d.b[:, :L].contiguous(), d.state, d.L)
         _, rl, ol = _delta_gpu(e, dev, 1)
