@@ -66,7 +66,7 @@ class VerifyStep:
                                                                      x.page_table.shape[1]), dev)
         self.argmax = torch.empty(x.R, dtype=torch.int32, device=dev)
         self.maxval = torch.empty(x.R, dtype=torch.float32, device=dev)
-        self.lm_ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(x.R, wl.H, wl.V), dev)
+        self.lm_ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(x.R, wl.H, wl.V), dev, zero=True)
         self.d2t = None if x.d2t is None else i32(x.d2t, dev)
         e = lambda: torch.empty(self.B, dtype=torch.int32, device=dev)
         self.pos_out, self.acc_len, self.n_emit, self.next_tok, self.acc_status = e(), e(), e(), e(), e()
@@ -178,7 +178,7 @@ def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
     for R in (80, 160, 288, 512, 1024):
         h = torch.randn((R, wl.H), generator=g, device=dev).to(torch.bfloat16)
         am = torch.empty(R, dtype=torch.int32, device=dev)
-        ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, wl.H, wl.V), dev)
+        ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, wl.H, wl.V), dev, zero=True)
         sec = time_call(lambda: gdv.spec_lm_head_argmax(h, w_packed, wl.V, am, None, workspace_buf=ws), reps)
         tf = 2.0 * R * wl.H * wl.V / sec / 1e12
         gbs = lm_head_bytes(R, wl.H, wl.V) / sec / 1e9

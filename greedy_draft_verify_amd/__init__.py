@@ -117,8 +117,12 @@ def lm_head_argmax_workspace_bytes(R, H, V) -> int:
     return lib().spec_lm_head_argmax_workspace_bytes(R, H, V)
 
 
-def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+def workspace(nbytes: int, device="cuda", zero: bool = False) -> torch.Tensor:
+    """A workspace buffer; spec_lm_head_argmax needs one that is zero on first use."""
+    n = max(int(nbytes), 1)
+    if zero:
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, scale, out, seq_status,
@@ -174,7 +178,8 @@ def spec_lm_head_pack(w, w_packed=None, stream=None):
 
 def spec_lm_head_argmax(hidden, w_packed, V, argmax, maxval=None, workspace_buf=None, stream=None):
     """hidden [R,H] bf16, w_packed from spec_lm_head_pack (vocabulary V) -> argmax [R] int32,
-    maxval [R] fp32 (optional)."""
+    maxval [R] fp32 (optional). A workspace_buf must be zero on its first use (every call
+    leaves it zero) and must not be shared by calls that may overlap."""
     _want(hidden, torch.bfloat16, "hidden", 2)
     _want(w_packed, torch.bfloat16, "w_packed", 1)
     _want(argmax, torch.int32, "argmax", 1)
@@ -188,7 +193,7 @@ def spec_lm_head_argmax(hidden, w_packed, V, argmax, maxval=None, workspace_buf=
     if maxval is not None:
         _shape(maxval, (R,), "maxval")
     if workspace_buf is None:
-        workspace_buf = workspace(lm_head_argmax_workspace_bytes(R, H, V), hidden.device)
+        workspace_buf = workspace(lm_head_argmax_workspace_bytes(R, H, V), hidden.device, zero=True)
     rc = lib().spec_lm_head_argmax(_ptr(hidden), _ptr(w_packed), R, H, V, _ptr(argmax), _ptr(maxval),
                                    _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
     _check(rc, "spec_lm_head_argmax")

@@ -21,11 +21,12 @@
 // LDS, one K-block ahead. After the K loop each wave reduces its logits to the best
 // (value, index) per row with the order "larger value, then smaller index" (the
 // first-maximum rule of span-02 greedy_logprob), the workgroup merges its four
-// waves, and one record per (row, group) goes to the workspace.
-// lm_head_final_kernel: one workgroup per row merges that row's records with the
-// same order. The order is total, so the result does not depend on how the
-// reduction is grouped; each logit is one MFMA chain over K in a fixed order, so a
-// row's result does not depend on R or the row group.
+// waves and folds the result into one 64-bit key per row with an atomic maximum
+// (the key's unsigned order is that same order). A ticket counter finds the last
+// workgroup, which writes argmax/maxval from the keys and resets the workspace to
+// zero. The order is total, so the result does not depend on which workgroup
+// finishes when; each logit is one MFMA chain over K in a fixed order, so a row's
+// result does not depend on R or the row group.
 #include <type_traits>
 
 #include "common.h"
@@ -79,12 +80,27 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
+// (value, index) as one 64-bit key whose unsigned order is the order above: the high
+// half maps the fp32 value monotonically (-0 taken as +0, like the comparison; a
+// workgroup's best is never NaN), the low half is ~index. Key 0 is below every key.
+__device__ __forceinline__ unsigned long long pack_best(Best b) {
+    const uint32_t u = __float_as_uint(b.v == 0.f ? 0.f : b.v);
+    const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (uint32_t)~(uint32_t)b.i;
+}
+
+__device__ __forceinline__ float unpack_value(unsigned long long key) {
+    const uint32_t hi = (uint32_t)(key >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+
 // SHARED: other row groups re-read this vocabulary group's W through the XCD's L2,
 // so W is loaded with the default cache policy instead of as a stream.
 template <int MT, bool SHARED>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
-    int n_rg, float* __restrict__ part_v, int* __restrict__ part_i) {
+    int n_rg, unsigned long long* __restrict__ keys, unsigned int* __restrict__ ticket,
+    int32_t* __restrict__ argmax, float* __restrict__ maxval) {
     constexpr int HSTR = kLmKB + 8;                            // LDS row stride (elements)
     constexpr int HCH = 16 * MT * kLmKB / 8 / kLmThreads;     // hidden chunks per thread per K-block
     static_assert(HCH * kLmThreads * 8 == 16 * MT * kLmKB, "hidden staging must tile evenly");
@@ -201,61 +217,41 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
             const Best o = wbest[wv][tid];
             if (better(o.v, o.i, b.v, b.i)) b = o;
         }
-        part_v[(size_t)(r0 + tid) * n_vt + vt] = b.v;
-        part_i[(size_t)(r0 + tid) * n_vt + vt] = b.i;
+        // the returned value is consumed, so the wave waits until the update is performed
+        const unsigned long long prev = atomicMax(keys + r0 + tid, pack_best(b));
+        asm volatile("" : : "v"(prev));
     }
-}
-
-__global__ __launch_bounds__(256) void lm_head_final_kernel(const float* __restrict__ part_v,
-                                                            const int* __restrict__ part_i, int R,
-                                                            int n_vt, int32_t* __restrict__ argmax,
-                                                            float* __restrict__ maxval) {
-    __shared__ Best sb[4];
-    const int r = blockIdx.x, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    const float* rv = part_v + (size_t)r * n_vt;
-    const int* ri = part_i + (size_t)r * n_vt;
-    for (int t = tid; t < n_vt; t += 256) {
-        const float v = rv[t];
-        const int i = ri[t];
-        if (better(v, i, bv, bi)) {
-            bv = v;
-            bi = i;
-        }
-    }
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const float ov = __shfl_xor(bv, d);
-        const int oi = __shfl_xor(bi, d);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    if (lane == 0) sb[wave] = Best{bv, bi};
+    // The last workgroup to finish turns the keys into the outputs and leaves the
+    // workspace zero for the next call. Keys and ticket are only touched by atomics,
+    // which are ordered where they are performed, so no cache flush is needed: every
+    // workgroup's key updates are performed before its ticket, and the last
+    // workgroup reads the keys after its own ticket.
+    __shared__ unsigned int s_last;
     __syncthreads();
-    if (tid == 0) {
-        Best b = sb[0];
-        for (int wv = 1; wv < 4; ++wv)
-            if (better(sb[wv].v, sb[wv].i, b.v, b.i)) b = sb[wv];
-        argmax[r] = b.i;
-        if (maxval) maxval[r] = b.v;
+    if (tid == 0) s_last = atomicAdd(ticket, 1u) == (unsigned int)(n_vt * n_rg - 1);
+    __syncthreads();
+    if (!s_last) return;
+    for (int r = tid; r < R; r += kLmThreads) {
+        const unsigned long long key = atomicExch(keys + r, 0ull);
+        argmax[r] = (int32_t)~(uint32_t)key;
+        if (maxval) maxval[r] = unpack_value(key);
     }
+    if (tid == 0) atomicExch(ticket, 0u);
 }
 
 static int n_vtiles(int V) { return (V + kLmVocabPerWg - 1) / kLmVocabPerWg; }
 
 template <int MT>
 static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
-                         float* pv, int* pi, hipStream_t st) {
+                         unsigned long long* keys, unsigned int* ticket, int32_t* argmax, float* maxval,
+                         hipStream_t st) {
     if (n_rg == 1) {
         hipLaunchKernelGGL((lm_head_tile_kernel<MT, false>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden, w, R,
-                           H, V, n_vt, n_rg, pv, pi);
+                           H, V, n_vt, n_rg, keys, ticket, argmax, maxval);
     } else if constexpr (MT >= 5) {   // several row groups always have >= 5 tiles each
         const int grid = (n_vt * n_rg + 7) / 8 * 8;
         hipLaunchKernelGGL((lm_head_tile_kernel<MT, true>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
-                           H, V, n_vt, n_rg, pv, pi);
+                           H, V, n_vt, n_rg, keys, ticket, argmax, maxval);
     }
 }
 
@@ -283,8 +279,7 @@ int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_pac
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
     if (R < 1 || V < 1) return 0;
-    const size_t n = (size_t)sv::n_vtiles(V) * R;
-    return ((n * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(int);
+    return 256 + (size_t)R * sizeof(unsigned long long);   // ticket (padded), one key per row
 }
 
 int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
@@ -302,9 +297,8 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(SPEC_EWORKSPACE, "spec_lm_head_argmax: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, need);
     const int n_vt = n_vtiles(V);
-    const size_t n = (size_t)n_vt * R;
-    float* pv = static_cast<float*>(workspace);
-    int* pi = reinterpret_cast<int*>(static_cast<char*>(workspace) + ((n * sizeof(float) + 255) & ~(size_t)255));
+    unsigned int* ticket = static_cast<unsigned int*>(workspace);
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
     // row groups of at most kLmMaxMT 16-row tiles, balanced (160 rows: 2 x 80)
     const int mtiles = (R + 15) / 16;
     const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
@@ -312,18 +306,16 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
     if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_argmax: grid too large");
     hipStream_t st = (hipStream_t)stream;
     switch (MT) {
-        case 1: launch_tiles<1>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 2: launch_tiles<2>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 3: launch_tiles<3>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 4: launch_tiles<4>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 5: launch_tiles<5>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 6: launch_tiles<6>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        case 7: launch_tiles<7>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
-        default: launch_tiles<8>(hidden, w, R, H, V, n_vt, n_rg, pv, pi, st); break;
+        case 1: launch_tiles<1>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 2: launch_tiles<2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 3: launch_tiles<3>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 4: launch_tiles<4>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 5: launch_tiles<5>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 6: launch_tiles<6>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        case 7: launch_tiles<7>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        default: launch_tiles<8>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
     }
-    SV_LAUNCH_CHECK("spec_lm_head_argmax(tiles)");
-    hipLaunchKernelGGL(lm_head_final_kernel, dim3(R), dim3(256), 0, st, pv, pi, R, n_vt, argmax, maxval);
-    SV_LAUNCH_CHECK("spec_lm_head_argmax(final)");
+    SV_LAUNCH_CHECK("spec_lm_head_argmax");
     return SPEC_OK;
 }
 

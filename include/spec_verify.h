@@ -149,7 +149,11 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
  * argmax [R] int32, maxval [R] fp32.
  * Limits: R >= 1, H % 256 == 0, 1 <= V < 2^31 - 1; 16-byte aligned hidden,
  * w_packed, workspace. NaN logits never win. workspace: at least
- * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes.
+ * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes (a ticket counter and one
+ * 64-bit key per row, through which the workgroups merge their per-row maxima). It
+ * must be all zero the first time it is used; every call leaves it zero again, so a
+ * workspace is zero-filled once and then reused (also across HIP graph replays).
+ * Calls that may overlap in time must not share a workspace.
  * ------------------------------------------------------------------------- */
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V);
 int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,

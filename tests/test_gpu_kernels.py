@@ -198,6 +198,26 @@ def test_lm_head_pack_is_the_documented_permutation(dev):
     assert np.array_equal(wp.reshape(exp.shape), exp)
 
 
+def test_lm_head_workspace_reuse(dev):
+    """One zero-filled workspace serves consecutive calls of different sizes; every call
+    leaves it zero and gives the same bytes as a call with a fresh workspace."""
+    import greedy_draft_verify_amd as gdv
+    rng = np.random.default_rng(31)
+    H, V = 512, 2000
+    w = torch.from_numpy((rng.standard_normal((V, H)) / math.sqrt(H)).astype(np.float32)).to(torch.bfloat16)
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(300, H, V), dev, zero=True)
+    for R in (300, 7, 160, 300, 1):
+        h = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(torch.bfloat16).to(dev)
+        am, mv = torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.float32, device=dev)
+        gdv.spec_lm_head_argmax(h, wp, V, am, mv, workspace_buf=ws)
+        am2, mv2 = torch.empty_like(am), torch.empty_like(mv)
+        gdv.spec_lm_head_argmax(h, wp, V, am2, mv2)
+        torch.cuda.synchronize()
+        assert torch.equal(am, am2) and torch.equal(mv.view(torch.int32), mv2.view(torch.int32)), R
+        assert int(ws.count_nonzero()) == 0, f"workspace not left zero after R={R}"
+
+
 def test_lm_head_tiny_workload(dev):
     x = synth.make_verify_inputs("tiny", seed=0)
     g, mv = gpu_lm_head(x.hidden, x.w, dev)
