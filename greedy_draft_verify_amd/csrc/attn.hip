@@ -49,6 +49,11 @@ struct SeqInfo {
     int32_t valid;  // 1 if the sequence passed validation
 };
 
+struct RowRec {
+    int32_t p;      // position of the row
+    int32_t nc;     // splits the combine merges for it (0: its sequence is skipped)
+};
+
 // In-block offsets of token t, channel d (see the pool format above).
 __device__ __forceinline__ int k_off(int t, int d) {
     return (d >> 5) * 512 + ((d & 31) >> 3) * 128 + t * 8 + (d & 7);
@@ -58,28 +63,64 @@ __device__ __forceinline__ int v_off(int t, int d) {
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kPrepItems = 4;   // append chunks per thread requested before validation ends
+
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, u16* __restrict__ k_pool,
     u16* __restrict__ v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int kmax, int B, int R, int Hq,
-    int Hkv, int D, SeqInfo* __restrict__ info, int32_t* __restrict__ row_seq, int32_t* __restrict__ status) {
-    __shared__ long long s_before[4], s_total[4];
+    int Hkv, int D, int split, SeqInfo* __restrict__ info, RowRec* __restrict__ rows,
+    int32_t* __restrict__ packing_ok, int32_t* __restrict__ status) {
     __shared__ int s_flags[4];
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    // one round of independent loads: this sequence's (pos, k), every k for the row
-    // packing, and the page ids the sequence needs
     const int ks = k[s];
     const int P = pos[s];
+    // Every wave forms the row packing on its own (each k is read by every wave, from
+    // cache), so the row offset is known without a barrier.
     long long before = 0, total = 0;
-    int flags = 0;
-    for (int i = tid; i < B; i += 256) {
+    int rowbad = 0;
+    for (int i = lane; i < B; i += kWave) {
         const long long kk = k[i];
         total += kk + 1;
         if (i < s) before += kk + 1;
-        if (kk < 0) flags |= SPEC_STATUS_BAD_ROWS;
+        rowbad |= kk < 0;
     }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        before += __shfl_xor(before, d);
+        total += __shfl_xor(total, d);
+        rowbad |= __shfl_xor(rowbad, d);
+    }
+    const bool packed = !rowbad && total == (long long)R;
+    const int off = (int)before;
     const bool pos_ok = P >= 0 && (ks < 0 || ((long long)P + ks) / kPage < max_pages);
+    int flags = (!packed || ks > kmax) ? SPEC_STATUS_BAD_ROWS : 0;
     if (!pos_ok) flags |= SPEC_STATUS_BAD_POS;
+    // One round of loads: the page ids the sequence needs (validation) and this
+    // thread's first append chunks (page id, new K row chunk, new V row chunk).
+    const bool can_append = packed && pos_ok && ks >= 0;
+    const int dch = D / 8;
+    const int n_items = can_append ? (ks + 1) * Hkv * dch : 0;
+    int32_t it_page[kPrepItems];
+    uint4 it_k[kPrepItems], it_v[kPrepItems];
+    auto item_src = [&](int i, int& j, int& hk, int& dc) {
+        dc = i % dch;
+        const int rest = i / dch;
+        hk = rest % Hkv;
+        j = rest / Hkv;
+    };
+#pragma unroll
+    for (int u = 0; u < kPrepItems; ++u) {
+        const int i = tid + u * 256;
+        if (i < n_items) {
+            int j, hk, dc;
+            item_src(i, j, hk, dc);
+            const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
+            it_page[u] = page_table[(size_t)s * max_pages + (P + j) / kPage];
+            it_k[u] = ld16(k_new + src);
+            it_v[u] = ld16(v_new + src);
+        }
+    }
     if (pos_ok && ks >= 0) {
         const int last_page = (int)(((long long)P + ks) / kPage);
         for (int pg = tid; pg <= last_page; pg += 256) {
@@ -88,49 +129,43 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         }
     }
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        before += __shfl_xor(before, d);
-        total += __shfl_xor(total, d);
-        flags |= __shfl_xor(flags, d);
-    }
-    if (lane == 0) {
-        s_before[wave] = before;
-        s_total[wave] = total;
-        s_flags[wave] = flags;
-    }
+    for (int d = 32; d > 0; d >>= 1) flags |= __shfl_xor(flags, d);
+    if (lane == 0) s_flags[wave] = flags;
     __syncthreads();
-    int bits = s_flags[0] | s_flags[1] | s_flags[2] | s_flags[3];
-    if (s_total[0] + s_total[1] + s_total[2] + s_total[3] != (long long)R || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
-    const int off = (int)(s_before[0] + s_before[1] + s_before[2] + s_before[3]);
+    const int bits = s_flags[0] | s_flags[1] | s_flags[2] | s_flags[3];
     if (tid == 0) {
         status[s] = bits;
         info[s].off = off;
         info[s].valid = bits == 0;
+        if (s == 0) *packing_ok = packed;
     }
-    // row -> sequence map for the combine (only when the packing is defined; otherwise
-    // every sequence is invalid and the combine writes nothing)
-    if (!(bits & SPEC_STATUS_BAD_ROWS))
-        for (int j = tid; j <= ks; j += 256) row_seq[off + j] = s;
+    // per-row record for the combine (only when the packing is defined; otherwise the
+    // combine writes nothing)
+    if (packed)
+        for (int j = tid; j <= ks; j += 256) rows[off + j] = RowRec{P + j, bits ? 0 : (P + j) / split + 1};
     if (bits) return;
-    // append: 8 channels (one 16-byte chunk of the row) per item
-    const int dch = D / 8;
-    const int n = (ks + 1) * Hkv * dch;
-    for (int i = tid; i < n; i += 256) {
-        const int dc = i % dch;
-        const int rest = i / dch;
-        const int hk = rest % Hkv;
-        const int j = rest / Hkv;
-        const int p = P + j;
-        const int64_t page = page_table[(size_t)s * max_pages + p / kPage];
-        const int t = p % kPage;
-        const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
-        const size_t blk = (size_t)(page * Hkv + hk) * (kPage * D);
-        st16(k_pool + blk + k_off(t, dc * 8), ld16(k_new + src));   // 8 channels contiguous
-        const uint4 vv = ld16(v_new + src);
+    // append: 8 channels (one 16-byte chunk of a row) per item
+    auto store_item = [&](int i, int32_t page, uint4 kv, uint4 vv) {
+        int j, hk, dc;
+        item_src(i, j, hk, dc);
+        const int t = (P + j) % kPage;
+        const size_t blk = ((size_t)page * Hkv + hk) * (kPage * D);
+        st16(k_pool + blk + k_off(t, dc * 8), kv);   // 8 channels contiguous
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             v_pool[blk + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+    };
+#pragma unroll
+    for (int u = 0; u < kPrepItems; ++u) {
+        const int i = tid + u * 256;
+        if (i < n_items) store_item(i, it_page[u], it_k[u], it_v[u]);
+    }
+    for (int i = tid + kPrepItems * 256; i < n_items; i += 256) {
+        int j, hk, dc;
+        item_src(i, j, hk, dc);
+        const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
+        store_item(i, page_table[(size_t)s * max_pages + (P + j) / kPage], ld16(k_new + src), ld16(v_new + src));
     }
 }
 
@@ -361,23 +396,32 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ k, const SeqInfo* __restrict__ info,
-    const int32_t* __restrict__ row_seq, int B, int R, int Hq, int split, int n_splits,
+    const RowRec* __restrict__ rows, const int32_t* __restrict__ packing_ok, int R, int Hq, int n_splits,
     const float2* __restrict__ part_ml, const float* __restrict__ part_o, u16* __restrict__ out) {
     constexpr int PER = D / kWave;
+    constexpr int kGroup = 8;    // splits whose partials are loaded at once
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const long long item = (long long)blockIdx.x * 4 + wave;
     if (item >= (long long)R * Hq) return;
     const int r = (int)(item / Hq), h = (int)(item % Hq);
-    const int sq = row_seq[r];
-    if (sq < 0 || sq >= B) return;               // packing undefined: every sequence is invalid
-    const SeqInfo si = info[sq];
-    if (!si.valid) return;
-    const int j = r - si.off;
-    if (j < 0 || j > k[sq]) return;
-    const int p = pos[sq] + j;
-    const int nc = p / split + 1;
+    const int ok = *packing_ok;
+    const RowRec rr = rows[r];
+    if (!ok || rr.nc <= 0) return;               // packing undefined, or the sequence is skipped
+    const int nc = rr.nc;
     const size_t base = ((size_t)r * Hq + h) * n_splits;
+    float2 ml[kGroup];
+    float po[kGroup][PER];
+    auto load_group = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int c = c0 + u < nc ? c0 + u : nc - 1;
+            ml[u] = part_ml[base + c];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) po[u][e] = part_o[(base + c) * D + e * kWave + lane];
+        }
+    };
+    // the first group's partials are requested in the same round as the maxima
+    load_group(0);
     float mx = -INFINITY;
     for (int c = lane; c < nc; c += kWave) mx = fmaxf(mx, part_ml[base + c].x);
 #pragma unroll
@@ -386,18 +430,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float L = 0.f;
-    // splits merged in ascending order; each group of 8 is loaded at once first
-    constexpr int kGroup = 8;
+    // splits merged in ascending order
     for (int c0 = 0; c0 < nc; c0 += kGroup) {
-        float2 ml[kGroup];
-        float po[kGroup][PER];
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const int c = c0 + u < nc ? c0 + u : nc - 1;
-            ml[u] = part_ml[base + c];
-#pragma unroll
-            for (int e = 0; e < PER; ++e) po[u][e] = part_o[(base + c) * D + e * kWave + lane];
-        }
+        if (c0 > 0) load_group(c0);
         // consume every loaded value here so that the group's loads are all issued first
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
@@ -426,15 +461,16 @@ static int64_t split_count(int32_t max_pages, int32_t split) {
 }
 
 struct AttnWs {
-    size_t info_off, rows_off, ml_off, o_off, total;
+    size_t info_off, flag_off, rows_off, ml_off, o_off, total;
 };
 
 static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_t n_splits) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     AttnWs w;
     w.info_off = 0;
-    w.rows_off = up(sizeof(SeqInfo) * (size_t)B);
-    w.ml_off = w.rows_off + up(sizeof(int32_t) * (size_t)R);
+    w.flag_off = up(sizeof(SeqInfo) * (size_t)B);
+    w.rows_off = w.flag_off + 256;
+    w.ml_off = w.rows_off + up(sizeof(RowRec) * (size_t)R);
     w.o_off = w.ml_off + up(sizeof(float2) * (size_t)R * Hq * n_splits);
     w.total = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
     return w;
@@ -443,16 +479,16 @@ static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_
 template <int D>
 static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, const int32_t* pt,
                         int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
-                        const int32_t* row_seq, int B, int R, int Hq, int Hkv, float scale, int split, int n_splits,
-                        float2* ml, float* po, u16* out, hipStream_t st) {
-    const int rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
-    const int mgroups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
+                        const RowRec* rows, const int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
+                        int split, int n_splits, float2* ml, float* po, u16* out, hipStream_t st) {
+    const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
+    const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
     hipLaunchKernelGGL(attn_split_kernel<D>, grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
                        max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po);
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
-                       pos, k, info, row_seq, B, R, Hq, split, n_splits, ml, po, out);
+                       rows, packing_ok, R, Hq, n_splits, ml, po, out);
 }
 
 }  // namespace sv
@@ -508,17 +544,19 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
         return fail(SPEC_EWORKSPACE, "spec_verify_attn: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, lay.total);
     char* ws = static_cast<char*>(workspace);
     SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + lay.info_off);
-    int32_t* row_seq = reinterpret_cast<int32_t*>(ws + lay.rows_off);
+    int32_t* packing_ok = reinterpret_cast<int32_t*>(ws + lay.flag_off);
+    RowRec* rows = reinterpret_cast<RowRec*>(ws + lay.rows_off);
     float2* ml = reinterpret_cast<float2*>(ws + lay.ml_off);
     float* po = reinterpret_cast<float*>(ws + lay.o_off);
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(attn_prep_kernel, dim3(B), dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, info, row_seq, seq_status);
+                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, split, info, rows, packing_ok,
+                       seq_status);
     SV_LAUNCH_CHECK("spec_verify_attn(prep)");
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, row_seq, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
     }
     SV_LAUNCH_CHECK("spec_verify_attn");
     return SPEC_OK;
