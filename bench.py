@@ -144,7 +144,9 @@ def time_call(f, reps: int, warmup: int = 3) -> float:
 def delta_leg(dev, reps: int):
     """Gated DeltaNet verify with per-token record and fused rollback (mode BOTH) on the
     hybrid workload: B=32, T=5, 32 heads, 128x128 fp32 state. Algorithmic bytes: S_0
-    read, every S_t recorded, q/k/v/a/b read, o written, S_L written for L > 0."""
+    read, every S_t recorded, q/k/v/a/b read, o written, S_L written for L > 0. Beside
+    it the input-stash pair: VERIFY (outputs only) and RESCAN (the committed prefix
+    re-run from the retained S_0)."""
     d = synth.make_delta_inputs(seed=0, device=dev)
     st_bytes = d.dv * d.dk * 4
     rec = torch.empty((d.B, d.T, d.Hd, d.dv, d.dk), dtype=torch.float32, device=dev)
@@ -161,11 +163,28 @@ def delta_leg(dev, reps: int):
                                                      rec, L, None)
     sec_r = time_call(restore, reps)
     byts_r = 2 * int((d.L > 0).sum()) * d.Hd * st_bytes
+    # input-stash alternative: verify writes outputs only; a partial accept re-runs the
+    # committed prefix from the retained S_0 (re-reads S_0, writes S_L)
+    s0 = d.state.clone()
+    ver = lambda: gdv.spec_delta_verify_rollback(gdv.DELTA_VERIFY, d.q, d.k, d.v, d.a, d.b, 1.0, s0, None, None, o)
+    sec_v = time_call(ver, reps)
+    byts_v = (n_sh * st_bytes + d.B * d.T * d.Hd * (2 * d.dk + d.dv) * 2 + d.B * d.T * d.Hd * 8
+              + d.B * d.T * d.Hd * d.dv * 2)
+    s5 = d.state.clone()
+    resc = lambda: gdv.spec_delta_verify_rollback(gdv.DELTA_RESCAN, d.q, d.k, d.v, d.a, d.b, 1.0, s5, None, L)
+    sec_s = time_call(resc, reps)
+    n_l = int((d.L > 0).sum())
+    byts_s = (2 * n_l * d.Hd * st_bytes + int(d.L.sum()) * d.Hd * ((2 * d.dk + d.dv) * 2 + 8))
     return {"workload": f"B={d.B} T={d.T} heads={d.Hd} state {d.dv}x{d.dk} fp32, L ~ U{{0..{d.T}}}",
             "verify_record_rollback_us": sec * 1e6, "algorithmic_bytes": byts, "achieved": gbs,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "bound": "hbm",
             "rollback_only_us": sec_r * 1e6, "rollback_only_bytes": byts_r,
-            "rollback_only_frac": byts_r / sec_r / 1e9 / HBM_PEAK_GBS}
+            "rollback_only_frac": byts_r / sec_r / 1e9 / HBM_PEAK_GBS,
+            "input_stash": {"verify_us": sec_v * 1e6, "verify_bytes": byts_v,
+                            "verify_frac": byts_v / sec_v / 1e9 / HBM_PEAK_GBS,
+                            "rescan_us": sec_s * 1e6, "rescan_bytes": byts_s,
+                            "rescan_frac": byts_s / sec_s / 1e9 / HBM_PEAK_GBS,
+                            "total_us": (sec_v + sec_s) * 1e6}}
 
 
 def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
@@ -351,9 +370,11 @@ def main():
         sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
         dl = extras["delta_roofline"]
         log(f"[bench] lm_head sweep: {sw}")
+        ist = dl["input_stash"]
         log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
             f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
-            f"{dl['rollback_only_us']:.1f} us")
+            f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
+            f"{ist['rescan_us']:.1f} us")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_PAGE_TOKENS = 16
 STATUS_BAD_PAGE, STATUS_BAD_POS, STATUS_BAD_ROWS, STATUS_BAD_TOKEN = 1, 2, 4, 8
-DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH = 1, 2, 3
+DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH, DELTA_VERIFY, DELTA_RESCAN = 1, 2, 3, 4, 5
 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_verify_attn_workspace_bytes", "spec_verify_attn",
@@ -226,14 +226,25 @@ def spec_greedy_accept(argmax, drafts, k, d2t, V, pos_in, pos_out, accept_len, n
 
 def spec_delta_verify_rollback(mode, q, k, v, a, b, q_scale, state, rec, L, o=None, stream=None):
     """q,k [B,T,Hd,dk], v [B,T,Hd,dv] bf16; a,b [B,T,Hd] fp32; state [B,Hd,dv,dk] fp32;
-    rec [B,T,Hd,dv,dk] fp32; L [B] int32 (None in mode 1); o [B,T,Hd,dv] bf16 or None."""
+    rec [B,T,Hd,dv,dk] fp32 (None in modes VERIFY/RESCAN); L [B] int32 (None in modes
+    RECORD/VERIFY); o [B,T,Hd,dv] bf16 or None."""
     _want(state, torch.float32, "state", 4)
-    _want(rec, torch.float32, "rec", 5)
-    B, T, Hd, dv, dk = rec.shape
-    _shape(state, (B, Hd, dv, dk), "state")
-    if mode & DELTA_RECORD:
+    scans = mode != DELTA_ROLLBACK
+    if scans:
         for t, n in ((q, "q"), (k, "k"), (v, "v")):
             _want(t, torch.bfloat16, n, 4)
+        B, T, Hd, dk = q.shape
+        dv = v.shape[3]
+    else:
+        _want(rec, torch.float32, "rec", 5)
+        B, T, Hd, dv, dk = rec.shape
+    _shape(state, (B, Hd, dv, dk), "state")
+    if rec is not None:
+        _want(rec, torch.float32, "rec", 5)
+        _shape(rec, (B, T, Hd, dv, dk), "rec")
+    elif mode in (DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH):
+        raise SpecError(f"spec_delta_verify_rollback: rec required in mode {mode}")
+    if scans:
         _want(a, torch.float32, "a", 3)
         _want(b, torch.float32, "b", 3)
         _shape(q, (B, T, Hd, dk), "q")

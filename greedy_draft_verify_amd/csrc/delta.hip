@@ -9,7 +9,8 @@
 //   u  = S k_t                     (half-wave reduce-scatter, then a broadcast per row)
 //   S <- a_t S + (b_t v_t - a_t b_t u) k_t^T     (= a_t S (I - b_t k k^T) + b_t v k^T)
 //   o_t = S (q_scale q_t)          (half-wave reduce-scatter)
-// and S_t is written to the record (mode 1/3) and, at t = L, to the state (mode 3).
+// and S_t is written to the record (modes 1, 3) and, at t = L, to the state (modes 3,
+// 5). Mode 4 writes only o; mode 5 runs only tokens 1..L and writes only S_L.
 // Iteration t does the same arithmetic whatever T is, so S_L of a T-token scan
 // equals the final state of an L-token scan bit for bit (memra linear_attn_verify_t:
 // one scan over T tokens equals T chained one-token steps).
@@ -65,6 +66,14 @@ __global__ __launch_bounds__(256, 3) void delta_scan_kernel(
     const int lane_base = tid % kWave - c32;     // first lane of this half-wave
     const int j0 = 4 * c32;
     constexpr int NR = kDv / 8;  // rows per thread
+    const bool record = mode == SPEC_DELTA_RECORD || mode == SPEC_DELTA_BOTH;
+    const bool write_o = o && mode != SPEC_DELTA_RESCAN;
+    int Ls = -1;
+    if (mode == SPEC_DELTA_BOTH || mode == SPEC_DELTA_RESCAN) {
+        Ls = L[s];
+        Ls = Ls < 0 ? 0 : (Ls > T ? T : Ls);
+    }
+    if (mode == SPEC_DELTA_RESCAN && Ls == 0) return;   // nothing committed: S_0 stays
     float S[NR][4];
     float* st = state + (size_t)sh * kDv * kDk;
 #pragma unroll
@@ -75,13 +84,9 @@ __global__ __launch_bounds__(256, 3) void delta_scan_kernel(
         S[i][2] = x[2];
         S[i][3] = x[3];
     }
-    int Ls = -1;
-    if (mode & SPEC_DELTA_ROLLBACK) {
-        Ls = L[s];
-        Ls = Ls < 0 ? 0 : (Ls > T ? T : Ls);
-    }
-    for (int tc = 0; tc < T; tc += kTokChunk) {
-        const int nt = min(kTokChunk, T - tc);
+    const int t_run = mode == SPEC_DELTA_RESCAN ? Ls : T;   // re-scan: only the committed tokens
+    for (int tc = 0; tc < t_run; tc += kTokChunk) {
+        const int nt = min(kTokChunk, t_run - tc);
         __syncthreads();   // the previous round's values are no longer read
         // stage: per token 3 x 16 chunks of 8 bf16 (k, q, v), and a_t, b_t
         for (int c = tid; c < nt * 48; c += 256) {
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(256, 3) void delta_scan_kernel(
                 part[i] = fmaf(S[i][3], qj[3], ov);
             }
             const float o_mine = reduce_scatter16(part, c32);   // row c32 / 2
-            if (o && (c32 & 1) == 0) o[th * kDv + rg + 8 * (c32 >> 1)] = f2bf(o_mine);
-            if (mode & SPEC_DELTA_RECORD) {
+            if (write_o && (c32 & 1) == 0) o[th * kDv + rg + 8 * (c32 >> 1)] = f2bf(o_mine);
+            if (record) {
                 float* dst = rec + th * kDv * kDk;
 #pragma unroll
                 for (int i = 0; i < NR; ++i)
@@ -178,15 +183,18 @@ int spec_delta_verify_rollback(int32_t mode, const spec_bf16* q, const spec_bf16
                                int32_t Hd, int32_t dk, int32_t dv, spec_bf16* o, void* stream) {
     using namespace sv;
     last_error().clear();
-    if (mode < 1 || mode > 3) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: mode=%d not in 1..3", mode);
+    if (mode < 1 || mode > 5) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: mode=%d not in 1..5", mode);
     if (dk != kDk || dv != kDv) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: dk=%d dv=%d (only 128 x 128)", dk, dv);
     if (B < 1 || Hd < 1 || T < 1 || T > 64) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: B=%d Hd=%d T=%d", B, Hd, T);
     if ((long long)B * Hd > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_delta_verify_rollback: B*Hd too large");
-    if (!state || !rec) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: null state or rec");
-    if ((mode & SPEC_DELTA_ROLLBACK) && !L) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: L required for rollback");
-    if ((mode & SPEC_DELTA_RECORD) && (!q || !k || !v || !a || !b))
-        return fail(SPEC_EINVAL, "spec_delta_verify_rollback: null q/k/v/a/b");
-    if (!aligned16(state) || !aligned16(rec)) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: state and rec must be 16-byte aligned");
+    const bool uses_rec = mode == SPEC_DELTA_RECORD || mode == SPEC_DELTA_ROLLBACK || mode == SPEC_DELTA_BOTH;
+    const bool scans = mode != SPEC_DELTA_ROLLBACK;
+    const bool needs_L = mode == SPEC_DELTA_ROLLBACK || mode == SPEC_DELTA_BOTH || mode == SPEC_DELTA_RESCAN;
+    if (!state || (uses_rec && !rec)) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: null state or rec");
+    if (needs_L && !L) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: L required in mode %d", mode);
+    if (scans && (!q || !k || !v || !a || !b)) return fail(SPEC_EINVAL, "spec_delta_verify_rollback: null q/k/v/a/b");
+    if (!aligned16(state) || (uses_rec && !aligned16(rec)))
+        return fail(SPEC_EINVAL, "spec_delta_verify_rollback: state and rec must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     if (mode == SPEC_DELTA_ROLLBACK) {
         hipLaunchKernelGGL(delta_restore_kernel, dim3(B * Hd), dim3(256), 0, st, state, rec, L, T, Hd);

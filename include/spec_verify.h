@@ -222,17 +222,29 @@ int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kma
  * mode 2 (ROLLBACK): state[s, h] = rec[s, L[s]-1, h] when L[s] >= 1; L[s] = 0
  *                    leaves S_0. Bit-exact copy.
  * mode 3 (BOTH):     mode 1, then state <- S_{L[s]} in the same pass.
+ * mode 4 (VERIFY):   from S_0 = state, run t = 1..T; o only (no record; state and
+ *                    rec untouched, rec may be NULL).
+ * mode 5 (RESCAN):   state <- S_{L[s]} by running t = 1..L[s] again from the
+ *                    retained S_0 = state (L[s] = 0 leaves it); o and rec untouched.
+ * Modes 4 + 5 are the input-stash alternative to 1 + 2 (memra-engine spec.rs: keep
+ * the round's inputs and the pre-round state, and on a partial accept re-run the
+ * accepted prefix): S_0 is read twice and S_L written, instead of T states recorded.
+ * Iteration t does the same arithmetic in every mode, so mode 5 gives the bytes of
+ * rec[L-1] from mode 1.
  * L[s] = committed tokens in 0..T (the greedy flow commits a_s + 1); values
  * outside 0..T are clamped.
  *
  * Layouts: q, k [B][T][Hd][dk] bf16; v [B][T][Hd][dv] bf16; a, b [B][T][Hd] fp32;
  * state [B][Hd][dv][dk] fp32; rec [B][T][Hd][dv][dk] fp32; L [B] int32 (may be
- * NULL in mode 1); o [B][T][Hd][dv] bf16 (may be NULL; unused in mode 2).
+ * NULL in modes 1 and 4); o [B][T][Hd][dv] bf16 (may be NULL; unused in modes 2
+ * and 5); rec may be NULL in modes 4 and 5.
  * Limits: dk == dv == 128, 1 <= T <= 64, B, Hd >= 1; 16-byte aligned state, rec.
  * ------------------------------------------------------------------------- */
 #define SPEC_DELTA_RECORD 1
 #define SPEC_DELTA_ROLLBACK 2
 #define SPEC_DELTA_BOTH 3
+#define SPEC_DELTA_VERIFY 4
+#define SPEC_DELTA_RESCAN 5
 int spec_delta_verify_rollback(int32_t mode, const spec_bf16* q, const spec_bf16* k,
                                const spec_bf16* v, const float* a, const float* b, float q_scale,
                                float* state, float* rec, const int32_t* L, int32_t B, int32_t T,

@@ -78,7 +78,10 @@ def test_host_argument_checks():
     assert L.spec_greedy_accept(p, p, 3, p, None, 0, 100, 0, 4, p, p, p, p, p, p, p, None) == -1
     assert L.spec_greedy_accept(p, None, 3, p, None, 0, 100, 1, 4, p, p, p, p, p, p, p, None) == -1
     # delta: mode, dims, missing L
-    assert L.spec_delta_verify_rollback(4, p, p, p, p, p, 1.0, p, p, p, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(6, p, p, p, p, p, 1.0, p, p, p, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(5, p, p, p, p, p, 1.0, p, None, None, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(4, None, p, p, p, p, 1.0, p, None, None, 1, 5, 1, 128, 128, None, None) == -1
+    assert L.spec_delta_verify_rollback(1, p, p, p, p, p, 1.0, p, None, None, 1, 5, 1, 128, 128, None, None) == -1
     assert L.spec_delta_verify_rollback(1, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 64, 128, None, None) == -1
     assert L.spec_delta_verify_rollback(2, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 128, 128, None, None) == -1
     assert L.spec_last_error() != b""

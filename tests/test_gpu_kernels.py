@@ -388,6 +388,36 @@ def test_delta_rollback_modes(dev):
         assert torch.equal(st3[s].cpu(), want), s
 
 
+def test_delta_input_stash_modes(dev):
+    """VERIFY writes the record path's outputs and nothing else; RESCAN re-runs the
+    committed prefix from the retained S_0 and leaves exactly the bytes ROLLBACK
+    restores from the record (L = 0 keeps S_0, out-of-range L is clamped)."""
+    import greedy_draft_verify_amd as gdv
+    d = synth.make_delta_inputs(seed=14, B=7, T=19, Hd=2)
+    L = np.array([0, 1, 5, 16, 17, 19, 40], np.int32)
+    st1, rec1, o1 = _delta_gpu(d, dev, gdv.DELTA_RECORD)
+    st2 = d.state.to(dev).clone()
+    gdv.spec_delta_verify_rollback(gdv.DELTA_ROLLBACK, None, None, None, None, None, 1.0, st2, rec1, i32(L, dev))
+    to = lambda t: t.to(dev)
+    s4 = d.state.to(dev).clone()
+    o4 = torch.full_like(o1, float("nan"))
+    gdv.spec_delta_verify_rollback(gdv.DELTA_VERIFY, to(d.q), to(d.k), to(d.v), to(d.a), to(d.b), 1.0, s4, None,
+                                   None, o4)
+    s5 = d.state.to(dev).clone()
+    gdv.spec_delta_verify_rollback(gdv.DELTA_RESCAN, to(d.q), to(d.k), to(d.v), to(d.a), to(d.b), 1.0, s5, None,
+                                   i32(L, dev), None)
+    torch.cuda.synchronize()
+    assert torch.equal(o4.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(s4.cpu(), d.state), "VERIFY must not modify the state"
+    assert torch.equal(s5, st2), "RESCAN must give the restored record's bytes"
+    rec_ref, _ = oracle.delta_verify(bits(d.q), bits(d.k), bits(d.v), d.a.numpy(), d.b.numpy(), 1.0,
+                                     d.state.numpy(), d.B, d.T, d.Hd, 128, 128)
+    for s in range(d.B):
+        Ls = min(int(L[s]), d.T)
+        want = d.state[s].numpy() if Ls == 0 else rec_ref[s, Ls - 1]
+        assert_close(s5[s].cpu().numpy(), want, f"RESCAN state, sequence {s}")
+
+
 @pytest.mark.parametrize("T,Ls", [(5, (1, 2, 3, 4)), (20, (1, 15, 16, 17))])
 def test_delta_record_is_prefix_invariant(dev, T, Ls):
     """S_L of a T-token scan equals the last state of an L-token scan, bit for bit (also
