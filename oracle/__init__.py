@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # Status bits, as the public header documents them for the library.
-BAD_PAGE, BAD_POS, BAD_ROWS, BAD_TOKEN = 1, 2, 4, 8
+BAD_PAGE, BAD_POS, BAD_ROWS, BAD_TOKEN, BAD_TREE = 1, 2, 4, 8, 16
 PAGE = 16
 
 
@@ -179,3 +179,55 @@ def delta_rollback(rec, L, state, B, T, Hd, dk, dv):
                                 ctypes.c_int32(B), ctypes.c_int32(T), ctypes.c_int32(Hd),
                                 ctypes.c_int32(dk), ctypes.c_int32(dv), _p(state))
     return state
+
+
+# ---------------------------------------------------------------------------
+# tree verify (fast.py _set_rows / _tree_cycle): rows = nodes in creation order,
+# parent [B][kmax + 1] with parent[s][0] = -1 and parent[s][i] in [0, i)
+def validate_tree(parent, kmax, k, B, st):
+    """ORs BAD_TREE into st (int32 [B], in place) where the parent list is not a tree."""
+    assert st.dtype == np.int32 and st.flags.c_contiguous
+    lib().oracle_validate_tree(_p(_i32(parent).reshape(B, kmax + 1)), ctypes.c_int32(kmax), _p(_i32(k)),
+                               ctypes.c_int32(B), _p(st))
+    return st
+
+
+def verify_attn_tree(q, k_pool, v_pool, page_table, max_pages, pos, k, parent, kmax, off, st, B, R, Hq, Hkv,
+                     D, scale, out=None):
+    """Tree rows: returns fp64 [R, Hq, D] (rows of bad sequences keep ``out``'s values)."""
+    if out is None:
+        out = np.full((R, Hq, D), np.nan, np.float64)
+    lib().oracle_verify_attn_tree(_p(_u16(q)), _p(_u16(k_pool)), _p(_u16(v_pool)), _p(_i32(page_table)),
+                                  ctypes.c_int32(max_pages), _p(_i32(pos)), _p(_i32(k)),
+                                  _p(_i32(parent).reshape(B, kmax + 1)), ctypes.c_int32(kmax),
+                                  _p(_i32(off)), _p(_i32(st)), ctypes.c_int32(B), ctypes.c_int32(Hq),
+                                  ctypes.c_int32(Hkv), ctypes.c_int32(D), ctypes.c_double(scale), _p(out))
+    return out
+
+
+def tree_accept(g, drafts, kmax, k, parent, d2t, n_draft_vocab, V, B, R, pos_in):
+    """Returns dict with pos_out, accept_len, n_emit, emit [B, kmax+1], next_tok, path [B, kmax], status."""
+    pos_out = np.zeros(B, np.int32)
+    acc = np.zeros(B, np.int32)
+    ne = np.zeros(B, np.int32)
+    emit = np.zeros((B, kmax + 1), np.int32)
+    nt = np.zeros(B, np.int32)
+    path = np.zeros((B, max(kmax, 1)), np.int32)
+    st = np.zeros(B, np.int32)
+    dr = _i32(drafts).reshape(B, max(kmax, 0)) if kmax > 0 else np.zeros((B, 1), np.int32)
+    d2 = None if d2t is None else _i32(d2t)
+    lib().oracle_tree_accept(_p(_i32(g)), _p(dr), ctypes.c_int32(kmax), _p(_i32(k)),
+                             _p(_i32(parent).reshape(B, kmax + 1)), _p(d2), ctypes.c_int32(n_draft_vocab),
+                             ctypes.c_int32(V), ctypes.c_int32(B), ctypes.c_int32(R), _p(_i32(pos_in)),
+                             _p(pos_out), _p(acc), _p(ne), _p(emit), _p(nt), _p(path), _p(st))
+    return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, path=path[:, :kmax],
+                status=st)
+
+
+def kv_compact(k_pool, v_pool, page_table, max_pages, pos, path, accept_len, kmax, st, B, Hkv, D):
+    """In place on k_pool / v_pool (uint16 arrays)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    ph = _i32(path).reshape(B, kmax) if kmax > 0 else np.zeros((B, 1), np.int32)
+    lib().oracle_kv_compact(_p(k_pool), _p(v_pool), _p(_i32(page_table)), ctypes.c_int32(max_pages),
+                            _p(_i32(pos)), _p(ph), _p(_i32(accept_len)), ctypes.c_int32(kmax), _p(_i32(st)),
+                            ctypes.c_int32(B), ctypes.c_int32(Hkv), ctypes.c_int32(D))

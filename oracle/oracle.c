@@ -29,6 +29,10 @@
  *    fp32 logits, device prefix match, pos += j + 1.
  *  - The Gated DeltaNet per-token update S_t = a_t S_{t-1} (I - b_t k_t k_t^T)
  *    + b_t v_t k_t^T, o_t = S_t q_t, as the problem statement gives it.
+ *  - "DSSD-dev/dssd/fast.py", _set_rows / _tree_cycle / _star_cycle: tree drafts
+ *    as rows in creation order, each on its own KV slot, attending to the
+ *    committed keys plus the slots of its own path; the verification walk from the
+ *    root; compaction of the accepted path's KV to contiguous slots.
  */
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +47,7 @@
 #define ORC_BAD_ROWS 4  /* packing undefined (some k < 0 or sum(k + 1) != R: all  */
                         /* sequences), or this k > kmax                          */
 #define ORC_BAD_TOKEN 8 /* draft id or d2t entry out of range                    */
+#define ORC_BAD_TREE 16 /* tree rows: a parent out of creation order             */
 
 static double bf(uint16_t b) {
     uint32_t u = (uint32_t)b << 16;
@@ -394,5 +399,201 @@ void oracle_delta_rollback(const double* rec, const int32_t* L, int32_t B, int32
         for (int h = 0; h < Hd; ++h)
             memcpy(state + ((int64_t)s * Hd + h) * n, rec + (((int64_t)s * T + t) * Hd + h) * n,
                    sizeof(double) * (size_t)n);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Tree (trie) verify rows (fast.py _set_rows, _tree_cycle, _star_cycle). The
+ * k_s + 1 rows of sequence s are the nodes of a draft tree in creation order:
+ * node 0 is the root (the last committed token, parent -1), every other node i
+ * has a parent in [0, i), and the draft token of node i >= 1 is drafts[s][i - 1].
+ * Node i sits at position pos + depth(i) and writes its K/V at slot pos + i (its
+ * creation index, the ordinary append); it attends to slots 0 .. pos (the
+ * committed keys and the root) and then to the slots pos + u of its own path
+ * below the root, root's child first, itself last. A chain (parent[i] = i - 1) is
+ * the ordinary verify row set. parent is [B][kmax + 1].
+ * ------------------------------------------------------------------------- */
+void oracle_validate_tree(const int32_t* parent, int32_t kmax, const int32_t* k, int32_t B, int32_t* st) {
+    for (int s = 0; s < B; ++s) {
+        int ks = k[s];
+        if (ks < 0 || ks > kmax) continue;  /* reported by the packing checks */
+        const int32_t* par = parent + (int64_t)s * (kmax + 1);
+        int bad = par[0] != -1;
+        for (int i = 1; i <= ks; ++i)
+            if (par[i] < 0 || par[i] >= i) bad = 1;
+        if (bad) st[s] |= ORC_BAD_TREE;
+    }
+}
+
+/* nodes of the path of node j below the root, root's child first, j last */
+static int tree_path(const int32_t* par, int j, int* path) {
+    int n = 0;
+    for (int u = j; u != 0; u = par[u]) path[n++] = u;
+    for (int a = 0, b = n - 1; a < b; ++a, --b) {
+        int t = path[a];
+        path[a] = path[b];
+        path[b] = t;
+    }
+    return n;
+}
+
+/* For row r = (s, j) and query head h (kv head h / (Hq / Hkv)), with the key slots
+ *   t = 0 .. pos_s, then pos_s + u for u in path(j):
+ *   z_t = scale * sum_d q[r,h,d] K[slot t][hk,d],  w = softmax(z),  o = sum_t w_t V[slot t]
+ * Rows of sequences with st[s] != 0 are left untouched. */
+void oracle_verify_attn_tree(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                             const int32_t* k, const int32_t* parent, int32_t kmax, const int32_t* off,
+                             const int32_t* st, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             double scale, double* out) {
+    int G = Hq / Hkv;
+    for (int s = 0; s < B; ++s) {
+        if (st[s]) continue;
+        int T = k[s] + 1;
+        const int32_t* par = parent + (int64_t)s * (kmax + 1);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+        for (int j = 0; j < T; ++j) {
+            for (int h = 0; h < Hq; ++h) {
+                int path[1024];
+                int np = tree_path(par, j, path);
+                int64_t P = pos[s];
+                int64_t n_keys = P + 1 + np;
+                int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_keys);
+                for (int64_t t = 0; t <= P; ++t) slot[t] = t;
+                for (int d = 0; d < np; ++d) slot[P + 1 + d] = P + path[d];
+                int64_t r = off[s] + j;
+                int hk = h / G;
+                const uint16_t* qr = q + (r * Hq + h) * D;
+                double* z = (double*)malloc(sizeof(double) * (size_t)n_keys);
+                double zmax = -INFINITY;
+                for (int64_t t = 0; t < n_keys; ++t) {
+                    int64_t page = page_table[(int64_t)s * max_pages + slot[t] / ORC_PAGE];
+                    int tt = (int)(slot[t] % ORC_PAGE);
+                    double acc = 0.0;
+                    for (int d = 0; d < D; ++d) acc += bf(qr[d]) * bf(k_pool[k_index(page, hk, tt, d, Hkv, D)]);
+                    z[t] = scale * acc;
+                    if (z[t] > zmax) zmax = z[t];
+                }
+                double denom = 0.0;
+                for (int64_t t = 0; t < n_keys; ++t) {
+                    z[t] = exp(z[t] - zmax);
+                    denom += z[t];
+                }
+                double* o = out + (r * Hq + h) * D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t t = 0; t < n_keys; ++t) {
+                    int64_t page = page_table[(int64_t)s * max_pages + slot[t] / ORC_PAGE];
+                    int tt = (int)(slot[t] % ORC_PAGE);
+                    double w = z[t] / denom;
+                    for (int d = 0; d < D; ++d) o[d] += w * bf(v_pool[v_index(page, hk, tt, d, Hkv, D)]);
+                }
+                free(z);
+                free(slot);
+            }
+        }
+    }
+}
+
+/* Tree acceptance (fast.py _tree_cycle verification walk), greedy: from the root,
+ * move to the child whose mapped draft token equals the greedy token of the
+ * current node (the lowest-index such child), as long as one exists.
+ *   accepted nodes u_1 .. u_a,  emit = map(tok(u_1 .. u_a)) ++ [g[node_a]]
+ *   pos_out = pos_in + a + 1,  next_tok = g[node_a],  path[s] = u_1 .. u_a (-1 after)
+ * Checks and the outputs of a rejected sequence as in oracle_greedy_accept; a
+ * parent list out of creation order sets ORC_BAD_TREE. */
+void oracle_tree_accept(const int32_t* g, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                        const int32_t* parent, const int32_t* d2t, int32_t n_draft_vocab, int32_t V,
+                        int32_t B, int32_t R, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
+                        int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* path, int32_t* st) {
+    int64_t total = 0;
+    int packing_ok = 1;
+    for (int s = 0; s < B; ++s) {
+        total += (int64_t)k[s] + 1;
+        if (k[s] < 0) packing_ok = 0;
+    }
+    if (total != R) packing_ok = 0;
+    int64_t off = 0;
+    for (int s = 0; s < B; ++s) {
+        int bits = 0;
+        int ks = k[s];
+        if (!packing_ok || ks > kmax) bits |= ORC_BAD_ROWS;
+        if (pos_in[s] < 0) bits |= ORC_BAD_POS;
+        const int32_t* par = parent + (int64_t)s * (kmax + 1);
+        if (!bits) {
+            if (par[0] != -1) bits |= ORC_BAD_TREE;
+            for (int i = 1; i <= ks; ++i)
+                if (par[i] < 0 || par[i] >= i) bits |= ORC_BAD_TREE;
+            for (int j = 0; j < ks; ++j) {
+                int32_t x = drafts[(int64_t)s * kmax + j];
+                if (d2t) {
+                    if (x < 0 || x >= n_draft_vocab || d2t[x] < 0 || d2t[x] >= V) bits |= ORC_BAD_TOKEN;
+                } else if (x < 0 || x >= V) {
+                    bits |= ORC_BAD_TOKEN;
+                }
+            }
+        }
+        int32_t* e = emit + (int64_t)s * (kmax + 1);
+        int32_t* ph = path + (int64_t)s * kmax;
+        for (int j = 0; j <= kmax; ++j) e[j] = -1;
+        for (int j = 0; j < kmax; ++j) ph[j] = -1;
+        if (bits) {
+            st[s] = bits;
+            accept_len[s] = -1;
+            n_emit[s] = 0;
+            next_tok[s] = -1;
+            pos_out[s] = pos_in[s];
+            off += (int64_t)ks + 1;
+            continue;
+        }
+        st[s] = 0;
+        int a = 0, u = 0;
+        for (;;) {
+            int next = -1;
+            for (int c = 1; c <= ks && next < 0; ++c) {
+                if (par[c] != u) continue;
+                int32_t x = drafts[(int64_t)s * kmax + c - 1];
+                int32_t mapped = d2t ? d2t[x] : x;
+                if (mapped == g[off + u]) next = c;
+            }
+            if (next < 0) break;
+            int32_t x = drafts[(int64_t)s * kmax + next - 1];
+            e[a] = d2t ? d2t[x] : x;
+            ph[a] = next;
+            ++a;
+            u = next;
+        }
+        e[a] = g[off + u];
+        accept_len[s] = a;
+        n_emit[s] = a + 1;
+        next_tok[s] = g[off + u];
+        pos_out[s] = pos_in[s] + a + 1;
+        off += ks + 1;
+    }
+}
+
+/* Compaction of the accepted path (fast.py _tree_cycle / _star_cycle): for every
+ * sequence with st[s] == 0, the K/V of slot pos + path[s][d] moves to slot
+ * pos + 1 + d, d = 0 .. accept_len[s] - 1, in ascending d (a source slot is never
+ * below its destination, so no source is overwritten before it is read). Slots
+ * past pos + accept_len are left as they are. */
+void oracle_kv_compact(uint16_t* k_pool, uint16_t* v_pool, const int32_t* page_table, int32_t max_pages,
+                       const int32_t* pos, const int32_t* path, const int32_t* accept_len, int32_t kmax,
+                       const int32_t* st, int32_t B, int32_t Hkv, int32_t D) {
+    for (int s = 0; s < B; ++s) {
+        if (st[s] || accept_len[s] <= 0) continue;
+        for (int d = 0; d < accept_len[s]; ++d) {
+            int64_t src = (int64_t)pos[s] + path[(int64_t)s * kmax + d];
+            int64_t dst = (int64_t)pos[s] + 1 + d;
+            if (src == dst) continue;
+            int64_t ps = page_table[(int64_t)s * max_pages + src / ORC_PAGE];
+            int64_t pd = page_table[(int64_t)s * max_pages + dst / ORC_PAGE];
+            for (int hk = 0; hk < Hkv; ++hk)
+                for (int c = 0; c < D; ++c) {
+                    k_pool[k_index(pd, hk, (int)(dst % ORC_PAGE), c, Hkv, D)] =
+                        k_pool[k_index(ps, hk, (int)(src % ORC_PAGE), c, Hkv, D)];
+                    v_pool[v_index(pd, hk, (int)(dst % ORC_PAGE), c, Hkv, D)] =
+                        v_pool[v_index(ps, hk, (int)(src % ORC_PAGE), c, Hkv, D)];
+                }
+        }
     }
 }

@@ -53,8 +53,10 @@ class ToyLM:
     def _proj(self, W, x):
         return oracle.f32_to_bf16_bits(np.array([W[i] @ x for i in range(W.shape[0])], np.float64).astype(np.float32))
 
-    def forward_rows(self, tokens, pos):
-        """Rows tokens[j] at positions pos + j (one sequence). Returns greedy tokens [T]."""
+    def forward_rows(self, tokens, pos, parent=None):
+        """Rows tokens[j] at positions pos + j (one sequence), or, with ``parent``, the
+        nodes of a draft tree in creation order (row j writes slot pos + j and attends
+        to slots 0..pos plus its own path). Returns greedy tokens [T]."""
         T = len(tokens)
         q = np.empty((T, self.Hq, self.D), np.uint16)
         kn = np.empty((T, self.Hkv, self.D), np.uint16)
@@ -70,8 +72,13 @@ class ToyLM:
         assert st[0] == 0
         oracle.append_kv(kn, vn, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa, ka, off,
                          st, 1, self.Hkv, self.D)
-        att = oracle.verify_attn(q, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa, ka, off,
-                                 st, 1, T, self.Hq, self.Hkv, self.D, 1 / math.sqrt(self.D))
+        if parent is None:
+            att = oracle.verify_attn(q, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa, ka,
+                                     off, st, 1, T, self.Hq, self.Hkv, self.D, 1 / math.sqrt(self.D))
+        else:
+            att = oracle.verify_attn_tree(q, self.k_pool, self.v_pool, self.page_table, self.max_pages, posa,
+                                          ka, np.asarray(parent, np.int32)[None, :], T - 1, off, st, 1, T,
+                                          self.Hq, self.Hkv, self.D, 1 / math.sqrt(self.D))
         att_bf = oracle.bf16_bits_to_f64(oracle.f32_to_bf16_bits(att.astype(np.float32)))
         h = np.empty((T, self.H), np.uint16)
         for j, x in enumerate(tokens):
@@ -106,6 +113,33 @@ class ToyLM:
             g = self.forward_rows([x0] + drafts, pos)
             res = oracle.greedy_accept(g, np.array([drafts], np.int32), k, np.array([k], np.int32), None, 0,
                                        self.V, 1, k + 1, np.array([pos], np.int32))
+            n = int(res["n_emit"][0])
+            out.extend(int(t) for t in res["emit"][0, :n])
+            accepted_hist.append(int(res["accept_len"][0]))
+            pos = int(res["pos_out"][0])
+            x0 = int(res["next_tok"][0])
+        return out[:n_new], accepted_hist
+
+    def generate_tree(self, prompt, n_new, drafter):
+        """Tree drafts (DSSD fast.py _tree_cycle / _star_cycle): ``drafter(out)`` returns
+        (parent, tokens) for the nodes below the root in creation order; one verify of
+        the whole tree -> tree acceptance walk -> compaction of the accepted path's KV
+        -> pos += a + 1."""
+        self.reset()
+        for i, x in enumerate(prompt[:-1]):
+            self.forward_rows([x], i)
+        x0, pos = prompt[-1], len(prompt) - 1
+        out, accepted_hist = [], []
+        while len(out) < n_new:
+            par, toks = drafter(out)
+            k = len(toks)
+            parent = np.array([-1] + list(par), np.int32)
+            g = self.forward_rows([x0] + [int(t) for t in toks], pos, parent=parent)
+            res = oracle.tree_accept(g, np.array([toks], np.int32), k, np.array([k], np.int32), parent[None, :],
+                                     None, 0, self.V, 1, k + 1, np.array([pos], np.int32))
+            assert res["status"][0] == 0
+            oracle.kv_compact(self.k_pool, self.v_pool, self.page_table, self.max_pages, np.array([pos], np.int32),
+                              res["path"], res["accept_len"], k, res["status"], 1, self.Hkv, self.D)
             n = int(res["n_emit"][0])
             out.extend(int(t) for t in res["emit"][0, :n])
             accepted_hist.append(int(res["accept_len"][0]))
