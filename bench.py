@@ -187,6 +187,89 @@ def delta_leg(dev, reps: int):
                             "total_us": (sec_v + sec_s) * 1e6}}
 
 
+def tree_leg(dev, w_packed, reps: int, seed: int = 0):
+    """Tree drafts on the b16k4 shapes (DSSD fast.py _tree_cycle): 16 sequences with a
+    16-node trie each (a spine of 8 head drafts, then side branches), 256 rows. One
+    tree step = spec_verify_attn_tree -> spec_lm_head_argmax (the workload's W) ->
+    spec_tree_accept -> spec_kv_compact, each timed with HIP events on the launch
+    stream; beside it the chain attention over the same 256 rows (k = 15) for the cost
+    of the ancestor masks."""
+    x = synth.make_verify_inputs("b16tree", seed=seed, device=dev, with_lm_head=False)
+    wl = x.wl
+    B, R, kmax = len(x.pos), x.R, wl.kmax
+    hidden = synth.normal_bf16((R, wl.H), 1.0, seed, wl.name, "hidden", dev)
+    parent_np = synth.make_parents(x.k, seed, wl.name, "trie")
+    parent = i32(parent_np, dev)
+    pt, pos, k = i32(x.page_table, dev), i32(x.pos, dev), i32(x.k, dev)
+    out = torch.empty((R, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_t = gdv.workspace(gdv.verify_attn_tree_workspace_bytes(B, R, wl.Hq, wl.Hkv, wl.D, x.page_table.shape[1],
+                                                              kmax), dev)
+    ws_c = gdv.workspace(gdv.verify_attn_workspace_bytes(B, R, wl.Hq, wl.Hkv, wl.D, x.page_table.shape[1]), dev)
+    attn_t = lambda: gdv.spec_verify_attn_tree(x.q, x.k_new, x.v_new, x.k_pool, x.v_pool, pt, pos, k, parent,
+                                               x.scale, out, st, workspace_buf=ws_t)
+    attn_c = lambda: gdv.spec_verify_attn(x.q, x.k_new, x.v_new, x.k_pool, x.v_pool, pt, pos, k, kmax, x.scale,
+                                          out, st, workspace_buf=ws_c)
+    am = torch.empty(R, dtype=torch.int32, device=dev)
+    lm_ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, wl.H, wl.V), dev, zero=True)
+    lm = lambda: gdv.spec_lm_head_argmax(hidden, w_packed, wl.V, am, None, workspace_buf=lm_ws)
+    lm()
+    attn_t()
+    torch.cuda.synchronize()
+    assert (st.cpu() == 0).all()
+    g0 = am.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    drafts = i32(synth.make_tree_drafts(wl, x.k, parent_np, [g0[off[s]:off[s + 1]] for s in range(B)], seed), dev)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, ast = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+    path = torch.empty((B, kmax), dtype=torch.int32, device=dev)
+    cst = torch.zeros(B, dtype=torch.int32, device=dev)
+    accept = lambda: gdv.spec_tree_accept(am, drafts, k, parent, None, wl.V, pos, pos_out, acc, ne, emit, nt, path,
+                                          ast)
+    compact = lambda: gdv.spec_kv_compact(x.k_pool, x.v_pool, pt, pos, path, acc, cst.zero_())
+    stream = torch.cuda.current_stream()
+    fns = [attn_t, lm, accept, compact]
+    for _ in range(3):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    assert (ast.cpu() == 0).all() and (cst.cpu() == 0).all()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for ev in evs:
+        ev[0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs])) * 1e3 for i in range(len(fns))]
+    # the chain attention over the same rows, timed in the same place (after an lm_head
+    # pass has streamed W through the caches)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for ev in evc:
+        lm()
+        ev[0].record(stream)
+        attn_c()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    chain_us = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evc])) * 1e3
+    acc_np = acc.cpu().numpy()
+    at_b = attn_bytes(x)
+    cmp_b = int(acc_np.sum()) * wl.Hkv * wl.D * 2 * 2 * 2
+    step_us = sum(us)
+    return {"workload": f"b16tree: B={B}, 16-node trie per sequence (spine 8 + branches), R={R}, context "
+                        f"U{{{wl.ctx_lo}..{wl.ctx_hi}}}, {wl.Hq}q/{wl.Hkv}kv, head_dim {wl.D}, vocab {wl.V}",
+            "step_us": step_us, "rows_per_s": R / (step_us / 1e6),
+            "emitted_tokens_per_s": float((acc_np + 1).sum()) / (step_us / 1e6),
+            "accept_len_hist": np.bincount(acc_np, minlength=kmax + 1).tolist(),
+            "kernel_us": {"spec_verify_attn_tree": us[0], "spec_lm_head_argmax": us[1], "spec_tree_accept": us[2],
+                          "spec_kv_compact": us[3]},
+            "attn_tree": {"bound": "hbm", "algorithmic_bytes": at_b, "achieved": at_b / us[0] / 1e3,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": at_b / us[0] / 1e3 / HBM_PEAK_GBS},
+            "attn_chain_same_rows_us": chain_us,
+            "kv_compact_bytes": cmp_b}
+
+
 def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
     """spec_lm_head_argmax alone at growing row counts with the workload's W: where the
     weight stream stops bounding it and the MFMA work starts to."""
@@ -367,6 +450,8 @@ def main():
     if not args.no_extras:
         extras["lm_head_row_sweep"] = lm_head_sweep(x, step.w_packed, dev, reps=10)
         extras["delta_roofline"] = delta_leg(dev, reps=20)
+        if wl.H == 4096 and wl.V == 151936:
+            extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
         sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
         dl = extras["delta_roofline"]
         log(f"[bench] lm_head sweep: {sw}")
@@ -375,6 +460,15 @@ def main():
             f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
             f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
             f"{ist['rescan_us']:.1f} us")
+        if "tree_verify" in extras:
+            tv = extras["tree_verify"]
+            ku = tv["kernel_us"]
+            log(f"[bench] tree step {tv['step_us']:.1f} us ({tv['rows_per_s']:.0f} rows/s, "
+                f"{tv['emitted_tokens_per_s']:.0f} tokens/s): attn {ku['spec_verify_attn_tree']:.1f} us "
+                f"({100 * tv['attn_tree']['frac']:.0f}% HBM; chain over the same rows "
+                f"{tv['attn_chain_same_rows_us']:.1f} us), lm_head {ku['spec_lm_head_argmax']:.1f} us, accept "
+                f"{ku['spec_tree_accept']:.1f} us, compact {ku['spec_kv_compact']:.1f} us; accept lengths "
+                f"{tv['accept_len_hist']}")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20

@@ -25,7 +25,9 @@ DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH, DELTA_VERIFY, DELTA_RESCAN = 1, 2, 3, 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_verify_attn_workspace_bytes", "spec_verify_attn",
             "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_packed_bytes",
-            "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback"]
+            "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
+            "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
+            "spec_kv_compact"]
 
 _lib = None
 
@@ -60,8 +62,16 @@ def lib() -> ctypes.CDLL:
                                          vp, vp]
         L.spec_delta_verify_rollback.argtypes = [i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
                                                  i32, vp, vp]
+        L.spec_verify_attn_tree_workspace_bytes.argtypes = [i32] * 8
+        L.spec_verify_attn_tree_workspace_bytes.restype = sz
+        L.spec_verify_attn_tree.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, f32, i32, vp, vp, sz, vp, vp]
+        L.spec_tree_accept.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp]
+        L.spec_kv_compact.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp]
         for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack", "spec_greedy_accept",
-                     "spec_delta_verify_rollback"):
+                     "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
+                     "spec_kv_compact"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -113,6 +123,10 @@ def verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens=0) 
     return lib().spec_verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens)
 
 
+def verify_attn_tree_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kmax, kv_split_tokens=0) -> int:
+    return lib().spec_verify_attn_tree_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens, kmax)
+
+
 def lm_head_argmax_workspace_bytes(R, H, V) -> int:
     return lib().spec_lm_head_argmax_workspace_bytes(R, H, V)
 
@@ -125,11 +139,7 @@ def workspace(nbytes: int, device="cuda", zero: bool = False) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, scale, out, seq_status,
-                     workspace_buf=None, kv_split_tokens=0, stream=None):
-    """q [R,Hq,D], k_new/v_new [R,Hkv,D], k_pool/v_pool [n_pages,Hkv,16*D] (pool block layout),
-    out [R,Hq,D] (bf16); page_table [B,max_pages], pos [B], k [B], seq_status [B] (int32);
-    kmax = an upper bound on k."""
+def _attn_shapes(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, out, seq_status):
     for t, n, nd in ((q, "q", 3), (k_new, "k_new", 3), (v_new, "v_new", 3), (k_pool, "k_pool", 3),
                      (v_pool, "v_pool", 3), (out, "out", 3)):
         _want(t, torch.bfloat16, n, nd)
@@ -147,6 +157,16 @@ def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, 
     _shape(out, (R, Hq, D), "out")
     for t, n in ((pos, "pos"), (k, "k"), (seq_status, "seq_status")):
         _shape(t, (B,), n)
+    return R, Hq, Hkv, D, B, max_pages, n_pages
+
+
+def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, scale, out, seq_status,
+                     workspace_buf=None, kv_split_tokens=0, stream=None):
+    """q [R,Hq,D], k_new/v_new [R,Hkv,D], k_pool/v_pool [n_pages,Hkv,16*D] (pool block layout),
+    out [R,Hq,D] (bf16); page_table [B,max_pages], pos [B], k [B], seq_status [B] (int32);
+    kmax = an upper bound on k."""
+    R, Hq, Hkv, D, B, max_pages, n_pages = _attn_shapes(q, k_new, v_new, k_pool, v_pool, page_table, pos, k,
+                                                        out, seq_status)
     if workspace_buf is None:
         workspace_buf = workspace(verify_attn_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kv_split_tokens),
                                   q.device)
@@ -155,6 +175,76 @@ def spec_verify_attn(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, kmax, 
                                 kv_split_tokens, _ptr(out), _ptr(workspace_buf), workspace_buf.numel(),
                                 _ptr(seq_status), _stream(stream))
     _check(rc, "spec_verify_attn")
+
+
+def spec_verify_attn_tree(q, k_new, v_new, k_pool, v_pool, page_table, pos, k, parent, scale, out, seq_status,
+                          workspace_buf=None, kv_split_tokens=0, stream=None):
+    """Tree rows: as spec_verify_attn, plus parent [B, kmax+1] int32 (parent[s][0] = -1,
+    parent[s][i] in [0, i)); kmax = parent.shape[1] - 1."""
+    R, Hq, Hkv, D, B, max_pages, n_pages = _attn_shapes(q, k_new, v_new, k_pool, v_pool, page_table, pos, k,
+                                                        out, seq_status)
+    _want(parent, torch.int32, "parent", 2)
+    if parent.shape[0] != B:
+        raise SpecError(f"parent: {tuple(parent.shape)}, expected ({B}, kmax + 1)")
+    kmax = parent.shape[1] - 1
+    if workspace_buf is None:
+        workspace_buf = workspace(verify_attn_tree_workspace_bytes(B, R, Hq, Hkv, D, max_pages, kmax,
+                                                                   kv_split_tokens), q.device)
+    rc = lib().spec_verify_attn_tree(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), n_pages,
+                                     _ptr(page_table), max_pages, _ptr(pos), _ptr(k), _ptr(parent), kmax, B, R,
+                                     Hq, Hkv, D, scale, kv_split_tokens, _ptr(out), _ptr(workspace_buf),
+                                     workspace_buf.numel(), _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_verify_attn_tree")
+
+
+def spec_tree_accept(argmax, drafts, k, parent, d2t, V, pos_in, pos_out, accept_len, n_emit, emit, next_tok,
+                     path, seq_status, stream=None):
+    """Tree acceptance walk: as spec_greedy_accept, plus parent [B, kmax+1] and the output
+    path [B, kmax] (int32)."""
+    for t, n in ((argmax, "argmax"), (drafts, "drafts"), (k, "k"), (parent, "parent"), (pos_in, "pos_in"),
+                 (pos_out, "pos_out"), (accept_len, "accept_len"), (n_emit, "n_emit"), (emit, "emit"),
+                 (next_tok, "next_tok"), (path, "path"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    B, kmax = drafts.shape
+    R = argmax.shape[0]
+    _shape(argmax, (R,), "argmax")
+    _shape(parent, (B, kmax + 1), "parent")
+    _shape(emit, (B, kmax + 1), "emit")
+    _shape(path, (B, kmax), "path")
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    rc = lib().spec_tree_accept(_ptr(argmax), _ptr(drafts), kmax, _ptr(k), _ptr(parent), _ptr(d2t),
+                                0 if d2t is None else d2t.shape[0], V, B, R, _ptr(pos_in), _ptr(pos_out),
+                                _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok), _ptr(path),
+                                _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_tree_accept")
+
+
+def spec_kv_compact(k_pool, v_pool, page_table, pos, path, accept_len, seq_status, stream=None):
+    """Moves slot pos + path[s][d] to pos + 1 + d (every kv head) for the sequences whose
+    seq_status is 0 (in/out); k_pool/v_pool [n_pages,Hkv,16*D] bf16, path [B,kmax] int32."""
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _want(t, torch.bfloat16, n, 3)
+    for t, n in ((page_table, "page_table"), (pos, "pos"), (path, "path"), (accept_len, "accept_len"),
+                 (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    _want(page_table, torch.int32, "page_table", 2)
+    _want(path, torch.int32, "path", 2)
+    B, max_pages = page_table.shape
+    n_pages, Hkv, blk = k_pool.shape
+    D = blk // SPEC_PAGE_TOKENS
+    _shape(v_pool, (n_pages, Hkv, blk), "v_pool")
+    kmax = path.shape[1]
+    _shape(path, (B, kmax), "path")
+    for t, n in ((pos, "pos"), (accept_len, "accept_len"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    rc = lib().spec_kv_compact(_ptr(k_pool), _ptr(v_pool), n_pages, _ptr(page_table), max_pages, _ptr(pos),
+                               _ptr(path), _ptr(accept_len), kmax, B, Hkv, D, _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_kv_compact")
 
 
 def lm_head_packed_bytes(V, H) -> int:

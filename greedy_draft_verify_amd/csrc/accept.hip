@@ -38,34 +38,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     __shared__ int s_off[kAcceptMaxB];
     __shared__ int s_bad_k;
     const int tid = threadIdx.x;
-    if (tid == 0) s_bad_k = 0;
-    __syncthreads();
-
-    // -- row offsets: exclusive prefix sums of (k_s + 1) over a contiguous segment per thread
-    const int per = (B + kAcceptThreads - 1) / kAcceptThreads;
-    const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
-    long long local = 0;
-    for (int s = s0; s < s1; ++s) {
-        int ks = k[s];
-        if (ks < 0) s_bad_k = 1;
-        local += (long long)ks + 1;
-    }
-    s_scan[tid] = local;
-    __syncthreads();
-    for (int d = 1; d < kAcceptThreads; d <<= 1) {
-        long long v = tid >= d ? s_scan[tid - d] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    const long long total = s_scan[kAcceptThreads - 1];
-    long long run = tid ? s_scan[tid - 1] : 0;
-    for (int s = s0; s < s1; ++s) {
-        s_off[s] = (int)run;
-        run += (long long)k[s] + 1;
-    }
-    __syncthreads();
-    const bool packing_ok = (total == (long long)R) && !s_bad_k;
+    // -- row offsets (ragged packing)
+    const bool packing_ok = block_row_offsets<kAcceptThreads>(k, B, R, s_scan, s_off, &s_bad_k);
 
     // -- one wave per sequence
     const int wave = tid / kWave, lane = tid % kWave;

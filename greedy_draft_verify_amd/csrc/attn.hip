@@ -8,9 +8,11 @@
 //            output tile dt each lane's 4 tokens of one channel are 8 contiguous bytes.
 //
 // Launches on the caller's stream:
-//   1. attn_prep_kernel  grid B: validates sequence s (row packing, positions, page
-//      ids), records its row offset in the workspace and writes the rows' K/V into
-//      their pool slots (span-02 spec.rs: KV appended in place at pos..pos+k).
+//   1. attn_prep_kernel  grid (B, append blocks): validates sequence s (row packing,
+//      positions, page ids), records its row offset in the workspace and writes the
+//      rows' K/V into their pool slots (span-02 spec.rs: KV appended in place at
+//      pos..pos+k); each workgroup of a sequence appends up to 1024 16-byte chunks,
+//      all requested in one round with the validation loads.
 //   2. attn_split_kernel: one workgroup per (sequence, kv head, split of
 //      kv_split_tokens positions, group of 64 query rows), kv head fastest in the
 //      launch order so that the Hkv blocks of a page (adjacent in the pool) are
@@ -27,6 +29,17 @@
 //   3. attn_combine_kernel one wave per (row, q head): merges the row's splits in
 //      ascending order (log-sum-exp weights) and writes bf16.
 //
+// Tree rows (spec_verify_attn_tree; DSSD fast.py, _set_rows and _tree_cycle): the
+// k+1 rows of a sequence are the nodes of a draft tree in creation order; node j
+// still writes slot pos + j, but attends to slots 0..pos and to the slots pos + u of
+// the nodes u on its own path. The prep kernel checks every parent list and turns it
+// into one 128-bit ancestor mask per row (pointer jumping over the parent links in
+// LDS: after r rounds a node's mask covers its 2^r nearest ancestors). The split
+// kernel then keeps key slot t for a row iff t <= pos, or bit t - pos of the row's
+// mask is set: for a tile that reaches past pos it shifts the mask into a 64-bit
+// window aligned with the tile. A chain (parent j - 1) keeps exactly the keys
+// t <= pos + j, so it gives the bytes of spec_verify_attn.
+//
 // Row invariance: splits sit at absolute multiples of kv_split_tokens and steps at
 // absolute multiples of 32; every row's operations run in the same order whichever
 // wave, row group or launch serves it; reductions run in a fixed order; a row reads
@@ -42,6 +55,7 @@ constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kMaxRowsPerKvHead = 128;
 constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup handles
 constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
+constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SeqInfo {
@@ -64,14 +78,18 @@ __device__ __forceinline__ int v_off(int t, int d) {
 
 // ---------------------------------------------------------------------------
 constexpr int kPrepItems = 4;   // append chunks per thread requested before validation ends
+constexpr int kPrepItemsPerWg = kPrepItems * 256;   // a sequence's append spans grid.y workgroups
 
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, u16* __restrict__ k_pool,
     u16* __restrict__ v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int kmax, int B, int R, int Hq,
     int Hkv, int D, int split, SeqInfo* __restrict__ info, RowRec* __restrict__ rows,
-    int32_t* __restrict__ packing_ok, int32_t* __restrict__ status) {
+    int32_t* __restrict__ packing_ok, int32_t* __restrict__ status, const int32_t* __restrict__ parent,
+    uint4* __restrict__ tree_mask) {
     __shared__ int s_flags[4];
+    __shared__ int s_anc[kMaxTreeNodes];
+    __shared__ uint4 s_mask[kMaxTreeNodes];
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int ks = k[s];
     const int P = pos[s];
@@ -109,9 +127,10 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         hk = rest % Hkv;
         j = rest / Hkv;
     };
+    const int item0 = blockIdx.y * kPrepItemsPerWg;
 #pragma unroll
     for (int u = 0; u < kPrepItems; ++u) {
-        const int i = tid + u * 256;
+        const int i = item0 + tid + u * 256;
         if (i < n_items) {
             int j, hk, dc;
             item_src(i, j, hk, dc);
@@ -120,6 +139,12 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
             it_k[u] = ld16(k_new + src);
             it_v[u] = ld16(v_new + src);
         }
+    }
+    // tree rows: node i's parent must come before it (the root's is -1)
+    int par_i = 0;
+    if (parent && ks >= 0 && ks <= kmax && tid <= ks) {
+        par_i = parent[(size_t)s * (kmax + 1) + tid];
+        if (tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid)) flags |= SPEC_STATUS_BAD_TREE;
     }
     if (pos_ok && ks >= 0) {
         const int last_page = (int)(((long long)P + ks) / kPage);
@@ -133,7 +158,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     if (lane == 0) s_flags[wave] = flags;
     __syncthreads();
     const int bits = s_flags[0] | s_flags[1] | s_flags[2] | s_flags[3];
-    if (tid == 0) {
+    const bool lead = blockIdx.y == 0;   // the workgroup that writes the sequence's records
+    if (lead && tid == 0) {
         status[s] = bits;
         info[s].off = off;
         info[s].valid = bits == 0;
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     }
     // per-row record for the combine (only when the packing is defined; otherwise the
     // combine writes nothing)
-    if (packed)
+    if (lead && packed)
         for (int j = tid; j <= ks; j += 256) rows[off + j] = RowRec{P + j, bits ? 0 : (P + j) / split + 1};
     if (bits) return;
     // append: 8 channels (one 16-byte chunk of a row) per item
@@ -158,15 +184,45 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
     };
 #pragma unroll
     for (int u = 0; u < kPrepItems; ++u) {
-        const int i = tid + u * 256;
+        const int i = item0 + tid + u * 256;
         if (i < n_items) store_item(i, it_page[u], it_k[u], it_v[u]);
     }
-    for (int i = tid + kPrepItems * 256; i < n_items; i += 256) {
-        int j, hk, dc;
-        item_src(i, j, hk, dc);
-        const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
-        store_item(i, page_table[(size_t)s * max_pages + (P + j) / kPage], ld16(k_new + src), ld16(v_new + src));
+    if (!parent || !lead) return;
+    // Ancestor masks. Invariant: mask(j) holds the nodes from j up to, not including,
+    // anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)), doubling the
+    // covered distance. The root is its own ancestor (mask {0}), and depth <= ks, so
+    // ceil(log2(ks + 1)) rounds reach it from every node.
+    uint4 mk = make_uint4(0, 0, 0, 0);
+    if (tid <= ks) {
+        const int b = tid;
+        mk.x = b < 32 ? 1u << b : 0u;
+        mk.y = b >= 32 && b < 64 ? 1u << (b - 32) : 0u;
+        mk.z = b >= 64 && b < 96 ? 1u << (b - 64) : 0u;
+        mk.w = b >= 96 ? 1u << (b - 96) : 0u;
+        s_anc[tid] = tid == 0 ? 0 : par_i;
+        s_mask[tid] = mk;
     }
+    __syncthreads();
+    for (int reach = 1; reach <= ks; reach *= 2) {
+        int a2 = 0;
+        uint4 m2 = make_uint4(0, 0, 0, 0);
+        if (tid <= ks) {
+            const int a = s_anc[tid];
+            a2 = s_anc[a];
+            m2 = s_mask[a];
+        }
+        __syncthreads();
+        if (tid <= ks) {
+            mk.x |= m2.x;
+            mk.y |= m2.y;
+            mk.z |= m2.z;
+            mk.w |= m2.w;
+            s_anc[tid] = a2;
+            s_mask[tid] = mk;
+        }
+        __syncthreads();
+    }
+    if (tid <= ks) tree_mask[(size_t)s * (kmax + 1) + tid] = mk;
 }
 
 // ---------------------------------------------------------------------------
@@ -189,10 +245,11 @@ struct TileMath {
     static constexpr int NDS = D / 32;
     static constexpr int NDT = D / 16;
 
-    template <class Src>
+    // win (tree rows only): bit o set iff the row keeps key slot t0 + o
+    template <bool TREE, class Src>
     __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int t0, int p_m,
-                                               bool full, int lq, float scale_log2, float& m_run,
-                                               float& l_lane, f32x4 (&o)[NDT]) {
+                                               uint64_t win, bool full, int lq, float scale_log2,
+                                               float& m_run, float& l_lane, f32x4 (&o)[NDT]) {
         float sc[16];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -203,10 +260,16 @@ struct TileMath {
             for (int i = 0; i < 4; ++i) sc[4 * p + i] = acc[i] * scale_log2;
         }
         if (!full) {   // some token of the tile lies past some row's position
+            // tree: this lane's tokens are 16 (jj / 4) + 4 lq + jj % 4, so after one
+            // shift by 4 lq every bit sits at a constant offset of a 32-bit half
+            const uint64_t wl = TREE ? win >> (4 * lq) : 0ull;
+            const uint32_t w_lo = (uint32_t)wl, w_hi = (uint32_t)(wl >> 32);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
-                const int kp = t0 + 16 * (jj >> 2) + 4 * lq + (jj & 3);
-                if (kp > p_m) sc[jj] = -INFINITY;
+                const int o_t = 16 * (jj >> 2) + 4 * lq + (jj & 3);
+                const uint32_t half = (jj >> 3) ? w_hi : w_lo;
+                const bool keep = TREE ? ((half >> (16 * ((jj >> 2) & 1) + (jj & 3))) & 1u) : (t0 + o_t <= p_m);
+                if (!keep) sc[jj] = -INFINITY;
             }
         }
         float tmax = sc[0];
@@ -265,6 +328,26 @@ __device__ __forceinline__ uint2 mask_v(uint2 v, int tok0, int last) {
     return make_uint2(w[0], w[1]);
 }
 
+// Bits n .. n + 63 of the 128-bit value hi:lo (0 <= n < 64).
+__device__ __forceinline__ uint64_t funnel64(uint64_t lo, uint64_t hi, int n) {
+    return n == 0 ? lo : (lo >> n) | (hi << (64 - n));
+}
+
+// Keep-window of a tree row for the tile starting at key slot t0: bit o says whether
+// slot t0 + o is kept. With u = slot - pos, slots u <= 0 (the committed keys and the
+// root) are always kept and 1 <= u <= 127 follow the ancestor mask; over the 192-bit
+// value [64 ones | mask bits 0..127] (the root's bit forced on) the window is the 64
+// bits from sh = t0 - pos + 64, which a tile that reaches past pos has in 1..191.
+// sh is the same for the whole wave.
+__device__ __forceinline__ uint64_t tree_window(uint4 mk, int sh) {
+    const uint64_t e0 = ~0ull;
+    const uint64_t e1 = ((uint64_t)mk.y << 32 | mk.x) | 1ull;
+    const uint64_t e2 = (uint64_t)mk.w << 32 | mk.z;
+    if (sh < 64) return funnel64(e0, e1, sh);
+    if (sh < 128) return funnel64(e1, e2, sh - 64);
+    return funnel64(e2, 0ull, sh - 128);
+}
+
 // Writes one query tile's split partial (unnormalised O, running max, sum).
 template <int D>
 __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_run, float l_lane, bool m_ok,
@@ -284,19 +367,20 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
 // Register budget: four workgroups per CU at D <= 128 (32 KB of LDS each), two at
 // D = 256 (64 KB each), so that enough tiles are in flight per CU.
-template <int D>
+template <int D, bool TREE>
 __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
     float scale_log2, int split, int n_splits, float2* __restrict__ part_ml,
-    float* __restrict__ part_o) {
+    float* __restrict__ part_o, const uint4* __restrict__ tree_mask, int kmax) {
     using TM = TileMath<D>;
     constexpr int NDS = TM::NDS, NDT = TM::NDT;
     constexpr int BLK = kPage * D;               // elements per block
     constexpr int BLK_CH = BLK / 8;              // 16-byte chunks per block
     constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
     __shared__ __attribute__((aligned(16))) u16 smem[8 * BLK];   // K0..K3, V0..V3
+    __shared__ uint4 s_mk[TREE ? kRowsPerGroup : 1];              // tree rows: ancestor masks
 
     // kv head fastest: the workgroups of one (sequence, split) start together and
     // fetch the Hkv blocks of each page (adjacent in the pool) at about the same time
@@ -315,16 +399,22 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
 #pragma unroll
     for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
         pid[r] = page_table[(size_t)s * max_pages + min(pg0 + r * kWave + lane, max_pages - 1)];
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int G = Hq / Hkv;
+    const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
+    // tree rows: this lane's ancestor mask (row clamped to the table; unused lanes
+    // discard it), requested with the metadata and parked in LDS for the tiles that
+    // reach past pos
+    uint4 mk = make_uint4(0, 0, 0, 0);
+    if (TREE) mk = tree_mask[(size_t)s * (kmax + 1) + min((m_tile0 + l16) / G, kmax)];
     const SeqInfo si = info[s];
     const int ks = k[s], P0 = pos[s];
     if (!si.valid) return;
-    const int G = Hq / Hkv, T = ks + 1, M = G * T, last = P0 + T - 1;
+    const int T = ks + 1, M = G * T, last = P0 + T - 1;
     if (c0 > last) return;
     if (mgroup * kRowsPerGroup >= M) return;
     const int c1 = min(c0 + split, last + 1);
 
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
     const bool active = m_tile0 < M;
     const int m = m_tile0 + l16;
     const bool m_ok = m < M;
@@ -377,6 +467,8 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
         }
     };
     load_tile(c0);
+    // after the first tile's loads are issued, so that they do not wait on the mask
+    if (TREE && lq == 0) s_mk[wave * 16 + l16] = mk;   // read after the first tile's barriers
     for (int t0 = c0; t0 < c1; t0 += kKT) {
         __syncthreads();  // previous tile's LDS reads are done
 #pragma unroll
@@ -384,9 +476,12 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
         __syncthreads();
         if (t0 + kKT < c1) load_tile(t0 + kKT);
         if (!active) continue;
-        const bool full = t0 + kKT - 1 <= P0 + m_tile0 / G;    // every token <= every row's position
+        // full: every row keeps every key of the tile (chain: the tile ends at or before
+        // the first row's position; tree: at or before the root)
+        const bool full = t0 + kKT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
+        const uint64_t win = (TREE && !full) ? tree_window(s_mk[wave * 16 + l16], t0 - P0 + 64) : 0ull;
         const LdsTile<D> src{smem + lane * 8, smem + 4 * BLK + lane * 4};
-        TM::run(qf, src, t0, p_m, full, lq, scale_log2, m_run, l_lane, o);
+        TM::template run<TREE>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
     }
     if (!active) return;
     const size_t idx = ((size_t)(si.off + jrow) * Hq + h) * n_splits + c;
@@ -461,10 +556,12 @@ static int64_t split_count(int32_t max_pages, int32_t split) {
 }
 
 struct AttnWs {
-    size_t info_off, flag_off, rows_off, ml_off, o_off, total;
+    size_t info_off, flag_off, rows_off, ml_off, o_off, mask_off, total;
 };
 
-static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_t n_splits) {
+// tree_rows: ancestor masks kept for a tree call (B * (kmax + 1)), 0 for chains
+static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_t n_splits,
+                             int64_t tree_rows = 0) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     AttnWs w;
     w.info_off = 0;
@@ -472,7 +569,8 @@ static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_
     w.rows_off = w.flag_off + 256;
     w.ml_off = w.rows_off + up(sizeof(RowRec) * (size_t)R);
     w.o_off = w.ml_off + up(sizeof(float2) * (size_t)R * Hq * n_splits);
-    w.total = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
+    w.mask_off = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
+    w.total = w.mask_off + up(sizeof(uint4) * (size_t)tree_rows);
     return w;
 }
 
@@ -480,12 +578,19 @@ template <int D>
 static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, const int32_t* pt,
                         int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
                         const RowRec* rows, const int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
-                        int split, int n_splits, float2* ml, float* po, u16* out, hipStream_t st) {
+                        int split, int n_splits, float2* ml, float* po, u16* out, const uint4* tree_mask,
+                        hipStream_t st) {
     const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
-    hipLaunchKernelGGL(attn_split_kernel<D>, grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
-                       max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po);
+    if (tree_mask)
+        hipLaunchKernelGGL((attn_split_kernel<D, true>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
+                           pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
+                           tree_mask, kmax);
+    else
+        hipLaunchKernelGGL((attn_split_kernel<D, false>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
+                           pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
+                           tree_mask, kmax);
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
                        rows, packing_ok, R, Hq, n_splits, ml, po, out);
@@ -512,54 +617,101 @@ size_t spec_verify_attn_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_
     return sv::attn_ws_layout(B, R, Hq, D, sv::split_count(max_pages, split)).total;
 }
 
-int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
-                     spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
-                     const int32_t* page_table, int32_t max_pages, const int32_t* pos,
-                     const int32_t* k, int32_t kmax, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
-                     int32_t D, float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
-                     size_t workspace_bytes, int32_t* seq_status, void* stream) {
-    using namespace sv;
+size_t spec_verify_attn_tree_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                             int32_t max_pages, int32_t kv_split_tokens, int32_t kmax) {
+    (void)Hkv;
+    if (B < 1 || R < 1 || Hq < 1 || D < 1 || max_pages < 1 || kmax < 0) return 0;
+    const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
+    return sv::attn_ws_layout(B, R, Hq, D, sv::split_count(max_pages, split), (int64_t)B * (kmax + 1)).total;
+}
+
+}  // extern "C"
+
+namespace sv {
+
+// Shared body of the chain and tree entry points (parent == nullptr: chain rows).
+static int verify_attn_impl(const char* name, const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
+                            spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages, const int32_t* page_table,
+                            int32_t max_pages, const int32_t* pos, const int32_t* k, const int32_t* parent,
+                            int32_t kmax, int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                            int32_t kv_split_tokens, spec_bf16* out, void* workspace, size_t workspace_bytes,
+                            int32_t* seq_status, void* stream) {
     last_error().clear();
-    if (D != 64 && D != 128 && D != 256) return fail(SPEC_EINVAL, "spec_verify_attn: D=%d not in {64,128,256}", D);
-    if (Hkv < 1 || Hq < Hkv || Hq % Hkv) return fail(SPEC_EINVAL, "spec_verify_attn: Hq=%d Hkv=%d (need Hq %% Hkv == 0)", Hq, Hkv);
-    if (Hq / Hkv > 16) return fail(SPEC_EINVAL, "spec_verify_attn: Hq/Hkv=%d > 16", Hq / Hkv);
-    if (B < 1 || B > 4096) return fail(SPEC_EINVAL, "spec_verify_attn: B=%d outside 1..4096", B);
-    if (R < 1) return fail(SPEC_EINVAL, "spec_verify_attn: R=%d < 1", R);
+    if (D != 64 && D != 128 && D != 256) return fail(SPEC_EINVAL, "%s: D=%d not in {64,128,256}", name, D);
+    if (Hkv < 1 || Hq < Hkv || Hq % Hkv) return fail(SPEC_EINVAL, "%s: Hq=%d Hkv=%d (need Hq %% Hkv == 0)", name, Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(SPEC_EINVAL, "%s: Hq/Hkv=%d > 16", name, Hq / Hkv);
+    if (B < 1 || B > 4096) return fail(SPEC_EINVAL, "%s: B=%d outside 1..4096", name, B);
+    if (R < 1) return fail(SPEC_EINVAL, "%s: R=%d < 1", name, R);
     if (kmax < 0 || (long long)(Hq / Hkv) * (kmax + 1) > kMaxRowsPerKvHead)
-        return fail(SPEC_EINVAL, "spec_verify_attn: kmax=%d (need 0 <= (Hq/Hkv)*(kmax+1) <= %d)", kmax, kMaxRowsPerKvHead);
-    if (max_pages < 1 || n_pages < 1) return fail(SPEC_EINVAL, "spec_verify_attn: max_pages=%d n_pages=%lld", max_pages, (long long)n_pages);
-    if (!(scale > 0.f)) return fail(SPEC_EINVAL, "spec_verify_attn: scale must be > 0");
+        return fail(SPEC_EINVAL, "%s: kmax=%d (need 0 <= (Hq/Hkv)*(kmax+1) <= %d)", name, kmax, kMaxRowsPerKvHead);
+    if (max_pages < 1 || n_pages < 1) return fail(SPEC_EINVAL, "%s: max_pages=%d n_pages=%lld", name, max_pages, (long long)n_pages);
+    if (!(scale > 0.f)) return fail(SPEC_EINVAL, "%s: scale must be > 0", name);
     if (kv_split_tokens < 0 || kv_split_tokens % kKT || kv_split_tokens > kMaxSplit)
-        return fail(SPEC_EINVAL, "spec_verify_attn: kv_split_tokens=%d not a multiple of 64 in 0..%d", kv_split_tokens, kMaxSplit);
+        return fail(SPEC_EINVAL, "%s: kv_split_tokens=%d not a multiple of 64 in 0..%d", name, kv_split_tokens, kMaxSplit);
     if (!q || !k_new || !v_new || !k_pool || !v_pool || !page_table || !pos || !k || !out || !seq_status)
-        return fail(SPEC_EINVAL, "spec_verify_attn: null required pointer");
+        return fail(SPEC_EINVAL, "%s: null required pointer", name);
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
-        return fail(SPEC_EINVAL, "spec_verify_attn: q, k_new, v_new, k_pool, v_pool and out must be 16-byte aligned");
+        return fail(SPEC_EINVAL, "%s: q, k_new, v_new, k_pool, v_pool and out must be 16-byte aligned", name);
     const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
     const int64_t n_splits = split_count(max_pages, split);
     if (n_splits * 2 * Hkv > 0x7fffffffLL || (long long)B * Hkv * n_splits > 0x7fffffffLL)
-        return fail(SPEC_ECAPACITY, "spec_verify_attn: too many splits");
-    const AttnWs lay = attn_ws_layout(B, R, Hq, D, n_splits);
+        return fail(SPEC_ECAPACITY, "%s: too many splits", name);
+    const AttnWs lay = attn_ws_layout(B, R, Hq, D, n_splits, parent ? (int64_t)B * (kmax + 1) : 0);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace))
-        return fail(SPEC_EWORKSPACE, "spec_verify_attn: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, lay.total);
+        return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes, lay.total);
     char* ws = static_cast<char*>(workspace);
     SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + lay.info_off);
     int32_t* packing_ok = reinterpret_cast<int32_t*>(ws + lay.flag_off);
     RowRec* rows = reinterpret_cast<RowRec*>(ws + lay.rows_off);
     float2* ml = reinterpret_cast<float2*>(ws + lay.ml_off);
     float* po = reinterpret_cast<float*>(ws + lay.o_off);
+    uint4* tree_mask = parent ? reinterpret_cast<uint4*>(ws + lay.mask_off) : nullptr;
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(attn_prep_kernel, dim3(B), dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
+    // enough workgroups per sequence that every thread appends at most kPrepItems chunks
+    const long long max_items = (long long)(kmax + 1) * Hkv * (D / 8);
+    const dim3 prep_grid(B, (unsigned)((max_items + kPrepItemsPerWg - 1) / kPrepItemsPerWg));
+    hipLaunchKernelGGL(attn_prep_kernel, prep_grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
                        n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, split, info, rows, packing_ok,
-                       seq_status);
-    SV_LAUNCH_CHECK("spec_verify_attn(prep)");
+                       seq_status, parent, tree_mask);
+    SV_LAUNCH_CHECK(name);
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
     }
-    SV_LAUNCH_CHECK("spec_verify_attn");
+    SV_LAUNCH_CHECK(name);
     return SPEC_OK;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
+                     spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
+                     const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                     const int32_t* k, int32_t kmax, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,
+                     int32_t D, float scale, int32_t kv_split_tokens, spec_bf16* out, void* workspace,
+                     size_t workspace_bytes, int32_t* seq_status, void* stream) {
+    return sv::verify_attn_impl("spec_verify_attn", q, k_new, v_new, k_pool, v_pool, n_pages, page_table, max_pages,
+                                pos, k, nullptr, kmax, B, R, Hq, Hkv, D, scale, kv_split_tokens, out, workspace,
+                                workspace_bytes, seq_status, stream);
+}
+
+int spec_verify_attn_tree(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
+                          spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
+                          const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                          const int32_t* k, const int32_t* parent, int32_t kmax, int32_t B, int32_t R,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t kv_split_tokens,
+                          spec_bf16* out, void* workspace, size_t workspace_bytes, int32_t* seq_status,
+                          void* stream) {
+    if (!parent) {
+        sv::last_error().clear();
+        return sv::fail(SPEC_EINVAL, "spec_verify_attn_tree: null parent");
+    }
+    return sv::verify_attn_impl("spec_verify_attn_tree", q, k_new, v_new, k_pool, v_pool, n_pages, page_table,
+                                max_pages, pos, k, parent, kmax, B, R, Hq, Hkv, D, scale, kv_split_tokens, out,
+                                workspace, workspace_bytes, seq_status, stream);
 }
 
 }  // extern "C"

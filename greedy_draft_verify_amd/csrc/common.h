@@ -51,6 +51,43 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
     return r;
 }
 
+// ---- ragged row packing ------------------------------------------------------
+// Exclusive prefix sums of (k_s + 1) over s (the packed row offsets) for B <= the
+// size of s_off, by a block of NT threads (each a contiguous segment of sequences,
+// then a Hillis-Steele scan of the segment sums). Returns whether the packing is
+// defined: every k_s >= 0 and the sum equals R. Every thread must call it.
+template <int NT>
+__device__ __forceinline__ bool block_row_offsets(const int32_t* __restrict__ k, int B, int R,
+                                                  long long* s_scan, int* s_off, int* s_bad) {
+    const int tid = threadIdx.x;
+    if (tid == 0) *s_bad = 0;
+    __syncthreads();
+    const int per = (B + NT - 1) / NT;
+    const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
+    long long local = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int ks = k[s];
+        if (ks < 0) *s_bad = 1;
+        local += (long long)ks + 1;
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int d = 1; d < NT; d <<= 1) {
+        const long long v = tid >= d ? s_scan[tid - d] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    const long long total = s_scan[NT - 1];
+    long long run = tid ? s_scan[tid - 1] : 0;
+    for (int s = s0; s < s1; ++s) {
+        s_off[s] = (int)run;
+        run += (long long)k[s] + 1;
+    }
+    __syncthreads();
+    return total == (long long)R && !*s_bad;
+}
+
 // ---- host error reporting ---------------------------------------------------
 std::string& last_error();
 int fail(int code, const char* fmt, ...);

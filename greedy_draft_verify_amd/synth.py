@@ -21,6 +21,9 @@ Workloads (names used by tests and the benchmark):
 * ``long``    B=8, k=6, context 131072, 16q/2kv, head_dim 256, hidden 5120,
               vocab 151936, 32768-entry draft->target id map.
 * ``delta``   Gated DeltaNet: B=32, T=5, 32 heads, d_k=d_v=128.
+* ``b16tree`` the b16k4 shapes with a 16-node draft tree per sequence (k=15):
+              a spine of head drafts created first, then side branches (trie) or
+              star siblings at the root; see ``make_parents``.
 
 The pool holds every page of every sequence plus a quarter spare, shuffled; the
 pages a sequence does not own are random bf16 too, so any leak into a result
@@ -78,10 +81,14 @@ WORKLOADS = {
                            n_d2t=32768, w_std=1 / math.sqrt(5120)),
 }
 
+WORKLOADS["b16tree"] = VerifyWorkload("b16tree", B=16, k=15, k_lo=15, k_hi=15, ctx_lo=512, ctx_hi=4096,
+                                      Hq=32, Hkv=8, D=128, H=4096, V=151936,
+                                      max_pages=(4096 + 64) // PAGE, w_std=1 / 64)
+
 TENSOR_IDS = {name: i for i, name in enumerate(
     ["pos", "k", "pool_perm", "k_pool", "v_pool", "q", "k_new", "v_new", "hidden", "w", "drafts",
-     "corrupt", "d2t", "dq", "dk", "dv", "da", "db", "dstate", "dL", "extra"])}
-WORKLOAD_IDS = {"tiny": 1, "b16k4": 2, "ragged": 3, "long": 4, "delta": 5}
+     "corrupt", "d2t", "dq", "dk", "dv", "da", "db", "dstate", "dL", "extra", "parent"])}
+WORKLOAD_IDS = {"tiny": 1, "b16k4": 2, "ragged": 3, "long": 4, "delta": 5, "b16tree": 6}
 
 
 def tensor_seed(seed: int, workload: str, tensor: str) -> int:
@@ -227,6 +234,69 @@ def make_drafts(wl: VerifyWorkload, k: np.ndarray, true_next: np.ndarray, seed: 
                 drafts[s, j] = x + (x >= truth)
             else:
                 drafts[s, j] = truth
+    return drafts
+
+
+def make_parents(k: np.ndarray, seed: int = 0, name: str = "b16tree", shape: str = "trie",
+                 kmax: int | None = None, spine_frac: float = 0.5) -> np.ndarray:
+    """Parent lists [B, kmax + 1] int32 of draft trees in creation order (node 0 = root,
+    parent -1; node i's parent in [0, i)); entries past k_s are -1.
+
+    shape "chain": parent i - 1. "star": every node a child of the root (depth 1).
+    "trie": like a tree draft grown by a head chain and then widened: the first
+    round(spine_frac * k_s) nodes form a spine under the root, each later node hangs
+    under a uniformly drawn earlier node (spine nodes twice as likely).
+    "random": every node under a uniformly drawn earlier node.
+    """
+    B = len(k)
+    kmax = int(np.max(k)) if kmax is None else kmax
+    rng = np_rng(seed, name, "parent")
+    par = np.full((B, kmax + 1), -1, np.int32)
+    for s in range(B):
+        ks = int(k[s])
+        n_spine = int(round(spine_frac * ks))
+        for i in range(1, ks + 1):
+            if shape == "chain":
+                par[s, i] = i - 1
+            elif shape == "star":
+                par[s, i] = 0
+            elif shape == "random":
+                par[s, i] = int(rng.integers(0, i))
+            elif shape == "trie":
+                if i <= n_spine:
+                    par[s, i] = i - 1
+                else:
+                    w = np.array([2.0 if j <= n_spine else 1.0 for j in range(i)])
+                    par[s, i] = int(rng.choice(i, p=w / w.sum()))
+            else:
+                raise ValueError(shape)
+    return par
+
+
+def make_tree_drafts(wl: VerifyWorkload, k: np.ndarray, parent: np.ndarray, target: np.ndarray,
+                     seed: int = 0) -> np.ndarray:
+    """Drafts [B, kmax] int32 for tree nodes from the target's greedy tokens.
+
+    ``target[s][u]`` is the greedy token of node u's row. Node i's draft starts as the
+    target of its parent (the token that would be accepted there) and, with the
+    sequence's corruption probability, is replaced by a uniform id different from it.
+    Unused slots are -1.
+    """
+    B = len(k)
+    kmax = parent.shape[1] - 1
+    rc = np_rng(seed, wl.name, "corrupt")
+    rd = np_rng(seed, wl.name, "drafts")
+    p_lo, p_hi = wl.p_corrupt
+    drafts = np.full((B, max(kmax, 1)), -1, np.int32)
+    for s in range(B):
+        p = rc.uniform(p_lo, p_hi)
+        for i in range(1, int(k[s]) + 1):
+            truth = int(target[s][parent[s, i]])
+            if rc.uniform() < p:
+                x = int(rd.integers(0, wl.V - 1))
+                drafts[s, i - 1] = x + (x >= truth)
+            else:
+                drafts[s, i - 1] = truth
     return drafts
 
 

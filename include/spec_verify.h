@@ -11,6 +11,12 @@
  *   spec_greedy_accept         greedy acceptance and position rollback
  *   spec_delta_verify_rollback Gated DeltaNet per-token state record and restore
  *
+ * and, for drafts shaped as a tree (trie or star) instead of a chain:
+ *
+ *   spec_verify_attn_tree      the attention step over tree rows
+ *   spec_tree_accept           the acceptance walk from the root
+ *   spec_kv_compact            the accepted path's K/V moved to contiguous slots
+ *
  * The method follows the page "span-02 engine/crates/model/src/spec.rs"
  * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
  * pages, KV appended in place at pos..pos+k, greedy acceptance, rollback by
@@ -68,6 +74,7 @@ typedef uint16_t spec_bf16;
 #define SPEC_STATUS_BAD_POS 2   /* pos_s < 0, or (pos_s + k_s) / 16 >= max_pages         */
 #define SPEC_STATUS_BAD_ROWS 4  /* packing undefined (see above), or k_s > kmax           */
 #define SPEC_STATUS_BAD_TOKEN 8 /* draft id outside its vocabulary, or d2t entry >= V     */
+#define SPEC_STATUS_BAD_TREE 16 /* tree calls: a parent not before its node, a bad path   */
 
 /* Library version (increases with any ABI or numerics change). */
 int spec_version(void);
@@ -249,6 +256,84 @@ int spec_delta_verify_rollback(int32_t mode, const spec_bf16* q, const spec_bf16
                                const spec_bf16* v, const float* a, const float* b, float q_scale,
                                float* state, float* rec, const int32_t* L, int32_t B, int32_t T,
                                int32_t Hd, int32_t dk, int32_t dv, spec_bf16* o, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tree drafts (trie or star).
+ *
+ * Defined by: DSSD fast.py _set_rows (tree rows carry a position, a KV slot, the
+ * length of the contiguous prefix they read and the slots of their path),
+ * _tree_cycle (rows are the trie's nodes in creation order; node i sits at
+ * position pos + depth(i), writes its K/V at slot pos + i and attends to slots
+ * [0, pos] and to the slots of its own path; the walk from the root follows the
+ * child whose token equals the current node's target; the accepted path's K/V is
+ * compacted to slots pos + 1, ...) and _star_cycle (the depth-1 case: children at
+ * position pos + 1 on slots pos + 1 + i; the first child whose token matches).
+ *
+ * The k_s + 1 rows of sequence s (packed as for the chain calls) are its tree's
+ * nodes in creation order: row j is node j, node 0 the root (the last emitted
+ * token), node i >= 1 carries drafts[s][i - 1]. parent [B][kmax + 1] int32 holds
+ * parent[s][0] = -1 and parent[s][i] in [0, i) for 1 <= i <= k_s (entries past
+ * k_s are unread); anything else flags the sequence SPEC_STATUS_BAD_TREE.
+ * path(j) = the nodes from the root's child down to j (empty for the root).
+ * The caller computes row j's position pos + depth(j) (for RoPE and the like)
+ * from the same parent list; the library needs only slots.
+ * A chain (parent[s][i] = i - 1) gives the results of the chain calls.
+ * ------------------------------------------------------------------------- */
+
+/* spec_verify_attn_tree — KV append + attention over tree rows (one layer).
+ * As spec_verify_attn (same layouts, limits, split-KV rule, workspace rules,
+ * status bits and skip behaviour), except that row j of sequence s appends at slot
+ * pos[s] + j and attends, for query head h, to the key slots
+ *   t in {0, ..., pos[s]}  followed by  {pos[s] + u : u in path(j)}
+ * (ascending slot order, which is the path's root-to-leaf order), i.e.
+ *   out[r, h, :] = sum_t softmax_t(scale * q[r,h,:] . K_t[hk,:]) V_t[hk,:].
+ * Extra limit: kmax <= 127. workspace: spec_verify_attn_tree_workspace_bytes. */
+size_t spec_verify_attn_tree_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                             int32_t max_pages, int32_t kv_split_tokens, int32_t kmax);
+int spec_verify_attn_tree(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,
+                          spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages,
+                          const int32_t* page_table, int32_t max_pages, const int32_t* pos,
+                          const int32_t* k, const int32_t* parent, int32_t kmax, int32_t B, int32_t R,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t kv_split_tokens,
+                          spec_bf16* out, void* workspace, size_t workspace_bytes, int32_t* seq_status,
+                          void* stream);
+
+/* spec_tree_accept — the greedy acceptance walk over a tree.
+ * argmax [R] int32 (the greedy token of every row), drafts [B][kmax], d2t,
+ * n_draft_vocab, V, pos_in and the outputs as spec_greedy_accept; parent as above;
+ * path [B][kmax] int32 (output).
+ * Walk: u = root; while some child c of u (parent[s][c] == u) has
+ * map(drafts[s][c - 1]) == argmax[off_s + u], move to the lowest-index such c.
+ * With accepted nodes u_1 .. u_a:
+ *   accept_len = a, emit[s][0..a] = map(tokens of u_1..u_a), argmax[off_s + u_a]
+ *   (-1 after), n_emit = a + 1, next_tok = argmax[off_s + u_a],
+ *   pos_out = pos_in + a + 1, path[s] = u_1 .. u_a (-1 after).
+ * A flagged sequence (status bits as spec_greedy_accept, plus BAD_TREE) gets
+ * accept_len -1, n_emit 0, next_tok -1, pos_out = pos_in, emit and path all -1.
+ * Limits: 1 <= B <= 8192, 0 <= kmax <= 127, R >= 1, V >= 1. */
+int spec_tree_accept(const int32_t* argmax, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                     const int32_t* parent, const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B,
+                     int32_t R, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
+                     int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* path, int32_t* seq_status,
+                     void* stream);
+
+/* spec_kv_compact — moves the accepted path's K/V to contiguous slots.
+ * For every sequence with seq_status[s] == 0 on entry: for d = 0 .. accept_len[s]-1
+ * the K and V of slot pos[s] + path[s][d] (every kv head) are copied to slot
+ * pos[s] + 1 + d, with the result of doing so in ascending d. Afterwards slots
+ * 0 .. pos + a hold what a chain of the accepted tokens would have written, and
+ * the next cycle's pos is pos + a + 1. Call it with the pos_in, path and
+ * accept_len of spec_tree_accept, once per layer's pool.
+ * Checks before any write (then the sequence is flagged and nothing moves):
+ * accept_len <= kmax, 1 <= path[d] <= kmax strictly increasing (BAD_TREE), pos >= 0
+ * and every slot's page inside the page table (BAD_POS), page ids in [0, n_pages)
+ * (BAD_PAGE). seq_status is in/out: nonzero entries are left as they are (the
+ * sequence is skipped), zero entries receive these bits.
+ * Layouts as spec_verify_attn. Limits: D in {64, 128, 256}, 1 <= Hkv <= 64,
+ * B >= 1, 0 <= kmax <= 127; 16-byte aligned pools. */
+int spec_kv_compact(spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages, const int32_t* page_table,
+                    int32_t max_pages, const int32_t* pos, const int32_t* path, const int32_t* accept_len,
+                    int32_t kmax, int32_t B, int32_t Hkv, int32_t D, int32_t* seq_status, void* stream);
 
 #ifdef __cplusplus
 }

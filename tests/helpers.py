@@ -130,3 +130,60 @@ def gpu_accept(g, drafts, k, d2t, V, pos, dev, kmax=None):
 def assert_accept_equal(got, ref, what):
     for key in ("status", "accept_len", "n_emit", "pos_out", "next_tok", "emit"):
         assert np.array_equal(got[key], ref[key]), f"{what}: {key} gpu {got[key]} ref {ref[key]}"
+
+
+# ---------------------------------------------------------------------------
+# tree rows
+# ---------------------------------------------------------------------------
+def gpu_attn_tree(x: synth.VerifyInputs, parent, dev, kv_split_tokens=0, k=None, k_pool=None, v_pool=None):
+    """Runs spec_verify_attn_tree; returns (out bf16 device, k_pool, v_pool, status np)."""
+    import greedy_draft_verify_amd as gdv
+    k = x.k if k is None else k
+    R = x.q.shape[0]
+    kp = (x.k_pool if k_pool is None else k_pool).to(dev).clone()
+    vp = (x.v_pool if v_pool is None else v_pool).to(dev).clone()
+    out = torch.full((R, x.wl.Hq, x.wl.D), float("nan"), dtype=torch.bfloat16, device=dev)
+    status = torch.full((len(x.pos),), -7, dtype=torch.int32, device=dev)
+    gdv.spec_verify_attn_tree(x.q.to(dev).contiguous(), x.k_new.to(dev).contiguous(), x.v_new.to(dev).contiguous(),
+                              kp, vp, i32(x.page_table, dev), i32(x.pos, dev), i32(k, dev), i32(parent, dev), x.scale,
+                              out, status, kv_split_tokens=kv_split_tokens)
+    torch.cuda.synchronize()
+    return out, kp, vp, status.cpu().numpy()
+
+
+def oracle_attn_tree(x: synth.VerifyInputs, parent, seqs=None):
+    """Oracle tree attention for the selected sequences: (rows, out fp64, k_pool, v_pool, status)."""
+    wl = x.wl
+    B = len(x.pos)
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    off_all = np.concatenate([[0], np.cumsum(x.k + 1)]).astype(np.int64)
+    rows = np.concatenate([np.arange(off_all[s], off_all[s + 1]) for s in seqs])
+    kp, vp = bits(x.k_pool).copy(), bits(x.v_pool).copy()
+    pos, k, pt = x.pos[seqs], x.k[seqs], x.page_table[seqs]
+    par = np.ascontiguousarray(np.asarray(parent)[seqs], np.int32)
+    kmax = par.shape[1] - 1
+    qb, knb, vnb = bits(x.q)[rows], bits(x.k_new)[rows], bits(x.v_new)[rows]
+    R = len(rows)
+    off, st = oracle.validate(pt, pt.shape[1], x.n_pages, pos, k, kmax, len(seqs), R)
+    oracle.validate_tree(par, kmax, k, len(seqs), st)
+    oracle.append_kv(knb, vnb, kp, vp, pt, pt.shape[1], pos, k, off, st, len(seqs), wl.Hkv, wl.D)
+    out = oracle.verify_attn_tree(qb, kp, vp, pt, pt.shape[1], pos, k, par, kmax, off, st, len(seqs), R, wl.Hq,
+                                  wl.Hkv, wl.D, x.scale)
+    return rows, out, kp, vp, st
+
+
+def gpu_tree_accept(g, drafts, k, parent, d2t, V, pos, dev):
+    import greedy_draft_verify_amd as gdv
+    B = len(k)
+    drafts = np.ascontiguousarray(drafts, np.int32)
+    kmax = drafts.shape[1]
+    z = lambda: torch.full((B,), -9, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, st = z(), z(), z(), z(), z()
+    emit = torch.full((B, kmax + 1), -9, dtype=torch.int32, device=dev)
+    path = torch.full((B, kmax), -9, dtype=torch.int32, device=dev)
+    gdv.spec_tree_accept(i32(g, dev), i32(drafts, dev), i32(k, dev), i32(parent, dev),
+                         None if d2t is None else i32(d2t, dev), V, i32(pos, dev), pos_out, acc, ne, emit, nt, path, st)
+    torch.cuda.synchronize()
+    return dict(pos_out=pos_out.cpu().numpy(), accept_len=acc.cpu().numpy(), n_emit=ne.cpu().numpy(),
+                emit=emit.cpu().numpy(), next_tok=nt.cpu().numpy(), path=path.cpu().numpy(),
+                status=st.cpu().numpy())

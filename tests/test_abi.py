@@ -22,7 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
-            "spec_delta_verify_rollback"} <= set(names)
+            "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
+            "spec_kv_compact"} <= set(names)
     lib = gdv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -85,6 +86,24 @@ def test_host_argument_checks():
     assert L.spec_delta_verify_rollback(1, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 64, 128, None, None) == -1
     assert L.spec_delta_verify_rollback(2, p, p, p, p, p, 1.0, p, p, None, 1, 5, 1, 128, 128, None, None) == -1
     assert L.spec_last_error() != b""
+    # tree calls
+    need = L.spec_verify_attn_tree_workspace_bytes(2, 8, 4, 1, 64, 4, 0, 3)
+    assert need > L.spec_verify_attn_workspace_bytes(2, 8, 4, 1, 64, 4, 0)
+    tree = lambda parent, kmax, ws: L.spec_verify_attn_tree(p, p, p, p, p, 10, p, 4, p, p, parent, kmax, 2, 8, 4, 1,
+                                                            64, 0.1, 0, p, p, ws, p, None)
+    assert tree(None, 3, 1 << 30) == -1 and b"parent" in L.spec_last_error()
+    assert tree(p, 128, 1 << 30) == -1 and b"kmax" in L.spec_last_error()
+    assert tree(p, 3, need - 1) == -4
+    acc = lambda kmax, parent, path: L.spec_tree_accept(p, p, kmax, p, parent, None, 0, 100, 2, 8, p, p, p, p, p,
+                                                        p, path, p, None)
+    assert acc(128, p, p) == -1 and b"kmax" in L.spec_last_error()
+    assert acc(3, None, p) == -1 and b"null" in L.spec_last_error()
+    assert acc(3, p, None) == -1
+    cmp = lambda D, Hkv, kmax: L.spec_kv_compact(p, p, 10, p, 4, p, p, p, kmax, 2, Hkv, D, p, None)
+    assert cmp(100, 1, 3) == -1 and b"D=100" in L.spec_last_error()
+    assert cmp(64, 0, 3) == -1 and cmp(64, 1, 128) == -1
+    assert L.spec_kv_compact(_vp(0x1002), p, 10, p, 4, p, p, p, 3, 2, 1, 64, p, None) == -1
+    assert b"aligned" in L.spec_last_error()
 
 
 def test_product_path_does_not_touch_the_oracle():

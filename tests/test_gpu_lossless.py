@@ -39,7 +39,9 @@ class GpuToy:
         self.Wv = bf16(r(HKV * D, H) / 16).double().numpy()
         self.Wo = bf16(r(H, HQ * D) / 16).double().numpy()
         self.dev = dev
-        self.wp = gdv.spec_lm_head_pack(bf16(r(V, H) / 16).to(dev))
+        wlm = bf16(r(V, H) / 16)
+        self.Wlm = wlm.double().numpy()
+        self.wp = gdv.spec_lm_head_pack(wlm.to(dev))
         self.max_pages = max_pages
         self.n_pages = 2 * max_pages
         self.pt = torch.from_numpy(rng.permutation(self.n_pages)[:max_pages].astype(np.int32)[None, :]).to(dev)
@@ -48,8 +50,10 @@ class GpuToy:
         self.kp = torch.zeros((self.n_pages, HKV, 16 * D), dtype=torch.bfloat16, device=self.dev)
         self.vp = torch.zeros_like(self.kp)
 
-    def rows(self, tokens, pos, kmax):
-        """Attention + lm_head for rows tokens[j] at positions pos + j; greedy tokens."""
+    def rows(self, tokens, pos, kmax, parent=None, gaps=None):
+        """Attention + lm_head for rows tokens[j] at positions pos + j (or the nodes of a
+        draft tree with parent list ``parent`` [kmax + 1]); greedy tokens. With ``gaps``
+        (a list), appends each row's top-2 logit gap, computed on the host in fp64."""
         gdv, dev = self.gdv, self.dev
         T = len(tokens)
         e = self.E[tokens]                                               # [T, H] fp64 (exact bf16 values)
@@ -60,27 +64,74 @@ class GpuToy:
         out = torch.empty((T, HQ, D), dtype=torch.bfloat16, device=dev)
         st = torch.empty(1, dtype=torch.int32, device=dev)
         i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
-        gdv.spec_verify_attn(q, kn, vn, self.kp, self.vp, self.pt, i32([pos]), i32([T - 1]), kmax, 1 / math.sqrt(D),
-                             out, st)
+        if parent is None:
+            gdv.spec_verify_attn(q, kn, vn, self.kp, self.vp, self.pt, i32([pos]), i32([T - 1]), kmax,
+                                 1 / math.sqrt(D), out, st)
+        else:
+            gdv.spec_verify_attn_tree(q, kn, vn, self.kp, self.vp, self.pt, i32([pos]), i32([T - 1]),
+                                      i32([list(parent)]), 1 / math.sqrt(D), out, st)
         att = out.double().cpu().numpy().reshape(T, HQ * D)
-        h = bf16(np.stack([e[j] + self.Wo @ att[j] for j in range(T)])).to(dev)
+        hb = bf16(np.stack([e[j] + self.Wo @ att[j] for j in range(T)]))
+        if gaps is not None:
+            for j in range(T):
+                top = np.sort(self.Wlm @ hb[j].double().numpy())
+                gaps.append(float(top[-1] - top[-2]))
+        h = hb.to(dev)
         am = torch.empty(T, dtype=torch.int32, device=dev)
         gdv.spec_lm_head_argmax(h, self.wp, V, am)
         torch.cuda.synchronize()
         assert st.item() == 0
         return am.cpu().numpy()
 
-    def generate_ar(self, prompt, n, kmax):
+    def generate_ar(self, prompt, n, kmax, gaps=None):
+        """One-row greedy decoding; ``gaps`` (a list) receives, for every emitted token,
+        the top-2 logit gap of the row that chose it."""
         self.reset()
         g = None
         for i, t in enumerate(prompt):
-            g = int(self.rows([t], i, kmax)[0])
+            gl = []
+            g = int(self.rows([t], i, kmax, gaps=gl)[0])
         out, pos = [], len(prompt)
         while len(out) < n:
             out.append(g)
-            g = int(self.rows([g], pos, kmax)[0])
+            if gaps is not None:
+                gaps.append(gl[0])
+            gl = []
+            g = int(self.rows([g], pos, kmax, gaps=gl)[0])
             pos += 1
         return out
+
+    def generate_tree(self, prompt, n, drafter, kmax):
+        """Tree drafts: ``drafter(out)`` gives (parents, tokens) of the nodes below the root in
+        creation order; one tree verify, the acceptance walk, compaction, pos += a + 1."""
+        gdv, dev = self.gdv, self.dev
+        self.reset()
+        for i, t in enumerate(prompt[:-1]):
+            self.rows([t], i, kmax)
+        x0, pos = prompt[-1], len(prompt) - 1
+        out, hist = [], []
+        i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+        while len(out) < n:
+            par, toks = drafter(out)
+            k = len(toks)
+            parent = [-1] + list(par) + [-1] * (kmax - k)
+            drafts = [int(t) for t in toks] + [-1] * (kmax - k)
+            g = self.rows([x0] + [int(t) for t in toks], pos, kmax, parent=parent)
+            z = lambda: torch.empty(1, dtype=torch.int32, device=dev)
+            pos_out, acc, ne, nt, st = z(), z(), z(), z(), z()
+            emit = torch.empty((1, kmax + 1), dtype=torch.int32, device=dev)
+            path = torch.empty((1, kmax), dtype=torch.int32, device=dev)
+            pos_t = i32([pos])
+            gdv.spec_tree_accept(i32(g), i32([drafts]), i32([k]), i32([parent]), None, V, pos_t, pos_out, acc, ne,
+                                 emit, nt, path, st)
+            gdv.spec_kv_compact(self.kp, self.vp, self.pt, pos_t, path, acc, st)
+            torch.cuda.synchronize()
+            assert st.item() == 0
+            m = ne.item()
+            out.extend(emit.cpu().numpy()[0, :m].tolist())
+            hist.append(acc.item())
+            pos, x0 = pos_out.item(), nt.item()
+        return out[:n], hist
 
     def generate_spec(self, prompt, n, drafter, k):
         gdv, dev = self.gdv, self.dev
@@ -114,6 +165,16 @@ def toy():
     return m, prompt, ref
 
 
+@pytest.fixture(scope="module")
+def toy_tree():
+    dev = torch.device("cuda:0")
+    m = GpuToy(dev)
+    prompt = list(np.random.default_rng(1).integers(0, V, 24))
+    gaps = []
+    ref = m.generate_ar(prompt, N_NEW + 16, kmax=15, gaps=gaps)
+    return m, prompt, ref, gaps
+
+
 @pytest.mark.parametrize("kind,k", [("perfect", 4), ("corrupt", 4), ("random", 3), ("corrupt", 6)])
 def test_gpu_spec_stream_equals_one_row_stream(toy, kind, k):
     m, prompt, ref = toy
@@ -132,3 +193,44 @@ def test_gpu_spec_stream_equals_one_row_stream(toy, kind, k):
     assert out == ref[:N_NEW]
     if kind == "perfect":
         assert min(hist[:-1]) == k
+
+
+@pytest.mark.parametrize("shape", ["star", "spine", "trie"])
+def test_gpu_tree_stream_equals_one_row_stream(toy_tree, shape):
+    """Tree cycles (attention over tree rows, the acceptance walk, compaction) emit the
+    one-row stream. A tree row sums its path keys in slot order, not in the order of
+    its one-row decode, so its bytes may differ in the last bits from that decode's
+    unless its path is a creation-order prefix (the "spine" shape accepts only such
+    paths, so it must match exactly); with branches, the streams may part only at a
+    token whose one-row top-2 logit gap is a near-tie (< 5e-2)."""
+    m, prompt, ref, gaps = toy_tree
+    rng = np.random.default_rng(12)
+
+    def drafter(out):
+        true = ref[len(out):len(out) + 8]
+        true = true + [0] * (8 - len(true))
+        wrong = lambda t: int((t + 1 + rng.integers(0, V - 1)) % V)
+        if shape == "star":
+            kids = [wrong(true[0]) for _ in range(4)]
+            if rng.uniform() < 0.8:
+                kids[int(rng.integers(0, 4))] = true[0]
+            return [0] * 4, kids
+        par, toks, spine = [], [], [0]
+        for d in range(6):
+            par.append(spine[-1])
+            toks.append(true[d] if rng.uniform() < 0.8 else wrong(true[d]))
+            spine.append(len(toks))
+        if shape == "trie":       # side branches created after the spine, some holding the truth
+            for d in range(6):
+                if rng.uniform() < 0.6:
+                    par.append(spine[d])
+                    toks.append(true[d] if toks[spine[d + 1] - 1] != true[d] else wrong(true[d]))
+        return par, toks
+
+    out, hist = m.generate_tree(prompt, N_NEW, drafter, kmax=15)
+    n_same = next((i for i, (a, b) in enumerate(zip(out, ref)) if a != b), N_NEW)
+    if shape == "spine":
+        assert n_same == N_NEW
+    else:
+        assert n_same == N_NEW or gaps[n_same] < 5e-2, (n_same, gaps[n_same])
+    assert max(hist) >= (1 if shape == "star" else 3)

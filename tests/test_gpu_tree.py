@@ -1,0 +1,282 @@
+"""GPU parity of the tree (trie / star) entry points against the CPU oracle.
+
+DSSD fast.py _set_rows / _tree_cycle / _star_cycle: rows are the nodes of a draft
+tree in creation order; node j appends at slot pos + j and attends to slots 0..pos
+plus the slots of its own path; the acceptance walk follows the child whose token is
+the current node's greedy token; the accepted path's K/V moves to slots pos + 1...
+
+Bars: tree attention within |err| <= 2e-2 + 1e-2 |ref| of the oracle, the K/V append
+and the compaction bit-exact, the acceptance walk bit-exact; a chain-shaped tree
+gives the chain entry point's bytes, and a row's bytes do not depend on the nodes
+outside its path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from greedy_draft_verify_amd import synth
+from tests.conftest import gpu_available
+from tests.helpers import (assert_close, bits, gpu_attn, gpu_attn_tree, gpu_tree_accept, i32,
+                           oracle_attn_tree)
+from tests.test_gpu_kernels import _wl
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import greedy_draft_verify_amd as gdv
+    gdv.lib()
+    return torch.device("cuda:0")
+
+
+TREE_CASES = [
+    # name, B, k range, ctx range, Hq, Hkv, D, max_pages
+    _wl("t64", 3, 3, 9, 1, 700, 4, 1, 64, 64),
+    _wl("t128", 4, 5, 15, 200, 1100, 32, 8, 128, 80),      # G * (kmax + 1) = 64
+    _wl("t256", 2, 6, 12, 500, 900, 16, 2, 256, 64),       # G * (kmax + 1) = 104
+    _wl("tbig", 2, 100, 127, 30, 300, 1, 1, 64, 32),       # 128 nodes: every mask word, two row groups
+]
+
+
+def _tree_case(wl, seed, shape):
+    x = synth.make_verify_inputs(wl, seed=seed, with_lm_head=False)
+    parent = synth.make_parents(x.k, seed, wl.name, shape, kmax=wl.kmax)
+    return x, parent
+
+
+@pytest.mark.parametrize("wl", TREE_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("shape", ["trie", "star", "random"])
+@pytest.mark.parametrize("split", [0, 64])
+def test_tree_attention_parity(dev, wl, shape, split):
+    print(f"tree attention {wl.name} {shape} split={split}", flush=True)
+    x, parent = _tree_case(wl, 0, shape)
+    out, kp, vp, st = gpu_attn_tree(x, parent, dev, kv_split_tokens=split)
+    rows, ref, kp_ref, vp_ref, st_ref = oracle_attn_tree(x, parent)
+    assert (st == 0).all() and (st_ref == 0).all()
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref)
+    assert_close(out.float().cpu().numpy(), ref, f"tree attention {wl.name} {shape}")
+
+
+def test_b16tree_attention_sampled(dev):
+    """The 16-node tree workload at full size (context up to 4096, 32q / 8kv, D = 128):
+    a third of the sequences against the oracle."""
+    x = synth.make_verify_inputs("b16tree", seed=0, with_lm_head=False)
+    parent = synth.make_parents(x.k, 0, "b16tree", "trie")
+    out, kp, vp, st = gpu_attn_tree(x, parent, dev)
+    assert (st == 0).all()
+    seqs = [0, 5, 10, 15, 3]
+    rows, ref, _, _, st_ref = oracle_attn_tree(x, parent, seqs=seqs)
+    assert (st_ref == 0).all()
+    assert_close(out.float().cpu().numpy()[rows], ref, "b16tree attention")
+
+
+@pytest.mark.parametrize("wl", TREE_CASES[:3], ids=lambda w: w.name)
+@pytest.mark.parametrize("split", [0, 64])
+def test_chain_tree_gives_chain_bytes(dev, wl, split):
+    x = synth.make_verify_inputs(wl, seed=1, with_lm_head=False)
+    parent = synth.make_parents(x.k, 1, wl.name, "chain", kmax=wl.kmax)
+    out_t, kp_t, vp_t, st_t = gpu_attn_tree(x, parent, dev, kv_split_tokens=split)
+    out_c, kp_c, vp_c, st_c = gpu_attn(x, dev, kv_split_tokens=split, kmax=wl.kmax)
+    assert (st_t == 0).all() and (st_c == 0).all()
+    assert torch.equal(out_t.view(torch.int16), out_c.view(torch.int16))
+    assert torch.equal(kp_t.view(torch.int16), kp_c.view(torch.int16))
+    assert torch.equal(vp_t.view(torch.int16), vp_c.view(torch.int16))
+
+
+@pytest.mark.parametrize("wl", [TREE_CASES[1], TREE_CASES[3]], ids=lambda w: w.name)
+def test_tree_row_ignores_nodes_off_its_path(dev, wl):
+    """Re-drawing the K/V of every node outside node j's path leaves the bytes of j and of
+    its ancestors unchanged."""
+    x, parent = _tree_case(wl, 2, "random")
+    out0, *_ = gpu_attn_tree(x, parent, dev)
+    rng = np.random.default_rng(4)
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    kn, vn = x.k_new.clone(), x.v_new.clone()
+    keep = []
+    for s in range(len(x.k)):
+        j = int(rng.integers(1, x.k[s] + 1))
+        on = {0}
+        u = j
+        while u != 0:
+            on.add(u)
+            u = int(parent[s, u])
+        keep += [int(off[s] + u) for u in sorted(on)]
+        for u in range(x.k[s] + 1):
+            if u not in on:
+                kn[off[s] + u] = torch.randn_like(kn[off[s] + u], dtype=torch.float32).to(torch.bfloat16)
+                vn[off[s] + u] = torch.randn_like(vn[off[s] + u], dtype=torch.float32).to(torch.bfloat16)
+    y = synth.VerifyInputs(x.wl, x.pos, x.k, x.R, x.page_table, x.n_pages, x.q, kn, vn, x.k_pool, x.v_pool,
+                           x.hidden, x.w, x.d2t)
+    out1, *_ = gpu_attn_tree(y, parent, dev)
+    keep = torch.tensor(keep, device=dev)
+    assert torch.equal(out0[keep].view(torch.int16), out1[keep].view(torch.int16))
+    assert not torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+
+
+def test_tree_attention_flags_bad_parents(dev):
+    wl = TREE_CASES[1]
+    x, parent = _tree_case(wl, 3, "trie")
+    parent = parent.copy()
+    parent[1, 3] = 3            # not before its node
+    parent[2, 0] = 0            # root must have parent -1
+    out, kp, vp, st = gpu_attn_tree(x, parent, dev)
+    assert list(st) == [0, oracle.BAD_TREE, oracle.BAD_TREE, 0]
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    o = out.float().cpu().numpy()
+    for s in (1, 2):
+        assert np.isnan(o[off[s]:off[s + 1]]).all()
+    # flagged sequences write nothing into the pool: compare with the oracle's pools,
+    # where flagged sequences are skipped the same way
+    rows, ref, kp_ref, vp_ref, st_ref = oracle_attn_tree(x, parent)
+    assert list(st_ref) == list(st)
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref)
+    good = np.concatenate([np.arange(off[s], off[s + 1]) for s in (0, 3)])
+    assert_close(o[good], ref[good], "tree attention next to flagged sequences")
+
+
+# --------------------------------------------------------------------------- acceptance
+def _accept_inputs(seed, B, kmax, shape, V=500, n_d2t=0, k_fixed=False, p_corrupt=0.3):
+    rng = np.random.default_rng(seed)
+    k = np.full(B, kmax, np.int32) if k_fixed else rng.integers(0, kmax + 1, B).astype(np.int32)
+    parent = synth.make_parents(k, seed, "b16tree", shape, kmax=kmax)
+    R = int((k + 1).sum())
+    g = rng.integers(0, V, R).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(k + 1)])
+    target = [g[off[s]:off[s + 1]] for s in range(B)]
+    wl = synth.VerifyWorkload("acc", B=B, k=None, k_lo=0, k_hi=kmax, ctx_lo=0, ctx_hi=0, Hq=1, Hkv=1, D=64, H=1,
+                              V=V, max_pages=1, p_corrupt=(p_corrupt, p_corrupt))
+    drafts = synth.make_tree_drafts(wl, k, parent, target, seed)
+    d2t = None
+    if n_d2t:
+        # drafts become draft-vocabulary ids of a map that reaches every target id
+        d2t = (rng.permutation(n_d2t) % V).astype(np.int32)
+        inv = {}
+        for i, t in enumerate(d2t):
+            inv.setdefault(int(t), i)
+        mapped = np.vectorize(lambda t: inv[int(t)])(np.maximum(drafts, 0))
+        drafts = np.where(drafts >= 0, mapped, -1).astype(np.int32)
+    pos = rng.integers(0, 100000, B).astype(np.int32)
+    return g, drafts, k, parent, d2t, V, pos, R
+
+
+def _oracle_accept(g, drafts, k, parent, d2t, V, pos, R):
+    B, kmax = drafts.shape
+    return oracle.tree_accept(g, drafts, kmax, k, parent, d2t, 0 if d2t is None else len(d2t), V, B, R, pos)
+
+
+def _assert_tree_accept_equal(got, ref, what):
+    for key in ("status", "accept_len", "n_emit", "pos_out", "next_tok", "emit", "path"):
+        assert np.array_equal(got[key], ref[key]), f"{what}: {key}\ngpu {got[key]}\nref {ref[key]}"
+
+
+@pytest.mark.parametrize("B,kmax,shape,n_d2t", [(16, 15, "trie", 0), (64, 15, "star", 0), (64, 31, "random", 0),
+                                                (200, 127, "trie", 0), (4096, 15, "trie", 0),
+                                                (32, 63, "trie", 700), (8192, 4, "random", 0)])
+def test_tree_accept_parity(dev, B, kmax, shape, n_d2t):
+    print(f"tree accept B={B} kmax={kmax} {shape} d2t={n_d2t}", flush=True)
+    args = _accept_inputs(B * 7 + kmax, B, kmax, shape, n_d2t=n_d2t)
+    ref = _oracle_accept(*args)
+    got = gpu_tree_accept(*args[:-1], dev)
+    _assert_tree_accept_equal(got, ref, f"tree accept B={B} kmax={kmax} {shape}")
+    assert (ref["status"] == 0).all()
+    assert ref["accept_len"].max() >= (1 if shape == "star" else min(kmax, 3))
+
+
+def test_tree_accept_deep_paths_and_duplicates(dev):
+    """Full 127-deep chains accepted to the end (both lane halves of the walk), and
+    duplicate sibling tokens (the lowest index wins)."""
+    B, kmax = 8, 127
+    args = list(_accept_inputs(99, B, kmax, "chain", k_fixed=True, p_corrupt=0.0))
+    ref = _oracle_accept(*args)
+    assert (ref["accept_len"] == kmax).all()
+    _assert_tree_accept_equal(gpu_tree_accept(*args[:-1], dev), ref, "deep chains")
+    # a star of identical children: node 1 wins whenever the token matches
+    g, drafts, k, parent, d2t, V, pos, R = _accept_inputs(5, 64, 8, "star", k_fixed=True, p_corrupt=0.0)
+    drafts[:, :] = drafts[:, :1]
+    ref = _oracle_accept(g, drafts, k, parent, d2t, V, pos, R)
+    assert (ref["path"][:, 0] == 1).all()
+    _assert_tree_accept_equal(gpu_tree_accept(g, drafts, k, parent, d2t, V, pos, dev), ref, "duplicate siblings")
+
+
+def test_tree_accept_error_paths(dev):
+    g, drafts, k, parent, d2t, V, pos, R = _accept_inputs(3, 6, 7, "trie", k_fixed=True)
+    parent = parent.copy()
+    drafts = drafts.copy()
+    pos = pos.copy()
+    parent[0, 2] = 5                 # after its node
+    parent[1, 0] = 3                 # root
+    drafts[2, 3] = V + 4             # token outside the vocabulary
+    pos[3] = -1
+    parent[4, 1] = -1                # a node without a parent
+    ref = _oracle_accept(g, drafts, k, parent, d2t, V, pos, R)
+    assert list(ref["status"]) == [oracle.BAD_TREE, oracle.BAD_TREE, oracle.BAD_TOKEN, oracle.BAD_POS,
+                                   oracle.BAD_TREE, 0]
+    _assert_tree_accept_equal(gpu_tree_accept(g, drafts, k, parent, d2t, V, pos, dev), ref, "error paths")
+    # packing that does not add up flags every sequence
+    ref = _oracle_accept(g, drafts, k, parent, d2t, V, pos, R + 1)
+    got = gpu_tree_accept(np.concatenate([g, [0]]), drafts, k, parent, d2t, V, pos, dev)
+    assert (got["status"] & oracle.BAD_ROWS).all()
+    _assert_tree_accept_equal(got, ref, "bad packing")
+
+
+# --------------------------------------------------------------------------- compaction
+@pytest.mark.parametrize("wl", [TREE_CASES[0], TREE_CASES[1], TREE_CASES[2], TREE_CASES[3]],
+                         ids=lambda w: w.name)
+def test_kv_compact_parity(dev, wl):
+    import greedy_draft_verify_amd as gdv
+    x, parent = _tree_case(wl, 6, "random")
+    B, kmax = len(x.k), wl.kmax
+    rng = np.random.default_rng(8)
+    path = np.full((B, kmax), -1, np.int32)
+    acc = np.zeros(B, np.int32)
+    for s in range(B):
+        j = int(rng.integers(0, x.k[s] + 1)) if s else int(x.k[s])   # sequence 0: the deepest-numbered node
+        p = []
+        while j != 0:
+            p.append(j)
+            j = int(parent[s, j])
+        p = p[::-1]
+        acc[s] = len(p)
+        path[s, :len(p)] = p
+    st_in = np.zeros(B, np.int32)
+    if B > 2:
+        st_in[2] = oracle.BAD_PAGE         # flagged upstream: must not move
+    kp = x.k_pool.to(dev).clone()
+    vp = x.v_pool.to(dev).clone()
+    st = i32(st_in, dev)
+    gdv.spec_kv_compact(kp, vp, i32(x.page_table, dev), i32(x.pos, dev), i32(path, dev), i32(acc, dev), st)
+    torch.cuda.synchronize()
+    kp_ref, vp_ref = bits(x.k_pool).copy(), bits(x.v_pool).copy()
+    oracle.kv_compact(kp_ref, vp_ref, x.page_table, x.page_table.shape[1], x.pos, path, acc, kmax, st_in, B,
+                      wl.Hkv, wl.D)
+    assert list(st.cpu().numpy()) == list(st_in)
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref)
+    assert acc.max() >= 2
+
+
+def test_kv_compact_rejects_bad_paths(dev):
+    import greedy_draft_verify_amd as gdv
+    wl = TREE_CASES[1]
+    x, parent = _tree_case(wl, 7, "trie")
+    B, kmax = len(x.k), wl.kmax
+    path = np.full((B, kmax), -1, np.int32)
+    acc = np.array([2, 2, 3, 1], np.int32)
+    path[0, :2] = [3, 3]           # not increasing
+    path[1, :2] = [1, kmax + 1]    # past kmax
+    path[2, :3] = [2, 4, 5]        # fine (k >= 5 in this workload)
+    path[3, :1] = [1]              # fine, and equal to its destination: nothing moves
+    kp = x.k_pool.to(dev).clone()
+    vp = x.v_pool.to(dev).clone()
+    st = i32(np.zeros(B), dev)
+    gdv.spec_kv_compact(kp, vp, i32(x.page_table, dev), i32(x.pos, dev), i32(path, dev), i32(acc, dev), st)
+    torch.cuda.synchronize()
+    assert list(st.cpu().numpy()) == [oracle.BAD_TREE, oracle.BAD_TREE, 0, 0]
+    kp_ref, vp_ref = bits(x.k_pool).copy(), bits(x.v_pool).copy()
+    oracle.kv_compact(kp_ref, vp_ref, x.page_table, x.page_table.shape[1], x.pos, path, acc, kmax,
+                      np.array([1, 1, 0, 0], np.int32), B, wl.Hkv, wl.D)
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref)
