@@ -231,3 +231,60 @@ def kv_compact(k_pool, v_pool, page_table, max_pages, pos, path, accept_len, kma
     lib().oracle_kv_compact(_p(k_pool), _p(v_pool), _p(_i32(page_table)), ctypes.c_int32(max_pages),
                             _p(_i32(pos)), _p(ph), _p(_i32(accept_len)), ctypes.c_int32(kmax), _p(_i32(st)),
                             ctypes.c_int32(B), ctypes.c_int32(Hkv), ctypes.c_int32(D))
+
+
+# ---------------------------------------------------------------------------
+# speculative-sampling verify (DSSD fast.py _sample_verify)
+def philox4x32_10(ctr, key):
+    """One Philox4x32-10 block: ctr 4 uint32 words, key 2 uint32 words -> 4 uint32 words."""
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def accept_uniform(row_ctr, seed):
+    f = lib().oracle_accept_uniform
+    f.restype = ctypes.c_double
+    return f(_p(np.ascontiguousarray(row_ctr, np.int32)), ctypes.c_uint64(seed))
+
+
+def sample_rows(logits, T, q_tok, q_prob, row_ctr, seed):
+    """logits fp64 [R, V]; q_tok int32 [R, NQ]; q_prob fp32 [R, NQ]; row_ctr int32 [R, 2].
+    Returns dict lse [R], z_supp [R, NQ], sample_p [R], sample_res [R]."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    R, V = logits.shape
+    q_tok = _i32(q_tok)
+    NQ = q_tok.shape[1]
+    q_prob = np.ascontiguousarray(q_prob, np.float32)
+    lse = np.zeros(R, np.float64)
+    z = np.zeros((R, NQ), np.float64)
+    sp = np.zeros(R, np.int32)
+    sr = np.zeros(R, np.int32)
+    lib().oracle_sample_rows(_p(logits), ctypes.c_int32(R), ctypes.c_int32(V), ctypes.c_double(T), _p(q_tok),
+                             _p(q_prob), ctypes.c_int32(NQ), _p(_i32(row_ctr)), ctypes.c_uint64(seed), _p(lse),
+                             _p(z), _p(sp), _p(sr))
+    return dict(lse=lse, z_supp=z, sample_p=sp, sample_res=sr)
+
+
+def sample_accept(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, q_tok, q_prob, rows, row_ctr, seed, pos_in):
+    """rows: the dict of sample_rows. Returns the same dict as greedy_accept."""
+    q_tok = _i32(q_tok)
+    NQ = q_tok.shape[1]
+    pos_out = np.zeros(B, np.int32)
+    acc = np.zeros(B, np.int32)
+    ne = np.zeros(B, np.int32)
+    emit = np.zeros((B, kmax + 1), np.int32)
+    nt = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    dr = _i32(drafts).reshape(B, max(kmax, 0)) if kmax > 0 else np.zeros((B, 1), np.int32)
+    d2 = None if d2t is None else _i32(d2t)
+    lib().oracle_sample_accept(_p(dr), ctypes.c_int32(kmax), _p(_i32(k)), _p(d2), ctypes.c_int32(n_draft_vocab),
+                               ctypes.c_int32(V), ctypes.c_int32(B), ctypes.c_int32(R), _p(q_tok),
+                               _p(np.ascontiguousarray(q_prob, np.float32)), ctypes.c_int32(NQ),
+                               _p(np.ascontiguousarray(rows["lse"], np.float64)),
+                               _p(np.ascontiguousarray(rows["z_supp"], np.float64)), _p(_i32(rows["sample_p"])),
+                               _p(_i32(rows["sample_res"])), _p(_i32(row_ctr)), ctypes.c_uint64(seed),
+                               _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit), _p(nt), _p(st))
+    return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st)

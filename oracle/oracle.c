@@ -597,3 +597,202 @@ void oracle_kv_compact(uint16_t* k_pool, uint16_t* v_pool, const int32_t* page_t
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Speculative-sampling verify (DSSD fast.py _sample_verify; oxinfer
+ * speculative_accept; memra's sampled-spec note: counter-based Philox keyed by
+ * (seed, event) so that runs are reproducible).
+ *
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011): a 4-word counter and a 2-word key; each
+ * of 10 rounds multiplies words 0 and 2 by the round multipliers, mixes the high
+ * halves of the products with the other words and the key, and the key advances by
+ * the Weyl constants between rounds. A 32-bit output word w becomes the uniform
+ * u = (floor(w / 256) + 1/2) / 2^24, which lies strictly inside (0, 1).
+ * ------------------------------------------------------------------------- */
+void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n1 = lo1;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        const uint32_t n3 = lo0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+static double u01(uint32_t w) { return ((double)(w >> 8) + 0.5) / 16777216.0; }
+
+/* Counter layout (both sides): for a row with counter words (a, b) = row_ctr[r]
+ *   Gumbel noise of vocabulary entry v:  ctr = (v / 4, a, b, 0), word v % 4
+ *   acceptance uniform of the row:       ctr = (0, a, b, 1), word 0
+ * key = (seed low 32 bits, seed high 32 bits). */
+static double row_gumbel(uint32_t v, const int32_t* rc, const uint32_t key[2]) {
+    const uint32_t ctr[4] = {v >> 2, (uint32_t)rc[0], (uint32_t)rc[1], 0u};
+    uint32_t o[4];
+    oracle_philox4x32_10(ctr, key, o);
+    return -log(-log(u01(o[v & 3])));
+}
+
+double oracle_accept_uniform(const int32_t* rc, uint64_t seed) {
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint32_t ctr[4] = {0u, (uint32_t)rc[0], (uint32_t)rc[1], 1u};
+    uint32_t o[4];
+    oracle_philox4x32_10(ctr, key, o);
+    return u01(o[0]);
+}
+
+/* Per row r of logits [R][V] (fp64) at temperature T, with the draft distribution's
+ * support q_tok[r][0..NQ) (-1 = unused) and masses q_prob[r][..]:
+ *   z_v = logit_v / T,  lse = log sum_v exp(z_v),  p_v = exp(z_v - lse)
+ *   z_supp[r][e] = z of q_tok[r][e] (NaN for unused entries)
+ *   sample_p[r]   = argmax_v (z_v + G_v)                      (a draw from p)
+ *   sample_res[r] = argmax_{v: r_v > 0} (log r_v + G_v), r_v = max(p_v - q_v, 0)
+ *                   (a draw from norm(max(p - q, 0)); sample_p if every r_v is 0)
+ * with G_v the Gumbel noise of the row (Gumbel-max: the argmax of log-weights plus
+ * independent standard Gumbel noise is a draw from the normalised weights; ties go
+ * to the smaller index). */
+void oracle_sample_rows(const double* logits, int32_t R, int32_t V, double T, const int32_t* q_tok,
+                        const float* q_prob, int32_t NQ, const int32_t* row_ctr, uint64_t seed, double* lse,
+                        double* z_supp, int32_t* sample_p, int32_t* sample_res) {
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+#pragma omp parallel for schedule(dynamic)
+    for (int r = 0; r < R; ++r) {
+        const double* l = logits + (int64_t)r * V;
+        double zmax = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if (l[v] / T > zmax) zmax = l[v] / T;
+        double s = 0.0;
+        for (int v = 0; v < V; ++v) s += exp(l[v] / T - zmax);
+        const double L = zmax + log(s);
+        lse[r] = L;
+        const int32_t* qt = q_tok + (int64_t)r * NQ;
+        const float* qp = q_prob + (int64_t)r * NQ;
+        for (int e = 0; e < NQ; ++e)
+            z_supp[(int64_t)r * NQ + e] = (qt[e] >= 0 && qt[e] < V) ? l[qt[e]] / T : NAN;
+        double bp = -INFINITY, br = -INFINITY;
+        int ip = -1, ir = -1;
+        for (int v = 0; v < V; ++v) {
+            const double z = l[v] / T;
+            const double g = row_gumbel((uint32_t)v, row_ctr + 2 * (int64_t)r, key);
+            if (z + g > bp) {
+                bp = z + g;
+                ip = v;
+            }
+            double q = 0.0;
+            for (int e = 0; e < NQ; ++e)
+                if (qt[e] == v) q += qp[e];
+            const double rv = exp(z - L) - q;
+            if (rv > 0.0 && log(rv) + g > br) {
+                br = log(rv) + g;
+                ir = v;
+            }
+        }
+        sample_p[r] = ip;
+        sample_res[r] = ir >= 0 ? ir : ip;
+    }
+}
+
+/* Chain walk of speculative sampling (DSSD _sample_verify): for j = 0 .. k_s - 1,
+ * row r = off_s + j, draft x = drafts[s][j] (a target id, or a draft-vocabulary id
+ * mapped through d2t), q(x) = the mass of x in the row's q support:
+ *   accept x iff u_r < p_r(x) / q(x)   (u_r the row's acceptance uniform; the
+ *                                       probability is min(1, p / q))
+ *   else emit sample_res[r], stop.
+ * If every draft is accepted, emit sample_p of the bonus row off_s + k_s.
+ *   accept_len = accepted drafts, emit = accepted tokens ++ [the sampled token],
+ *   pos_out = pos_in + accept_len + 1, next_tok = the sampled token.
+ * Status bits as oracle_greedy_accept; a draft whose (mapped) id is not in its
+ * row's q support with a positive mass sets ORC_BAD_TOKEN. */
+void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
+                          int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const int32_t* q_tok,
+                          const float* q_prob, int32_t NQ, const double* lse, const double* z_supp,
+                          const int32_t* sample_p, const int32_t* sample_res, const int32_t* row_ctr,
+                          uint64_t seed, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len,
+                          int32_t* n_emit, int32_t* emit, int32_t* next_tok, int32_t* st) {
+    int64_t total = 0;
+    int packing_ok = 1;
+    for (int s = 0; s < B; ++s) {
+        total += (int64_t)k[s] + 1;
+        if (k[s] < 0) packing_ok = 0;
+    }
+    if (total != R) packing_ok = 0;
+    int64_t off = 0;
+    for (int s = 0; s < B; ++s) {
+        const int ks = k[s];
+        int bits = 0;
+        if (!packing_ok || ks > kmax) bits |= ORC_BAD_ROWS;
+        if (pos_in[s] < 0) bits |= ORC_BAD_POS;
+        int32_t* e = emit + (int64_t)s * (kmax + 1);
+        for (int j = 0; j <= kmax; ++j) e[j] = -1;
+        int supp_e[1024];
+        if (!bits) {
+            for (int j = 0; j < ks; ++j) {
+                const int32_t x = drafts[(int64_t)s * kmax + j];
+                int32_t t = x;
+                if (d2t) {
+                    if (x < 0 || x >= n_draft_vocab || d2t[x] < 0 || d2t[x] >= V) {
+                        bits |= ORC_BAD_TOKEN;
+                        continue;
+                    }
+                    t = d2t[x];
+                } else if (x < 0 || x >= V) {
+                    bits |= ORC_BAD_TOKEN;
+                    continue;
+                }
+                const int64_t r = off + j;
+                supp_e[j] = -1;
+                for (int q = 0; q < NQ; ++q)
+                    if (q_tok[r * NQ + q] == t && q_prob[r * NQ + q] > 0.f) {
+                        supp_e[j] = q;
+                        break;
+                    }
+                if (supp_e[j] < 0) bits |= ORC_BAD_TOKEN;
+            }
+        }
+        if (bits) {
+            st[s] = bits;
+            accept_len[s] = -1;
+            n_emit[s] = 0;
+            next_tok[s] = -1;
+            pos_out[s] = pos_in[s];
+            off += (int64_t)ks + 1;
+            continue;
+        }
+        int a = 0, tok = -1;
+        for (; a < ks; ++a) {
+            const int64_t r = off + a;
+            const int q = supp_e[a];
+            const double px = exp(z_supp[r * NQ + q] - lse[r]);
+            const double u = oracle_accept_uniform(row_ctr + 2 * r, seed);
+            if (u < px / (double)q_prob[r * NQ + q]) {
+                e[a] = q_tok[r * NQ + q];
+                continue;
+            }
+            tok = sample_res[r];
+            break;
+        }
+        if (tok < 0) tok = sample_p[off + ks];
+        e[a] = tok;
+        st[s] = 0;
+        accept_len[s] = a;
+        n_emit[s] = a + 1;
+        next_tok[s] = tok;
+        pos_out[s] = pos_in[s] + a + 1;
+        off += ks + 1;
+    }
+}
