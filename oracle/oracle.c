@@ -608,7 +608,8 @@ void oracle_kv_compact(uint16_t* k_pool, uint16_t* v_pool, const int32_t* page_t
  * of 10 rounds multiplies words 0 and 2 by the round multipliers, mixes the high
  * halves of the products with the other words and the key, and the key advances by
  * the Weyl constants between rounds. A 32-bit output word w becomes the uniform
- * u = (floor(w / 256) + 1/2) / 2^24, which lies strictly inside (0, 1).
+ * u = (floor(w / 512) + 1/2) / 2^23, which lies strictly inside (0, 1) and is
+ * exactly representable in fp32 (24 significant bits).
  * ------------------------------------------------------------------------- */
 void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
     uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
@@ -635,7 +636,7 @@ void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], ui
     out[3] = c3;
 }
 
-static double u01(uint32_t w) { return ((double)(w >> 8) + 0.5) / 16777216.0; }
+static double u01(uint32_t w) { return ((double)(w >> 9) + 0.5) / 8388608.0; }
 
 /* Counter layout (both sides): for a row with counter words (a, b) = row_ctr[r]
  *   Gumbel noise of vocabulary entry v:  ctr = (v / 4, a, b, 0), word v % 4
