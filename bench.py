@@ -270,6 +270,66 @@ def tree_leg(dev, w_packed, reps: int, seed: int = 0):
             "kv_compact_bytes": cmp_b}
 
 
+def sampling_leg(step: "VerifyStep", dev, reps: int, temperature: float = 0.1):
+    """Speculative-sampling verify on the benchmark's inputs (DSSD fast.py
+    _sample_verify): spec_verify_attn -> spec_lm_head_sample (softmax statistics and
+    the two Gumbel-max draws fused into the lm_head pass) -> spec_sample_accept, with
+    point-mass draft distributions at the step's drafts. The synthetic logits have unit
+    variance over 151936 entries, nearly flat at temperature 1 (a greedy draft is kept
+    with probability ~1e-4 there), so the leg runs at temperature 0.1. Each call timed
+    with HIP events on the launch stream."""
+    x = step.x
+    wl = x.wl
+    B, R, kmax = step.B, step.R, wl.kmax
+    drafts = step.drafts.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    q_tok = np.full((R, 1), -1, np.int32)
+    for s in range(B):
+        q_tok[off[s]:off[s] + x.k[s], 0] = drafts[s, :x.k[s]] if x.d2t is None else x.d2t[drafts[s, :x.k[s]]]
+    q_prob = torch.from_numpy((q_tok >= 0).astype(np.float32)).to(dev)
+    q_tok_d = i32(q_tok, dev)
+    row_ctr = i32(np.stack([np.concatenate([x.pos[s] + np.arange(x.k[s] + 1) for s in range(B)]),
+                            np.repeat(np.arange(B), x.k + 1)], 1), dev)
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    z_supp = torch.empty((R, 1), dtype=torch.float32, device=dev)
+    sp = torch.empty(R, dtype=torch.int32, device=dev)
+    sr = torch.empty(R, dtype=torch.int32, device=dev)
+    ws = gdv.workspace(gdv.lm_head_sample_workspace_bytes(R, wl.H, wl.V), dev, zero=True)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, st = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+    seed = 0x5EED
+    lm = lambda: gdv.spec_lm_head_sample(x.hidden, step.w_packed, wl.V, temperature, q_tok_d, q_prob, row_ctr, seed,
+                                         lse, z_supp, sp, sr, workspace_buf=ws)
+    accept = lambda: gdv.spec_sample_accept(step.drafts, step.k, step.d2t, wl.V, q_tok_d, q_prob, lse, z_supp, sp,
+                                            sr, row_ctr, seed, step.pos, pos_out, acc, ne, emit, nt, st)
+    fns = [step.attn, lm, accept]
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    assert (st.cpu() == 0).all()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for ev in evs:
+        ev[0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs])) * 1e3 for i in range(len(fns))]
+    acc_np = acc.cpu().numpy()
+    step_us = sum(us)
+    lm_b = lm_head_bytes(R, wl.H, wl.V)
+    return {"workload": f"{wl.name} inputs, temperature {temperature}, point-mass drafts",
+            "step_us": step_us, "rows_per_s": R / (step_us / 1e6),
+            "emitted_tokens_per_s": float((acc_np + 1).sum()) / (step_us / 1e6),
+            "accept_len_hist": np.bincount(acc_np, minlength=kmax + 1).tolist(),
+            "kernel_us": {"spec_verify_attn": us[0], "spec_lm_head_sample": us[1], "spec_sample_accept": us[2]},
+            "lm_head_sample": {"bound": "hbm", "algorithmic_bytes": lm_b, "achieved": lm_b / us[1] / 1e3,
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_b / us[1] / 1e3 / HBM_PEAK_GBS}}
+
+
 def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
     """spec_lm_head_argmax alone at growing row counts with the workload's W: where the
     weight stream stops bounding it and the MFMA work starts to."""
@@ -452,6 +512,7 @@ def main():
         extras["delta_roofline"] = delta_leg(dev, reps=20)
         if wl.H == 4096 and wl.V == 151936:
             extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
+        extras["sampling_verify"] = sampling_leg(step, dev, reps=20)
         sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
         dl = extras["delta_roofline"]
         log(f"[bench] lm_head sweep: {sw}")
@@ -460,6 +521,11 @@ def main():
             f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
             f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
             f"{ist['rescan_us']:.1f} us")
+        sv_ = extras["sampling_verify"]
+        log(f"[bench] sampling step {sv_['step_us']:.1f} us ({sv_['rows_per_s']:.0f} rows/s, "
+            f"{sv_['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample {sv_['kernel_us']['spec_lm_head_sample']:.1f} us "
+            f"({100 * sv_['lm_head_sample']['frac']:.0f}% HBM), accept {sv_['kernel_us']['spec_sample_accept']:.1f} us; "
+            f"accept lengths {sv_['accept_len_hist']}")
         if "tree_verify" in extras:
             tv = extras["tree_verify"]
             ku = tv["kernel_us"]

@@ -27,7 +27,8 @@ EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_packed_bytes",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
-            "spec_kv_compact"]
+            "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
+            "spec_sample_accept"]
 
 _lib = None
 
@@ -69,9 +70,16 @@ def lib() -> ctypes.CDLL:
         L.spec_tree_accept.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp]
         L.spec_kv_compact.argtypes = [vp, vp, i64, vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        u64 = ctypes.c_uint64
+        L.spec_lm_head_sample_workspace_bytes.argtypes = [i32, i32, i32]
+        L.spec_lm_head_sample_workspace_bytes.restype = sz
+        L.spec_lm_head_sample.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp, i32, vp, u64, vp, vp, vp, vp, vp, sz,
+                                          vp]
+        L.spec_sample_accept.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, u64,
+                                         vp, vp, vp, vp, vp, vp, vp, vp]
         for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack", "spec_greedy_accept",
                      "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
-                     "spec_kv_compact"):
+                     "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -312,6 +320,76 @@ def spec_greedy_accept(argmax, drafts, k, d2t, V, pos_in, pos_out, accept_len, n
                                   _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
                                   _ptr(seq_status), _stream(stream))
     _check(rc, "spec_greedy_accept")
+
+
+def lm_head_sample_workspace_bytes(R, H, V) -> int:
+    return lib().spec_lm_head_sample_workspace_bytes(R, H, V)
+
+
+def spec_lm_head_sample(hidden, w_packed, V, temperature, q_tok, q_prob, row_ctr, seed, lse, z_supp, sample_p,
+                        sample_res, workspace_buf=None, stream=None):
+    """hidden [R,H] bf16, w_packed from spec_lm_head_pack; q_tok [R,NQ] int32 / q_prob [R,NQ] fp32
+    (NQ may be 0: pass tensors of shape [R,0]); row_ctr [R,2] int32; outputs lse [R] fp32,
+    z_supp [R,NQ] fp32, sample_p/sample_res [R] int32. A workspace_buf must be zero on first use."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
+    R, H = hidden.shape
+    for t, n in ((q_tok, "q_tok"), (row_ctr, "row_ctr"), (sample_p, "sample_p"), (sample_res, "sample_res")):
+        _want(t, torch.int32, n)
+    for t, n in ((q_prob, "q_prob"), (lse, "lse"), (z_supp, "z_supp")):
+        _want(t, torch.float32, n)
+    NQ = q_tok.shape[1]
+    _shape(q_tok, (R, NQ), "q_tok")
+    _shape(q_prob, (R, NQ), "q_prob")
+    _shape(z_supp, (R, NQ), "z_supp")
+    _shape(row_ctr, (R, 2), "row_ctr")
+    for t, n in ((lse, "lse"), (sample_p, "sample_p"), (sample_res, "sample_res")):
+        _shape(t, (R,), n)
+    if w_packed.numel() * 2 != lm_head_packed_bytes(V, H):
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {lm_head_packed_bytes(V, H)}")
+    if workspace_buf is None:
+        workspace_buf = workspace(lm_head_sample_workspace_bytes(R, H, V), hidden.device, zero=True)
+    nz = lambda t: _ptr(t) if t.numel() else None
+    rc = lib().spec_lm_head_sample(_ptr(hidden), _ptr(w_packed), R, H, V, float(temperature), nz(q_tok), nz(q_prob),
+                                   NQ, _ptr(row_ctr), int(seed) & ((1 << 64) - 1), _ptr(lse), nz(z_supp),
+                                   _ptr(sample_p), _ptr(sample_res), _ptr(workspace_buf), workspace_buf.numel(),
+                                   _stream(stream))
+    _check(rc, "spec_lm_head_sample")
+
+
+def spec_sample_accept(drafts, k, d2t, V, q_tok, q_prob, lse, z_supp, sample_p, sample_res, row_ctr, seed, pos_in,
+                       pos_out, accept_len, n_emit, emit, next_tok, seq_status, stream=None):
+    """The speculative-sampling chain walk; drafts [B,kmax], the per-row arrays of
+    spec_lm_head_sample, outputs as spec_greedy_accept."""
+    for t, n in ((drafts, "drafts"), (k, "k"), (q_tok, "q_tok"), (sample_p, "sample_p"), (sample_res, "sample_res"),
+                 (row_ctr, "row_ctr"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (emit, "emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    for t, n in ((q_prob, "q_prob"), (lse, "lse"), (z_supp, "z_supp")):
+        _want(t, torch.float32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    B, kmax = drafts.shape
+    R = lse.shape[0]
+    NQ = q_tok.shape[1]
+    _shape(q_tok, (R, NQ), "q_tok")
+    _shape(q_prob, (R, NQ), "q_prob")
+    _shape(z_supp, (R, NQ), "z_supp")
+    _shape(row_ctr, (R, 2), "row_ctr")
+    _shape(emit, (B, kmax + 1), "emit")
+    for t, n in ((sample_p, "sample_p"), (sample_res, "sample_res")):
+        _shape(t, (R,), n)
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    nz = lambda t: _ptr(t) if t.numel() else None
+    rc = lib().spec_sample_accept(nz(drafts), kmax, _ptr(k), _ptr(d2t), 0 if d2t is None else d2t.shape[0], V, B, R,
+                                  nz(q_tok), nz(q_prob), NQ, _ptr(lse), nz(z_supp), _ptr(sample_p), _ptr(sample_res),
+                                  _ptr(row_ctr), int(seed) & ((1 << 64) - 1), _ptr(pos_in), _ptr(pos_out),
+                                  _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok), _ptr(seq_status),
+                                  _stream(stream))
+    _check(rc, "spec_sample_accept")
 
 
 def spec_delta_verify_rollback(mode, q, k, v, a, b, q_scale, state, rec, L, o=None, stream=None):

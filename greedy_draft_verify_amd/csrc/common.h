@@ -51,6 +51,37 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
     return r;
 }
 
+// ---- counter-based random numbers ----------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC 2011): 10 rounds of two 32x32->64 products whose halves are mixed
+// with the other words and the key; the key advances by the Weyl constants after
+// each round.
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Uniform in (0, 1) from the top 23 bits of a word (exact in fp32), and standard
+// Gumbel noise -log(-log u) from it.
+__device__ __forceinline__ float u01_23(uint32_t w) { return ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f); }
+__device__ __forceinline__ float gumbel(uint32_t w) { return -__logf(-__logf(u01_23(w))); }
+
+// Counter layout of the sampling path: for a row with counter words (a, b)
+//   Gumbel noise of vocabulary entry v:  ctr (v / 4, a, b, 0), word v % 4
+//   acceptance uniform of the row:       ctr (0, a, b, 1), word 0
+__device__ __forceinline__ float row_gumbel(uint32_t v, uint32_t a, uint32_t b, uint32_t k0, uint32_t k1) {
+    const uint4 w = philox10(make_uint4(v >> 2, a, b, 0u), k0, k1);
+    const uint32_t sel = v & 3u;
+    return gumbel(sel == 0 ? w.x : sel == 1 ? w.y : sel == 2 ? w.z : w.w);
+}
+
 // ---- ragged row packing ------------------------------------------------------
 // Exclusive prefix sums of (k_s + 1) over s (the packed row offsets) for B <= the
 // size of s_off, by a block of NT threads (each a contiguous segment of sequences,

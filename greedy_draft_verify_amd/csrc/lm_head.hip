@@ -94,18 +94,133 @@ __device__ __forceinline__ float unpack_value(unsigned long long key) {
     return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
 }
 
+// Sampling epilogue (speculative-sampling verify): per row, the workgroup's
+// softmax partial (max and sum of exp of z = logit / T over its 128 entries), the
+// z of the row's draft-support tokens, and the best z + Gumbel noise over the
+// entries outside that support.
+struct SampleArgs {
+    const int32_t* q_tok;     // [R][NQ] draft support per row (-1: unused)
+    const int32_t* row_ctr;   // [R][2] Philox counter words of the row
+    float2* part;             // [R][n_vt] (max, sum of exp) per vocabulary group
+    float* z_supp;            // [R][NQ]
+    float inv_t;
+    int NQ;
+    uint32_t key0, key1;
+};
+
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;   // both empty
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}
+
+// acc[mt][nt][i] = logit of row 16 mt + 4 (lane / 16) + i, entry 16 (tile0 + nt) + lane % 16.
+// Gumbel noise of (row, v) is word v % 4 of Philox(ctr = (v / 4, row_ctr[row]), key):
+// the four lanes 4c..4c+3 of a 16-lane group hold the same v / 4 and the same four
+// rows, so lane 4c + b computes row b's block and a 4x4 transpose by shuffles hands
+// every lane the words it needs (one block per lane per (mt, nt)).
+template <int MT>
+__device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], const SampleArgs& sa, int r0, int R,
+                                                int V, int vt, int n_vt, int tile0, int tid, int wave, int lane,
+                                                const uint4* s_sup, float2 (*s_ms)[16 * MT],
+                                                Best (*wbest)[16 * MT], unsigned long long* keys) {
+    const int l16 = lane % 16, lq = lane / 16, b = lane & 3;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        // this lane's Philox row: row 16 mt + 4 lq + b
+        const int rb = min(r0 + mt * 16 + lq * 4 + b, R - 1);
+        const uint32_t ca = (uint32_t)sa.row_ctr[2 * (size_t)rb], cb = (uint32_t)sa.row_ctr[2 * (size_t)rb + 1];
+        float g[kLmNT][4];   // g[nt][i]: noise of (row 4 lq + i, entry of this lane)
+#pragma unroll
+        for (int nt = 0; nt < kLmNT; ++nt) {
+            const uint32_t v4 = (uint32_t)(((tile0 + nt) * 16 + l16) >> 2);
+            const uint4 w = philox10(make_uint4(v4, ca, cb, 0u), sa.key0, sa.key1);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                // lane b takes word b of lane (b + d) % 4's block (row (b + d) % 4) and
+                // gives word (b - d) % 4 of its own
+                const int sel = (b - d) & 3;
+                const uint32_t send = sel == 0 ? w.x : sel == 1 ? w.y : sel == 2 ? w.z : w.w;
+                const int src = (lane & ~3) | ((b + d) & 3);
+                const uint32_t got = d == 0 ? send : (uint32_t)__shfl((int)send, src);
+                g[nt][(b + d) & 3] = gumbel(got);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = mt * 16 + lq * 4 + i;     // row inside the row group
+            const int r = r0 + rl;
+            const uint4 sup = s_sup[rl];
+            float m = -INFINITY, sm = 0.f;
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int nt = 0; nt < kLmNT; ++nt) {
+                const int v = (tile0 + nt) * 16 + l16;
+                if (v >= V) continue;
+                const float z = acc[mt][nt][i] * sa.inv_t;
+                ms_merge(m, sm, z, 1.f);
+                const int loc = v - vt * kLmVocabPerWg;
+                const uint32_t word = loc < 32 ? sup.x : loc < 64 ? sup.y : loc < 96 ? sup.z : sup.w;
+                if ((word >> (loc & 31)) & 1u) {
+                    // a support token: its z goes to the finalize (rare path)
+                    if (r < R)
+                        for (int e = 0; e < sa.NQ; ++e)
+                            if (sa.q_tok[(size_t)r * sa.NQ + e] == v) sa.z_supp[(size_t)r * sa.NQ + e] = z;
+                } else if (better(z + g[nt][i], v, bv, bi)) {
+                    bv = z + g[nt][i];
+                    bi = v;
+                }
+            }
+            // the 16 lanes of the row, in a fixed butterfly (every lane ends with the same)
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) {
+                const float om = __shfl_xor(m, d), os = __shfl_xor(sm, d);
+                ms_merge(m, sm, om, os);
+                const float ov = __shfl_xor(bv, d);
+                const int oi = __shfl_xor(bi, d);
+                if (better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (l16 == 0) {
+                s_ms[wave][rl] = make_float2(m, sm);
+                wbest[wave][rl] = Best{bv, bi};
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < 16 * MT && r0 + tid < R) {
+        const int r = r0 + tid;
+        float m = s_ms[0][tid].x, sm = s_ms[0][tid].y;
+        Best bb = wbest[0][tid];
+#pragma unroll
+        for (int wv = 1; wv < 4; ++wv) {   // waves in order
+            ms_merge(m, sm, s_ms[wv][tid].x, s_ms[wv][tid].y);
+            const Best o = wbest[wv][tid];
+            if (better(o.v, o.i, bb.v, bb.i)) bb = o;
+        }
+        sa.part[(size_t)r * n_vt + vt] = make_float2(m, sm);
+        if (bb.i != 0x7fffffff) atomicMax(keys + r, pack_best(bb));
+    }
+}
+
 // SHARED: other row groups re-read this vocabulary group's W through the XCD's L2,
 // so W is loaded with the default cache policy instead of as a stream.
-template <int MT, bool SHARED>
+template <int MT, bool SHARED, bool SAMPLE = false>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, unsigned long long* __restrict__ keys, unsigned int* __restrict__ ticket,
-    int32_t* __restrict__ argmax, float* __restrict__ maxval) {
+    int32_t* __restrict__ argmax, float* __restrict__ maxval, SampleArgs sa) {
     constexpr int HSTR = kLmKB + 8;                            // LDS row stride (elements)
     constexpr int HCH = 16 * MT * kLmKB / 8 / kLmThreads;     // hidden chunks per thread per K-block
     static_assert(HCH * kLmThreads * 8 == 16 * MT * kLmKB, "hidden staging must tile evenly");
     __shared__ __attribute__((aligned(16))) u16 hs[16 * MT * HSTR];
     __shared__ Best wbest[4][16 * MT];
+    __shared__ uint4 s_sup[SAMPLE ? 16 * MT : 1];   // draft support inside this group, one bit per entry
+    __shared__ float2 s_ms[SAMPLE ? 4 : 1][SAMPLE ? 16 * MT : 1];
 
     // Logical tile: with several row groups, hardware workgroup i runs on XCD i % 8;
     // give the row groups of one vocabulary group consecutive slots of one XCD so
@@ -175,11 +290,37 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
             if constexpr (more) load_slot(kb + 1, s, ring[s]);
         }
     };
+    // sampling: thread t < 16 MT gathers row t's support tokens that fall in this
+    // group (its loads are issued before the W stream starts)
+    int qt[8];
+    if constexpr (SAMPLE) {
+        if (tid < 16 * MT) {
+            const int r = min(r0 + tid, R - 1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qt[e] = e < sa.NQ ? sa.q_tok[(size_t)r * sa.NQ + e] : -1;
+        }
+    }
     load_h(0);
 #pragma unroll
     for (int s = 0; s < kLmKS; ++s) load_slot(0, s, ring[s]);
+    if constexpr (SAMPLE) {
+        if (tid < 16 * MT) {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int loc = qt[e] - vt * kLmVocabPerWg;
+                if (qt[e] >= 0 && loc >= 0 && loc < kLmVocabPerWg) w[loc >> 5] |= 1u << (loc & 31);
+            }
+            s_sup[tid] = make_uint4(w[0], w[1], w[2], w[3]);   // read after the K loop's barriers
+        }
+    }
     for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, std::true_type{});
     block(nkb - 1, std::false_type{});
+
+    if constexpr (SAMPLE) {
+        sample_epilogue<MT>(acc, sa, r0, R, V, vt, n_vt, tile0, tid, wave, lane, s_sup, s_ms, wbest, keys);
+        return;
+    }
 
     // epilogue: C[row = 16 mt + 4 lq + i][vocab = 16 (tile0 + nt) + l16]
 #pragma unroll
@@ -241,18 +382,84 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 
 static int n_vtiles(int V) { return (V + kLmVocabPerWg - 1) / kLmVocabPerWg; }
 
-template <int MT>
+template <int MT, bool SAMPLE = false>
 static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
                          unsigned long long* keys, unsigned int* ticket, int32_t* argmax, float* maxval,
-                         hipStream_t st) {
+                         hipStream_t st, const SampleArgs& sa = SampleArgs{}) {
     if (n_rg == 1) {
-        hipLaunchKernelGGL((lm_head_tile_kernel<MT, false>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden, w, R,
-                           H, V, n_vt, n_rg, keys, ticket, argmax, maxval);
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, false, SAMPLE>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden, w,
+                           R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
     } else if constexpr (MT >= 5) {   // several row groups always have >= 5 tiles each
         const int grid = (n_vt * n_rg + 7) / 8 * 8;
-        hipLaunchKernelGGL((lm_head_tile_kernel<MT, true>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w, R,
-                           H, V, n_vt, n_rg, keys, ticket, argmax, maxval);
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, true, SAMPLE>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w,
+                           R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
     }
+}
+
+// One workgroup per row: the row's softmax statistics from the groups' partials (a
+// fixed reduction order), then the two draws. Candidates are the best entry outside
+// the draft support (from the tile kernel's key, z + G) and each distinct support
+// token (z + G recomputed here):
+//   draw from p:                    argmax z_v + G_v
+//   draw from norm(max(p - q, 0)):  argmax log(max(p_v - q_v, 0)) + G_v, which is
+//                                   z_v - lse + G_v outside the support
+// with ties to the smaller index. The row's key is reset to zero.
+__global__ __launch_bounds__(256) void sample_finalize_kernel(
+    const float2* __restrict__ part, int n_vt, int V, unsigned long long* __restrict__ keys,
+    const int32_t* __restrict__ q_tok, const float* __restrict__ q_prob, int NQ, const int32_t* __restrict__ row_ctr,
+    uint32_t key0, uint32_t key1, float* __restrict__ lse_out, float* __restrict__ z_supp,
+    int32_t* __restrict__ sample_p, int32_t* __restrict__ sample_res) {
+    __shared__ float2 s_w[4];
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    float m = -INFINITY, sm = 0.f;
+    for (int c = tid; c < n_vt; c += 256) {
+        const float2 pm = part[(size_t)r * n_vt + c];
+        ms_merge(m, sm, pm.x, pm.y);
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        const float om = __shfl_xor(m, d), os = __shfl_xor(sm, d);
+        ms_merge(m, sm, om, os);
+    }
+    if (lane == 0) s_w[wave] = make_float2(m, sm);
+    __syncthreads();
+    if (tid != 0) return;
+    float M = s_w[0].x, S = s_w[0].y;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) ms_merge(M, S, s_w[w].x, s_w[w].y);
+    const float lse = M + __logf(S);
+    lse_out[r] = lse;
+    const unsigned long long key = atomicExch(keys + r, 0ull);
+    Best bp{-INFINITY, 0x7fffffff}, br{-INFINITY, 0x7fffffff};
+    if (key != 0ull) {
+        const float zg = unpack_value(key);
+        const int idx = (int)~(uint32_t)key;
+        bp = Best{zg, idx};
+        br = Best{zg - lse, idx};
+    }
+    const uint32_t ca = (uint32_t)row_ctr[2 * (size_t)r], cb = (uint32_t)row_ctr[2 * (size_t)r + 1];
+    for (int e = 0; e < NQ; ++e) {
+        const int t = q_tok[(size_t)r * NQ + e];
+        if (t < 0 || t >= V) {
+            z_supp[(size_t)r * NQ + e] = __int_as_float(0x7fc00000);   // NaN: unused entry
+            continue;
+        }
+        bool dup = false;
+        float q = 0.f;
+        for (int e2 = 0; e2 < NQ; ++e2) {
+            if (q_tok[(size_t)r * NQ + e2] != t) continue;
+            if (e2 < e) dup = true;
+            q += q_prob[(size_t)r * NQ + e2];
+        }
+        if (dup) continue;
+        const float z = z_supp[(size_t)r * NQ + e];
+        const float g = row_gumbel((uint32_t)t, ca, cb, key0, key1);
+        if (better(z + g, t, bp.v, bp.i)) bp = Best{z + g, t};
+        const float rv = __expf(z - lse) - q;
+        if (rv > 0.f && better(__logf(rv) + g, t, br.v, br.i)) br = Best{__logf(rv) + g, t};
+    }
+    sample_p[r] = bp.i;
+    sample_res[r] = br.i != 0x7fffffff ? br.i : bp.i;
 }
 
 }  // namespace sv
@@ -273,6 +480,57 @@ int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_pac
     if (!aligned16(w) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_pack: w and w_packed must be 16-byte aligned");
     hipLaunchKernelGGL(lm_head_pack_kernel, dim3(8192), dim3(256), 0, (hipStream_t)stream, w, V, H, w_packed);
     SV_LAUNCH_CHECK("spec_lm_head_pack");
+    return SPEC_OK;
+}
+
+size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V) {
+    (void)H;
+    if (R < 1 || V < 1) return 0;
+    // one key per row, then (max, sum of exp) per (row, vocabulary group)
+    return 256 + (size_t)R * sizeof(unsigned long long) + (size_t)R * sv::n_vtiles(V) * sizeof(float2);
+}
+
+int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                        float temperature, const int32_t* q_tok, const float* q_prob, int32_t NQ,
+                        const int32_t* row_ctr, uint64_t seed, float* lse, float* z_supp, int32_t* sample_p,
+                        int32_t* sample_res, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (R < 1) return fail(SPEC_EINVAL, "spec_lm_head_sample: R=%d < 1", R);
+    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "spec_lm_head_sample: H=%d not a positive multiple of %d", H, kLmHAlign);
+    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_sample: V=%d", V);
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return fail(SPEC_EINVAL, "spec_lm_head_sample: temperature must be finite and > 0");
+    if (NQ < 0 || NQ > 8) return fail(SPEC_EINVAL, "spec_lm_head_sample: NQ=%d outside 0..8", NQ);
+    if (!hidden || !w_packed || !row_ctr || !lse || !sample_p || !sample_res || (NQ > 0 && (!q_tok || !q_prob || !z_supp)))
+        return fail(SPEC_EINVAL, "spec_lm_head_sample: null required pointer");
+    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_sample: hidden and w_packed must be 16-byte aligned");
+    const size_t need = spec_lm_head_sample_workspace_bytes(R, H, V);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(SPEC_EWORKSPACE, "spec_lm_head_sample: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, need);
+    const int n_vt = n_vtiles(V);
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
+    float2* part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + 256 + (size_t)R * sizeof(unsigned long long));
+    const int mtiles = (R + 15) / 16;
+    const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
+    const int MT = (mtiles + n_rg - 1) / n_rg;
+    if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_sample: grid too large");
+    SampleArgs sa{q_tok, row_ctr, part, z_supp, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
+    hipStream_t st = (hipStream_t)stream;
+    const spec_bf16* w = w_packed;
+    switch (MT) {
+        case 1: launch_tiles<1, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 2: launch_tiles<2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 3: launch_tiles<3, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 4: launch_tiles<4, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 5: launch_tiles<5, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 6: launch_tiles<6, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 7: launch_tiles<7, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        default: launch_tiles<8, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+    }
+    SV_LAUNCH_CHECK("spec_lm_head_sample(tiles)");
+    hipLaunchKernelGGL(sample_finalize_kernel, dim3(R), dim3(256), 0, st, part, n_vt, V, keys, q_tok, q_prob, NQ, row_ctr,
+                       sa.key0, sa.key1, lse, z_supp, sample_p, sample_res);
+    SV_LAUNCH_CHECK("spec_lm_head_sample(finalize)");
     return SPEC_OK;
 }
 

@@ -17,6 +17,11 @@
  *   spec_tree_accept           the acceptance walk from the root
  *   spec_kv_compact            the accepted path's K/V moved to contiguous slots
  *
+ * and, for sampled (temperature > 0) instead of greedy decoding:
+ *
+ *   spec_lm_head_sample        lm_head with softmax statistics and two draws fused in
+ *   spec_sample_accept         the speculative-sampling chain walk
+ *
  * The method follows the page "span-02 engine/crates/model/src/spec.rs"
  * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
  * pages, KV appended in place at pos..pos+k, greedy acceptance, rollback by
@@ -334,6 +339,74 @@ int spec_tree_accept(const int32_t* argmax, const int32_t* drafts, int32_t kmax,
 int spec_kv_compact(spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages, const int32_t* page_table,
                     int32_t max_pages, const int32_t* pos, const int32_t* path, const int32_t* accept_len,
                     int32_t kmax, int32_t B, int32_t Hkv, int32_t D, int32_t* seq_status, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Speculative-sampling verify.
+ *
+ * Defined by: DSSD fast.py _sample_verify (exact speculative sampling on a chain:
+ * draft i is kept with probability min(1, p_i(x_i) / q_i(x_i)); at the first
+ * rejection the token is drawn from norm(max(p_i - q_i, 0)); if every draft is kept
+ * the bonus is drawn from p_n; p = softmax(logits / temperature)); oxinfer
+ * speculative_accept (the same test, q given as (token, probability) pairs, the
+ * resulting token distributed exactly as p); memra's sampled-spec note
+ * (counter-based Philox keyed by seed and event, so that runs are reproducible).
+ *
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011) with key
+ * (seed & 0xffffffff, seed >> 32); a word w gives u = (floor(w / 512) + 1/2) / 2^23.
+ * Each row r carries two caller-chosen counter words row_ctr[r] = (a, b), e.g. the
+ * row's position and a request id, so that a sequence's draws do not depend on the
+ * batch it shares:
+ *   Gumbel noise of entry v of row r:  G = -ln(-ln u), u from word v % 4 of
+ *                                      counter (v / 4, a, b, 0)
+ *   acceptance uniform of row r:       u from word 0 of counter (0, a, b, 1)
+ * Draws use the Gumbel-max rule: the argmax of log-weight + G over the entries is a
+ * draw from the normalised weights (ties to the smaller index).
+ *
+ * The draft distribution of row r (the row that verifies draft j of its sequence)
+ * is sparse: up to NQ <= 8 support tokens q_tok[r][e] (-1 = unused) with masses
+ * q_prob[r][e] (a point mass: one token with mass 1). Bonus rows have no support.
+ * ------------------------------------------------------------------------- */
+
+/* spec_lm_head_sample — for every row r of hidden [R][H] against the packed W:
+ *   z_v = logit_v / temperature  (logit as in spec_lm_head_argmax, fp32)
+ *   lse[r]        = ln sum_v exp(z_v)
+ *   z_supp[r][e]  = z of q_tok[r][e] (NaN for unused entries)
+ *   sample_p[r]   = argmax_v z_v + G_v                         (a draw from p)
+ *   sample_res[r] = argmax_{v : p_v > q_v} ln(p_v - q_v) + G_v  (a draw from
+ *                   norm(max(p - q, 0)); sample_p[r] if that set is empty)
+ * with q_v the summed mass of v in the row's support. Logits never reach memory:
+ * the tile kernel leaves per-(row, vocabulary group) softmax partials, the support
+ * z's and the best z + G outside the support (a packed 64-bit key per row); a
+ * per-row kernel reduces the partials in a fixed order and forms the draws.
+ * workspace: spec_lm_head_sample_workspace_bytes(R, H, V) bytes, zero on first use;
+ * every call leaves it zero (calls sharing one must not overlap). Limits as
+ * spec_lm_head_argmax; 0 <= NQ <= 8; temperature finite and > 0. */
+size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V);
+int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                        float temperature, const int32_t* q_tok, const float* q_prob, int32_t NQ,
+                        const int32_t* row_ctr, uint64_t seed, float* lse, float* z_supp, int32_t* sample_p,
+                        int32_t* sample_res, void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_sample_accept — the chain walk. For sequence s (rows off_s .. off_s + k_s,
+ * packed as for the greedy call) and j = 0 .. k_s - 1, row r = off_s + j, draft
+ * x = map(drafts[s][j]) (d2t as in spec_greedy_accept) whose support entry e has
+ * q_tok[r][e] == x and q_prob[r][e] > 0 (the first such entry):
+ *   keep x iff u_r < exp(z_supp[r][e] - lse[r]) / q_prob[r][e]
+ *   else emit sample_res[r] and stop;
+ * if every draft is kept, emit sample_p[off_s + k_s]. Outputs as
+ * spec_greedy_accept (accept_len, n_emit = accept_len + 1, emit [B][kmax + 1] with
+ * -1 after the last token, next_tok = the drawn token, pos_out = pos_in +
+ * accept_len + 1). A draft outside its row's support, or outside its vocabulary,
+ * sets SPEC_STATUS_BAD_TOKEN; status bits and the outputs of a flagged sequence as
+ * spec_greedy_accept. lse, z_supp, sample_p and sample_res are the outputs of
+ * spec_lm_head_sample for the same rows, row_ctr and seed.
+ * Limits: 1 <= B <= 8192, 0 <= kmax <= 1024, R >= 1, V >= 1, 0 <= NQ <= 8. */
+int spec_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
+                       int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const int32_t* q_tok,
+                       const float* q_prob, int32_t NQ, const float* lse, const float* z_supp,
+                       const int32_t* sample_p, const int32_t* sample_res, const int32_t* row_ctr, uint64_t seed,
+                       const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                       int32_t* emit, int32_t* next_tok, int32_t* seq_status, void* stream);
 
 #ifdef __cplusplus
 }

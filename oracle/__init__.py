@@ -252,7 +252,8 @@ def accept_uniform(row_ctr, seed):
 
 def sample_rows(logits, T, q_tok, q_prob, row_ctr, seed):
     """logits fp64 [R, V]; q_tok int32 [R, NQ]; q_prob fp32 [R, NQ]; row_ctr int32 [R, 2].
-    Returns dict lse [R], z_supp [R, NQ], sample_p [R], sample_res [R]."""
+    Returns dict lse [R], z_supp [R, NQ], sample_p [R], sample_res [R], and gap_p / gap_res
+    [R]: how far each draw's winner is above the runner-up (in log-weight + noise)."""
     logits = np.ascontiguousarray(logits, np.float64)
     R, V = logits.shape
     q_tok = _i32(q_tok)
@@ -262,10 +263,12 @@ def sample_rows(logits, T, q_tok, q_prob, row_ctr, seed):
     z = np.zeros((R, NQ), np.float64)
     sp = np.zeros(R, np.int32)
     sr = np.zeros(R, np.int32)
+    gp = np.zeros(R, np.float64)
+    gr = np.zeros(R, np.float64)
     lib().oracle_sample_rows(_p(logits), ctypes.c_int32(R), ctypes.c_int32(V), ctypes.c_double(T), _p(q_tok),
                              _p(q_prob), ctypes.c_int32(NQ), _p(_i32(row_ctr)), ctypes.c_uint64(seed), _p(lse),
-                             _p(z), _p(sp), _p(sr))
-    return dict(lse=lse, z_supp=z, sample_p=sp, sample_res=sr)
+                             _p(z), _p(sp), _p(sr), _p(gp), _p(gr))
+    return dict(lse=lse, z_supp=z, sample_p=sp, sample_res=sr, gap_p=gp, gap_res=gr)
 
 
 def sample_accept(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, q_tok, q_prob, rows, row_ctr, seed, pos_in):

@@ -669,7 +669,7 @@ double oracle_accept_uniform(const int32_t* rc, uint64_t seed) {
  * to the smaller index). */
 void oracle_sample_rows(const double* logits, int32_t R, int32_t V, double T, const int32_t* q_tok,
                         const float* q_prob, int32_t NQ, const int32_t* row_ctr, uint64_t seed, double* lse,
-                        double* z_supp, int32_t* sample_p, int32_t* sample_res) {
+                        double* z_supp, int32_t* sample_p, int32_t* sample_res, double* gap_p, double* gap_res) {
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
 #pragma omp parallel for schedule(dynamic)
     for (int r = 0; r < R; ++r) {
@@ -685,26 +685,36 @@ void oracle_sample_rows(const double* logits, int32_t R, int32_t V, double T, co
         const float* qp = q_prob + (int64_t)r * NQ;
         for (int e = 0; e < NQ; ++e)
             z_supp[(int64_t)r * NQ + e] = (qt[e] >= 0 && qt[e] < V) ? l[qt[e]] / T : NAN;
-        double bp = -INFINITY, br = -INFINITY;
+        /* best and runner-up of each draw (the runner-up only reports how decided the
+           draw is: gap = best - runner-up) */
+        double bp = -INFINITY, br = -INFINITY, bp2 = -INFINITY, br2 = -INFINITY;
         int ip = -1, ir = -1;
         for (int v = 0; v < V; ++v) {
             const double z = l[v] / T;
             const double g = row_gumbel((uint32_t)v, row_ctr + 2 * (int64_t)r, key);
             if (z + g > bp) {
+                bp2 = bp;
                 bp = z + g;
                 ip = v;
+            } else if (z + g > bp2) {
+                bp2 = z + g;
             }
             double q = 0.0;
             for (int e = 0; e < NQ; ++e)
                 if (qt[e] == v) q += qp[e];
             const double rv = exp(z - L) - q;
             if (rv > 0.0 && log(rv) + g > br) {
+                br2 = br;
                 br = log(rv) + g;
                 ir = v;
+            } else if (rv > 0.0 && log(rv) + g > br2) {
+                br2 = log(rv) + g;
             }
         }
         sample_p[r] = ip;
         sample_res[r] = ir >= 0 ? ir : ip;
+        if (gap_p) gap_p[r] = bp - bp2;
+        if (gap_res) gap_res[r] = ir >= 0 ? br - br2 : bp - bp2;
     }
 }
 

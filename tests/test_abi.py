@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
             "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
-            "spec_kv_compact"} <= set(names)
+            "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"} <= set(names)
     lib = gdv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +104,19 @@ def test_host_argument_checks():
     assert cmp(64, 0, 3) == -1 and cmp(64, 1, 128) == -1
     assert L.spec_kv_compact(_vp(0x1002), p, 10, p, 4, p, p, p, 3, 2, 1, 64, p, None) == -1
     assert b"aligned" in L.spec_last_error()
+    # sampling calls
+    need = L.spec_lm_head_sample_workspace_bytes(8, 256, 1000)
+    assert need >= 256 + 8 * 8 + 8 * 8 * 8      # keys + (max, sum) per (row, 128-entry group)
+    smp = lambda T, NQ, ws: L.spec_lm_head_sample(p, p, 8, 256, 1000, T, p, p, NQ, p, 1, p, p, p, p, p, ws, None)
+    assert smp(0.0, 1, 1 << 30) == -1 and b"temperature" in L.spec_last_error()
+    assert smp(float("inf"), 1, 1 << 30) == -1
+    assert smp(1.0, 9, 1 << 30) == -1 and b"NQ" in L.spec_last_error()
+    assert smp(1.0, 1, need - 1) == -4
+    acc = lambda B, NQ: L.spec_sample_accept(p, 3, p, None, 0, 100, B, 8, p, p, NQ, p, p, p, p, p, 1, p, p, p, p, p,
+                                             p, p, None)
+    assert acc(0, 1) == -1 and acc(2, 9) == -1
+    assert L.spec_sample_accept(None, 3, p, None, 0, 100, 2, 8, p, p, 1, p, p, p, p, p, 1, p, p, p, p, p, p, p,
+                                None) == -1
 
 
 def test_product_path_does_not_touch_the_oracle():
