@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # Status bits, as the public header documents them for the library.
-BAD_PAGE, BAD_POS, BAD_ROWS, BAD_TOKEN, BAD_TREE = 1, 2, 4, 8, 16
+BAD_PAGE, BAD_POS, BAD_ROWS, BAD_TOKEN, BAD_TREE, BAD_LIMIT = 1, 2, 4, 8, 16, 32
 PAGE = 16
 
 
@@ -291,3 +291,25 @@ def sample_accept(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, q_tok, q_prob, r
                                _p(_i32(rows["sample_res"])), _p(_i32(row_ctr)), ctypes.c_uint64(seed),
                                _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit), _p(nt), _p(st))
     return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st)
+
+
+def greedy_accept_stop(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, stop_ids, remaining, pos_in):
+    """Greedy acceptance truncated at the first stop token and at remaining[s] tokens
+    (remaining None: no limit). Returns the greedy_accept dict plus done [B]."""
+    pos_out = np.zeros(B, np.int32)
+    acc = np.zeros(B, np.int32)
+    ne = np.zeros(B, np.int32)
+    emit = np.zeros((B, kmax + 1), np.int32)
+    nt = np.zeros(B, np.int32)
+    done = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    dr = _i32(drafts).reshape(B, max(kmax, 0)) if kmax > 0 else np.zeros((B, 1), np.int32)
+    d2 = None if d2t is None else _i32(d2t)
+    stops = _i32(stop_ids) if len(stop_ids) else np.zeros(1, np.int32)
+    rem = None if remaining is None else _i32(remaining)
+    lib().oracle_greedy_accept_stop(_p(_i32(g)), _p(dr), ctypes.c_int32(kmax), _p(_i32(k)), _p(d2),
+                                    ctypes.c_int32(n_draft_vocab), ctypes.c_int32(V), ctypes.c_int32(B),
+                                    ctypes.c_int32(R), _p(stops), ctypes.c_int32(len(stop_ids)), _p(rem),
+                                    _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit), _p(nt), _p(done),
+                                    _p(st))
+    return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, done=done, status=st)

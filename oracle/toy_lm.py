@@ -87,8 +87,9 @@ class ToyLM:
         g, _, _, _ = oracle.lm_head_argmax(h, self.Wlm, T, self.H, self.V)
         return g
 
-    def generate_ar(self, prompt, n_new):
-        """One-row greedy decoding (DSSD fast.py generate_ar)."""
+    def generate_ar(self, prompt, n_new, stop_ids=()):
+        """One-row greedy decoding (DSSD fast.py generate_ar): n_new tokens, or fewer
+        when a stop token is emitted (it is kept, and nothing follows it)."""
         self.reset()
         out = []
         g = None
@@ -97,12 +98,16 @@ class ToyLM:
         pos = len(prompt)
         while len(out) < n_new:
             out.append(g)
+            if g in stop_ids:
+                break
             g = int(self.forward_rows([g], pos)[0])
             pos += 1
         return out
 
-    def generate_spec(self, prompt, n_new, drafter, k):
-        """Draft -> one verify of k+1 rows -> greedy accept -> pos += a + 1."""
+    def generate_spec(self, prompt, n_new, drafter, k, stop_ids=None):
+        """Draft -> one verify of k+1 rows -> greedy accept -> pos += a + 1. With
+        stop_ids, the acceptance truncates at the first stop token and at the tokens
+        still allowed (n_new minus those emitted), and generation ends when it says so."""
         self.reset()
         for i, x in enumerate(prompt[:-1]):
             self.forward_rows([x], i)
@@ -111,13 +116,19 @@ class ToyLM:
         while len(out) < n_new:
             drafts = [int(d) for d in drafter(out, k)]
             g = self.forward_rows([x0] + drafts, pos)
-            res = oracle.greedy_accept(g, np.array([drafts], np.int32), k, np.array([k], np.int32), None, 0,
-                                       self.V, 1, k + 1, np.array([pos], np.int32))
+            args = (g, np.array([drafts], np.int32), k, np.array([k], np.int32), None, 0, self.V, 1, k + 1)
+            if stop_ids is None:
+                res = oracle.greedy_accept(*args, np.array([pos], np.int32))
+            else:
+                res = oracle.greedy_accept_stop(*args, list(stop_ids), np.array([n_new - len(out)], np.int32),
+                                                np.array([pos], np.int32))
             n = int(res["n_emit"][0])
             out.extend(int(t) for t in res["emit"][0, :n])
             accepted_hist.append(int(res["accept_len"][0]))
             pos = int(res["pos_out"][0])
             x0 = int(res["next_tok"][0])
+            if stop_ids is not None and res["done"][0]:
+                break
         return out[:n_new], accepted_hist
 
     def generate_tree(self, prompt, n_new, drafter):

@@ -1,0 +1,112 @@
+"""Pins of the oracle's greedy acceptance with stop tokens and a generation limit
+(oxinfer step: an accepted stop token ends the round, the committed tokens end at
+the first stop token, the session advances by the number committed; DSSD _commit:
+truncation at a stop token or at max_new; DSSD generate_ar: one-row decoding stops
+after the same token), CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.toy_lm import ToyLM
+
+
+def _round_like_oxinfer(g, drafts, stops, remaining):
+    """One round written the way oxinfer's step reads: accept while the draft equals the
+    row's greedy token, break after an accepted stop token, else take the row's token and
+    break; the bonus only if every draft was kept and the last kept one is no stop token;
+    then truncate after the first stop token and at the limit."""
+    out = []
+    for j, d in enumerate(drafts):
+        if d == g[j]:
+            out.append(d)
+            if d in stops:
+                break
+        else:
+            out.append(g[j])
+            break
+    else:
+        if not (out and out[-1] in stops):
+            out.append(g[len(drafts)])
+    for i, t in enumerate(out):
+        if t in stops:
+            out = out[:i + 1]
+            break
+    if remaining is not None:
+        out = out[:remaining]
+    return out
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_stop_rule_matches_the_round_written_out(seed):
+    rng = np.random.default_rng(seed)
+    B, kmax, V = 300, 6, 8
+    k = rng.integers(0, kmax + 1, B).astype(np.int32)
+    R = int((k + 1).sum())
+    g = rng.integers(0, V, R).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(k + 1)])
+    drafts = np.full((B, kmax), -1, np.int32)
+    for s in range(B):
+        for j in range(k[s]):
+            drafts[s, j] = g[off[s] + j] if rng.uniform() < 0.75 else rng.integers(0, V)
+    stops = [2, 5]
+    remaining = rng.integers(1, 8, B).astype(np.int32) if seed % 2 else None
+    pos = rng.integers(0, 50, B).astype(np.int32)
+    r = oracle.greedy_accept_stop(g, drafts, kmax, k, None, 0, V, B, R, stops, remaining, pos)
+    assert (r["status"] == 0).all()
+    for s in range(B):
+        want = _round_like_oxinfer(list(g[off[s]:off[s + 1]]), list(drafts[s, :k[s]]), stops,
+                                   None if remaining is None else int(remaining[s]))
+        c = len(want)
+        assert list(r["emit"][s, :c]) == want and (r["emit"][s, c:] == -1).all()
+        assert r["n_emit"][s] == c and r["pos_out"][s] == pos[s] + c and r["next_tok"][s] == want[-1]
+        kept = 0
+        while kept < min(k[s], c) and drafts[s, kept] == g[off[s] + kept]:
+            kept += 1
+        assert r["accept_len"][s] == kept
+        lim = remaining is not None and c == remaining[s]
+        assert r["done"][s] == int(want[-1] in stops or lim)
+
+
+def test_stop_hand_cases():
+    # drafts [3, 2, 4] against g [3, 2, 4, 7]; stop token 2 accepted at draft 1
+    g = np.array([3, 2, 4, 7], np.int32)
+    d = np.array([[3, 2, 4]], np.int32)
+    one = lambda stops, rem=None: oracle.greedy_accept_stop(g, d, 3, np.array([3], np.int32), None, 0, 10, 1, 4,
+                                                             stops, rem, np.array([100], np.int32))
+    r = one([2])
+    assert list(r["emit"][0]) == [3, 2, -1, -1] and r["n_emit"][0] == 2 and r["accept_len"][0] == 2
+    assert r["pos_out"][0] == 102 and r["next_tok"][0] == 2 and r["done"][0] == 1
+    r = one([7])                                        # the bonus is the stop token
+    assert list(r["emit"][0]) == [3, 2, 4, 7] and r["done"][0] == 1 and r["pos_out"][0] == 104
+    r = one([9])                                        # no stop: the plain greedy round
+    assert r["n_emit"][0] == 4 and r["done"][0] == 0
+    r = one([9], np.array([2], np.int32))               # the limit cuts after two tokens
+    assert list(r["emit"][0]) == [3, 2, -1, -1] and r["done"][0] == 1 and r["accept_len"][0] == 2
+    r = one([9], np.array([0], np.int32))
+    assert r["status"][0] == oracle.BAD_LIMIT and r["n_emit"][0] == 0 and r["pos_out"][0] == 100
+    # a rejected draft that is a stop token stops nothing: the row's own token is emitted
+    r = oracle.greedy_accept_stop(g, np.array([[3, 5, 4]], np.int32), 3, np.array([3], np.int32), None, 0, 10, 1,
+                                  4, [5], None, np.array([0], np.int32))
+    assert list(r["emit"][0]) == [3, 2, -1, -1] and r["done"][0] == 0
+
+
+def test_toy_spec_with_stop_ends_where_one_row_decoding_ends():
+    """DSSD generate_ar and generate_spec share the stop rule, so both streams end at the
+    same token; with the limit alone both give exactly max_new tokens."""
+    m = ToyLM(seed=0)
+    prompt = list(np.random.default_rng(1).integers(0, m.V, 20))
+    free = m.generate_ar(prompt, 60)
+    stop = free[23]                                    # a token the stream emits
+    ref = m.generate_ar(prompt, 60, stop_ids=(stop,))
+    assert ref[-1] == stop and len(ref) <= 24
+    rng = np.random.default_rng(7)
+
+    def drafter(out, kk):
+        true = free[len(out):len(out) + kk]
+        true = true + [0] * (kk - len(true))
+        return [t if rng.uniform() >= 0.2 else int((t + 1) % m.V) for t in true]
+
+    out, _ = m.generate_spec(prompt, 60, drafter, 4, stop_ids=(stop,))
+    assert out == ref
+    out, _ = m.generate_spec(prompt, 37, drafter, 4, stop_ids=())
+    assert out == free[:37]
