@@ -28,7 +28,7 @@ EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
             "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
-            "spec_sample_accept"]
+            "spec_sample_accept", "spec_greedy_accept_stop"]
 
 _lib = None
 
@@ -77,7 +77,10 @@ def lib() -> ctypes.CDLL:
                                           vp]
         L.spec_sample_accept.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, u64,
                                          vp, vp, vp, vp, vp, vp, vp, vp]
-        for name in ("spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack", "spec_greedy_accept",
+        L.spec_greedy_accept_stop.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp]
+        for name in ("spec_greedy_accept_stop", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
+                     "spec_greedy_accept",
                      "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
                      "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"):
             getattr(L, name).restype = ctypes.c_int
@@ -390,6 +393,36 @@ def spec_sample_accept(drafts, k, d2t, V, q_tok, q_prob, lse, z_supp, sample_p, 
                                   _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok), _ptr(seq_status),
                                   _stream(stream))
     _check(rc, "spec_sample_accept")
+
+
+def spec_greedy_accept_stop(argmax, drafts, k, d2t, V, stop_ids, remaining, pos_in, pos_out, accept_len, n_emit,
+                            emit, next_tok, done, seq_status, stream=None):
+    """spec_greedy_accept with stop tokens (stop_ids [n_stop] int32 device tensor, n_stop <= 16)
+    and an optional per-sequence limit remaining [B] (None: no limit); done [B] out."""
+    for t, n in ((argmax, "argmax"), (drafts, "drafts"), (k, "k"), (stop_ids, "stop_ids"), (pos_in, "pos_in"),
+                 (pos_out, "pos_out"), (accept_len, "accept_len"), (n_emit, "n_emit"), (emit, "emit"),
+                 (next_tok, "next_tok"), (done, "done"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    if remaining is not None:
+        _want(remaining, torch.int32, "remaining", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    B, kmax = drafts.shape
+    R = argmax.shape[0]
+    _shape(emit, (B, kmax + 1), "emit")
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (done, "done"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    if remaining is not None:
+        _shape(remaining, (B,), "remaining")
+    n_stop = stop_ids.numel()
+    rc = lib().spec_greedy_accept_stop(_ptr(argmax), _ptr(drafts) if drafts.numel() else None, kmax, _ptr(k),
+                                       _ptr(d2t), 0 if d2t is None else d2t.shape[0], V, B, R,
+                                       _ptr(stop_ids) if n_stop else None, n_stop, _ptr(remaining), _ptr(pos_in),
+                                       _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
+                                       _ptr(done), _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_greedy_accept_stop")
 
 
 def spec_delta_verify_rollback(mode, q, k, v, a, b, q_scale, state, rec, L, o=None, stream=None):

@@ -27,13 +27,18 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int kAcceptThreads = 1024;
 constexpr int kAcceptMaxB = 8192;
+constexpr int kMaxStop = 16;
 
+// STOP: the emitted tokens end after the first stop token and after remaining[s]
+// tokens (oxinfer step, DSSD _commit); pos advances by the tokens emitted.
+template <bool STOP>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int32_t* __restrict__ g, const int32_t* __restrict__ drafts, int kmax,
     const int32_t* __restrict__ k, const int32_t* __restrict__ d2t, int n_draft_vocab, int V, int B,
     int R, const int32_t* __restrict__ pos_in, int32_t* pos_out, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ n_emit, int32_t* __restrict__ emit, int32_t* __restrict__ next_tok,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, const int32_t* __restrict__ stop_ids, int n_stop,
+    const int32_t* __restrict__ remaining, int32_t* __restrict__ done) {
     __shared__ long long s_scan[kAcceptThreads];
     __shared__ int s_off[kAcceptMaxB];
     __shared__ int s_bad_k;
@@ -50,6 +55,13 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         int bits = 0;
         if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
         if (pos_in[s] < 0) bits |= SPEC_STATUS_BAD_POS;
+        int lim = 0x7fffffff;
+        if constexpr (STOP) {
+            if (remaining) {
+                lim = remaining[s];
+                if (!bits && lim < 1) bits = SPEC_STATUS_BAD_LIMIT;
+            }
+        }
         int32_t* e = emit + (size_t)s * (kmax + 1);
         if (bits) {
             for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
@@ -59,6 +71,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
                 n_emit[s] = 0;
                 next_tok[s] = -1;
                 pos_out[s] = pos_in[s];
+                if constexpr (STOP) done[s] = 0;
             }
             continue;
         }
@@ -94,6 +107,57 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
                 n_emit[s] = 0;
                 next_tok[s] = -1;
                 pos_out[s] = pos_in[s];
+                if constexpr (STOP) done[s] = 0;
+            }
+            continue;
+        }
+        if constexpr (STOP) {
+            // out[j] = map(draft j) for j < a, out[a] = g[off + a]; c = up to and including the
+            // first stop token, then at most lim tokens
+            int c = a + 1;
+            for (int base = 0; base <= a; base += kWave) {
+                const int j = base + lane;
+                bool is_stop = false;
+                if (j <= a) {
+                    int t;
+                    if (j < a) {
+                        const int x = drafts[(size_t)s * kmax + j];
+                        t = d2t ? d2t[x] : x;
+                    } else {
+                        t = g[off + a];
+                    }
+                    for (int q = 0; q < n_stop; ++q) is_stop |= t == stop_ids[q];
+                }
+                const unsigned long long mm = __ballot(is_stop);
+                if (mm && c == a + 1) c = base + (int)__builtin_ctzll(mm) + 1;
+            }
+            const bool at_lim = c >= lim;
+            if (at_lim) c = lim;
+            int last = -1;
+            for (int j = lane; j <= kmax; j += kWave) {
+                int val = -1;
+                if (j < c) {
+                    if (j < a) {
+                        const int x = drafts[(size_t)s * kmax + j];
+                        val = d2t ? d2t[x] : x;
+                    } else {
+                        val = g[off + a];
+                    }
+                }
+                e[j] = val;
+                if (j == c - 1) last = val;
+            }
+            // the last emitted token, from the lane that wrote it
+            last = __shfl(last, (c - 1) % kWave);
+            if (lane == 0) {
+                bool is_stop = false;
+                for (int q = 0; q < n_stop; ++q) is_stop |= last == stop_ids[q];
+                status[s] = 0;
+                accept_len[s] = a < c ? a : c;
+                n_emit[s] = c;
+                next_tok[s] = last;
+                pos_out[s] = pos_in[s] + c;
+                done[s] = is_stop || at_lim;
             }
             continue;
         }
@@ -141,10 +205,33 @@ int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kma
     if (d2t && n_draft_vocab < 1) return fail(SPEC_EINVAL, "spec_greedy_accept: d2t given with n_draft_vocab=%d", n_draft_vocab);
     if (!argmax || !k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !seq_status || (kmax > 0 && !drafts))
         return fail(SPEC_EINVAL, "spec_greedy_accept: null required pointer");
-    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
+    hipLaunchKernelGGL(accept_kernel<false>, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
                        drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
-                       n_emit, emit, next_tok, seq_status);
+                       n_emit, emit, next_tok, seq_status, nullptr, 0, nullptr, nullptr);
     SV_LAUNCH_CHECK("spec_greedy_accept");
+    return SPEC_OK;
+}
+
+int spec_greedy_accept_stop(const int32_t* argmax, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                            const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R,
+                            const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
+                            const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                            int32_t* emit, int32_t* next_tok, int32_t* done, int32_t* seq_status, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (B < 1 || B > kAcceptMaxB) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: B=%d outside 1..%d", B, kAcceptMaxB);
+    if (kmax < 0 || kmax > 1024) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: kmax=%d outside 0..1024", kmax);
+    if (R < 1) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: R=%d < 1", R);
+    if (V < 1) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: V=%d < 1", V);
+    if (n_stop < 0 || n_stop > kMaxStop) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: n_stop=%d outside 0..%d", n_stop, kMaxStop);
+    if (d2t && n_draft_vocab < 1) return fail(SPEC_EINVAL, "spec_greedy_accept_stop: d2t given with n_draft_vocab=%d", n_draft_vocab);
+    if (!argmax || !k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !done || !seq_status ||
+        (kmax > 0 && !drafts) || (n_stop > 0 && !stop_ids))
+        return fail(SPEC_EINVAL, "spec_greedy_accept_stop: null required pointer");
+    hipLaunchKernelGGL(accept_kernel<true>, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
+                       drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
+                       n_emit, emit, next_tok, seq_status, stop_ids, n_stop, remaining, done);
+    SV_LAUNCH_CHECK("spec_greedy_accept_stop");
     return SPEC_OK;
 }
 

@@ -80,6 +80,7 @@ typedef uint16_t spec_bf16;
 #define SPEC_STATUS_BAD_ROWS 4  /* packing undefined (see above), or k_s > kmax           */
 #define SPEC_STATUS_BAD_TOKEN 8 /* draft id outside its vocabulary, or d2t entry >= V     */
 #define SPEC_STATUS_BAD_TREE 16 /* tree calls: a parent not before its node, a bad path   */
+#define SPEC_STATUS_BAD_LIMIT 32 /* stop call: a generation limit below one token          */
 
 /* Library version (increases with any ABI or numerics change). */
 int spec_version(void);
@@ -214,6 +215,25 @@ int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kma
                        int32_t B, int32_t R, const int32_t* pos_in, int32_t* pos_out,
                        int32_t* accept_len, int32_t* n_emit, int32_t* emit, int32_t* next_tok,
                        int32_t* seq_status, void* stream);
+
+/* spec_greedy_accept_stop — spec_greedy_accept with stop tokens and a generation
+ * limit (oxinfer step: an accepted stop token ends the round, the committed tokens
+ * end at the first stop token and the session advances by the number committed;
+ * DSSD _commit: truncation at a stop token or at max_new).
+ * With out = map(drafts[s][0..a)) ++ [argmax[off_s + a]] (the greedy round):
+ *   c = the length of out up to and including its first token in stop_ids (host
+ *       count n_stop <= 16, device array), then min(c, remaining[s]);
+ *   n_emit = c, emit = out[0..c) (-1 after), accept_len = min(a, c),
+ *   next_tok = out[c - 1], pos_out = pos_in + c,
+ *   done [B] int32 = 1 iff out[c - 1] is a stop token or c == remaining[s].
+ * remaining [B] int32 (tokens the sequence may still emit) may be NULL (no limit);
+ * remaining[s] < 1 sets SPEC_STATUS_BAD_LIMIT. Flagged sequences as
+ * spec_greedy_accept, with done = 0. */
+int spec_greedy_accept_stop(const int32_t* argmax, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                            const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R,
+                            const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
+                            const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                            int32_t* emit, int32_t* next_tok, int32_t* done, int32_t* seq_status, void* stream);
 
 /* ---------------------------------------------------------------------------
  * spec_delta_verify_rollback — Gated DeltaNet verify with per-token state

@@ -23,7 +23,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept",
             "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
-            "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"} <= set(names)
+            "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept",
+            "spec_greedy_accept_stop"} <= set(names)
     lib = gdv.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -117,6 +118,10 @@ def test_host_argument_checks():
     assert acc(0, 1) == -1 and acc(2, 9) == -1
     assert L.spec_sample_accept(None, 3, p, None, 0, 100, 2, 8, p, p, 1, p, p, p, p, p, 1, p, p, p, p, p, p, p,
                                 None) == -1
+    stop = lambda n_stop, stops, done: L.spec_greedy_accept_stop(p, p, 3, p, None, 0, 100, 2, 8, stops, n_stop, None,
+                                                                 p, p, p, p, p, p, done, p, None)
+    assert stop(17, p, p) == -1 and b"n_stop" in L.spec_last_error()
+    assert stop(2, None, p) == -1 and stop(2, p, None) == -1
 
 
 def test_product_path_does_not_touch_the_oracle():
