@@ -50,7 +50,7 @@ class VerifyStep:
     """Device buffers and the three launches of one verify step (on the current
     stream, so that the same calls run eagerly or under HIP graph capture)."""
 
-    def __init__(self, x: synth.VerifyInputs, dev):
+    def __init__(self, x: synth.VerifyInputs, dev, w_packed=None):
         wl = x.wl
         self.x, self.dev = x, dev
         self.B, self.R = len(x.pos), x.R
@@ -59,7 +59,8 @@ class VerifyStep:
         self.page_table = i32(x.page_table, dev)
         self.pos, self.k = i32(x.pos, dev), i32(x.k, dev)
         self.hidden = x.hidden
-        self.w_packed = gdv.spec_lm_head_pack(x.w)   # one-time weight re-layout, outside the timed loop
+        # one-time weight re-layout, outside the timed loop
+        self.w_packed = gdv.spec_lm_head_pack(x.w) if w_packed is None else w_packed
         self.attn_out = torch.empty((x.R, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
         self.attn_status = torch.empty(self.B, dtype=torch.int32, device=dev)
         self.attn_ws = gdv.workspace(gdv.verify_attn_workspace_bytes(self.B, x.R, wl.Hq, wl.Hkv, wl.D,
@@ -330,6 +331,49 @@ def sampling_leg(step: "VerifyStep", dev, reps: int, temperature: float = 0.1):
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_b / us[1] / 1e3 / HBM_PEAK_GBS}}
 
 
+def kpolicy_leg(step: "VerifyStep", dev, reps: int, seed: int = 0):
+    """The verify cost against rows that drives the adaptive draft depth (span-02
+    KPolicy): the b16k4 step (attention + lm_head + accept) at B = 16 with k = 0..7
+    drafts per sequence (16..128 rows), each call timed with events in the step's own
+    order; then the library policy's choice of k for a few acceptance rates and draft
+    costs."""
+    base = step.x.wl
+    table = []
+    for k in range(8):
+        wl = synth.VerifyWorkload(f"b16k{k}", B=16, k=k, k_lo=k, k_hi=k, ctx_lo=base.ctx_lo, ctx_hi=base.ctx_hi,
+                                  Hq=base.Hq, Hkv=base.Hkv, D=base.D, H=base.H, V=base.V, max_pages=base.max_pages,
+                                  w_std=base.w_std)
+        x = synth.make_verify_inputs(wl, seed=seed, device=dev, with_lm_head=False)
+        x.hidden = synth.normal_bf16((x.R, wl.H), 1.0, seed, "b16k4", "extra", dev)
+        st = VerifyStep(x, dev, w_packed=step.w_packed)
+        st.drafts = i32(np.zeros((16, max(k, 1)), np.int32)[:, :k] if k else np.zeros((16, 0), np.int32), dev)
+        fns = [st.attn, st.lm_head, st.accept]
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for f in fns:
+                f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        table.append((x.R, e0.elapsed_time(e1) / reps * 1e3))
+        del st, x
+        torch.cuda.empty_cache()
+    choices = []
+    for p in (0.3, 0.5, 0.7, 0.9):
+        for draft_us in (0.0, 15.0, 50.0):
+            pol = gdv.KPolicy(kmin=0, kmax=7, prior_p=p, prior_n=1e12, draft_us=draft_us, table=table)
+            k = pol.choose(16)
+            choices.append({"accept_p": p, "draft_us": draft_us, "k": k,
+                            "us_per_token": (pol.verify_cost(16 * (k + 1)) + k * draft_us) / pol.expected_tokens(k)
+                            / 16})
+    return {"workload": "b16k4 shapes at B=16, k = 0..7", "verify_us_by_rows": table, "choices": choices}
+
+
 def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
     """spec_lm_head_argmax alone at growing row counts with the workload's W: where the
     weight stream stops bounding it and the MFMA work starts to."""
@@ -513,6 +557,8 @@ def main():
         if wl.H == 4096 and wl.V == 151936:
             extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
         extras["sampling_verify"] = sampling_leg(step, dev, reps=20)
+        if wl.name == "b16k4":
+            extras["adaptive_k"] = kpolicy_leg(step, dev, reps=10, seed=args.seed)
         sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
         dl = extras["delta_roofline"]
         log(f"[bench] lm_head sweep: {sw}")
@@ -521,6 +567,11 @@ def main():
             f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
             f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
             f"{ist['rescan_us']:.1f} us")
+        if "adaptive_k" in extras:
+            ak = extras["adaptive_k"]
+            tbl = ", ".join(f"{r}: {t:.0f}" for r, t in ak["verify_us_by_rows"])
+            ch = ", ".join(f"p={c['accept_p']}/d={c['draft_us']:.0f}->k={c['k']}" for c in ak["choices"])
+            log(f"[bench] verify us by rows (B=16): {tbl}; policy: {ch}")
         sv_ = extras["sampling_verify"]
         log(f"[bench] sampling step {sv_['step_us']:.1f} us ({sv_['rows_per_s']:.0f} rows/s, "
             f"{sv_['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample {sv_['kernel_us']['spec_lm_head_sample']:.1f} us "

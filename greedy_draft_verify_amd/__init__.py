@@ -28,7 +28,19 @@ EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
             "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
-            "spec_sample_accept", "spec_greedy_accept_stop"]
+            "spec_sample_accept", "spec_greedy_accept_stop", "spec_kpolicy_init", "spec_kpolicy_accept_prob",
+            "spec_kpolicy_verify_cost", "spec_kpolicy_expected_tokens", "spec_kpolicy_choose",
+            "spec_kpolicy_update", "spec_kpolicy_update_batch"]
+
+SPEC_KPOLICY_MAXK, SPEC_KPOLICY_MAXPTS = 64, 32
+
+
+class _KPolicyStruct(ctypes.Structure):
+    """Mirror of the header's spec_kpolicy."""
+    _fields_ = [("kmin", ctypes.c_int32), ("kmax", ctypes.c_int32), ("prior_p", ctypes.c_double),
+                ("prior_n", ctypes.c_double), ("draft_us", ctypes.c_double), ("n_points", ctypes.c_int32),
+                ("cost_rows", ctypes.c_double * SPEC_KPOLICY_MAXPTS), ("cost_us", ctypes.c_double * SPEC_KPOLICY_MAXPTS),
+                ("att", ctypes.c_double * SPEC_KPOLICY_MAXK), ("succ", ctypes.c_double * SPEC_KPOLICY_MAXK)]
 
 _lib = None
 
@@ -79,6 +91,20 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp, vp, vp, vp, vp, vp]
         L.spec_greedy_accept_stop.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp]
+        pp = ctypes.POINTER(_KPolicyStruct)
+        dbl, dp = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
+        L.spec_kpolicy_init.argtypes = [pp, i32, i32, dbl, dbl, dbl, dp, dp, i32]
+        L.spec_kpolicy_init.restype = ctypes.c_int
+        for name, args in (("spec_kpolicy_accept_prob", [pp, i32]), ("spec_kpolicy_verify_cost", [pp, dbl]),
+                           ("spec_kpolicy_expected_tokens", [pp, i32])):
+            getattr(L, name).argtypes = args
+            getattr(L, name).restype = dbl
+        L.spec_kpolicy_choose.argtypes = [pp, i32, i32]
+        L.spec_kpolicy_choose.restype = i32
+        L.spec_kpolicy_update.argtypes = [pp, i32, i32]
+        L.spec_kpolicy_update.restype = None
+        L.spec_kpolicy_update_batch.argtypes = [pp, vp, vp, i32]
+        L.spec_kpolicy_update_batch.restype = ctypes.c_int
         for name in ("spec_greedy_accept_stop", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
                      "spec_greedy_accept",
                      "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
@@ -423,6 +449,40 @@ def spec_greedy_accept_stop(argmax, drafts, k, d2t, V, stop_ids, remaining, pos_
                                        _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
                                        _ptr(done), _ptr(seq_status), _stream(stream))
     _check(rc, "spec_greedy_accept_stop")
+
+
+class KPolicy:
+    """The library's adaptive draft-depth policy (spec_kpolicy_*), host side."""
+
+    def __init__(self, kmin=1, kmax=6, prior_p=0.7, prior_n=8.0, draft_us=0.0, table=((1.0, 1.0),)):
+        rows = (ctypes.c_double * len(table))(*[float(r) for r, _ in table])
+        us = (ctypes.c_double * len(table))(*[float(t) for _, t in table])
+        self.st = _KPolicyStruct()
+        _check(lib().spec_kpolicy_init(ctypes.byref(self.st), kmin, kmax, prior_p, prior_n, draft_us, rows, us,
+                                       len(table)), "spec_kpolicy_init")
+
+    def p(self, j):
+        return lib().spec_kpolicy_accept_prob(ctypes.byref(self.st), j)
+
+    def verify_cost(self, rows):
+        return lib().spec_kpolicy_verify_cost(ctypes.byref(self.st), float(rows))
+
+    def expected_tokens(self, k):
+        return lib().spec_kpolicy_expected_tokens(ctypes.byref(self.st), k)
+
+    def choose(self, B, row_cap=0):
+        return lib().spec_kpolicy_choose(ctypes.byref(self.st), B, row_cap)
+
+    def update(self, k, accepted):
+        lib().spec_kpolicy_update(ctypes.byref(self.st), k, accepted)
+
+    def update_batch(self, k, accept_len):
+        """k, accept_len: host int32 arrays [B] (e.g. the accept call's outputs, copied back)."""
+        import numpy as np
+        k = np.ascontiguousarray(k, np.int32)
+        a = np.ascontiguousarray(accept_len, np.int32)
+        _check(lib().spec_kpolicy_update_batch(ctypes.byref(self.st), k.ctypes.data_as(ctypes.c_void_p),
+                                               a.ctypes.data_as(ctypes.c_void_p), len(k)), "spec_kpolicy_update_batch")
 
 
 def spec_delta_verify_rollback(mode, q, k, v, a, b, q_scale, state, rec, L, o=None, stream=None):

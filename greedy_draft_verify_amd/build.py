@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 VALU ops are kept out of the device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

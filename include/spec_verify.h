@@ -22,6 +22,9 @@
  *   spec_lm_head_sample        lm_head with softmax statistics and two draws fused in
  *   spec_sample_accept         the speculative-sampling chain walk
  *
+ * and the host-side pieces around them: spec_greedy_accept_stop (stop tokens and a
+ * generation limit) and the adaptive draft-depth policy spec_kpolicy_*.
+ *
  * The method follows the page "span-02 engine/crates/model/src/spec.rs"
  * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
  * pages, KV appended in place at pos..pos+k, greedy acceptance, rollback by
@@ -427,6 +430,51 @@ int spec_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, co
                        const int32_t* sample_p, const int32_t* sample_res, const int32_t* row_ctr, uint64_t seed,
                        const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
                        int32_t* emit, int32_t* next_tok, int32_t* seq_status, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Adaptive draft depth (host side; no GPU work, no allocation).
+ *
+ * Defined by: span-02 spec.rs KPolicy (a running estimate of the conditional
+ * acceptance of draft position j given that positions < j were kept, with prior
+ * pseudo-counts; a piecewise-linear verify cost in the number of rows; k chosen to
+ * minimise the expected time per emitted token) and oxinfer DraftCosts (the same
+ * trade-off from measured round times and per-position acceptance rates).
+ *   p_j       = (succ[j] + prior_p * prior_n) / (att[j] + prior_n)
+ *   E(k)      = 1 + sum_{i=1..k} prod_{j<i} p_j        (tokens per sequence per cycle)
+ *   verify(r) = the cost table at r rows: linear through the origin below the first
+ *               point, linear between points, the last segment extended beyond
+ *   choose(B) = argmin over k in kmin .. kmax of (verify(B (k + 1)) + k draft_us) / E(k)
+ *               (the smaller k on ties); with row_cap > 0, k <= max(row_cap / B - 1, kmin)
+ *   update(k, a): for j < k, att[j] += (j <= a), succ[j] += (j < a)
+ * The caller owns the struct (plain data; copy it freely).
+ * ------------------------------------------------------------------------- */
+#define SPEC_KPOLICY_MAXK 64
+#define SPEC_KPOLICY_MAXPTS 32
+typedef struct {
+    int32_t kmin, kmax;
+    double prior_p, prior_n;
+    double draft_us;                  /* cost of drafting one more token, per cycle */
+    int32_t n_points;                 /* verify cost table: rows (increasing) -> us */
+    double cost_rows[SPEC_KPOLICY_MAXPTS];
+    double cost_us[SPEC_KPOLICY_MAXPTS];
+    double att[SPEC_KPOLICY_MAXK];    /* attempts of draft position j */
+    double succ[SPEC_KPOLICY_MAXK];   /* ... and how many were kept */
+} spec_kpolicy;
+
+/* Sets every field and zeroes the counters. EINVAL unless 0 <= kmin <= kmax < 64,
+ * 0 < prior_p <= 1, prior_n > 0, draft_us >= 0, 1 <= n_points <= 32 with positive,
+ * strictly increasing rows and finite non-negative costs. All pointers are host. */
+int spec_kpolicy_init(spec_kpolicy* p, int32_t kmin, int32_t kmax, double prior_p, double prior_n, double draft_us,
+                      const double* cost_rows, const double* cost_us, int32_t n_points);
+double spec_kpolicy_accept_prob(const spec_kpolicy* p, int32_t j);
+double spec_kpolicy_verify_cost(const spec_kpolicy* p, double rows);
+double spec_kpolicy_expected_tokens(const spec_kpolicy* p, int32_t k);
+/* The chosen k (>= kmin), or -1 for a null policy or B < 1. */
+int32_t spec_kpolicy_choose(const spec_kpolicy* p, int32_t B, int32_t row_cap);
+void spec_kpolicy_update(spec_kpolicy* p, int32_t k, int32_t accepted);
+/* update for every sequence with accept_len[s] >= 0 (host arrays k[B], accept_len[B];
+ * flagged sequences, -1, are skipped). */
+int spec_kpolicy_update_batch(spec_kpolicy* p, const int32_t* k, const int32_t* accept_len, int32_t B);
 
 #ifdef __cplusplus
 }

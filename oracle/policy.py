@@ -7,7 +7,8 @@ attempted when every earlier draft was kept, and succeeds when it is kept too).
     p_j        = (succ[j] + prior_p * prior_n) / (att[j] + prior_n)
     E(k)       = 1 + sum_{i=1..k} prod_{j<i} p_j          (tokens per sequence per cycle)
     verify(r)  = the piecewise-linear cost table at r rows (through the origin below the
-                 first point, the last segment extended past the last point)
+                 first point, the last segment extended past the last point; a one-point
+                 table is the line through the origin)
     cost(k; B) = (verify(B (k + 1)) + k * draft) / E(k)
     choose(B)  = the k in kmin .. min(kmax, row_cap / B - 1) with the least cost (the
                  smaller k on ties); without a row cap, kmin .. kmax
@@ -36,6 +37,8 @@ class KPolicy:
         for (r0, c0), (r1, c1) in zip(t, t[1:]):
             if r <= r1:
                 return c0 + (c1 - c0) * (r - r0) / (r1 - r0)
+        if len(t) == 1:          # one point: the line through the origin continues
+            return t[0][1] * r / t[0][0]
         (r0, c0), (r1, c1) = t[-2], t[-1]
         return c1 + (c1 - c0) * (r - r1) / (r1 - r0)
 
