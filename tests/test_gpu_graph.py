@@ -60,3 +60,120 @@ def test_graph_replay_matches_eager(name):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i} differs"
         run()                                          # the program's own eager work between replays
         torch.cuda.synchronize()
+
+
+def _replays_match(run, outputs, reps=4):
+    """Captures run() as a graph; every replay (with stale output bytes before it and
+    eager work after it) must give the eager bytes."""
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(reps):
+        for t in outputs:
+            t.view(torch.uint8).fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref, outputs)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i} differs"
+        run()
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_tree_step():
+    """Tree step (spec_verify_attn_tree -> spec_lm_head_argmax -> spec_tree_accept ->
+    spec_kv_compact) on the 16-node tree workload: the append rewrites every node's slot,
+    so a step after a compaction sees the same pool and the replays are idempotent."""
+    import greedy_draft_verify_amd as gdv
+    import bench
+    dev = torch.device("cuda:0")
+    x = synth.make_verify_inputs("b16tree", seed=1, device=dev, with_lm_head=False)
+    wl = x.wl
+    B, R, kmax = len(x.pos), x.R, wl.kmax
+    hidden = synth.normal_bf16((R, 256), 1.0, 1, "tiny", "extra", dev)
+    w = synth.normal_bf16((1000, 256), 1 / 16, 1, "tiny", "w", dev)
+    wp = gdv.spec_lm_head_pack(w)
+    parent_np = synth.make_parents(x.k, 1, wl.name, "trie")
+    parent = bench.i32(parent_np, dev)
+    pt, pos, k = bench.i32(x.page_table, dev), bench.i32(x.pos, dev), bench.i32(x.k, dev)
+    out = torch.empty((R, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+    am = torch.empty(R, dtype=torch.int32, device=dev)
+    lm_ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, 256, 1000), dev, zero=True)
+    gdv.spec_lm_head_argmax(hidden, wp, 1000, am, None, workspace_buf=lm_ws)
+    torch.cuda.synchronize()
+    g0 = am.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    tw = synth.VerifyWorkload("tw", B=B, k=kmax, k_lo=kmax, k_hi=kmax, ctx_lo=0, ctx_hi=0, Hq=1, Hkv=1, D=64, H=1,
+                              V=1000, max_pages=1)
+    drafts = bench.i32(synth.make_tree_drafts(tw, x.k, parent_np, [g0[off[s]:off[s + 1]] for s in range(B)], 1), dev)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, ast = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+    path = torch.empty((B, kmax), dtype=torch.int32, device=dev)
+    cst = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = gdv.workspace(gdv.verify_attn_tree_workspace_bytes(B, R, wl.Hq, wl.Hkv, wl.D, x.page_table.shape[1], kmax),
+                       dev)
+
+    def run():
+        gdv.spec_verify_attn_tree(x.q, x.k_new, x.v_new, x.k_pool, x.v_pool, pt, pos, k, parent, x.scale, out, st,
+                                  workspace_buf=ws)
+        gdv.spec_lm_head_argmax(hidden, wp, 1000, am, None, workspace_buf=lm_ws)
+        gdv.spec_tree_accept(am, drafts, k, parent, None, 1000, pos, pos_out, acc, ne, emit, nt, path, ast)
+        cst.zero_()
+        gdv.spec_kv_compact(x.k_pool, x.v_pool, pt, pos, path, acc, cst)
+
+    _replays_match(run, [out, am, acc, emit, path, pos_out, st, cst])
+    assert (st.cpu() == 0).all() and (cst.cpu() == 0).all() and acc.cpu().numpy().max() >= 1
+
+
+def test_graph_replay_sampling_step():
+    """Sampling step (spec_verify_attn -> spec_lm_head_sample -> spec_sample_accept) on the
+    b16k4 shapes with a small vocabulary: the sample workspace's keys are reset by every
+    call, so replays give the eager bytes."""
+    import greedy_draft_verify_amd as gdv
+    import bench
+    dev = torch.device("cuda:0")
+    x = synth.make_verify_inputs("b16k4", seed=2, device=dev, with_lm_head=False)
+    B, R, kmax, V, H = len(x.pos), x.R, x.wl.kmax, 3000, 512
+    hidden = synth.normal_bf16((R, H), 1.0, 2, "tiny", "extra", dev)
+    w = synth.normal_bf16((V, H), 0.2, 2, "tiny", "w", dev)
+    wp = gdv.spec_lm_head_pack(w)
+    step = bench.VerifyStep(x, dev, w_packed=wp)
+    rng = np.random.default_rng(4)
+    drafts_np = rng.integers(0, V, (B, kmax)).astype(np.int32)
+    step.drafts = bench.i32(drafts_np, dev)
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    q_tok = np.full((R, 2), -1, np.int32)
+    q_prob = np.zeros((R, 2), np.float32)
+    for s in range(B):
+        for j in range(x.k[s]):
+            q_tok[off[s] + j] = [drafts_np[s, j], rng.integers(0, V)]
+            q_prob[off[s] + j] = [0.6, 0.4]
+    q_tok_d, q_prob_d = bench.i32(q_tok, dev), torch.from_numpy(q_prob).to(dev)
+    row_ctr = bench.i32(np.stack([np.arange(R), np.zeros(R)], 1), dev)
+    lse = torch.empty(R, device=dev)
+    z = torch.empty((R, 2), device=dev)
+    sp = torch.empty(R, dtype=torch.int32, device=dev)
+    sr = torch.empty(R, dtype=torch.int32, device=dev)
+    ws = gdv.workspace(gdv.lm_head_sample_workspace_bytes(R, H, V), dev, zero=True)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, sst = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+
+    def run():
+        step.attn()
+        gdv.spec_lm_head_sample(hidden, wp, V, 0.7, q_tok_d, q_prob_d, row_ctr, 99, lse, z, sp, sr, workspace_buf=ws)
+        gdv.spec_sample_accept(step.drafts, step.k, None, V, q_tok_d, q_prob_d, lse, z, sp, sr, row_ctr, 99, step.pos,
+                               pos_out, acc, ne, emit, nt, sst)
+
+    _replays_match(run, [step.attn_out, lse, z, sp, sr, acc, emit, pos_out, sst])
+    assert (sst.cpu() == 0).all()
