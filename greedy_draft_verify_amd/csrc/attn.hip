@@ -147,10 +147,16 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
         if (tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid)) flags |= SPEC_STATUS_BAD_TREE;
     }
     if (pos_ok && ks >= 0) {
+        // 8 page ids per thread requested at once (clamped to the last page), then checked
         const int last_page = (int)(((long long)P + ks) / kPage);
-        for (int pg = tid; pg <= last_page; pg += 256) {
-            const int id = page_table[(size_t)s * max_pages + pg];
-            if (id < 0 || id >= n_pages) flags |= SPEC_STATUS_BAD_PAGE;
+        for (int pgb = tid; pgb <= last_page; pgb += 256 * 8) {
+            int ids[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                ids[u] = page_table[(size_t)s * max_pages + min(pgb + u * 256, last_page)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (pgb + u * 256 <= last_page && (ids[u] < 0 || ids[u] >= n_pages)) flags |= SPEC_STATUS_BAD_PAGE;
         }
     }
 #pragma unroll
@@ -317,15 +323,12 @@ struct LdsTile {
 };
 
 // Zeroes the V values of tokens past the sequence's last written position in one
-// 8-byte fragment (tokens tok0 .. tok0 + 3): a zero softmax weight must not meet
-// whatever those slots hold.
+// 8-byte fragment (tokens tok0 .. tok0 + 3, token e in half e % 2 of word e / 2): a
+// zero softmax weight must not meet whatever those slots hold. Branch-free.
 __device__ __forceinline__ uint2 mask_v(uint2 v, int tok0, int last) {
-    if (tok0 + 3 <= last) return v;
-    uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (tok0 + e > last) w[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-    return make_uint2(w[0], w[1]);
+    const uint32_t m0 = (tok0 <= last ? 0x0000ffffu : 0u) | (tok0 + 1 <= last ? 0xffff0000u : 0u);
+    const uint32_t m1 = (tok0 + 2 <= last ? 0x0000ffffu : 0u) | (tok0 + 3 <= last ? 0xffff0000u : 0u);
+    return make_uint2(v.x & m0, v.y & m1);
 }
 
 // Bits n .. n + 63 of the 128-bit value hi:lo (0 <= n < 64).
@@ -442,47 +445,64 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
         return id;
     };
 
-    // The next tile is requested into registers while the current one is used from
-    // LDS; V slots past the last written position are zeroed as they arrive.
-    uint4 stage[PER_THREAD];
-    auto load_tile = [&](int t0) {
+    // A tile's 16-byte chunks: chunk it of this thread lies in block b (0..3 K, 4..7 V of
+    // the tile's four pages; the same for the whole wave) at offset ch. The loads carry
+    // no data-dependent work, so all of a tile's loads are in flight together; pages past
+    // the sequence read a valid chunk of the split's first page instead, and their data
+    // is zeroed when the tile is written to LDS, where the V slots past the last written
+    // position are cleared too (a zero softmax weight must not meet what they hold).
+    auto chunk_blk = [&](int it) {
+        return __builtin_amdgcn_readfirstlane((it * kAttnThreads + wave * kWave) / BLK_CH);
+    };
+    auto load_tile = [&](int t0, uint4 (&dst)[PER_THREAD]) {
 #pragma unroll
         for (int it = 0; it < PER_THREAD; ++it) {
-            const int cidx = it * kAttnThreads + tid;
-            const int b = cidx / BLK_CH, ch = cidx % BLK_CH;      // block 0..3 K, 4..7 V
+            const int b = chunk_blk(it), ch = (it * kAttnThreads + tid) % BLK_CH;
             const int pg = t0 / kPage + (b & 3);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (pg <= last_page) {
-                const u16* base = (b < 4 ? k_pool : v_pool) + (size_t)(page_of(pg) * Hkv + hk) * BLK;
-                v = ld16(base + ch * 8);
-                if (b >= 4) {
-                    // chunk = 8 consecutive V elements: tokens 4 g .. 4 g + 3 of two channels
-                    const int tok0 = pg * kPage + 4 * ((ch * 8 % 256) / 64);
-                    const uint2 lo = mask_v(make_uint2(v.x, v.y), tok0, last);
-                    const uint2 hi = mask_v(make_uint2(v.z, v.w), tok0, last);
-                    v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                }
-            }
-            stage[it] = v;
+            const bool real = t0 < c1 && pg <= last_page;
+            const u16* base = (b < 4 ? k_pool : v_pool) + (size_t)(page_of(real ? pg : pg0) * Hkv + hk) * BLK;
+            dst[it] = ld16(base + ch * 8);
         }
     };
-    load_tile(c0);
-    // after the first tile's loads are issued, so that they do not wait on the mask
-    if (TREE && lq == 0) s_mk[wave * 16 + l16] = mk;   // read after the first tile's barriers
-    for (int t0 = c0; t0 < c1; t0 += kKT) {
-        __syncthreads();  // previous tile's LDS reads are done
+    auto store_tile = [&](int t0, const uint4 (&src)[PER_THREAD]) {
 #pragma unroll
-        for (int it = 0; it < PER_THREAD; ++it) st16(smem + (it * kAttnThreads + tid) * 8, stage[it]);
+        for (int it = 0; it < PER_THREAD; ++it) {
+            const int b = chunk_blk(it), ch = (it * kAttnThreads + tid) % BLK_CH;
+            const int pg = t0 / kPage + (b & 3);
+            uint4 v = src[it];
+            if (pg > last_page) v = make_uint4(0, 0, 0, 0);
+            if (b >= 4) {
+                // chunk = 8 consecutive V elements: tokens 4 g .. 4 g + 3 of two channels
+                const int tok0 = pg * kPage + 4 * ((ch * 8 % 256) / 64);
+                const uint2 lo = mask_v(make_uint2(v.x, v.y), tok0, last);
+                const uint2 hi = mask_v(make_uint2(v.z, v.w), tok0, last);
+                v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+            st16(smem + (it * kAttnThreads + tid) * 8, v);
+        }
+    };
+    auto use_tile = [&](int t0, const uint4 (&stg)[PER_THREAD], auto refill) {
+        __syncthreads();  // previous tile's LDS reads are done
+        store_tile(t0, stg);
         __syncthreads();
-        if (t0 + kKT < c1) load_tile(t0 + kKT);
-        if (!active) continue;
+        refill();
+        if (!active) return;
         // full: every row keeps every key of the tile (chain: the tile ends at or before
         // the first row's position; tree: at or before the root)
         const bool full = t0 + kKT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
         const uint64_t win = (TREE && !full) ? tree_window(s_mk[wave * 16 + l16], t0 - P0 + 64) : 0ull;
         const LdsTile<D> src{smem + lane * 8, smem + 4 * BLK + lane * 4};
         TM::template run<TREE>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
-    }
+    };
+    // The next tile is requested into registers while the current one is used from LDS.
+    uint4 stage[PER_THREAD];
+    load_tile(c0, stage);
+    // after the first tile's loads are issued, so that they do not wait on the mask
+    if (TREE && lq == 0) s_mk[wave * 16 + l16] = mk;   // read after the first tile's barriers
+    for (int t0 = c0; t0 < c1; t0 += kKT)
+        use_tile(t0, stage, [&] {
+            if (t0 + kKT < c1) load_tile(t0 + kKT, stage);
+        });
     if (!active) return;
     const size_t idx = ((size_t)(si.off + jrow) * Hq + h) * n_splits + c;
     store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
