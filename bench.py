@@ -430,12 +430,35 @@ def cpu_baseline(x_host: synth.VerifyInputs, n_seq: int, min_seconds: float = 10
         t4 = time.perf_counter()
         t_attn, t_lm, t_acc, reps = t_attn + (t1 - t0), t_lm + (t2 - t1), t_acc + (t4 - t3), reps + 1
     secs = (t_attn + t_lm + t_acc) / reps
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # threads the step actually ran on: the oracle's OpenMP pool and numpy's BLAS pool
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([int(p_.get("num_threads", 1)) for p_ in threadpool_info()] or [1])
+    # the same step once more on one core (both pools limited to one thread)
+    with threadpool_limits(limits=1):
+        kpr, vpr = kp.copy(), vp.copy()
+        t0 = time.perf_counter()
+        off, st = oracle.validate(pt, pt.shape[1], x_host.n_pages, pos, k, wl.kmax, n_seq, R)
+        oracle.append_kv(knb, vnb, kpr, vpr, pt, pt.shape[1], pos, k, off, st, n_seq, wl.Hkv, wl.D)
+        oracle.verify_attn(qb, kpr, vpr, pt, pt.shape[1], pos, k, off, st, n_seq, R, wl.Hq, wl.Hkv, wl.D,
+                           x_host.scale)
+        g, _, _, _ = oracle.lm_head_argmax(hb, wb, R, wl.H, wl.V)
+        oracle.greedy_accept(g, drafts, wl.kmax, k, x_host.d2t, 0 if x_host.d2t is None else len(x_host.d2t),
+                             wl.V, n_seq, R, pos)
+        secs_1 = time.perf_counter() - t0
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=R / secs, unit="rows/s", cores=cores, kind="oracle",
                 sample=f"first {n_seq} of {len(x_host.pos)} sequences ({R} rows), the whole oracle step "
                        f"repeated {reps} times ({t_attn + t_lm + t_acc:.1f} s); per repetition: fp64 "
                        f"attention+append {t_attn / reps:.3f}s, lm_head+argmax {t_lm / reps:.3f}s, accept "
-                       f"{t_acc / reps:.5f}s",
+                       f"{t_acc / reps:.5f}s; host: {model}, os.cpu_count() = {os.cpu_count()}",
+                single_core_value=R / secs_1, single_core_seconds=secs_1,
                 seconds=secs)
 
 
