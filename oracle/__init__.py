@@ -313,3 +313,21 @@ def greedy_accept_stop(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, stop_ids
                                     _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit), _p(nt), _p(done),
                                     _p(st))
     return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, done=done, status=st)
+
+
+def truncate_stop(res, kmax, stop_ids, remaining, pos_in, path=None):
+    """Stop tokens and a limit applied to an acceptance walk's outputs (a dict as the
+    accept functions return; copied). path: the tree walk's path [B, kmax] or None."""
+    out = {k: np.ascontiguousarray(v, np.int32).copy() for k, v in res.items()}
+    B = len(out["n_emit"])
+    done = np.zeros(B, np.int32)
+    stops = _i32(stop_ids) if len(stop_ids) else np.zeros(1, np.int32)
+    rem = None if remaining is None else _i32(remaining)
+    ph = None if path is None else np.ascontiguousarray(path, np.int32).reshape(B, kmax).copy()
+    lib().oracle_truncate_stop(_p(out["emit"]), _p(out["n_emit"]), _p(out["accept_len"]), _p(_i32(pos_in)),
+                               _p(out["pos_out"]), _p(out["next_tok"]), _p(ph), ctypes.c_int32(kmax), _p(stops),
+                               ctypes.c_int32(len(stop_ids)), _p(rem), _p(done), _p(out["status"]), ctypes.c_int32(B))
+    out["done"] = done
+    if ph is not None:
+        out["path"] = ph
+    return out

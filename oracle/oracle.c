@@ -810,37 +810,36 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
 }
 
 /* ---------------------------------------------------------------------------
- * Greedy acceptance with stop tokens and a generation limit (oxinfer step: keep
- * drafts while they match, stop drafting after an accepted stop token, truncate the
- * committed tokens after the first stop token, advance the session by the number
- * committed; DSSD _commit: truncate at a stop token or at max_new).
- *   out = map(drafts[0..a)) ++ [g[off + a]]   (the greedy rule, a = accepted drafts)
+ * Stop tokens and a generation limit, applied to the outputs of an acceptance walk
+ * (oxinfer step: the committed tokens end after the first stop token and the session
+ * advances by the number committed; DSSD _commit: truncation at a stop token or at
+ * max_new). For every sequence with st[s] == 0, with out = emit[s][0 .. n_emit):
  *   c = the length of out up to and including its first stop token (|out| if none),
  *       then min(c, remaining[s])
- *   n_emit = c, emit = out[0..c), accept_len = min(a, c), next_tok = out[c - 1],
- *   pos_out = pos_in + c, done = 1 iff out[c - 1] is a stop token or c == remaining.
- * remaining == NULL: no limit. remaining[s] < 1 sets ORC_BAD_LIMIT. Otherwise as
- * oracle_greedy_accept (a flagged sequence gets done = 0). */
-void oracle_greedy_accept_stop(const int32_t* g, const int32_t* drafts, int32_t kmax, const int32_t* k,
-                               const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R,
-                               const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
-                               const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
-                               int32_t* emit, int32_t* next_tok, int32_t* done, int32_t* st) {
-    oracle_greedy_accept(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len, n_emit, emit,
-                         next_tok, st);
+ *   n_emit = c, emit = out[0..c) (-1 after), accept_len = min(accept_len, c),
+ *   next_tok = out[c - 1], pos_out = pos_in + c,
+ *   path (tree walks; NULL otherwise) keeps its first accept_len entries (-1 after),
+ *   done = 1 iff out[c - 1] is a stop token or c == remaining[s].
+ * remaining == NULL: no limit; remaining[s] < 1 sets ORC_BAD_LIMIT and gives the
+ * outputs of a flagged sequence. Sequences flagged on entry get done = 0. */
+void oracle_truncate_stop(int32_t* emit, int32_t* n_emit, int32_t* accept_len, const int32_t* pos_in,
+                          int32_t* pos_out, int32_t* next_tok, int32_t* path, int32_t kmax, const int32_t* stop_ids,
+                          int32_t n_stop, const int32_t* remaining, int32_t* done, int32_t* st, int32_t B) {
     for (int s = 0; s < B; ++s) {
         done[s] = 0;
+        int32_t* e = emit + (int64_t)s * (kmax + 1);
+        int32_t* ph = path ? path + (int64_t)s * kmax : NULL;
         if (st[s] == 0 && remaining && remaining[s] < 1) {
             st[s] = ORC_BAD_LIMIT;
-            int32_t* e = emit + (int64_t)s * (kmax + 1);
             for (int j = 0; j <= kmax; ++j) e[j] = -1;
+            if (ph)
+                for (int j = 0; j < kmax; ++j) ph[j] = -1;
             accept_len[s] = -1;
             n_emit[s] = 0;
             next_tok[s] = -1;
             pos_out[s] = pos_in[s];
         }
         if (st[s]) continue;
-        int32_t* e = emit + (int64_t)s * (kmax + 1);
         const int a = accept_len[s];
         int c = n_emit[s];
         int stopped = 0;
@@ -855,6 +854,8 @@ void oracle_greedy_accept_stop(const int32_t* g, const int32_t* drafts, int32_t 
         for (int j = c; j <= kmax; ++j) e[j] = -1;
         n_emit[s] = c;
         accept_len[s] = a < c ? a : c;
+        if (ph)
+            for (int j = accept_len[s]; j < kmax; ++j) ph[j] = -1;
         next_tok[s] = e[c - 1];
         pos_out[s] = pos_in[s] + c;
         int is_stop = 0;
@@ -862,4 +863,17 @@ void oracle_greedy_accept_stop(const int32_t* g, const int32_t* drafts, int32_t 
             if (e[c - 1] == stop_ids[q]) is_stop = 1;
         done[s] = is_stop || (remaining && c == remaining[s]);
     }
+}
+
+/* Greedy acceptance with stop tokens and a generation limit: oracle_greedy_accept,
+ * then oracle_truncate_stop on its outputs (a flagged sequence gets done = 0). */
+void oracle_greedy_accept_stop(const int32_t* g, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                               const int32_t* d2t, int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R,
+                               const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
+                               const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                               int32_t* emit, int32_t* next_tok, int32_t* done, int32_t* st) {
+    oracle_greedy_accept(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len, n_emit, emit,
+                         next_tok, st);
+    oracle_truncate_stop(emit, n_emit, accept_len, pos_in, pos_out, next_tok, NULL, kmax, stop_ids, n_stop, remaining,
+                         done, st, B);
 }

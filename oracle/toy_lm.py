@@ -131,11 +131,13 @@ class ToyLM:
                 break
         return out[:n_new], accepted_hist
 
-    def generate_tree(self, prompt, n_new, drafter):
+    def generate_tree(self, prompt, n_new, drafter, stop_ids=None):
         """Tree drafts (DSSD fast.py _tree_cycle / _star_cycle): ``drafter(out)`` returns
         (parent, tokens) for the nodes below the root in creation order; one verify of
         the whole tree -> tree acceptance walk -> compaction of the accepted path's KV
-        -> pos += a + 1."""
+        -> pos += a + 1. With stop_ids, the walk's outputs are truncated at the first
+        stop token and at the tokens still allowed (DSSD _commit), the compaction moves
+        only the committed nodes, and generation ends when the round says so."""
         self.reset()
         for i, x in enumerate(prompt[:-1]):
             self.forward_rows([x], i)
@@ -149,6 +151,9 @@ class ToyLM:
             res = oracle.tree_accept(g, np.array([toks], np.int32), k, np.array([k], np.int32), parent[None, :],
                                      None, 0, self.V, 1, k + 1, np.array([pos], np.int32))
             assert res["status"][0] == 0
+            if stop_ids is not None:
+                res = oracle.truncate_stop(res, k, list(stop_ids), np.array([n_new - len(out)], np.int32),
+                                           np.array([pos], np.int32), path=res["path"])
             oracle.kv_compact(self.k_pool, self.v_pool, self.page_table, self.max_pages, np.array([pos], np.int32),
                               res["path"], res["accept_len"], k, res["status"], 1, self.Hkv, self.D)
             n = int(res["n_emit"][0])
@@ -156,4 +161,6 @@ class ToyLM:
             accepted_hist.append(int(res["accept_len"][0]))
             pos = int(res["pos_out"][0])
             x0 = int(res["next_tok"][0])
+            if stop_ids is not None and res["done"][0]:
+                break
         return out[:n_new], accepted_hist

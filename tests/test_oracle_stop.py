@@ -110,3 +110,47 @@ def test_toy_spec_with_stop_ends_where_one_row_decoding_ends():
     assert out == ref
     out, _ = m.generate_spec(prompt, 37, drafter, 4, stop_ids=())
     assert out == free[:37]
+
+
+def test_truncation_of_a_tree_walk_keeps_only_committed_path_nodes():
+    """Walk: root -> node 2 (token 7) -> node 3 (token 5), bonus 9; stop token 7 ends the
+    round after node 2, so the path keeps node 2 only and pos advances by one."""
+    g = np.array([7, 1, 5, 9], np.int32)                 # greedy tokens of nodes 0..3
+    drafts = np.array([[4, 7, 5]], np.int32)             # nodes 1..3
+    parent = np.array([[-1, 0, 0, 2]], np.int32)
+    res = oracle.tree_accept(g, drafts, 3, np.array([3], np.int32), parent, None, 0, 10, 1, 4,
+                             np.array([50], np.int32))
+    assert list(res["path"][0]) == [2, 3, -1] and list(res["emit"][0]) == [7, 5, 9, -1]
+    t = oracle.truncate_stop(res, 3, [7], None, np.array([50], np.int32), path=res["path"])
+    assert list(t["path"][0]) == [2, -1, -1] and list(t["emit"][0]) == [7, -1, -1, -1]
+    assert t["accept_len"][0] == 1 and t["n_emit"][0] == 1 and t["pos_out"][0] == 51 and t["done"][0] == 1
+    assert t["next_tok"][0] == 7
+    t = oracle.truncate_stop(res, 3, [], np.array([2], np.int32), np.array([50], np.int32), path=res["path"])
+    assert list(t["path"][0]) == [2, 3, -1] and t["n_emit"][0] == 2 and t["accept_len"][0] == 2
+    assert t["done"][0] == 1 and t["next_tok"][0] == 5
+
+
+def test_toy_tree_with_stop_ends_where_one_row_decoding_ends():
+    m = ToyLM(seed=0)
+    prompt = list(np.random.default_rng(1).integers(0, m.V, 20))
+    free = m.generate_ar(prompt, 60)
+    stop = free[29]
+    ref = m.generate_ar(prompt, 60, stop_ids=(stop,))
+    assert ref[-1] == stop
+    rng = np.random.default_rng(4)
+
+    def drafter(out):
+        true = free[len(out):len(out) + 6] + [0] * 6
+        par, toks, spine = [], [], [0]
+        for d in range(4):
+            par.append(spine[-1])
+            toks.append(true[d] if rng.uniform() < 0.8 else int((true[d] + 1) % m.V))
+            spine.append(len(toks))
+            par.append(spine[-2])                        # a sibling holding the other choice
+            toks.append(true[d] if toks[-1] != true[d] else int((true[d] + 2) % m.V))
+        return par, toks
+
+    out, _ = m.generate_tree(prompt, 60, drafter, stop_ids=(stop,))
+    assert out == ref
+    out, _ = m.generate_tree(prompt, 41, drafter, stop_ids=())
+    assert out == free[:41]
