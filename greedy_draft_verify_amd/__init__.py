@@ -28,7 +28,7 @@ EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
             "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
-            "spec_sample_accept", "spec_greedy_accept_stop", "spec_kpolicy_init", "spec_kpolicy_accept_prob",
+            "spec_sample_accept", "spec_greedy_accept_stop", "spec_truncate_stop", "spec_kpolicy_init", "spec_kpolicy_accept_prob",
             "spec_kpolicy_verify_cost", "spec_kpolicy_expected_tokens", "spec_kpolicy_choose",
             "spec_kpolicy_update", "spec_kpolicy_update_batch"]
 
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp, vp, vp, vp, vp, vp]
         L.spec_greedy_accept_stop.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp]
+        L.spec_truncate_stop.argtypes = [i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         pp = ctypes.POINTER(_KPolicyStruct)
         dbl, dp = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
         L.spec_kpolicy_init.argtypes = [pp, i32, i32, dbl, dbl, dbl, dp, dp, i32]
@@ -105,7 +106,7 @@ def lib() -> ctypes.CDLL:
         L.spec_kpolicy_update.restype = None
         L.spec_kpolicy_update_batch.argtypes = [pp, vp, vp, i32]
         L.spec_kpolicy_update_batch.restype = ctypes.c_int
-        for name in ("spec_greedy_accept_stop", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
+        for name in ("spec_greedy_accept_stop", "spec_truncate_stop", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
                      "spec_greedy_accept",
                      "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
                      "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"):
@@ -449,6 +450,34 @@ def spec_greedy_accept_stop(argmax, drafts, k, d2t, V, stop_ids, remaining, pos_
                                        _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
                                        _ptr(done), _ptr(seq_status), _stream(stream))
     _check(rc, "spec_greedy_accept_stop")
+
+
+def spec_truncate_stop(stop_ids, remaining, pos_in, pos_out, accept_len, n_emit, emit, next_tok, done, seq_status,
+                       path=None, stream=None):
+    """The stop-token / limit rule applied in place to an acceptance walk's outputs
+    (emit [B, kmax+1], the [B] scalars, and the tree walk's path [B, kmax] or None);
+    stop_ids [n_stop] int32 device tensor (n_stop <= 16), remaining [B] or None; done [B] out."""
+    for t, n in ((stop_ids, "stop_ids"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (emit, "emit"), (next_tok, "next_tok"), (done, "done"),
+                 (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    _want(emit, torch.int32, "emit", 2)
+    B, kmax = emit.shape[0], emit.shape[1] - 1
+    for t, n in ((pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"), (n_emit, "n_emit"),
+                 (next_tok, "next_tok"), (done, "done"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    if remaining is not None:
+        _want(remaining, torch.int32, "remaining", 1)
+        _shape(remaining, (B,), "remaining")
+    if path is not None:
+        _want(path, torch.int32, "path", 2)
+        _shape(path, (B, kmax), "path")
+    n_stop = stop_ids.numel()
+    rc = lib().spec_truncate_stop(kmax, B, _ptr(stop_ids) if n_stop else None, n_stop, _ptr(remaining), _ptr(pos_in),
+                                  _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
+                                  _ptr(path) if path is not None and path.numel() else None, _ptr(done),
+                                  _ptr(seq_status), _stream(stream))
+    _check(rc, "spec_truncate_stop")
 
 
 class KPolicy:

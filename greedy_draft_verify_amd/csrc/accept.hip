@@ -183,6 +183,84 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     }
 }
 
+// The stop rule on its own, applied in place to the outputs of any acceptance walk
+// (greedy chain, tree, sampling): one wave per sequence, a ballot over the emitted
+// tokens finds the first stop token, the tail of emit (and of the tree path) is
+// cleared, and the per-sequence scalars are rewritten. No row offsets are needed,
+// so the grid simply covers B with 4 waves per workgroup.
+constexpr int kTruncThreads = 256;
+
+__global__ __launch_bounds__(kTruncThreads) void truncate_kernel(
+    int B, int kmax, const int32_t* __restrict__ stop_ids, int n_stop, const int32_t* __restrict__ remaining,
+    const int32_t* __restrict__ pos_in, int32_t* __restrict__ pos_out, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ n_emit, int32_t* __restrict__ emit, int32_t* __restrict__ next_tok,
+    int32_t* __restrict__ path, int32_t* __restrict__ done, int32_t* __restrict__ status) {
+    const int lane = threadIdx.x % kWave;
+    const int s = blockIdx.x * (kTruncThreads / kWave) + threadIdx.x / kWave;
+    if (s >= B) return;
+    const int st = status[s];
+    const int a_in = accept_len[s];
+    int c = n_emit[s];
+    int32_t* e = emit + (size_t)s * (kmax + 1);
+    int32_t* ph = path ? path + (size_t)s * kmax : nullptr;
+    int flag = 0;
+    if (st == 0) {
+        if (c < 1 || c > kmax + 1 || a_in < 0 || a_in > c)
+            flag = SPEC_STATUS_BAD_ROWS;
+        else if (remaining && remaining[s] < 1)
+            flag = SPEC_STATUS_BAD_LIMIT;
+    }
+    if (st || flag) {
+        if (flag) {
+            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
+            if (ph)
+                for (int j = lane; j < kmax; j += kWave) ph[j] = -1;
+        }
+        if (lane == 0) {
+            if (flag) {
+                status[s] = flag;
+                accept_len[s] = -1;
+                n_emit[s] = 0;
+                next_tok[s] = -1;
+                pos_out[s] = pos_in[s];
+            }
+            done[s] = 0;
+        }
+        return;
+    }
+    // first stop token among emit[0 .. c), 64 tokens at a time
+    const int n = c;
+    for (int base = 0; base < n; base += kWave) {
+        const int j = base + lane;
+        bool is_stop = false;
+        if (j < n) {
+            const int t = e[j];
+            for (int q = 0; q < n_stop; ++q) is_stop |= t == stop_ids[q];
+        }
+        const unsigned long long mm = __ballot(is_stop);
+        if (mm) {
+            c = base + (int)__builtin_ctzll(mm) + 1;
+            break;
+        }
+    }
+    const bool at_lim = remaining && c >= remaining[s];
+    if (at_lim) c = remaining[s];
+    const int last = e[c - 1];
+    const int a = a_in < c ? a_in : c;
+    for (int j = c + lane; j <= kmax; j += kWave) e[j] = -1;
+    if (ph)
+        for (int j = a + lane; j < kmax; j += kWave) ph[j] = -1;
+    if (lane == 0) {
+        bool is_stop = false;
+        for (int q = 0; q < n_stop; ++q) is_stop |= last == stop_ids[q];
+        accept_len[s] = a;
+        n_emit[s] = c;
+        next_tok[s] = last;
+        pos_out[s] = pos_in[s] + c;
+        done[s] = is_stop || at_lim;
+    }
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -232,6 +310,25 @@ int spec_greedy_accept_stop(const int32_t* argmax, const int32_t* drafts, int32_
                        drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
                        n_emit, emit, next_tok, seq_status, stop_ids, n_stop, remaining, done);
     SV_LAUNCH_CHECK("spec_greedy_accept_stop");
+    return SPEC_OK;
+}
+
+int spec_truncate_stop(int32_t kmax, int32_t B, const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
+                       const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit, int32_t* emit,
+                       int32_t* next_tok, int32_t* path, int32_t* done, int32_t* seq_status, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (B < 1) return fail(SPEC_EINVAL, "spec_truncate_stop: B=%d < 1", B);
+    if (kmax < 0 || kmax > 1024) return fail(SPEC_EINVAL, "spec_truncate_stop: kmax=%d outside 0..1024", kmax);
+    if (n_stop < 0 || n_stop > kMaxStop) return fail(SPEC_EINVAL, "spec_truncate_stop: n_stop=%d outside 0..%d", n_stop, kMaxStop);
+    if (!pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !done || !seq_status ||
+        (n_stop > 0 && !stop_ids))
+        return fail(SPEC_EINVAL, "spec_truncate_stop: null required pointer");
+    constexpr int per_wg = kTruncThreads / kWave;
+    hipLaunchKernelGGL(truncate_kernel, dim3((B + per_wg - 1) / per_wg), dim3(kTruncThreads), 0, (hipStream_t)stream,
+                       B, kmax, stop_ids, n_stop, remaining, pos_in, pos_out, accept_len, n_emit, emit, next_tok,
+                       path, done, seq_status);
+    SV_LAUNCH_CHECK("spec_truncate_stop");
     return SPEC_OK;
 }
 

@@ -22,8 +22,9 @@
  *   spec_lm_head_sample        lm_head with softmax statistics and two draws fused in
  *   spec_sample_accept         the speculative-sampling chain walk
  *
- * and the host-side pieces around them: spec_greedy_accept_stop (stop tokens and a
- * generation limit) and the adaptive draft-depth policy spec_kpolicy_*.
+ * and the pieces around them: spec_greedy_accept_stop and spec_truncate_stop (stop
+ * tokens and a generation limit) and the host-side adaptive draft-depth policy
+ * spec_kpolicy_*.
  *
  * The method follows the page "span-02 engine/crates/model/src/spec.rs"
  * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
@@ -237,6 +238,32 @@ int spec_greedy_accept_stop(const int32_t* argmax, const int32_t* drafts, int32_
                             const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
                             const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
                             int32_t* emit, int32_t* next_tok, int32_t* done, int32_t* seq_status, void* stream);
+
+/* spec_truncate_stop — the same stop-token and limit rule, applied in place to the
+ * outputs of any acceptance walk: spec_greedy_accept, spec_tree_accept (with its
+ * path) or spec_sample_accept (oxinfer step and DSSD _commit as above; a tree or a
+ * sampled round commits its emitted tokens in the same way).
+ * In/out [B] int32: pos_out, accept_len, n_emit, next_tok, seq_status;
+ * emit [B][kmax+1] and path [B][kmax] (NULL for chain walks) int32, in/out; pos_in
+ * [B] the walk's input positions; done [B] int32 output. For each s with
+ * seq_status[s] == 0 on entry, with out = emit[s][0 .. n_emit):
+ *   c = the length of out up to and including its first token in stop_ids, then
+ *       min(c, remaining[s]);
+ *   n_emit = c, emit = out[0..c) (-1 after), accept_len = min(accept_len, c),
+ *   path keeps its first accept_len entries (-1 after), next_tok = out[c - 1],
+ *   pos_out = pos_in + c, done = 1 iff out[c - 1] is a stop token or
+ *   c == remaining[s].
+ * A tree round then calls spec_kv_compact with the truncated path and accept_len,
+ * so that only committed nodes move. remaining may be NULL (no limit);
+ * remaining[s] < 1 sets SPEC_STATUS_BAD_LIMIT, and n_emit outside 1 .. kmax + 1 or
+ * accept_len outside 0 .. n_emit sets SPEC_STATUS_BAD_ROWS; such a sequence gets
+ * the flagged outputs of its walk (accept_len -1, n_emit 0, next_tok -1,
+ * pos_out = pos_in, emit and path all -1). Sequences flagged on entry are left as
+ * they are, with done = 0. Applying the call twice gives the result of once.
+ * Limits: B >= 1, 0 <= kmax <= 1024, 0 <= n_stop <= 16. */
+int spec_truncate_stop(int32_t kmax, int32_t B, const int32_t* stop_ids, int32_t n_stop, const int32_t* remaining,
+                       const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit, int32_t* emit,
+                       int32_t* next_tok, int32_t* path, int32_t* done, int32_t* seq_status, void* stream);
 
 /* ---------------------------------------------------------------------------
  * spec_delta_verify_rollback — Gated DeltaNet verify with per-token state

@@ -820,8 +820,10 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
  *   next_tok = out[c - 1], pos_out = pos_in + c,
  *   path (tree walks; NULL otherwise) keeps its first accept_len entries (-1 after),
  *   done = 1 iff out[c - 1] is a stop token or c == remaining[s].
- * remaining == NULL: no limit; remaining[s] < 1 sets ORC_BAD_LIMIT and gives the
- * outputs of a flagged sequence. Sequences flagged on entry get done = 0. */
+ * remaining == NULL: no limit; remaining[s] < 1 sets ORC_BAD_LIMIT, and walk outputs
+ * that are no committed round (n_emit outside 1 .. kmax + 1, accept_len outside
+ * 0 .. n_emit) set ORC_BAD_ROWS; both give the outputs of a flagged sequence.
+ * Sequences flagged on entry are left as they are, with done = 0. */
 void oracle_truncate_stop(int32_t* emit, int32_t* n_emit, int32_t* accept_len, const int32_t* pos_in,
                           int32_t* pos_out, int32_t* next_tok, int32_t* path, int32_t kmax, const int32_t* stop_ids,
                           int32_t n_stop, const int32_t* remaining, int32_t* done, int32_t* st, int32_t B) {
@@ -829,8 +831,15 @@ void oracle_truncate_stop(int32_t* emit, int32_t* n_emit, int32_t* accept_len, c
         done[s] = 0;
         int32_t* e = emit + (int64_t)s * (kmax + 1);
         int32_t* ph = path ? path + (int64_t)s * kmax : NULL;
-        if (st[s] == 0 && remaining && remaining[s] < 1) {
-            st[s] = ORC_BAD_LIMIT;
+        /* a walk's output that is not a committed round (no token, more than kmax + 1,
+         * or an accepted count outside 0 .. n_emit) has no truncation */
+        int flag = 0;
+        if (st[s] == 0 && (n_emit[s] < 1 || n_emit[s] > kmax + 1 || accept_len[s] < 0 || accept_len[s] > n_emit[s]))
+            flag = ORC_BAD_ROWS;
+        else if (st[s] == 0 && remaining && remaining[s] < 1)
+            flag = ORC_BAD_LIMIT;
+        if (flag) {
+            st[s] = flag;
             for (int j = 0; j <= kmax; ++j) e[j] = -1;
             if (ph)
                 for (int j = 0; j < kmax; ++j) ph[j] = -1;

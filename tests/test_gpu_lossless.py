@@ -101,9 +101,11 @@ class GpuToy:
             pos += 1
         return out
 
-    def generate_tree(self, prompt, n, drafter, kmax):
+    def generate_tree(self, prompt, n, drafter, kmax, stop_ids=None):
         """Tree drafts: ``drafter(out)`` gives (parents, tokens) of the nodes below the root in
-        creation order; one tree verify, the acceptance walk, compaction, pos += a + 1."""
+        creation order; one tree verify, the acceptance walk, compaction, pos += a + 1.
+        With stop_ids, the walk's outputs are truncated on the device (stop tokens and the
+        tokens still allowed) before compaction, and generation ends when a round says so."""
         gdv, dev = self.gdv, self.dev
         self.reset()
         for i, t in enumerate(prompt[:-1]):
@@ -124,6 +126,10 @@ class GpuToy:
             pos_t = i32([pos])
             gdv.spec_tree_accept(i32(g), i32([drafts]), i32([k]), i32([parent]), None, V, pos_t, pos_out, acc, ne,
                                  emit, nt, path, st)
+            done = torch.zeros(1, dtype=torch.int32, device=dev)
+            if stop_ids is not None:
+                gdv.spec_truncate_stop(i32(list(stop_ids)), i32([n - len(out)]), pos_t, pos_out, acc, ne, emit, nt,
+                                       done, st, path=path)
             gdv.spec_kv_compact(self.kp, self.vp, self.pt, pos_t, path, acc, st)
             torch.cuda.synchronize()
             assert st.item() == 0
@@ -131,6 +137,8 @@ class GpuToy:
             out.extend(emit.cpu().numpy()[0, :m].tolist())
             hist.append(acc.item())
             pos, x0 = pos_out.item(), nt.item()
+            if done.item():
+                break
         return out[:n], hist
 
     def generate_spec(self, prompt, n, drafter, k):
@@ -234,3 +242,32 @@ def test_gpu_tree_stream_equals_one_row_stream(toy_tree, shape):
     else:
         assert n_same == N_NEW or gaps[n_same] < 5e-2, (n_same, gaps[n_same])
     assert max(hist) >= (1 if shape == "star" else 3)
+
+
+@pytest.mark.parametrize("limit", [False, True])
+def test_gpu_tree_stream_with_stop_ends_where_one_row_decoding_ends(toy_tree, limit):
+    """Spine-shaped trees (exact bytes) with a stop token, truncated on the device:
+    the stream is the one-row stream up to and including the stop token's first
+    appearance; with only a limit, it is the first n tokens exactly."""
+    m, prompt, ref, _ = toy_tree
+    rng = np.random.default_rng(13)
+
+    def drafter(out):
+        true = ref[len(out):len(out) + 8]
+        true = true + [0] * (8 - len(true))
+        par, toks = [], []
+        for d in range(6):
+            par.append(d)
+            toks.append(true[d] if rng.uniform() < 0.8 else int((true[d] + 1 + rng.integers(0, V - 1)) % V))
+        return par, toks
+
+    if limit:
+        n = N_NEW - 7
+        out, _ = m.generate_tree(prompt, n, drafter, kmax=15, stop_ids=())
+        assert out == ref[:n]
+    else:
+        stop = ref[N_NEW // 2]
+        want = ref[:ref.index(stop) + 1]
+        out, _ = m.generate_tree(prompt, N_NEW, drafter, kmax=15, stop_ids=(stop,))
+        assert out == want
+

@@ -154,3 +154,52 @@ def test_toy_tree_with_stop_ends_where_one_row_decoding_ends():
     assert out == ref
     out, _ = m.generate_tree(prompt, 41, drafter, stop_ids=())
     assert out == free[:41]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_truncation_is_idempotent_and_matches_the_combined_greedy_call(seed):
+    """Truncating a greedy round equals the fused stop call, and truncating the result
+    again changes nothing (its last token is already the first stop, and its length is
+    already within the limit)."""
+    rng = np.random.default_rng(seed)
+    B, kmax, V = 12, 6, 40
+    k = rng.integers(0, kmax + 1, B).astype(np.int32)
+    R = int((k + 1).sum())
+    g = rng.integers(0, V, R).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(k + 1)[:-1]])
+    drafts = np.zeros((B, kmax), np.int32)
+    for s in range(B):
+        a = rng.integers(0, k[s] + 1)
+        drafts[s, :k[s]] = rng.integers(0, V, k[s])
+        drafts[s, :a] = g[off[s]:off[s] + a]
+    pos = rng.integers(0, 100, B).astype(np.int32)
+    stops = list(rng.choice(g, 3, replace=False))
+    rem = rng.integers(1, kmax + 3, B).astype(np.int32)
+    base = oracle.greedy_accept(g, drafts, kmax, k, None, 0, V, B, R, pos)
+    t1 = oracle.truncate_stop(base, kmax, stops, rem, pos)
+    fused = oracle.greedy_accept_stop(g, drafts, kmax, k, None, 0, V, B, R, stops, rem, pos)
+    for key in ("emit", "n_emit", "accept_len", "next_tok", "pos_out", "done", "status"):
+        assert np.array_equal(t1[key], fused[key]), key
+    t2 = oracle.truncate_stop(t1, kmax, stops, rem, pos)
+    for key in ("emit", "n_emit", "accept_len", "next_tok", "pos_out", "done", "status"):
+        assert np.array_equal(t1[key], t2[key]), key
+
+
+def test_truncation_flags_outputs_that_are_no_round():
+    """n_emit outside 1..kmax+1 or accept_len outside 0..n_emit: BAD_ROWS, flagged
+    outputs; a sequence flagged on entry is left untouched with done 0."""
+    kmax = 3
+    res = {
+        "emit": np.array([[5, -1, -1, -1], [5, 6, -1, -1], [5, 6, 7, 8], [-1, -1, -1, -1]], np.int32),
+        "n_emit": np.array([0, 2, 4, 0], np.int32),
+        "accept_len": np.array([0, 3, 3, -1], np.int32),
+        "next_tok": np.array([5, 6, 8, -1], np.int32),
+        "pos_out": np.array([10, 12, 14, 10], np.int32),
+        "status": np.array([0, 0, 0, oracle.BAD_TOKEN], np.int32),
+    }
+    pos = np.array([10, 10, 10, 10], np.int32)
+    t = oracle.truncate_stop(res, kmax, [99], None, pos)
+    assert list(t["status"]) == [oracle.BAD_ROWS, oracle.BAD_ROWS, 0, oracle.BAD_TOKEN]
+    assert list(t["n_emit"]) == [0, 0, 4, 0] and list(t["pos_out"]) == [10, 10, 14, 10]
+    assert list(t["done"]) == [0, 0, 0, 0]
+    assert (t["emit"][:2] == -1).all() and list(t["accept_len"][:2]) == [-1, -1]
