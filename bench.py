@@ -472,7 +472,10 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the DeltaNet leg and the lm_head row sweep (reported beside the step)")
+                    help="skip every leg reported beside the step")
+    ap.add_argument("--extras", default="sweep,delta,tree,sampling,adaptive",
+                    help="comma list of the legs reported beside the step: sweep (lm_head rows), delta "
+                         "(DeltaNet), tree, sampling, adaptive (verify cost by rows + draft-depth policy)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed loop, copy this many MiB 3 times (a plain copy kernel of known "
                          "size, used to scale hardware byte counters)")
@@ -574,32 +577,42 @@ def main():
         f"accept-length histogram {hist}")
 
     extras = {}
-    if not args.no_extras:
-        extras["lm_head_row_sweep"] = lm_head_sweep(x, step.w_packed, dev, reps=10)
-        extras["delta_roofline"] = delta_leg(dev, reps=20)
-        if wl.H == 4096 and wl.V == 151936:
+    legs = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    unknown = legs - {"sweep", "delta", "tree", "sampling", "adaptive"}
+    if unknown:
+        raise SystemExit(f"bench.py: unknown --extras legs {sorted(unknown)}")
+    if legs:
+        if "sweep" in legs:
+            extras["lm_head_row_sweep"] = lm_head_sweep(x, step.w_packed, dev, reps=10)
+        if "delta" in legs:
+            extras["delta_roofline"] = delta_leg(dev, reps=20)
+        if "tree" in legs and wl.H == 4096 and wl.V == 151936:
             extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
-        extras["sampling_verify"] = sampling_leg(step, dev, reps=20)
-        if wl.name == "b16k4":
+        if "sampling" in legs:
+            extras["sampling_verify"] = sampling_leg(step, dev, reps=20)
+        if "adaptive" in legs and wl.name == "b16k4":
             extras["adaptive_k"] = kpolicy_leg(step, dev, reps=10, seed=args.seed)
-        sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
-        dl = extras["delta_roofline"]
-        log(f"[bench] lm_head sweep: {sw}")
-        ist = dl["input_stash"]
-        log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
-            f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
-            f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
-            f"{ist['rescan_us']:.1f} us")
+        if "lm_head_row_sweep" in extras:
+            sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
+            log(f"[bench] lm_head sweep: {sw}")
+        if "delta_roofline" in extras:
+            dl = extras["delta_roofline"]
+            ist = dl["input_stash"]
+            log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
+                f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
+                f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
+                f"{ist['rescan_us']:.1f} us")
         if "adaptive_k" in extras:
             ak = extras["adaptive_k"]
             tbl = ", ".join(f"{r}: {t:.0f}" for r, t in ak["verify_us_by_rows"])
             ch = ", ".join(f"p={c['accept_p']}/d={c['draft_us']:.0f}->k={c['k']}" for c in ak["choices"])
             log(f"[bench] verify us by rows (B=16): {tbl}; policy: {ch}")
-        sv_ = extras["sampling_verify"]
-        log(f"[bench] sampling step {sv_['step_us']:.1f} us ({sv_['rows_per_s']:.0f} rows/s, "
-            f"{sv_['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample {sv_['kernel_us']['spec_lm_head_sample']:.1f} us "
-            f"({100 * sv_['lm_head_sample']['frac']:.0f}% HBM), accept {sv_['kernel_us']['spec_sample_accept']:.1f} us; "
-            f"accept lengths {sv_['accept_len_hist']}")
+        sv_ = extras.get("sampling_verify")
+        if sv_:
+            log(f"[bench] sampling step {sv_['step_us']:.1f} us ({sv_['rows_per_s']:.0f} rows/s, "
+                f"{sv_['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample {sv_['kernel_us']['spec_lm_head_sample']:.1f} us "
+                f"({100 * sv_['lm_head_sample']['frac']:.0f}% HBM), accept {sv_['kernel_us']['spec_sample_accept']:.1f} us; "
+                f"accept lengths {sv_['accept_len_hist']}")
         if "tree_verify" in extras:
             tv = extras["tree_verify"]
             ku = tv["kernel_us"]
