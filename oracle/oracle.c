@@ -12,7 +12,7 @@
  * widened exactly. Loops run in the order of the definitions; OpenMP only
  * spreads independent units (rows, heads, vocabulary entries) over cores.
  *
- * Sources (the web pages this build follows):
+ * Sources (the web pages these definitions follow):
  *  - "span-02 engine/crates/model/src/spec.rs", module doc: one verify forward
  *    of B(k+1) rows, KV appended in place at pos..pos+k, greedy acceptance,
  *    rollback = pos advances by the accepted tokens, kv_hi = position;
