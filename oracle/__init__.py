@@ -293,6 +293,29 @@ def sample_accept(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, q_tok, q_prob, r
     return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st)
 
 
+def sample_accept_dense(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, logits, T, q, row_ctr, seed, pos_in):
+    """Speculative sampling with a dense draft distribution q [R, V] (fp32) over the target
+    vocabulary; logits fp64 [R, V]. Returns the greedy_accept dict plus margin [B] (how
+    decided the acceptance tests are, in log(u) vs log(p/q)) and gap [B] (how decided the
+    deciding draw is)."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    q = np.ascontiguousarray(q, np.float32)
+    assert logits.shape == (R, V) and q.shape == (R, V)
+    pos_out, acc, ne, nt, st = (np.zeros(B, np.int32) for _ in range(5))
+    emit = np.zeros((B, kmax + 1), np.int32)
+    margin = np.zeros(B, np.float64)
+    gap = np.zeros(B, np.float64)
+    dr = _i32(drafts).reshape(B, max(kmax, 0)) if kmax > 0 else np.zeros((B, 1), np.int32)
+    d2 = None if d2t is None else _i32(d2t)
+    lib().oracle_sample_accept_dense(_p(dr), ctypes.c_int32(kmax), _p(_i32(k)), _p(d2),
+                                     ctypes.c_int32(n_draft_vocab), ctypes.c_int32(V), ctypes.c_int32(B),
+                                     ctypes.c_int32(R), _p(logits), ctypes.c_double(T), _p(q), _p(_i32(row_ctr)),
+                                     ctypes.c_uint64(seed), _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit),
+                                     _p(nt), _p(st), _p(margin), _p(gap))
+    return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st, margin=margin,
+                gap=gap)
+
+
 def greedy_accept_stop(g, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, stop_ids, remaining, pos_in):
     """Greedy acceptance truncated at the first stop token and at remaining[s] tokens
     (remaining None: no limit). Returns the greedy_accept dict plus done [B]."""

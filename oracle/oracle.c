@@ -809,6 +809,138 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
     }
 }
 
+/* Speculative sampling with a dense draft distribution (DSSD _sample_verify with the
+ * draft head's full distribution): q [R][V] holds q_r(v) for every target entry.
+ * With z = logit / T and p_r = softmax(z_r) (fp64), for j = 0 .. k_s - 1, row r =
+ * off_s + j, draft x (mapped through d2t when given):
+ *   q_r(x) <= 0, or x out of range: ORC_BAD_TOKEN (a draft has positive mass under
+ *   the distribution it was drawn from);
+ *   accept x iff u_r < p_r(x) / q_r(x);
+ *   else the token is a draw from norm(max(p_r - q_r, 0)): the first v maximising
+ *   log(p_r(v) - q_r(v)) + G_r(v) over the v with p_r(v) > q_r(v) (the row's
+ *   Gumbel noise, as for the draw from p); no such v: the row's draw from p.
+ * All kept: the draw from p of the bonus row (first v maximising z + G).
+ * Outputs as oracle_sample_accept; margin[s] = the smallest |log u_r - log(p_r(x) /
+ * q_r(x))| over the drafts tested (how decided the walk is; +inf if none), gap[s] =
+ * best - runner-up of the deciding draw (how decided the token is). */
+void oracle_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
+                                int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const double* logits,
+                                double T, const float* q, const int32_t* row_ctr, uint64_t seed,
+                                const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                                int32_t* emit, int32_t* next_tok, int32_t* st, double* margin, double* gap) {
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    int64_t total = 0;
+    int packing_ok = 1;
+    for (int s = 0; s < B; ++s) {
+        total += (int64_t)k[s] + 1;
+        if (k[s] < 0) packing_ok = 0;
+    }
+    if (total != R) packing_ok = 0;
+    int64_t off = 0;
+    for (int s = 0; s < B; ++s) {
+        const int ks = k[s];
+        int bits = 0;
+        if (!packing_ok || ks > kmax) bits |= ORC_BAD_ROWS;
+        if (pos_in[s] < 0) bits |= ORC_BAD_POS;
+        int32_t* e = emit + (int64_t)s * (kmax + 1);
+        for (int j = 0; j <= kmax; ++j) e[j] = -1;
+        margin[s] = INFINITY;
+        gap[s] = INFINITY;
+        if (!bits)
+            for (int j = 0; j < ks; ++j) {
+                const int32_t x = drafts[(int64_t)s * kmax + j];
+                int32_t t = x;
+                if (d2t) {
+                    if (x < 0 || x >= n_draft_vocab || d2t[x] < 0 || d2t[x] >= V) {
+                        bits |= ORC_BAD_TOKEN;
+                        continue;
+                    }
+                    t = d2t[x];
+                } else if (x < 0 || x >= V) {
+                    bits |= ORC_BAD_TOKEN;
+                    continue;
+                }
+                if (!(q[(off + j) * (int64_t)V + t] > 0.f)) bits |= ORC_BAD_TOKEN;
+            }
+        if (bits) {
+            st[s] = bits;
+            accept_len[s] = -1;
+            n_emit[s] = 0;
+            next_tok[s] = -1;
+            pos_out[s] = pos_in[s];
+            off += (int64_t)ks + 1;
+            continue;
+        }
+        int a = 0, tok = -1;
+        for (; a <= ks; ++a) {
+            const int64_t r = off + a;
+            const double* l = logits + r * V;
+            double zmax = -INFINITY;
+            for (int v = 0; v < V; ++v)
+                if (l[v] / T > zmax) zmax = l[v] / T;
+            double sum = 0.0;
+            for (int v = 0; v < V; ++v) sum += exp(l[v] / T - zmax);
+            const double L = zmax + log(sum);
+            const int32_t* rc = row_ctr + 2 * r;
+            int rejected = 0;
+            if (a < ks) {
+                const int32_t x = drafts[(int64_t)s * kmax + a];
+                const int32_t t = d2t ? d2t[x] : x;
+                const double px = exp(l[t] / T - L), qx = (double)q[r * V + t];
+                const double u = oracle_accept_uniform(rc, seed);
+                const double m = fabs(log(u) - log(px / qx));
+                if (m < margin[s]) margin[s] = m;
+                if (u < px / qx) {
+                    e[a] = t;
+                    continue;
+                }
+                rejected = 1;
+            }
+            /* the deciding draw: residual of the rejected row, or p of the bonus row */
+            double b1 = -INFINITY, b2 = -INFINITY, p1 = -INFINITY, p2 = -INFINITY;
+            int i1 = -1, ip = -1;
+            for (int v = 0; v < V; ++v) {
+                const double g = row_gumbel((uint32_t)v, rc, key);
+                const double z = l[v] / T;
+                if (z + g > p1) {
+                    p2 = p1;
+                    p1 = z + g;
+                    ip = v;
+                } else if (z + g > p2) {
+                    p2 = z + g;
+                }
+                if (!rejected) continue;
+                const double w = exp(z - L) - (double)q[r * V + v];
+                if (w > 0.0) {
+                    const double sc = log(w) + g;
+                    if (sc > b1) {
+                        b2 = b1;
+                        b1 = sc;
+                        i1 = v;
+                    } else if (sc > b2) {
+                        b2 = sc;
+                    }
+                }
+            }
+            if (rejected && i1 >= 0) {
+                tok = i1;
+                gap[s] = b1 - b2;
+            } else {
+                tok = ip;
+                gap[s] = p1 - p2;
+            }
+            break;
+        }
+        e[a] = tok;
+        st[s] = 0;
+        accept_len[s] = a;
+        n_emit[s] = a + 1;
+        next_tok[s] = tok;
+        pos_out[s] = pos_in[s] + a + 1;
+        off += ks + 1;
+    }
+}
+
 /* ---------------------------------------------------------------------------
  * Stop tokens and a generation limit, applied to the outputs of an acceptance walk
  * (oxinfer step: the committed tokens end after the first stop token and the session
