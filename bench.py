@@ -331,6 +331,74 @@ def sampling_leg(step: "VerifyStep", dev, reps: int, temperature: float = 0.1):
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_b / us[1] / 1e3 / HBM_PEAK_GBS}}
 
 
+def sampling_dense_leg(step: "VerifyStep", dev, reps: int, temperature: float = 0.1):
+    """Speculative sampling with dense draft distributions (DSSD fast.py _sample_verify
+    with the draft head's whole q): spec_verify_attn -> spec_lm_head_sample_dense (the
+    pass also writes z = logit / T of every entry, R x V fp32) -> spec_sample_accept_dense
+    (the walk, then the residual of each rejected row drawn over the whole vocabulary).
+    Setup, untimed: z from one pass, q = softmax(0.8 z + N(0, 1)) per row (a draft
+    distribution near the target), each draft drawn from its row's q."""
+    x = step.x
+    wl = x.wl
+    B, R, kmax, V = step.B, step.R, wl.kmax, wl.V
+    row_ctr = i32(np.stack([np.concatenate([x.pos[s] + np.arange(x.k[s] + 1) for s in range(B)]),
+                            np.repeat(np.arange(B), x.k + 1)], 1), dev)
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    sp = torch.empty(R, dtype=torch.int32, device=dev)
+    z = torch.empty((R, V), dtype=torch.float32, device=dev)
+    ws = gdv.workspace(gdv.lm_head_sample_workspace_bytes(R, wl.H, V), dev, zero=True)
+    seed = 0xD5EED
+    lm = lambda: gdv.spec_lm_head_sample_dense(x.hidden, step.w_packed, V, temperature, row_ctr, seed, lse, sp, z,
+                                               workspace_buf=ws)
+    lm()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    q = torch.softmax(0.8 * z + torch.randn((R, V), generator=gen, device=dev), dim=1).contiguous()
+    draws = torch.multinomial(q, 1, generator=gen).to(torch.int32).view(-1).cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    drafts_np = np.zeros((B, kmax), np.int32)
+    for s in range(B):
+        drafts_np[s, :x.k[s]] = draws[off[s]:off[s] + x.k[s]]
+    drafts = i32(drafts_np, dev)
+    wsd = gdv.workspace(gdv.sample_accept_dense_workspace_bytes(B), dev)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, st = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+    accept = lambda: gdv.spec_sample_accept_dense(drafts, step.k, None, q, z, lse, sp, row_ctr, seed, step.pos,
+                                                  pos_out, acc, ne, emit, nt, st, workspace_buf=wsd)
+    fns = [step.attn, lm, accept]
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    assert (st.cpu() == 0).all()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for ev in evs:
+        ev[0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs])) * 1e3 for i in range(len(fns))]
+    acc_np = acc.cpu().numpy()
+    step_us = sum(us)
+    lm_b = lm_head_bytes(R, wl.H, V) + R * V * 4          # + z written
+    rejected = int((acc_np < x.k).sum())
+    acc_b = rejected * V * 8 + R * 12                    # rejected rows' z and q, per-draft lookups
+    return {"workload": f"{wl.name} inputs, temperature {temperature}, dense q = softmax(0.8 z + N(0,1))",
+            "step_us": step_us, "rows_per_s": R / (step_us / 1e6),
+            "emitted_tokens_per_s": float((acc_np + 1).sum()) / (step_us / 1e6),
+            "accept_len_hist": np.bincount(acc_np, minlength=kmax + 1).tolist(),
+            "rejected_sequences": rejected,
+            "kernel_us": {"spec_verify_attn": us[0], "spec_lm_head_sample_dense": us[1],
+                          "spec_sample_accept_dense": us[2]},
+            "lm_head_sample_dense": {"bound": "hbm", "algorithmic_bytes": lm_b, "achieved": lm_b / us[1] / 1e3,
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": lm_b / us[1] / 1e3 / HBM_PEAK_GBS},
+            "accept_dense_bytes": acc_b}
+
+
 def kpolicy_leg(step: "VerifyStep", dev, reps: int, seed: int = 0):
     """The verify cost against rows that drives the adaptive draft depth (span-02
     KPolicy): the b16k4 step (attention + lm_head + accept) at B = 16 with k = 0..7
@@ -590,6 +658,7 @@ def main():
             extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
         if "sampling" in legs:
             extras["sampling_verify"] = sampling_leg(step, dev, reps=20)
+            extras["sampling_dense_verify"] = sampling_dense_leg(step, dev, reps=20)
         if "adaptive" in legs and wl.name == "b16k4":
             extras["adaptive_k"] = kpolicy_leg(step, dev, reps=10, seed=args.seed)
         if "lm_head_row_sweep" in extras:
@@ -613,6 +682,14 @@ def main():
                 f"{sv_['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample {sv_['kernel_us']['spec_lm_head_sample']:.1f} us "
                 f"({100 * sv_['lm_head_sample']['frac']:.0f}% HBM), accept {sv_['kernel_us']['spec_sample_accept']:.1f} us; "
                 f"accept lengths {sv_['accept_len_hist']}")
+        sd = extras.get("sampling_dense_verify")
+        if sd:
+            log(f"[bench] dense sampling step {sd['step_us']:.1f} us ({sd['rows_per_s']:.0f} rows/s, "
+                f"{sd['emitted_tokens_per_s']:.0f} tokens/s): lm_head+sample+z "
+                f"{sd['kernel_us']['spec_lm_head_sample_dense']:.1f} us "
+                f"({100 * sd['lm_head_sample_dense']['frac']:.0f}% HBM), accept+residual "
+                f"{sd['kernel_us']['spec_sample_accept_dense']:.1f} us ({sd['rejected_sequences']} residual draws); "
+                f"accept lengths {sd['accept_len_hist']}")
         if "tree_verify" in extras:
             tv = extras["tree_verify"]
             ku = tv["kernel_us"]

@@ -28,7 +28,8 @@ EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
             "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
-            "spec_sample_accept", "spec_greedy_accept_stop", "spec_truncate_stop", "spec_kpolicy_init", "spec_kpolicy_accept_prob",
+            "spec_sample_accept", "spec_lm_head_sample_dense", "spec_sample_accept_dense_workspace_bytes",
+            "spec_sample_accept_dense", "spec_greedy_accept_stop", "spec_truncate_stop", "spec_kpolicy_init", "spec_kpolicy_accept_prob",
             "spec_kpolicy_verify_cost", "spec_kpolicy_expected_tokens", "spec_kpolicy_choose",
             "spec_kpolicy_update", "spec_kpolicy_update_batch"]
 
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp, vp, vp, vp, vp, vp]
         L.spec_greedy_accept_stop.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp]
+        L.spec_lm_head_sample_dense.argtypes = [vp, vp, i32, i32, i32, f32, vp, u64, vp, vp, vp, vp, sz, vp]
+        L.spec_sample_accept_dense_workspace_bytes.argtypes = [i32]
+        L.spec_sample_accept_dense_workspace_bytes.restype = sz
+        L.spec_sample_accept_dense.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, u64, vp, vp,
+                                               vp, vp, vp, vp, vp, vp, sz, vp]
         L.spec_truncate_stop.argtypes = [i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         pp = ctypes.POINTER(_KPolicyStruct)
         dbl, dp = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
@@ -106,7 +112,8 @@ def lib() -> ctypes.CDLL:
         L.spec_kpolicy_update.restype = None
         L.spec_kpolicy_update_batch.argtypes = [pp, vp, vp, i32]
         L.spec_kpolicy_update_batch.restype = ctypes.c_int
-        for name in ("spec_greedy_accept_stop", "spec_truncate_stop", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
+        for name in ("spec_greedy_accept_stop", "spec_truncate_stop", "spec_lm_head_sample_dense",
+                     "spec_sample_accept_dense", "spec_verify_attn", "spec_lm_head_argmax", "spec_lm_head_pack",
                      "spec_greedy_accept",
                      "spec_delta_verify_rollback", "spec_verify_attn_tree", "spec_tree_accept",
                      "spec_kv_compact", "spec_lm_head_sample", "spec_sample_accept"):
@@ -420,6 +427,71 @@ def spec_sample_accept(drafts, k, d2t, V, q_tok, q_prob, lse, z_supp, sample_p, 
                                   _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok), _ptr(seq_status),
                                   _stream(stream))
     _check(rc, "spec_sample_accept")
+
+
+def spec_lm_head_sample_dense(hidden, w_packed, V, temperature, row_ctr, seed, lse, sample_p, z, workspace_buf=None,
+                              stream=None):
+    """The sampling pass for dense draft distributions: lse [R] fp32, sample_p [R] int32 (a
+    draw from p of every row) and z [R,V] fp32 (logit / temperature of every entry). A
+    workspace_buf must be zero on first use (spec_lm_head_sample's size)."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
+    R, H = hidden.shape
+    for t, n in ((row_ctr, "row_ctr"), (sample_p, "sample_p")):
+        _want(t, torch.int32, n)
+    for t, n in ((lse, "lse"), (z, "z")):
+        _want(t, torch.float32, n)
+    _shape(row_ctr, (R, 2), "row_ctr")
+    _shape(z, (R, V), "z")
+    for t, n in ((lse, "lse"), (sample_p, "sample_p")):
+        _shape(t, (R,), n)
+    if w_packed.numel() * 2 != lm_head_packed_bytes(V, H):
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {lm_head_packed_bytes(V, H)}")
+    if workspace_buf is None:
+        workspace_buf = workspace(lm_head_sample_workspace_bytes(R, H, V), hidden.device, zero=True)
+    rc = lib().spec_lm_head_sample_dense(_ptr(hidden), _ptr(w_packed), R, H, V, float(temperature), _ptr(row_ctr),
+                                         int(seed) & ((1 << 64) - 1), _ptr(lse), _ptr(sample_p), _ptr(z),
+                                         _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
+    _check(rc, "spec_lm_head_sample_dense")
+
+
+def sample_accept_dense_workspace_bytes(B) -> int:
+    return lib().spec_sample_accept_dense_workspace_bytes(B)
+
+
+def spec_sample_accept_dense(drafts, k, d2t, q, z, lse, sample_p, row_ctr, seed, pos_in, pos_out, accept_len, n_emit,
+                             emit, next_tok, seq_status, workspace_buf=None, stream=None):
+    """The chain walk with a dense draft distribution q [R,V] fp32 over the target
+    vocabulary; z, lse and sample_p from spec_lm_head_sample_dense; outputs as
+    spec_greedy_accept."""
+    for t, n in ((drafts, "drafts"), (k, "k"), (sample_p, "sample_p"), (row_ctr, "row_ctr"), (pos_in, "pos_in"),
+                 (pos_out, "pos_out"), (accept_len, "accept_len"), (n_emit, "n_emit"), (emit, "emit"),
+                 (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    for t, n in ((q, "q"), (z, "z"), (lse, "lse")):
+        _want(t, torch.float32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    _want(q, torch.float32, "q", 2)
+    B, kmax = drafts.shape
+    R, V = q.shape
+    _shape(z, (R, V), "z")
+    _shape(row_ctr, (R, 2), "row_ctr")
+    _shape(emit, (B, kmax + 1), "emit")
+    for t, n in ((lse, "lse"), (sample_p, "sample_p")):
+        _shape(t, (R,), n)
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    if workspace_buf is None:
+        workspace_buf = workspace(sample_accept_dense_workspace_bytes(B), q.device)
+    rc = lib().spec_sample_accept_dense(_ptr(drafts) if drafts.numel() else None, kmax, _ptr(k), _ptr(d2t),
+                                        0 if d2t is None else d2t.shape[0], V, B, R, _ptr(q), _ptr(z), _ptr(lse),
+                                        _ptr(sample_p), _ptr(row_ctr), int(seed) & ((1 << 64) - 1), _ptr(pos_in),
+                                        _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
+                                        _ptr(seq_status), _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
+    _check(rc, "spec_sample_accept_dense")
 
 
 def spec_greedy_accept_stop(argmax, drafts, k, d2t, V, stop_ids, remaining, pos_in, pos_out, accept_len, n_emit,

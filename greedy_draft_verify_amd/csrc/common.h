@@ -82,6 +82,31 @@ __device__ __forceinline__ float row_gumbel(uint32_t v, uint32_t a, uint32_t b, 
     return gumbel(sel == 0 ? w.x : sel == 1 ? w.y : sel == 2 ? w.z : w.w);
 }
 
+// ---- (value, index) maxima merged across workgroups ----------------------------
+// The order: larger value first, then smaller index.
+struct Best {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// (value, index) as one 64-bit key whose unsigned order is the order above: the high
+// half maps the fp32 value monotonically (-0 taken as +0, like the comparison; a
+// workgroup's best is never NaN), the low half is ~index. Key 0 is below every key.
+__device__ __forceinline__ unsigned long long pack_best(Best b) {
+    const uint32_t u = __float_as_uint(b.v == 0.f ? 0.f : b.v);
+    const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (uint32_t)~(uint32_t)b.i;
+}
+
+__device__ __forceinline__ float unpack_value(unsigned long long key) {
+    const uint32_t hi = (uint32_t)(key >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+
 // ---- ragged row packing ------------------------------------------------------
 // Exclusive prefix sums of (k_s + 1) over s (the packed row offsets) for B <= the
 // size of s_off, by a block of NT threads (each a contiguous segment of sequences,

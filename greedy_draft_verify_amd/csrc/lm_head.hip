@@ -71,38 +71,16 @@ __global__ __launch_bounds__(256) void lm_head_pack_kernel(const u16* __restrict
     }
 }
 
-struct Best {
-    float v;
-    int i;
-};
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
-// (value, index) as one 64-bit key whose unsigned order is the order above: the high
-// half maps the fp32 value monotonically (-0 taken as +0, like the comparison; a
-// workgroup's best is never NaN), the low half is ~index. Key 0 is below every key.
-__device__ __forceinline__ unsigned long long pack_best(Best b) {
-    const uint32_t u = __float_as_uint(b.v == 0.f ? 0.f : b.v);
-    const uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)hi << 32) | (uint32_t)~(uint32_t)b.i;
-}
-
-__device__ __forceinline__ float unpack_value(unsigned long long key) {
-    const uint32_t hi = (uint32_t)(key >> 32);
-    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
-}
-
 // Sampling epilogue (speculative-sampling verify): per row, the workgroup's
 // softmax partial (max and sum of exp of z = logit / T over its 128 entries), the
-// z of the row's draft-support tokens, and the best z + Gumbel noise over the
-// entries outside that support.
+// z of the row's draft-support tokens, the best z + Gumbel noise over the entries
+// outside that support, and (dense drafts) every entry's z.
 struct SampleArgs {
     const int32_t* q_tok;     // [R][NQ] draft support per row (-1: unused)
     const int32_t* row_ctr;   // [R][2] Philox counter words of the row
     float2* part;             // [R][n_vt] (max, sum of exp) per vocabulary group
     float* z_supp;            // [R][NQ]
+    float* z_out;             // [R][V] z of every entry, or null
     float inv_t;
     int NQ;
     uint32_t key0, key1;
@@ -160,6 +138,7 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
                 const int v = (tile0 + nt) * 16 + l16;
                 if (v >= V) continue;
                 const float z = acc[mt][nt][i] * sa.inv_t;
+                if (sa.z_out && r < R) sa.z_out[(size_t)r * V + v] = z;
                 ms_merge(m, sm, z, 1.f);
                 const int loc = v - vt * kLmVocabPerWg;
                 const uint32_t word = loc < 32 ? sup.x : loc < 64 ? sup.y : loc < 96 ? sup.z : sup.w;
@@ -490,31 +469,36 @@ size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     return 256 + (size_t)R * sizeof(unsigned long long) + (size_t)R * sv::n_vtiles(V) * sizeof(float2);
 }
 
-int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
-                        float temperature, const int32_t* q_tok, const float* q_prob, int32_t NQ,
-                        const int32_t* row_ctr, uint64_t seed, float* lse, float* z_supp, int32_t* sample_p,
-                        int32_t* sample_res, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace sv {
+
+static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R,
+                               int32_t H, int32_t V, float temperature, const int32_t* q_tok, const float* q_prob,
+                               int32_t NQ, const int32_t* row_ctr, uint64_t seed, float* lse, float* z_supp,
+                               int32_t* sample_p, int32_t* sample_res, float* z_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     using namespace sv;
     last_error().clear();
-    if (R < 1) return fail(SPEC_EINVAL, "spec_lm_head_sample: R=%d < 1", R);
-    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "spec_lm_head_sample: H=%d not a positive multiple of %d", H, kLmHAlign);
-    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_sample: V=%d", V);
-    if (!(temperature > 0.f) || !(temperature < INFINITY)) return fail(SPEC_EINVAL, "spec_lm_head_sample: temperature must be finite and > 0");
-    if (NQ < 0 || NQ > 8) return fail(SPEC_EINVAL, "spec_lm_head_sample: NQ=%d outside 0..8", NQ);
+    if (R < 1) return fail(SPEC_EINVAL, "%s: R=%d < 1", name, R);
+    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "%s: H=%d not a positive multiple of %d", name, H, kLmHAlign);
+    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "%s: V=%d", name, V);
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return fail(SPEC_EINVAL, "%s: temperature must be finite and > 0", name);
+    if (NQ < 0 || NQ > 8) return fail(SPEC_EINVAL, "%s: NQ=%d outside 0..8", name, NQ);
     if (!hidden || !w_packed || !row_ctr || !lse || !sample_p || !sample_res || (NQ > 0 && (!q_tok || !q_prob || !z_supp)))
-        return fail(SPEC_EINVAL, "spec_lm_head_sample: null required pointer");
-    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_sample: hidden and w_packed must be 16-byte aligned");
+        return fail(SPEC_EINVAL, "%s: null required pointer", name);
+    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "%s: hidden and w_packed must be 16-byte aligned", name);
     const size_t need = spec_lm_head_sample_workspace_bytes(R, H, V);
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(SPEC_EWORKSPACE, "spec_lm_head_sample: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, need);
+        return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes, need);
     const int n_vt = n_vtiles(V);
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
     float2* part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + 256 + (size_t)R * sizeof(unsigned long long));
     const int mtiles = (R + 15) / 16;
     const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
     const int MT = (mtiles + n_rg - 1) / n_rg;
-    if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_sample: grid too large");
-    SampleArgs sa{q_tok, row_ctr, part, z_supp, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
+    if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "%s: grid too large", name);
+    SampleArgs sa{q_tok, row_ctr, part, z_supp, z_out, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
     hipStream_t st = (hipStream_t)stream;
     const spec_bf16* w = w_packed;
     switch (MT) {
@@ -527,11 +511,35 @@ int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int3
         case 7: launch_tiles<7, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
         default: launch_tiles<8, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
     }
-    SV_LAUNCH_CHECK("spec_lm_head_sample(tiles)");
+    SV_LAUNCH_CHECK(name);
     hipLaunchKernelGGL(sample_finalize_kernel, dim3(R), dim3(256), 0, st, part, n_vt, V, keys, q_tok, q_prob, NQ, row_ctr,
                        sa.key0, sa.key1, lse, z_supp, sample_p, sample_res);
-    SV_LAUNCH_CHECK("spec_lm_head_sample(finalize)");
+    SV_LAUNCH_CHECK(name);
     return SPEC_OK;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                        float temperature, const int32_t* q_tok, const float* q_prob, int32_t NQ,
+                        const int32_t* row_ctr, uint64_t seed, float* lse, float* z_supp, int32_t* sample_p,
+                        int32_t* sample_res, void* workspace, size_t workspace_bytes, void* stream) {
+    return sv::lm_head_sample_impl("spec_lm_head_sample", hidden, w_packed, R, H, V, temperature, q_tok, q_prob, NQ, row_ctr,
+                                   seed, lse, z_supp, sample_p, sample_res, nullptr, workspace, workspace_bytes, stream);
+}
+
+int spec_lm_head_sample_dense(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                              float temperature, const int32_t* row_ctr, uint64_t seed, float* lse, int32_t* sample_p,
+                              float* z, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!z) {
+        sv::last_error().clear();
+        return sv::fail(SPEC_EINVAL, "spec_lm_head_sample_dense: null required pointer");
+    }
+    // no support list: every entry is outside it, so the second draw is the first
+    return sv::lm_head_sample_impl("spec_lm_head_sample_dense", hidden, w_packed, R, H, V, temperature, nullptr, nullptr, 0,
+                                   row_ctr, seed, lse, nullptr, sample_p, sample_p, z, workspace, workspace_bytes, stream);
 }
 
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {

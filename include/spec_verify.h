@@ -21,6 +21,8 @@
  *
  *   spec_lm_head_sample        lm_head with softmax statistics and two draws fused in
  *   spec_sample_accept         the speculative-sampling chain walk
+ *   spec_lm_head_sample_dense  the same pass for dense draft distributions (keeps z)
+ *   spec_sample_accept_dense   the chain walk with a dense q and its residual draw
  *
  * and the pieces around them: spec_greedy_accept_stop and spec_truncate_stop (stop
  * tokens and a generation limit) and the host-side adaptive draft-depth policy
@@ -457,6 +459,41 @@ int spec_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, co
                        const int32_t* sample_p, const int32_t* sample_res, const int32_t* row_ctr, uint64_t seed,
                        const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
                        int32_t* emit, int32_t* next_tok, int32_t* seq_status, void* stream);
+
+/* Dense draft distributions (DSSD _sample_verify with the draft head's whole
+ * distribution): q [R][V] fp32 gives q_r(v) for every target-vocabulary entry. The
+ * residual of a rejected row, norm(max(p_r - q_r, 0)), then needs that row's whole
+ * p, so the pass keeps every z (R * V * 4 bytes) and the walk draws the residual. */
+
+/* spec_lm_head_sample_dense — spec_lm_head_sample with no support list: lse[r] and
+ * sample_p[r] (a draw from p of every row) as there, and z [R][V] fp32 = z_v of every
+ * entry (logit / temperature). Workspace, limits and temperature as
+ * spec_lm_head_sample (the same workspace size). */
+int spec_lm_head_sample_dense(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                              float temperature, const int32_t* row_ctr, uint64_t seed, float* lse, int32_t* sample_p,
+                              float* z, void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_sample_accept_dense — the chain walk with q [R][V]. For sequence s and
+ * j = 0 .. k_s - 1, row r = off_s + j, draft x = map(drafts[s][j]):
+ *   q[r][x] <= 0 (a draft the draft distribution cannot produce) or x outside its
+ *   vocabulary: SPEC_STATUS_BAD_TOKEN;
+ *   keep x iff u_r < exp(z[r][x] - lse[r]) / q[r][x];
+ *   else the token is argmax over {v : p_v > q_v} of ln(p_v - q_v) + G_v with
+ *   p_v = exp(z[r][v] - lse[r]) and the row's Gumbel noise G (the first such v on
+ *   a tie; sample_p[r] if that set is empty in fp32), and the walk stops;
+ * if every draft is kept, emit sample_p[off_s + k_s]. Outputs, status bits and the
+ * outputs of a flagged sequence as spec_sample_accept. z, lse and sample_p come from
+ * spec_lm_head_sample_dense for the same rows, row_ctr and seed.
+ * workspace: spec_sample_accept_dense_workspace_bytes(B) bytes (any contents; the
+ * call initialises what it uses; calls sharing one must not overlap).
+ * Limits: 1 <= B <= 8192, 0 <= kmax <= 1024, R >= 1, V >= 1. */
+size_t spec_sample_accept_dense_workspace_bytes(int32_t B);
+int spec_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
+                             int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const float* q, const float* z,
+                             const float* lse, const int32_t* sample_p, const int32_t* row_ctr, uint64_t seed,
+                             const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                             int32_t* emit, int32_t* next_tok, int32_t* seq_status, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Adaptive draft depth (host side; no GPU work, no allocation).

@@ -293,11 +293,12 @@ def sample_accept(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, q_tok, q_prob, r
     return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st)
 
 
-def sample_accept_dense(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, logits, T, q, row_ctr, seed, pos_in):
+def sample_accept_dense(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, logits, T, q, row_ctr, seed, pos_in,
+                        rel=0.0):
     """Speculative sampling with a dense draft distribution q [R, V] (fp32) over the target
     vocabulary; logits fp64 [R, V]. Returns the greedy_accept dict plus margin [B] (how
     decided the acceptance tests are, in log(u) vs log(p/q)) and gap [B] (how decided the
-    deciding draw is)."""
+    deciding draw is when p is known to relative precision rel; <= 0: not decided)."""
     logits = np.ascontiguousarray(logits, np.float64)
     q = np.ascontiguousarray(q, np.float32)
     assert logits.shape == (R, V) and q.shape == (R, V)
@@ -311,7 +312,7 @@ def sample_accept_dense(drafts, kmax, k, d2t, n_draft_vocab, V, B, R, logits, T,
                                      ctypes.c_int32(n_draft_vocab), ctypes.c_int32(V), ctypes.c_int32(B),
                                      ctypes.c_int32(R), _p(logits), ctypes.c_double(T), _p(q), _p(_i32(row_ctr)),
                                      ctypes.c_uint64(seed), _p(_i32(pos_in)), _p(pos_out), _p(acc), _p(ne), _p(emit),
-                                     _p(nt), _p(st), _p(margin), _p(gap))
+                                     _p(nt), _p(st), ctypes.c_double(rel), _p(margin), _p(gap))
     return dict(pos_out=pos_out, accept_len=acc, n_emit=ne, emit=emit, next_tok=nt, status=st, margin=margin,
                 gap=gap)
 

@@ -821,13 +821,19 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
  *   Gumbel noise, as for the draw from p); no such v: the row's draw from p.
  * All kept: the draw from p of the bonus row (first v maximising z + G).
  * Outputs as oracle_sample_accept; margin[s] = the smallest |log u_r - log(p_r(x) /
- * q_r(x))| over the drafts tested (how decided the walk is; +inf if none), gap[s] =
- * best - runner-up of the deciding draw (how decided the token is). */
+ * q_r(x))| over the drafts tested (how decided the walk is; +inf if none); gap[s] =
+ * how decided the deciding draw is when p is known only to a relative precision
+ * rel: for the residual, the winner's lowest possible score log(w - rel p) + G
+ * minus the highest possible score log(w + rel p) + G of any other entry (w = p - q;
+ * where p and q nearly cancel, a small error in p moves log w a lot); for a draw
+ * from p, best - runner-up - 2 log(1 + rel). gap <= 0: not decided at that
+ * precision. */
 void oracle_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
                                 int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const double* logits,
                                 double T, const float* q, const int32_t* row_ctr, uint64_t seed,
                                 const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
-                                int32_t* emit, int32_t* next_tok, int32_t* st, double* margin, double* gap) {
+                                int32_t* emit, int32_t* next_tok, int32_t* st, double rel, double* margin,
+                                double* gap) {
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     int64_t total = 0;
     int packing_ok = 1;
@@ -896,9 +902,10 @@ void oracle_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32
                 }
                 rejected = 1;
             }
-            /* the deciding draw: residual of the rejected row, or p of the bonus row */
-            double b1 = -INFINITY, b2 = -INFINITY, p1 = -INFINITY, p2 = -INFINITY;
-            int i1 = -1, ip = -1;
+            /* the deciding draw: residual of the rejected row, or p of the bonus row;
+             * hi1/hi2: the two highest upper-bound residual scores (for the gap) */
+            double b1 = -INFINITY, p1 = -INFINITY, p2 = -INFINITY, hi1 = -INFINITY, hi2 = -INFINITY;
+            int i1 = -1, ip = -1, ih1 = -1;
             for (int v = 0; v < V; ++v) {
                 const double g = row_gumbel((uint32_t)v, rc, key);
                 const double z = l[v] / T;
@@ -910,24 +917,33 @@ void oracle_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32
                     p2 = z + g;
                 }
                 if (!rejected) continue;
-                const double w = exp(z - L) - (double)q[r * V + v];
-                if (w > 0.0) {
-                    const double sc = log(w) + g;
-                    if (sc > b1) {
-                        b2 = b1;
-                        b1 = sc;
-                        i1 = v;
-                    } else if (sc > b2) {
-                        b2 = sc;
+                const double pv = exp(z - L);
+                const double w = pv - (double)q[r * V + v];
+                if (w > 0.0 && log(w) + g > b1) {
+                    b1 = log(w) + g;
+                    i1 = v;
+                }
+                const double whi = w + rel * pv;
+                if (whi > 0.0) {
+                    const double sh = log(whi) + g;
+                    if (sh > hi1) {
+                        hi2 = hi1;
+                        hi1 = sh;
+                        ih1 = v;
+                    } else if (sh > hi2) {
+                        hi2 = sh;
                     }
                 }
             }
             if (rejected && i1 >= 0) {
                 tok = i1;
-                gap[s] = b1 - b2;
+                const double pw = exp(l[i1] / T - L);
+                const double wlo = pw - (double)q[r * V + i1] - rel * pw;
+                const double lo = wlo > 0.0 ? log(wlo) + row_gumbel((uint32_t)i1, rc, key) : -INFINITY;
+                gap[s] = lo - (ih1 == i1 ? hi2 : hi1);
             } else {
                 tok = ip;
-                gap[s] = p1 - p2;
+                gap[s] = p1 - p2 - 2.0 * log1p(rel);
             }
             break;
         }

@@ -177,3 +177,46 @@ def test_graph_replay_sampling_step():
 
     _replays_match(run, [step.attn_out, lse, z, sp, sr, acc, emit, pos_out, sst])
     assert (sst.cpu() == 0).all()
+
+
+def test_graph_replay_dense_sampling():
+    """Dense-draft sampling (spec_lm_head_sample_dense -> spec_sample_accept_dense) captured
+    and replayed: the walk initialises its workspace on every call, the sample pass leaves
+    its own zero, so replays give the eager bytes."""
+    import greedy_draft_verify_amd as gdv
+    dev = torch.device("cuda:0")
+    B, kmax, V, H = 16, 4, 3000, 512
+    rng = np.random.default_rng(8)
+    k = rng.integers(0, kmax + 1, B).astype(np.int32)
+    R = int((k + 1).sum())
+    hidden = synth.normal_bf16((R, H), 1.0, 3, "tiny", "extra", dev)
+    w = synth.normal_bf16((V, H), 0.2, 3, "tiny", "w", dev)
+    wp = gdv.spec_lm_head_pack(w)
+    q = torch.softmax(torch.randn((R, V), generator=torch.Generator().manual_seed(5)), dim=1).to(dev)
+    drafts = torch.multinomial(q[:B].cpu(), kmax, replacement=True).to(torch.int32)
+    # each draft drawn from its own row's q
+    off = np.concatenate([[0], np.cumsum(k + 1)])
+    qc = q.cpu()
+    for s in range(B):
+        for j in range(k[s]):
+            drafts[s, j] = int(torch.multinomial(qc[off[s] + j], 1))
+    drafts = drafts.to(dev)
+    kk = torch.from_numpy(k).to(dev)
+    row_ctr = torch.from_numpy(np.stack([np.arange(R), np.full(R, 4)], 1).astype(np.int32)).to(dev)
+    pos = torch.from_numpy(rng.integers(0, 900, B).astype(np.int32)).to(dev)
+    lse = torch.empty(R, device=dev)
+    sp = torch.empty(R, dtype=torch.int32, device=dev)
+    z = torch.empty((R, V), device=dev)
+    ws = gdv.workspace(gdv.lm_head_sample_workspace_bytes(R, H, V), dev, zero=True)
+    wsd = gdv.workspace(gdv.sample_accept_dense_workspace_bytes(B), dev)
+    e = lambda: torch.empty(B, dtype=torch.int32, device=dev)
+    pos_out, acc, ne, nt, sst = e(), e(), e(), e(), e()
+    emit = torch.empty((B, kmax + 1), dtype=torch.int32, device=dev)
+
+    def run():
+        gdv.spec_lm_head_sample_dense(hidden, wp, V, 0.9, row_ctr, 123, lse, sp, z, workspace_buf=ws)
+        gdv.spec_sample_accept_dense(drafts, kk, None, q, z, lse, sp, row_ctr, 123, pos, pos_out, acc, ne, emit, nt,
+                                     sst, workspace_buf=wsd)
+
+    _replays_match(run, [lse, sp, z, acc, emit, pos_out, sst])
+    assert (sst.cpu() == 0).all()
