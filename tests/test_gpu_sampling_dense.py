@@ -184,3 +184,30 @@ def test_dense_end_to_end_from_the_lm_head(dev, T):
     assert decided.mean() > 0.5, decided.mean()
     for key in KEYS:
         assert np.array_equal(got[key][decided], ref[key][decided]), key
+
+
+def test_dense_pass_b16k4_rows(dev):
+    """The b16k4 lm_head (H = 4096, V = 151936, 80 rows) at temperature 0.1, as the
+    benchmark runs it: every fifth row's z, lse and draw from p against the oracle."""
+    import greedy_draft_verify_amd as gdv
+    x = synth.make_verify_inputs("b16k4", seed=0, device=dev)
+    R, H, V, T = x.R, x.wl.H, x.wl.V, 0.1
+    row_ctr = np.stack([np.arange(R) + 900, np.arange(R) // 5], 1).astype(np.int32)
+    wp = gdv.spec_lm_head_pack(x.w)
+    lse = torch.zeros(R, device=dev)
+    sp = torch.zeros(R, dtype=torch.int32, device=dev)
+    z = torch.zeros((R, V), device=dev)
+    gdv.spec_lm_head_sample_dense(x.hidden, wp, V, T, i32(row_ctr, dev), 41, lse, sp, z)
+    torch.cuda.synchronize()
+    rows = np.arange(0, R, 5)
+    logits = oracle.lm_head_logits(bits(x.hidden)[rows], bits(x.w), len(rows), H, V)
+    ref = oracle.sample_rows(logits, T, np.zeros((len(rows), 0), np.int32), np.zeros((len(rows), 0), np.float32),
+                             row_ctr[rows], 41)
+    zg = z.cpu().numpy()[rows].astype(np.float64)
+    ztol = (2e-2 + 1e-2 * np.abs(logits)) / T
+    assert (np.abs(zg - logits / T) <= ztol).all(), np.abs(zg - logits / T).max()
+    lg = lse.cpu().numpy()[rows].astype(np.float64)
+    assert (np.abs(lg - ref["lse"]) <= (2e-2 + 1e-2 * np.abs(ref["lse"])) / T).all()
+    dec = ref["gap_p"] > 5e-2 / T
+    assert dec.mean() > 0.5
+    assert np.array_equal(sp.cpu().numpy()[rows][dec], ref["sample_p"][dec])
