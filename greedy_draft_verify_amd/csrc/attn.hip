@@ -368,15 +368,19 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // ---------------------------------------------------------------------------
 // attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
-// Register budget: four workgroups per CU at D <= 128 (32 KB of LDS each), two at
-// D = 256 (64 KB each), so that enough tiles are in flight per CU.
+// Register budget: D = 256 two workgroups per CU (64 KB of LDS each); D <= 128 four
+// for tree rows (32 KB each) and three for chain rows, whose workgroups also do the
+// prep kernel's work (at four the extra registers spill: measured slower).
 template <int D, bool TREE>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
     float scale_log2, int split, int n_splits, float2* __restrict__ part_ml,
-    float* __restrict__ part_o, const uint4* __restrict__ tree_mask, int kmax) {
+    float* __restrict__ part_o, const uint4* __restrict__ tree_mask, int kmax,
+    const u16* __restrict__ k_new, const u16* __restrict__ v_new, int64_t n_pages, int B, int R,
+    int32_t* __restrict__ status, RowRec* __restrict__ rows, int32_t* __restrict__ packing_ok,
+    u16* k_pool_w, u16* v_pool_w) {
     using TM = TileMath<D>;
     constexpr int NDS = TM::NDS, NDT = TM::NDT;
     constexpr int BLK = kPage * D;               // elements per block
@@ -410,12 +414,54 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
     // reach past pos
     uint4 mk = make_uint4(0, 0, 0, 0);
     if (TREE) mk = tree_mask[(size_t)s * (kmax + 1) + min((m_tile0 + l16) / G, kmax)];
-    const SeqInfo si = info[s];
     const int ks = k[s], P0 = pos[s];
-    if (!si.valid) return;
+    int off;           // the sequence's first packed row
+    bool ok;           // this workgroup may read its pages and write partials
+    int basic = 0;     // chain rows: packing and position flags
+    bool packed = true;
+    if constexpr (TREE) {
+        const SeqInfo si = info[s];   // formed by the prep kernel (which also builds the masks)
+        off = si.off;
+        ok = si.valid;
+    } else {
+        // Chain rows need no prep kernel: every wave forms the row packing on its own
+        // (each k is read by every wave, from cache), and the workgroup's own page ids
+        // are checked before any of its tiles is read. The whole page list is checked
+        // at the end by the workgroups that write the sequence's records or append its
+        // rows, the only writes a flagged sequence must not make.
+        long long before = 0, total = 0;
+        int rowbad = 0;
+        for (int i = lane; i < B; i += kWave) {
+            const long long kk = k[i];
+            total += kk + 1;
+            if (i < s) before += kk + 1;
+            rowbad |= kk < 0;
+        }
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) {
+            before += __shfl_xor(before, d);
+            total += __shfl_xor(total, d);
+            rowbad |= __shfl_xor(rowbad, d);
+        }
+        // wave-uniform: kept in scalar registers
+        packed = __builtin_amdgcn_readfirstlane(!rowbad && total == (long long)R);
+        off = __builtin_amdgcn_readfirstlane((int)before);
+        const bool pos_ok = P0 >= 0 && (ks < 0 || ((long long)P0 + ks) / kPage < max_pages);
+        if (!packed || ks > kmax) basic |= SPEC_STATUS_BAD_ROWS;
+        if (!pos_ok) basic |= SPEC_STATUS_BAD_POS;
+        bool own_bad = false;
+        if (!basic) {
+            const int hi = min((P0 + ks) / kPage, pg0 + split / kPage - 1);
+#pragma unroll
+            for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
+                const int p = pg0 + r * kWave + lane;
+                if (p <= hi && (pid[r] < 0 || (int64_t)pid[r] >= n_pages)) own_bad = true;
+            }
+        }
+        ok = __builtin_amdgcn_readfirstlane(!basic && __ballot(own_bad) == 0ull);   // the same for every wave
+    }
     const int T = ks + 1, M = G * T, last = P0 + T - 1;
-    if (c0 > last) return;
-    if (mgroup * kRowsPerGroup >= M) return;
+    if (ok && c0 <= last && mgroup * kRowsPerGroup < M) {
     const int c1 = min(c0 + split, last + 1);
 
     const bool active = m_tile0 < M;
@@ -426,7 +472,7 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
     const int p_m = m_ok ? P0 + jrow : -1;
     bf16x8 qf[NDS];
     if (active) {
-        const size_t qoff = ((size_t)(si.off + jrow) * Hq + h) * D;
+        const size_t qoff = ((size_t)(off + jrow) * Hq + h) * D;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
             qf[ds] = as_bf16x8(m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0));
@@ -481,9 +527,34 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
             st16(smem + (it * kAttnThreads + tid) * 8, v);
         }
     };
+    // Chain rows: in a tile that reaches the new rows, those rows' K and V are taken
+    // from k_new / v_new (the bytes the append writes to the pool, which this kernel
+    // itself may be writing), over the staged pool bytes; one item per (row, 8
+    // channels): a 16-byte K chunk and 8 V elements (each in its token's slot of a
+    // 4-token group).
+    auto new_rows_tile = [&](int t0) {
+        const int r_lo = max(t0, P0), r_hi = min(t0 + kKT - 1, last);
+        constexpr int dch = D / 8;
+        const int n_it = (r_hi - r_lo + 1) * dch;
+        for (int i = tid; i < n_it; i += kAttnThreads) {
+            const int tp = r_lo + i / dch, dc = i % dch;
+            const size_t src = ((size_t)(off + tp - P0) * Hkv + hk) * D + dc * 8;
+            const uint4 kv = ld16(k_new + src), vv = ld16(v_new + src);
+            const int p = (tp - t0) / kPage, t = tp % kPage;
+            st16(smem + p * BLK + k_off(t, dc * 8), kv);
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                smem[(4 + p) * BLK + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+        }
+    };
     auto use_tile = [&](int t0, const uint4 (&stg)[PER_THREAD], auto refill) {
         __syncthreads();  // previous tile's LDS reads are done
         store_tile(t0, stg);
+        if (!TREE && t0 + kKT > P0) {
+            __syncthreads();   // the staged pool bytes are in place
+            new_rows_tile(t0);
+        }
         __syncthreads();
         refill();
         if (!active) return;
@@ -503,9 +574,68 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 4 : 2) void attn_split_ker
         use_tile(t0, stage, [&] {
             if (t0 + kKT < c1) load_tile(t0 + kKT, stage);
         });
-    if (!active) return;
-    const size_t idx = ((size_t)(si.off + jrow) * Hq + h) * n_splits + c;
-    store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
+    if (active) {
+        const size_t idx = ((size_t)(off + jrow) * Hq + h) * n_splits + c;
+        store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
+    }
+    }   // this workgroup's tiles
+    if constexpr (!TREE) {
+        // the sequence's records (one workgroup per sequence) and the append of this kv
+        // head's new rows that fall in this split (the workgroups of row group 0)
+        const bool lead = hk == 0 && c == 0 && mgroup == 0;
+        const bool writer = mgroup == 0 && !basic && c0 <= last && c0 + split > P0;
+        if (!lead && !writer) return;
+        int flags = basic;
+        if (!basic) {
+            // 8 page ids per thread requested at once (clamped to the last page), then checked
+            const int last_page = last / kPage;
+            for (int pgb = tid; pgb <= last_page; pgb += kAttnThreads * 8) {
+                int ids[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    ids[u] = page_table[(size_t)s * max_pages + min(pgb + u * kAttnThreads, last_page)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (pgb + u * kAttnThreads <= last_page && (ids[u] < 0 || (int64_t)ids[u] >= n_pages))
+                        flags |= SPEC_STATUS_BAD_PAGE;
+            }
+        }
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) flags |= __shfl_xor(flags, d);
+        int* s_fl = reinterpret_cast<int*>(smem);
+        __syncthreads();   // the tiles' LDS reads are done
+        if (lane == 0) s_fl[wave] = flags;
+        __syncthreads();
+        const int bits = s_fl[0] | s_fl[1] | s_fl[2] | s_fl[3];
+        if (lead) {
+            if (tid == 0) {
+                status[s] = bits;
+                if (s == 0) *packing_ok = packed;
+            }
+            // per-row record for the combine (only when the packing is defined; otherwise
+            // the combine writes nothing)
+            if (packed)
+                for (int j = tid; j <= ks; j += kAttnThreads) rows[off + j] = RowRec{P0 + j, bits ? 0 : (P0 + j) / split + 1};
+        }
+        if (!writer || bits) return;
+        // 8 channels (one 16-byte chunk of a row) per item
+        const int j_lo = max(c0, P0) - P0, j_hi = min(c0 + split - 1, last) - P0;
+        constexpr int dch = D / 8;
+        const int n_it = (j_hi - j_lo + 1) * dch;
+        for (int i = tid; i < n_it; i += kAttnThreads) {
+            const int j = j_lo + i / dch, dc = i % dch;
+            const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
+            const uint4 kv = ld16(k_new + src), vv = ld16(v_new + src);
+            const int page = page_table[(size_t)s * max_pages + (P0 + j) / kPage];
+            const int t = (P0 + j) % kPage;
+            const size_t blk = ((size_t)page * Hkv + hk) * BLK;
+            st16(k_pool_w + blk + k_off(t, dc * 8), kv);   // 8 channels contiguous
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v_pool_w[blk + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -595,22 +725,23 @@ static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_
 }
 
 template <int D>
-static void launch_attn(const u16* q, const u16* k_pool, const u16* v_pool, const int32_t* pt,
+static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* pt,
                         int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
-                        const RowRec* rows, const int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
+                        RowRec* rows, int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
                         int split, int n_splits, float2* ml, float* po, u16* out, const uint4* tree_mask,
-                        hipStream_t st) {
+                        const u16* k_new, const u16* v_new, int64_t n_pages, int32_t* status, hipStream_t st) {
     const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
     if (tree_mask)
         hipLaunchKernelGGL((attn_split_kernel<D, true>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
                            pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
-                           tree_mask, kmax);
+                           tree_mask, kmax, nullptr, nullptr, n_pages, B, R, nullptr, nullptr, nullptr, nullptr,
+                           nullptr);
     else
         hipLaunchKernelGGL((attn_split_kernel<D, false>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
                            pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
-                           tree_mask, kmax);
+                           tree_mask, kmax, k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
                        rows, packing_ok, R, Hq, n_splits, ml, po, out);
@@ -690,14 +821,17 @@ static int verify_attn_impl(const char* name, const spec_bf16* q, const spec_bf1
     // enough workgroups per sequence that every thread appends at most kPrepItems chunks
     const long long max_items = (long long)(kmax + 1) * Hkv * (D / 8);
     const dim3 prep_grid(B, (unsigned)((max_items + kPrepItemsPerWg - 1) / kPrepItemsPerWg));
-    hipLaunchKernelGGL(attn_prep_kernel, prep_grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, split, info, rows, packing_ok,
-                       seq_status, parent, tree_mask);
-    SV_LAUNCH_CHECK(name);
+    // chain rows: the split kernel does the prep kernel's checks, records and append
+    if (parent) {
+        hipLaunchKernelGGL(attn_prep_kernel, prep_grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
+                           n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, split, info, rows,
+                           packing_ok, seq_status, parent, tree_mask);
+        SV_LAUNCH_CHECK(name);
+    }
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
     }
     SV_LAUNCH_CHECK(name);
     return SPEC_OK;
