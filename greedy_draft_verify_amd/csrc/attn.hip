@@ -8,11 +8,18 @@
 //            output tile dt each lane's 4 tokens of one channel are 8 contiguous bytes.
 //
 // Launches on the caller's stream:
-//   1. attn_prep_kernel  grid (B, append blocks): validates sequence s (row packing,
-//      positions, page ids), records its row offset in the workspace and writes the
-//      rows' K/V into their pool slots (span-02 spec.rs: KV appended in place at
-//      pos..pos+k); each workgroup of a sequence appends up to 1024 16-byte chunks,
-//      all requested in one round with the validation loads.
+//   1. (tree rows only) attn_prep_kernel  grid (B, append blocks): validates sequence
+//      s (row packing, positions, page ids, parent list), records its row offset in
+//      the workspace, writes the rows' K/V into their pool slots (span-02 spec.rs: KV
+//      appended in place at pos..pos+k) and builds the rows' ancestor masks; each
+//      workgroup of a sequence appends up to 1024 16-byte chunks, all requested in
+//      one round with the validation loads. For chain rows the split kernel does this
+//      work itself (no launch, no round trips of its own): each workgroup forms the
+//      row packing and checks its positions and its own page ids with its first
+//      metadata loads, a tile that reaches the new rows takes them from k_new/v_new,
+//      and one workgroup per sequence writes the status and row records while one per
+//      (kv head, split) appends the rows that fall in its split, after checking the
+//      whole page list.
 //   2. attn_split_kernel: one workgroup per (sequence, kv head, split of
 //      kv_split_tokens positions, group of 64 query rows), kv head fastest in the
 //      launch order so that the Hkv blocks of a page (adjacent in the pool) are
