@@ -7,20 +7,16 @@
 //   V block: token t, channel d at (d/16)*256 + (t/4)*64 + (d%16)*4 + t%4, i.e. for
 //            output tile dt each lane's 4 tokens of one channel are 8 contiguous bytes.
 //
-// Launches on the caller's stream:
-//   1. (tree rows only) attn_prep_kernel  grid (B, append blocks): validates sequence
-//      s (row packing, positions, page ids, parent list), records its row offset in
-//      the workspace, writes the rows' K/V into their pool slots (span-02 spec.rs: KV
-//      appended in place at pos..pos+k) and builds the rows' ancestor masks; each
-//      workgroup of a sequence appends up to 1024 16-byte chunks, all requested in
-//      one round with the validation loads. For chain rows the split kernel does this
-//      work itself (no launch, no round trips of its own): each workgroup forms the
-//      row packing and checks its positions and its own page ids with its first
-//      metadata loads, a tile that reaches the new rows takes them from k_new/v_new,
-//      and one workgroup per sequence writes the status and row records while one per
-//      (kv head, split) appends the rows that fall in its split, after checking the
-//      whole page list.
-//   2. attn_split_kernel: one workgroup per (sequence, kv head, split of
+// Launches on the caller's stream (two; the row metadata and the append have no
+// launch or round trips of their own):
+//   1. attn_split_kernel: each workgroup forms the row packing and checks its
+//      positions, the parent list (tree rows) and its own page ids with its first
+//      metadata loads; a tile that reaches the new rows takes them from k_new/v_new;
+//      one workgroup per sequence writes the status and row records, and one per (kv
+//      head, split) appends the rows that fall in its split to their pool slots
+//      (span-02 spec.rs: KV appended in place at pos..pos+k), both after checking the
+//      whole page list, so a flagged sequence writes nothing. Its main work: one
+//      workgroup per (sequence, kv head, split of
 //      kv_split_tokens positions, group of 64 query rows), kv head fastest in the
 //      launch order so that the Hkv blocks of a page (adjacent in the pool) are
 //      fetched at about the same time. It stages 64-token tiles
@@ -33,16 +29,16 @@
 //      (kv_hi = position, memra full_attn_verify's per-row bound). The split's page
 //      ids are requested with the sequence metadata, once per wave, and taken with
 //      readlane, so tiles never wait on a page-table load.
-//   3. attn_combine_kernel one wave per (row, q head): merges the row's splits in
+//   2. attn_combine_kernel one wave per (row, q head): merges the row's splits in
 //      ascending order (log-sum-exp weights) and writes bf16.
 //
 // Tree rows (spec_verify_attn_tree; DSSD fast.py, _set_rows and _tree_cycle): the
 // k+1 rows of a sequence are the nodes of a draft tree in creation order; node j
 // still writes slot pos + j, but attends to slots 0..pos and to the slots pos + u of
-// the nodes u on its own path. The prep kernel checks every parent list and turns it
-// into one 128-bit ancestor mask per row (pointer jumping over the parent links in
-// LDS: after r rounds a node's mask covers its 2^r nearest ancestors). The split
-// kernel then keeps key slot t for a row iff t <= pos, or bit t - pos of the row's
+// the nodes u on its own path. Each split workgroup checks the parent list and turns
+// it into one 128-bit ancestor mask per node (pointer jumping over the parent links in
+// LDS while its first tile's loads are in flight: after r rounds a node's mask covers
+// its 2^r nearest ancestors). It keeps key slot t for a row iff t <= pos, or bit t - pos of the row's
 // mask is set: for a tile that reaches past pos it shifts the mask into a 64-bit
 // window aligned with the tile. A chain (parent j - 1) keeps exactly the keys
 // t <= pos + j, so it gives the bytes of spec_verify_attn.
@@ -65,11 +61,6 @@ constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
 constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct SeqInfo {
-    int32_t off;    // first packed row
-    int32_t valid;  // 1 if the sequence passed validation
-};
-
 struct RowRec {
     int32_t p;      // position of the row
     int32_t nc;     // splits the combine merges for it (0: its sequence is skipped)
@@ -81,161 +72,6 @@ __device__ __forceinline__ int k_off(int t, int d) {
 }
 __device__ __forceinline__ int v_off(int t, int d) {
     return (d >> 4) * 256 + (t >> 2) * 64 + (d & 15) * 4 + (t & 3);
-}
-
-// ---------------------------------------------------------------------------
-constexpr int kPrepItems = 4;   // append chunks per thread requested before validation ends
-constexpr int kPrepItemsPerWg = kPrepItems * 256;   // a sequence's append spans grid.y workgroups
-
-__global__ __launch_bounds__(256) void attn_prep_kernel(
-    const u16* __restrict__ k_new, const u16* __restrict__ v_new, u16* __restrict__ k_pool,
-    u16* __restrict__ v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ k, int kmax, int B, int R, int Hq,
-    int Hkv, int D, int split, SeqInfo* __restrict__ info, RowRec* __restrict__ rows,
-    int32_t* __restrict__ packing_ok, int32_t* __restrict__ status, const int32_t* __restrict__ parent,
-    uint4* __restrict__ tree_mask) {
-    __shared__ int s_flags[4];
-    __shared__ int s_anc[kMaxTreeNodes];
-    __shared__ uint4 s_mask[kMaxTreeNodes];
-    const int s = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int ks = k[s];
-    const int P = pos[s];
-    // Every wave forms the row packing on its own (each k is read by every wave, from
-    // cache), so the row offset is known without a barrier.
-    long long before = 0, total = 0;
-    int rowbad = 0;
-    for (int i = lane; i < B; i += kWave) {
-        const long long kk = k[i];
-        total += kk + 1;
-        if (i < s) before += kk + 1;
-        rowbad |= kk < 0;
-    }
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        before += __shfl_xor(before, d);
-        total += __shfl_xor(total, d);
-        rowbad |= __shfl_xor(rowbad, d);
-    }
-    const bool packed = !rowbad && total == (long long)R;
-    const int off = (int)before;
-    const bool pos_ok = P >= 0 && (ks < 0 || ((long long)P + ks) / kPage < max_pages);
-    int flags = (!packed || ks > kmax) ? SPEC_STATUS_BAD_ROWS : 0;
-    if (!pos_ok) flags |= SPEC_STATUS_BAD_POS;
-    // One round of loads: the page ids the sequence needs (validation) and this
-    // thread's first append chunks (page id, new K row chunk, new V row chunk).
-    const bool can_append = packed && pos_ok && ks >= 0;
-    const int dch = D / 8;
-    const int n_items = can_append ? (ks + 1) * Hkv * dch : 0;
-    int32_t it_page[kPrepItems];
-    uint4 it_k[kPrepItems], it_v[kPrepItems];
-    auto item_src = [&](int i, int& j, int& hk, int& dc) {
-        dc = i % dch;
-        const int rest = i / dch;
-        hk = rest % Hkv;
-        j = rest / Hkv;
-    };
-    const int item0 = blockIdx.y * kPrepItemsPerWg;
-#pragma unroll
-    for (int u = 0; u < kPrepItems; ++u) {
-        const int i = item0 + tid + u * 256;
-        if (i < n_items) {
-            int j, hk, dc;
-            item_src(i, j, hk, dc);
-            const size_t src = ((size_t)(off + j) * Hkv + hk) * D + dc * 8;
-            it_page[u] = page_table[(size_t)s * max_pages + (P + j) / kPage];
-            it_k[u] = ld16(k_new + src);
-            it_v[u] = ld16(v_new + src);
-        }
-    }
-    // tree rows: node i's parent must come before it (the root's is -1)
-    int par_i = 0;
-    if (parent && ks >= 0 && ks <= kmax && tid <= ks) {
-        par_i = parent[(size_t)s * (kmax + 1) + tid];
-        if (tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid)) flags |= SPEC_STATUS_BAD_TREE;
-    }
-    if (pos_ok && ks >= 0) {
-        // 8 page ids per thread requested at once (clamped to the last page), then checked
-        const int last_page = (int)(((long long)P + ks) / kPage);
-        for (int pgb = tid; pgb <= last_page; pgb += 256 * 8) {
-            int ids[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                ids[u] = page_table[(size_t)s * max_pages + min(pgb + u * 256, last_page)];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (pgb + u * 256 <= last_page && (ids[u] < 0 || ids[u] >= n_pages)) flags |= SPEC_STATUS_BAD_PAGE;
-        }
-    }
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) flags |= __shfl_xor(flags, d);
-    if (lane == 0) s_flags[wave] = flags;
-    __syncthreads();
-    const int bits = s_flags[0] | s_flags[1] | s_flags[2] | s_flags[3];
-    const bool lead = blockIdx.y == 0;   // the workgroup that writes the sequence's records
-    if (lead && tid == 0) {
-        status[s] = bits;
-        info[s].off = off;
-        info[s].valid = bits == 0;
-        if (s == 0) *packing_ok = packed;
-    }
-    // per-row record for the combine (only when the packing is defined; otherwise the
-    // combine writes nothing)
-    if (lead && packed)
-        for (int j = tid; j <= ks; j += 256) rows[off + j] = RowRec{P + j, bits ? 0 : (P + j) / split + 1};
-    if (bits) return;
-    // append: 8 channels (one 16-byte chunk of a row) per item
-    auto store_item = [&](int i, int32_t page, uint4 kv, uint4 vv) {
-        int j, hk, dc;
-        item_src(i, j, hk, dc);
-        const int t = (P + j) % kPage;
-        const size_t blk = ((size_t)page * Hkv + hk) * (kPage * D);
-        st16(k_pool + blk + k_off(t, dc * 8), kv);   // 8 channels contiguous
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v_pool[blk + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
-    };
-#pragma unroll
-    for (int u = 0; u < kPrepItems; ++u) {
-        const int i = item0 + tid + u * 256;
-        if (i < n_items) store_item(i, it_page[u], it_k[u], it_v[u]);
-    }
-    if (!parent || !lead) return;
-    // Ancestor masks. Invariant: mask(j) holds the nodes from j up to, not including,
-    // anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)), doubling the
-    // covered distance. The root is its own ancestor (mask {0}), and depth <= ks, so
-    // ceil(log2(ks + 1)) rounds reach it from every node.
-    uint4 mk = make_uint4(0, 0, 0, 0);
-    if (tid <= ks) {
-        const int b = tid;
-        mk.x = b < 32 ? 1u << b : 0u;
-        mk.y = b >= 32 && b < 64 ? 1u << (b - 32) : 0u;
-        mk.z = b >= 64 && b < 96 ? 1u << (b - 64) : 0u;
-        mk.w = b >= 96 ? 1u << (b - 96) : 0u;
-        s_anc[tid] = tid == 0 ? 0 : par_i;
-        s_mask[tid] = mk;
-    }
-    __syncthreads();
-    for (int reach = 1; reach <= ks; reach *= 2) {
-        int a2 = 0;
-        uint4 m2 = make_uint4(0, 0, 0, 0);
-        if (tid <= ks) {
-            const int a = s_anc[tid];
-            a2 = s_anc[a];
-            m2 = s_mask[a];
-        }
-        __syncthreads();
-        if (tid <= ks) {
-            mk.x |= m2.x;
-            mk.y |= m2.y;
-            mk.z |= m2.z;
-            mk.w |= m2.w;
-            s_anc[tid] = a2;
-            s_mask[tid] = mk;
-        }
-        __syncthreads();
-    }
-    if (tid <= ks) tree_mask[(size_t)s * (kmax + 1) + tid] = mk;
 }
 
 // ---------------------------------------------------------------------------
@@ -375,16 +211,15 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // ---------------------------------------------------------------------------
 // attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
-// Register budget: D = 256 two workgroups per CU (64 KB of LDS each); D <= 128 four
-// for tree rows (32 KB each) and three for chain rows, whose workgroups also do the
-// prep kernel's work (at four the extra registers spill: measured slower).
+// Register budget: three workgroups per CU at D <= 128 (32 KB of LDS each; at four
+// the checks, records and append spilled registers and measured slower), two at
+// D = 256 (64 KB each).
 template <int D, bool TREE>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ k, const SeqInfo* __restrict__ info, int Hq, int Hkv,
-    float scale_log2, int split, int n_splits, float2* __restrict__ part_ml,
-    float* __restrict__ part_o, const uint4* __restrict__ tree_mask, int kmax,
+    const int32_t* __restrict__ k, int Hq, int Hkv, float scale_log2, int split, int n_splits,
+    float2* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ parent, int kmax,
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, int64_t n_pages, int B, int R,
     int32_t* __restrict__ status, RowRec* __restrict__ rows, int32_t* __restrict__ packing_ok,
     u16* k_pool_w, u16* v_pool_w) {
@@ -394,7 +229,8 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void a
     constexpr int BLK_CH = BLK / 8;              // 16-byte chunks per block
     constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
     __shared__ __attribute__((aligned(16))) u16 smem[8 * BLK];   // K0..K3, V0..V3
-    __shared__ uint4 s_mk[TREE ? kRowsPerGroup : 1];              // tree rows: ancestor masks
+    __shared__ int s_anc[TREE ? kMaxTreeNodes : 1];               // tree rows: ancestor links
+    __shared__ uint4 s_mask[TREE ? kMaxTreeNodes : 1];            // tree rows: ancestor masks
 
     // kv head fastest: the workgroups of one (sequence, split) start together and
     // fetch the Hkv blocks of each page (adjacent in the pool) at about the same time
@@ -416,57 +252,55 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void a
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int G = Hq / Hkv;
     const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
-    // tree rows: this lane's ancestor mask (row clamped to the table; unused lanes
-    // discard it), requested with the metadata and parked in LDS for the tiles that
-    // reach past pos
-    uint4 mk = make_uint4(0, 0, 0, 0);
-    if (TREE) mk = tree_mask[(size_t)s * (kmax + 1) + min((m_tile0 + l16) / G, kmax)];
+    // tree rows: thread i's node parent (clamped to the table), requested with the metadata
+    int par_i = 0;
+    if (TREE) par_i = parent[(size_t)s * (kmax + 1) + min(tid, kmax)];
     const int ks = k[s], P0 = pos[s];
-    int off;           // the sequence's first packed row
-    bool ok;           // this workgroup may read its pages and write partials
-    int basic = 0;     // chain rows: packing and position flags
-    bool packed = true;
-    if constexpr (TREE) {
-        const SeqInfo si = info[s];   // formed by the prep kernel (which also builds the masks)
-        off = si.off;
-        ok = si.valid;
-    } else {
-        // Chain rows need no prep kernel: every wave forms the row packing on its own
-        // (each k is read by every wave, from cache), and the workgroup's own page ids
-        // are checked before any of its tiles is read. The whole page list is checked
-        // at the end by the workgroups that write the sequence's records or append its
-        // rows, the only writes a flagged sequence must not make.
-        long long before = 0, total = 0;
-        int rowbad = 0;
-        for (int i = lane; i < B; i += kWave) {
-            const long long kk = k[i];
-            total += kk + 1;
-            if (i < s) before += kk + 1;
-            rowbad |= kk < 0;
-        }
-#pragma unroll
-        for (int d = 32; d > 0; d >>= 1) {
-            before += __shfl_xor(before, d);
-            total += __shfl_xor(total, d);
-            rowbad |= __shfl_xor(rowbad, d);
-        }
-        // wave-uniform: kept in scalar registers
-        packed = __builtin_amdgcn_readfirstlane(!rowbad && total == (long long)R);
-        off = __builtin_amdgcn_readfirstlane((int)before);
-        const bool pos_ok = P0 >= 0 && (ks < 0 || ((long long)P0 + ks) / kPage < max_pages);
-        if (!packed || ks > kmax) basic |= SPEC_STATUS_BAD_ROWS;
-        if (!pos_ok) basic |= SPEC_STATUS_BAD_POS;
-        bool own_bad = false;
-        if (!basic) {
-            const int hi = min((P0 + ks) / kPage, pg0 + split / kPage - 1);
-#pragma unroll
-            for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
-                const int p = pg0 + r * kWave + lane;
-                if (p <= hi && (pid[r] < 0 || (int64_t)pid[r] >= n_pages)) own_bad = true;
-            }
-        }
-        ok = __builtin_amdgcn_readfirstlane(!basic && __ballot(own_bad) == 0ull);   // the same for every wave
+    // The sequence's checks and records, with no kernel of their own: every wave forms
+    // the row packing on its own (each k is read by every wave, from cache), and the
+    // workgroup checks its positions, the parent list (tree rows) and its own page ids
+    // before any of its tiles is read. The whole page list is checked at the end by the
+    // workgroups that write the sequence's records or append its rows, the only writes
+    // a flagged sequence must not make.
+    long long before = 0, total = 0;
+    int rowbad = 0;
+    for (int i = lane; i < B; i += kWave) {
+        const long long kk = k[i];
+        total += kk + 1;
+        if (i < s) before += kk + 1;
+        rowbad |= kk < 0;
     }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        before += __shfl_xor(before, d);
+        total += __shfl_xor(total, d);
+        rowbad |= __shfl_xor(rowbad, d);
+    }
+    // wave-uniform: kept in scalar registers
+    const bool packed = __builtin_amdgcn_readfirstlane(!rowbad && total == (long long)R);
+    const int off = __builtin_amdgcn_readfirstlane((int)before);    // the sequence's first packed row
+    const bool pos_ok = P0 >= 0 && (ks < 0 || ((long long)P0 + ks) / kPage < max_pages);
+    int basic = 0;     // packing and position flags
+    if (!packed || ks > kmax) basic |= SPEC_STATUS_BAD_ROWS;
+    if (!pos_ok) basic |= SPEC_STATUS_BAD_POS;
+    // tree rows: node i's parent must come before it (the root's is -1)
+    bool tree_bad = false;
+    if constexpr (TREE) {
+        bool bad = false;
+        if (ks >= 0 && ks <= kmax && tid <= ks) bad = tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid);
+        tree_bad = __syncthreads_or(bad) != 0;
+    }
+    bool own_bad = false;
+    if (!basic) {
+        const int hi = min((P0 + ks) / kPage, pg0 + split / kPage - 1);
+#pragma unroll
+        for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
+            const int p = pg0 + r * kWave + lane;
+            if (p <= hi && (pid[r] < 0 || (int64_t)pid[r] >= n_pages)) own_bad = true;
+        }
+    }
+    // this workgroup may read its pages and write partials (the same for every wave)
+    const bool ok = __builtin_amdgcn_readfirstlane(!basic && !tree_bad && __ballot(own_bad) == 0ull);
     const int T = ks + 1, M = G * T, last = P0 + T - 1;
     if (ok && c0 <= last && mgroup * kRowsPerGroup < M) {
     const int c1 = min(c0 + split, last + 1);
@@ -558,7 +392,7 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void a
     auto use_tile = [&](int t0, const uint4 (&stg)[PER_THREAD], auto refill) {
         __syncthreads();  // previous tile's LDS reads are done
         store_tile(t0, stg);
-        if (!TREE && t0 + kKT > P0) {
+        if (t0 + kKT > P0) {
             __syncthreads();   // the staged pool bytes are in place
             new_rows_tile(t0);
         }
@@ -568,15 +402,49 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void a
         // full: every row keeps every key of the tile (chain: the tile ends at or before
         // the first row's position; tree: at or before the root)
         const bool full = t0 + kKT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
-        const uint64_t win = (TREE && !full) ? tree_window(s_mk[wave * 16 + l16], t0 - P0 + 64) : 0ull;
+        const uint64_t win = (TREE && !full) ? tree_window(s_mask[jrow], t0 - P0 + 64) : 0ull;
         const LdsTile<D> src{smem + lane * 8, smem + 4 * BLK + lane * 4};
         TM::template run<TREE>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
     };
     // The next tile is requested into registers while the current one is used from LDS.
     uint4 stage[PER_THREAD];
     load_tile(c0, stage);
-    // after the first tile's loads are issued, so that they do not wait on the mask
-    if (TREE && lq == 0) s_mk[wave * 16 + l16] = mk;   // read after the first tile's barriers
+    if constexpr (TREE) {
+        // Ancestor masks, built while the first tile's loads are in flight (nodes past
+        // k_s are never read). Invariant: mask(j) holds the nodes from j up to, not
+        // including, anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)),
+        // doubling the covered distance. The root is its own ancestor (mask {0}), and
+        // depth <= ks, so ceil(log2(ks + 1)) rounds reach it from every node.
+        uint4 mk = make_uint4(0, 0, 0, 0);
+        if (tid <= ks) {
+            mk.x = tid < 32 ? 1u << tid : 0u;
+            mk.y = tid >= 32 && tid < 64 ? 1u << (tid - 32) : 0u;
+            mk.z = tid >= 64 && tid < 96 ? 1u << (tid - 64) : 0u;
+            mk.w = tid >= 96 ? 1u << (tid - 96) : 0u;
+            s_anc[tid] = tid == 0 ? 0 : par_i;
+            s_mask[tid] = mk;
+        }
+        __syncthreads();
+        for (int reach = 1; reach <= ks; reach *= 2) {
+            int a2 = 0;
+            uint4 m2 = make_uint4(0, 0, 0, 0);
+            if (tid <= ks) {
+                const int an = s_anc[tid];
+                a2 = s_anc[an];
+                m2 = s_mask[an];
+            }
+            __syncthreads();
+            if (tid <= ks) {
+                mk.x |= m2.x;
+                mk.y |= m2.y;
+                mk.z |= m2.z;
+                mk.w |= m2.w;
+                s_anc[tid] = a2;
+                s_mask[tid] = mk;
+            }
+            __syncthreads();
+        }
+    }
     for (int t0 = c0; t0 < c1; t0 += kKT)
         use_tile(t0, stage, [&] {
             if (t0 + kKT < c1) load_tile(t0 + kKT, stage);
@@ -586,14 +454,14 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? (TREE ? 4 : 3) : 2) void a
         store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
     }
     }   // this workgroup's tiles
-    if constexpr (!TREE) {
+    {
         // the sequence's records (one workgroup per sequence) and the append of this kv
         // head's new rows that fall in this split (the workgroups of row group 0)
         const bool lead = hk == 0 && c == 0 && mgroup == 0;
-        const bool writer = mgroup == 0 && !basic && c0 <= last && c0 + split > P0;
+        const bool writer = mgroup == 0 && !basic && !tree_bad && c0 <= last && c0 + split > P0;
         if (!lead && !writer) return;
-        int flags = basic;
-        if (!basic) {
+        int flags = basic | (tree_bad ? SPEC_STATUS_BAD_TREE : 0);
+        if (pos_ok && ks >= 0) {
             // 8 page ids per thread requested at once (clamped to the last page), then checked
             const int last_page = last / kPage;
             for (int pgb = tid; pgb <= last_page; pgb += kAttnThreads * 8) {
@@ -713,42 +581,37 @@ static int64_t split_count(int32_t max_pages, int32_t split) {
 }
 
 struct AttnWs {
-    size_t info_off, flag_off, rows_off, ml_off, o_off, mask_off, total;
+    size_t flag_off, rows_off, ml_off, o_off, total;
 };
 
-// tree_rows: ancestor masks kept for a tree call (B * (kmax + 1)), 0 for chains
-static AttnWs attn_ws_layout(int32_t B, int32_t R, int32_t Hq, int32_t D, int64_t n_splits,
-                             int64_t tree_rows = 0) {
+static AttnWs attn_ws_layout(int32_t R, int32_t Hq, int32_t D, int64_t n_splits) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     AttnWs w;
-    w.info_off = 0;
-    w.flag_off = up(sizeof(SeqInfo) * (size_t)B);
-    w.rows_off = w.flag_off + 256;
+    w.flag_off = 0;
+    w.rows_off = 256;
     w.ml_off = w.rows_off + up(sizeof(RowRec) * (size_t)R);
     w.o_off = w.ml_off + up(sizeof(float2) * (size_t)R * Hq * n_splits);
-    w.mask_off = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
-    w.total = w.mask_off + up(sizeof(uint4) * (size_t)tree_rows);
+    w.total = w.o_off + up(sizeof(float) * (size_t)R * Hq * n_splits * D);
     return w;
 }
 
 template <int D>
 static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* pt,
-                        int max_pages, const int32_t* pos, const int32_t* k, int kmax, const SeqInfo* info,
+                        int max_pages, const int32_t* pos, const int32_t* k, int kmax,
                         RowRec* rows, int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
-                        int split, int n_splits, float2* ml, float* po, u16* out, const uint4* tree_mask,
+                        int split, int n_splits, float2* ml, float* po, u16* out, const int32_t* parent,
                         const u16* k_new, const u16* v_new, int64_t n_pages, int32_t* status, hipStream_t st) {
     const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
-    if (tree_mask)
+    if (parent)
         hipLaunchKernelGGL((attn_split_kernel<D, true>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
-                           pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
-                           tree_mask, kmax, nullptr, nullptr, n_pages, B, R, nullptr, nullptr, nullptr, nullptr,
-                           nullptr);
+                           pt, max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax,
+                           k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
     else
         hipLaunchKernelGGL((attn_split_kernel<D, false>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
-                           pt, max_pages, pos, k, info, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po,
-                           tree_mask, kmax, k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
+                           pt, max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax,
+                           k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
                        rows, packing_ok, R, Hq, n_splits, ml, po, out);
@@ -772,7 +635,7 @@ size_t spec_verify_attn_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_
     (void)Hkv;
     if (B < 1 || R < 1 || Hq < 1 || D < 1 || max_pages < 1) return 0;
     const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
-    return sv::attn_ws_layout(B, R, Hq, D, sv::split_count(max_pages, split)).total;
+    return sv::attn_ws_layout(R, Hq, D, sv::split_count(max_pages, split)).total;
 }
 
 size_t spec_verify_attn_tree_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
@@ -780,7 +643,7 @@ size_t spec_verify_attn_tree_workspace_bytes(int32_t B, int32_t R, int32_t Hq, i
     (void)Hkv;
     if (B < 1 || R < 1 || Hq < 1 || D < 1 || max_pages < 1 || kmax < 0) return 0;
     const int32_t split = kv_split_tokens > 0 ? kv_split_tokens : spec_attn_split_tokens(max_pages);
-    return sv::attn_ws_layout(B, R, Hq, D, sv::split_count(max_pages, split), (int64_t)B * (kmax + 1)).total;
+    return sv::attn_ws_layout(R, Hq, D, sv::split_count(max_pages, split)).total;   // as the chain call
 }
 
 }  // extern "C"
@@ -814,31 +677,19 @@ static int verify_attn_impl(const char* name, const spec_bf16* q, const spec_bf1
     const int64_t n_splits = split_count(max_pages, split);
     if (n_splits * 2 * Hkv > 0x7fffffffLL || (long long)B * Hkv * n_splits > 0x7fffffffLL)
         return fail(SPEC_ECAPACITY, "%s: too many splits", name);
-    const AttnWs lay = attn_ws_layout(B, R, Hq, D, n_splits, parent ? (int64_t)B * (kmax + 1) : 0);
+    const AttnWs lay = attn_ws_layout(R, Hq, D, n_splits);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace))
         return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes, lay.total);
     char* ws = static_cast<char*>(workspace);
-    SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + lay.info_off);
     int32_t* packing_ok = reinterpret_cast<int32_t*>(ws + lay.flag_off);
     RowRec* rows = reinterpret_cast<RowRec*>(ws + lay.rows_off);
     float2* ml = reinterpret_cast<float2*>(ws + lay.ml_off);
     float* po = reinterpret_cast<float*>(ws + lay.o_off);
-    uint4* tree_mask = parent ? reinterpret_cast<uint4*>(ws + lay.mask_off) : nullptr;
     hipStream_t st = (hipStream_t)stream;
-    // enough workgroups per sequence that every thread appends at most kPrepItems chunks
-    const long long max_items = (long long)(kmax + 1) * Hkv * (D / 8);
-    const dim3 prep_grid(B, (unsigned)((max_items + kPrepItemsPerWg - 1) / kPrepItemsPerWg));
-    // chain rows: the split kernel does the prep kernel's checks, records and append
-    if (parent) {
-        hipLaunchKernelGGL(attn_prep_kernel, prep_grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                           n_pages, page_table, max_pages, pos, k, kmax, B, R, Hq, Hkv, D, split, info, rows,
-                           packing_ok, seq_status, parent, tree_mask);
-        SV_LAUNCH_CHECK(name);
-    }
     switch (D) {
-        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
-        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
-        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, info, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, tree_mask, k_new, v_new, n_pages, seq_status, st); break;
+        case 64: launch_attn<64>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, parent, k_new, v_new, n_pages, seq_status, st); break;
+        case 128: launch_attn<128>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, parent, k_new, v_new, n_pages, seq_status, st); break;
+        default: launch_attn<256>(q, k_pool, v_pool, page_table, max_pages, pos, k, kmax, rows, packing_ok, B, R, Hq, Hkv, scale, split, (int)n_splits, ml, po, out, parent, k_new, v_new, n_pages, seq_status, st); break;
     }
     SV_LAUNCH_CHECK(name);
     return SPEC_OK;

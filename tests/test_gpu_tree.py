@@ -19,7 +19,7 @@ import torch
 import oracle
 from greedy_draft_verify_amd import synth
 from tests.conftest import gpu_available
-from tests.helpers import (assert_close, bits, gpu_attn, gpu_attn_tree, gpu_tree_accept, i32,
+from tests.helpers import (assert_close, bits, gpu_attn, gpu_attn_tree, gpu_tree_accept, i32, oracle_attn,
                            oracle_attn_tree)
 from tests.test_gpu_kernels import _wl
 
@@ -280,3 +280,50 @@ def test_kv_compact_rejects_bad_paths(dev):
     oracle.kv_compact(kp_ref, vp_ref, x.page_table, x.page_table.shape[1], x.pos, path, acc, kmax,
                       np.array([1, 1, 0, 0], np.int32), B, wl.Hkv, wl.D)
     assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref)
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_attention_status_combinations_match_the_oracle(dev, tree):
+    """Each check reports on its own, as the oracle does: an undefined packing flags
+    every sequence BAD_ROWS and the page, position and parent checks still add their
+    bits to it; a flagged sequence writes nothing into the pool and leaves its rows."""
+    wl = TREE_CASES[1] if tree else _wl("cmb", 5, 1, 3, 40, 200, 8, 2, 64, 32)
+    x, parent = _tree_case(wl, 6, "trie") if tree else (synth.make_verify_inputs(wl, seed=6, with_lm_head=False), None)
+    B = len(x.pos)
+    pt = x.page_table.copy()
+    pt[1, 1] = -4                            # a page id out of range
+    pos = x.pos.copy()
+    pos[2] = -1                              # a negative position
+    if tree:
+        parent = parent.copy()
+        parent[1, 1] = 5                     # a parent after its node (with the bad page)
+        parent[3, 0] = 2                     # the root's parent must be -1
+    kmax = wl.kmax
+    for k_use in (x.k, x.k + np.eye(B, dtype=np.int32)[B - 1]):     # rows that add up, then rows that do not
+        R = x.R
+        y = synth.VerifyInputs(x.wl, pos, k_use, R, pt, x.n_pages, x.q, x.k_new, x.v_new, x.k_pool, x.v_pool,
+                               x.hidden, x.w, x.d2t)
+        if tree:
+            out, kp, vp, st = gpu_attn_tree(y, parent, dev)
+        else:
+            out, kp, vp, st = gpu_attn(y, dev, kmax=kmax)
+        _, st_ref = oracle.validate(pt, pt.shape[1], x.n_pages, pos, k_use, kmax, B, R)
+        if tree:
+            oracle.validate_tree(parent, kmax, k_use, B, st_ref)
+        assert np.array_equal(st, st_ref), (st, st_ref)
+        assert (st != 0).sum() >= 2
+        flagged = np.flatnonzero(st != 0)
+        if (st == 0).any():
+            off = np.concatenate([[0], np.cumsum(k_use + 1)])
+            o = out.float().cpu().numpy()
+            for s in flagged:
+                assert np.isnan(o[off[s]:off[s + 1]]).all()
+            good = [s for s in range(B) if st[s] == 0]
+            if tree:
+                ref_k, ref_v = oracle_attn_tree(y, parent, seqs=good)[2:4]
+            else:
+                ref_k, ref_v = oracle_attn(y, seqs=good)[2:4]
+            assert np.array_equal(bits(kp), ref_k) and np.array_equal(bits(vp), ref_v)
+        else:
+            assert np.isnan(out.float().cpu().numpy()).all()
+            assert np.array_equal(bits(kp), bits(x.k_pool)) and np.array_equal(bits(vp), bits(x.v_pool))
