@@ -28,10 +28,22 @@
 // finishes when; each logit is one MFMA chain over K in a fixed order, so a row's
 // result does not depend on R or the row group.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
 namespace sv {
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop
+// whose index is a compile-time constant in every copy of the body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kLmThreads = 256;
 constexpr int kLmNT = 2;                  // 16-entry vocabulary tiles per wave
@@ -104,8 +116,10 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
                                                 const uint4* s_sup, float2 (*s_ms)[16 * MT],
                                                 Best (*wbest)[16 * MT], unsigned long long* keys) {
     const int l16 = lane % 16, lq = lane / 16, b = lane & 3;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    // The row tiles are expanded at compile time: the body is too large for the
+    // unroller at MT = 8, and a loop-carried tile index would put acc in scratch memory.
+    static_for<MT>([&](auto mt_c) {
+        constexpr int mt = decltype(mt_c)::value;
         // this lane's Philox row: row 16 mt + 4 lq + b
         const int rb = min(r0 + mt * 16 + lq * 4 + b, R - 1);
         const uint32_t ca = (uint32_t)sa.row_ctr[2 * (size_t)rb], cb = (uint32_t)sa.row_ctr[2 * (size_t)rb + 1];
@@ -122,7 +136,13 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
                 const uint32_t send = sel == 0 ? w.x : sel == 1 ? w.y : sel == 2 ? w.z : w.w;
                 const int src = (lane & ~3) | ((b + d) & 3);
                 const uint32_t got = d == 0 ? send : (uint32_t)__shfl((int)send, src);
-                g[nt][(b + d) & 3] = gumbel(got);
+                // slot (b + d) % 4 differs per lane: select it with constant indices (a
+                // lane-dependent index would put g in scratch memory)
+                const float gv = gumbel(got);
+                const int slot = (b + d) & 3;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (slot == q) g[nt][q] = gv;
             }
         }
 #pragma unroll
@@ -138,7 +158,6 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
                 const int v = (tile0 + nt) * 16 + l16;
                 if (v >= V) continue;
                 const float z = acc[mt][nt][i] * sa.inv_t;
-                if (sa.z_out && r < R) sa.z_out[(size_t)r * V + v] = z;
                 ms_merge(m, sm, z, 1.f);
                 const int loc = v - vt * kLmVocabPerWg;
                 const uint32_t word = loc < 32 ? sup.x : loc < 64 ? sup.y : loc < 96 ? sup.z : sup.w;
@@ -169,7 +188,7 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
                 wbest[wave][rl] = Best{bv, bi};
             }
         }
-    }
+    });
     __syncthreads();
     if (tid < 16 * MT && r0 + tid < R) {
         const int r = r0 + tid;
@@ -183,6 +202,47 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
         }
         sa.part[(size_t)r * n_vt + vt] = make_float2(m, sm);
         if (bb.i != 0x7fffffff) atomicMax(keys + r, pack_best(bb));
+    }
+}
+
+// Dense drafts: every entry's z, staged through LDS two 16-row tiles at a time so
+// that each row's 128 entries of this group leave as 16-byte row-contiguous stores.
+constexpr int kZStride = kLmVocabPerWg + 4;   // LDS row stride (floats): spreads the 4 row groups over banks
+
+template <int MT>
+__device__ __forceinline__ void write_z(const f32x4 (&acc)[MT][kLmNT], const SampleArgs& sa, int r0, int R, int V,
+                                        int vt, int tid, int wave, int lane, float* zbuf) {
+    const int l16 = lane % 16, lq = lane / 16;
+    const bool vec = (V & 3) == 0;
+#pragma unroll
+    for (int m0 = 0; m0 < MT; m0 += 2) {
+        __syncthreads();   // the previous pass's reads of zbuf are done
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            if (m0 + mm >= MT) break;
+#pragma unroll
+            for (int nt = 0; nt < kLmNT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    zbuf[(mm * 16 + lq * 4 + i) * kZStride + (wave * kLmNT + nt) * 16 + l16] =
+                        acc[m0 + mm][nt][i] * sa.inv_t;
+        }
+        __syncthreads();
+        const int rows = (m0 + 1 < MT ? 2 : 1) * 16;
+        for (int c = tid; c < rows * (kLmVocabPerWg / 4); c += kLmThreads) {
+            const int rl = c / (kLmVocabPerWg / 4), q4 = c % (kLmVocabPerWg / 4);
+            const int r = r0 + m0 * 16 + rl;
+            const int v0 = vt * kLmVocabPerWg + q4 * 4;
+            if (r >= R || v0 >= V) continue;
+            const float4 val = *reinterpret_cast<const float4*>(zbuf + rl * kZStride + q4 * 4);
+            float* dst = sa.z_out + (size_t)r * V + v0;
+            if (vec && v0 + 3 < V) {
+                *reinterpret_cast<float4*>(dst) = val;
+            } else {
+                const float e4[4] = {val.x, val.y, val.z, val.w};
+                for (int e = 0; e < 4 && v0 + e < V; ++e) dst[e] = e4[e];
+            }
+        }
     }
 }
 
@@ -200,6 +260,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     __shared__ Best wbest[4][16 * MT];
     __shared__ uint4 s_sup[SAMPLE ? 16 * MT : 1];   // draft support inside this group, one bit per entry
     __shared__ float2 s_ms[SAMPLE ? 4 : 1][SAMPLE ? 16 * MT : 1];
+    __shared__ __attribute__((aligned(16))) float zbuf[SAMPLE ? 32 * kZStride : 4];
 
     // Logical tile: with several row groups, hardware workgroup i runs on XCD i % 8;
     // give the row groups of one vocabulary group consecutive slots of one XCD so
@@ -288,7 +349,11 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int loc = qt[e] - vt * kLmVocabPerWg;
-                if (qt[e] >= 0 && loc >= 0 && loc < kLmVocabPerWg) w[loc >> 5] |= 1u << (loc & 31);
+                if (qt[e] >= 0 && loc >= 0 && loc < kLmVocabPerWg) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)   // constant indices (see the noise transpose)
+                        if ((loc >> 5) == q) w[q] |= 1u << (loc & 31);
+                }
             }
             s_sup[tid] = make_uint4(w[0], w[1], w[2], w[3]);   // read after the K loop's barriers
         }
@@ -298,6 +363,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 
     if constexpr (SAMPLE) {
         sample_epilogue<MT>(acc, sa, r0, R, V, vt, n_vt, tile0, tid, wave, lane, s_sup, s_ms, wbest, keys);
+        if (sa.z_out) write_z<MT>(acc, sa, r0, R, V, vt, tid, wave, lane, zbuf);
         return;
     }
 

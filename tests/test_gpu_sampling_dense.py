@@ -211,3 +211,32 @@ def test_dense_pass_b16k4_rows(dev):
     dec = ref["gap_p"] > 5e-2 / T
     assert dec.mean() > 0.5
     assert np.array_equal(sp.cpu().numpy()[rows][dec], ref["sample_p"][dec])
+
+
+@pytest.mark.parametrize("R,V", [(37, 1001), (128, 1030), (200, 515), (1, 3)])
+def test_dense_pass_ragged_shapes(dev, R, V):
+    """z of every entry on ragged shapes: a vocabulary that is not a multiple of 4 (the
+    element-wise tail of the row stores) nor of a workgroup's 128 entries, an odd
+    number of 16-row tiles, 8 tiles, and two row groups; plus lse and the draw from p."""
+    import greedy_draft_verify_amd as gdv
+    H, T, seed = 256, 0.7, 77
+    print(f"dense pass R={R} V={V}", flush=True)
+    g = torch.Generator().manual_seed(R * 7 + V)
+    hidden = torch.randn((R, H), generator=g).to(torch.bfloat16)
+    w = (torch.randn((V, H), generator=g) / 8).to(torch.bfloat16)
+    row_ctr = np.stack([np.arange(R) + 3, np.full(R, 9)], 1).astype(np.int32)
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    lse = torch.zeros(R, device=dev)
+    sp = torch.zeros(R, dtype=torch.int32, device=dev)
+    z = torch.full((R, V), float("nan"), device=dev)
+    gdv.spec_lm_head_sample_dense(hidden.to(dev), wp, V, T, i32(row_ctr, dev), seed, lse, sp, z)
+    torch.cuda.synchronize()
+    logits = oracle.lm_head_logits(bits(hidden), bits(w), R, H, V)
+    zg = z.cpu().numpy().astype(np.float64)
+    ztol = (2e-2 + 1e-2 * np.abs(logits)) / T
+    assert (np.abs(zg - logits / T) <= ztol).all(), np.nanmax(np.abs(zg - logits / T))
+    ref = oracle.sample_rows(logits, T, np.zeros((R, 0), np.int32), np.zeros((R, 0), np.float32), row_ctr, seed)
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert (np.abs(lg - ref["lse"]) <= (2e-2 + 1e-2 * np.abs(ref["lse"])) / T).all()
+    dec = ref["gap_p"] > 5e-2 / T
+    assert np.array_equal(sp.cpu().numpy()[dec], ref["sample_p"][dec])
