@@ -1,11 +1,11 @@
 // spec_greedy_accept: greedy acceptance and position rollback, plus the library's
 // version and error-string entry points.
 //
-// One workgroup of 1024 threads: a block scan gives every sequence its row offset
-// (ragged packing), then each wave takes sequences in turn. Within a wave, lane j
-// compares draft j with the greedy token of row j; a ballot of the mismatches and
-// a count of trailing ones give the accepted length in one step (the device-side
-// prefix match of flashrt whole_step.py generate_speculative).
+// Workgroups of 1024 threads, each computing every sequence's row offset (ragged
+// packing) by a block scan and then taking its sequences, a wave per sequence.
+// Within a wave, lane j compares draft j with the greedy token of row j; a ballot
+// of the mismatches and a count of trailing ones give the accepted length in one
+// step (the device-side prefix match of flashrt whole_step.py generate_speculative).
 #include "common.h"
 
 namespace sv {
@@ -31,6 +31,13 @@ constexpr int kMaxStop = 16;
 
 // STOP: the emitted tokens end after the first stop token and after remaining[s]
 // tokens (oxinfer step, DSSD _commit); pos advances by the tokens emitted.
+//
+// Latency: each workgroup computes the row offsets itself (the scan reads only k)
+// and takes every (gridDim.x)-th group of 16 sequences, a wave per sequence. A
+// wave's first sequence has its scalars and drafts requested before the scan and
+// its greedy tokens right after it; the bonus token and the emitted tokens are then
+// taken from registers (draft j and row j live in lane j), so a sequence with
+// k < 64 costs two dependent global round trips.
 template <bool STOP>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int32_t* __restrict__ g, const int32_t* __restrict__ drafts, int kmax,
@@ -39,146 +46,134 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     int32_t* __restrict__ n_emit, int32_t* __restrict__ emit, int32_t* __restrict__ next_tok,
     int32_t* __restrict__ status, const int32_t* __restrict__ stop_ids, int n_stop,
     const int32_t* __restrict__ remaining, int32_t* __restrict__ done) {
-    __shared__ long long s_scan[kAcceptThreads];
+    constexpr int NW = kAcceptThreads / kWave;
+    __shared__ long long s_wsum[NW];
+    __shared__ int s_wbad[NW];
     __shared__ int s_off[kAcceptMaxB];
-    __shared__ int s_bad_k;
-    const int tid = threadIdx.x;
-    // -- row offsets (ragged packing)
-    const bool packing_ok = block_row_offsets<kAcceptThreads>(k, B, R, s_scan, s_off, &s_bad_k);
+    __shared__ int s_stop[kMaxStop];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    if (STOP && tid < n_stop) s_stop[tid] = stop_ids[tid];   // visible after the scan's barriers
 
-    // -- one wave per sequence
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int n_waves = kAcceptThreads / kWave;
-    for (int s = wave; s < B; s += n_waves) {
-        const int ks = k[s];
+    // the first sequence of this wave: requested before the scan
+    const int s_first = blockIdx.x * NW + wave;
+    int ks = 0, p = 0, lim = 0x7fffffff, x = 0;
+    if (s_first < B) {
+        ks = k[s_first];
+        p = pos_in[s_first];
+        if (STOP && remaining) lim = remaining[s_first];
+        if (lane < kmax) x = drafts[(size_t)s_first * kmax + lane];
+    }
+    const bool packing_ok = block_row_offsets<kAcceptThreads>(k, B, R, s_wsum, s_wbad, s_off);
+
+    for (int s = s_first; s < B; s += gridDim.x * NW) {
+        if (s != s_first) {
+            ks = k[s];
+            p = pos_in[s];
+            if (STOP && remaining) lim = remaining[s];
+            x = lane < kmax ? drafts[(size_t)s * kmax + lane] : 0;
+        }
         const int off = s_off[s];
         int bits = 0;
         if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
-        if (pos_in[s] < 0) bits |= SPEC_STATUS_BAD_POS;
-        int lim = 0x7fffffff;
-        if constexpr (STOP) {
-            if (remaining) {
-                lim = remaining[s];
-                if (!bits && lim < 1) bits = SPEC_STATUS_BAD_LIMIT;
-            }
-        }
+        if (p < 0) bits |= SPEC_STATUS_BAD_POS;
+        if (STOP && remaining && !bits && lim < 1) bits = SPEC_STATUS_BAD_LIMIT;
         int32_t* e = emit + (size_t)s * (kmax + 1);
-        if (bits) {
+        auto flag = [&](int why) {
             for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
             if (lane == 0) {
-                status[s] = bits;
+                status[s] = why;
                 accept_len[s] = -1;
                 n_emit[s] = 0;
                 next_tok[s] = -1;
-                pos_out[s] = pos_in[s];
+                pos_out[s] = p;
                 if constexpr (STOP) done[s] = 0;
             }
+        };
+        if (bits) {
+            flag(bits);
             continue;
         }
-        // first mismatch, 64 drafts at a time; token range checks over every used draft
-        int a = ks;
+        // rows off .. off + ks are in range (the packing is defined); lane j < 64 holds
+        // draft j mapped (x0) and the greedy token of row j (g0)
+        const int g0 = lane <= ks ? g[off + lane] : 0;
         bool bad_tok = false;
-        for (int base = 0; base < ks; base += kWave) {
+        auto map_draft = [&](int xv, bool& bad) {
+            if (d2t) {
+                if (xv < 0 || xv >= n_draft_vocab) {
+                    bad = true;
+                    return 0;
+                }
+                const int m = d2t[xv];
+                if (m < 0 || m >= V) bad = true;
+                return m;
+            }
+            if (xv < 0 || xv >= V) bad = true;
+            return xv;
+        };
+        const int x0 = lane < ks ? map_draft(x, bad_tok) : 0;
+        // first mismatch; token range checks over every used draft
+        int a = ks;
+        {
+            const unsigned long long mm = __ballot(lane < ks && (bad_tok || x0 != g0));
+            if (mm) a = (int)__builtin_ctzll(mm);
+        }
+        for (int base = kWave; base < ks; base += kWave) {
             const int j = base + lane;
             bool miss = false;
             if (j < ks) {
-                const int x = drafts[(size_t)s * kmax + j];
-                int mapped = x;
-                if (d2t) {
-                    if (x < 0 || x >= n_draft_vocab) {
-                        bad_tok = true;
-                    } else {
-                        mapped = d2t[x];
-                        if (mapped < 0 || mapped >= V) bad_tok = true;
-                    }
-                } else if (x < 0 || x >= V) {
-                    bad_tok = true;
-                }
-                miss = bad_tok || mapped != g[off + j];
+                const int mj = map_draft(drafts[(size_t)s * kmax + j], bad_tok);
+                miss = bad_tok || mj != g[off + j];
             }
             const unsigned long long mm = __ballot(miss);
             if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
         }
         if (__ballot(bad_tok)) {
-            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
-            if (lane == 0) {
-                status[s] = SPEC_STATUS_BAD_TOKEN;
-                accept_len[s] = -1;
-                n_emit[s] = 0;
-                next_tok[s] = -1;
-                pos_out[s] = pos_in[s];
-                if constexpr (STOP) done[s] = 0;
-            }
+            flag(SPEC_STATUS_BAD_TOKEN);
             continue;
         }
+        // token j of the output: mapped draft j for j < a, the greedy token of row a at a
+        const int g_a = a < kWave ? __shfl(g0, a) : g[off + a];
+        auto token = [&](int j) {
+            if (j == a) return g_a;
+            if (j < kWave) return x0;   // j == lane
+            const int xv = drafts[(size_t)s * kmax + j];
+            return d2t ? d2t[xv] : xv;
+        };
+        int c = a + 1;   // tokens emitted
         if constexpr (STOP) {
-            // out[j] = map(draft j) for j < a, out[a] = g[off + a]; c = up to and including the
-            // first stop token, then at most lim tokens
-            int c = a + 1;
+            // up to and including the first stop token, then at most lim tokens
             for (int base = 0; base <= a; base += kWave) {
                 const int j = base + lane;
                 bool is_stop = false;
                 if (j <= a) {
-                    int t;
-                    if (j < a) {
-                        const int x = drafts[(size_t)s * kmax + j];
-                        t = d2t ? d2t[x] : x;
-                    } else {
-                        t = g[off + a];
-                    }
-                    for (int q = 0; q < n_stop; ++q) is_stop |= t == stop_ids[q];
+                    const int t = token(j);
+                    for (int q = 0; q < n_stop; ++q) is_stop |= t == s_stop[q];
                 }
                 const unsigned long long mm = __ballot(is_stop);
                 if (mm && c == a + 1) c = base + (int)__builtin_ctzll(mm) + 1;
             }
-            const bool at_lim = c >= lim;
-            if (at_lim) c = lim;
-            int last = -1;
-            for (int j = lane; j <= kmax; j += kWave) {
-                int val = -1;
-                if (j < c) {
-                    if (j < a) {
-                        const int x = drafts[(size_t)s * kmax + j];
-                        val = d2t ? d2t[x] : x;
-                    } else {
-                        val = g[off + a];
-                    }
-                }
-                e[j] = val;
-                if (j == c - 1) last = val;
-            }
-            // the last emitted token, from the lane that wrote it
-            last = __shfl(last, (c - 1) % kWave);
-            if (lane == 0) {
+        }
+        const bool at_lim = c >= lim;
+        if (at_lim) c = lim;
+        int last = -1;
+        for (int j = lane; j <= kmax; j += kWave) {
+            const int val = j < c ? token(j) : -1;
+            e[j] = val;
+            if (j == c - 1) last = val;
+        }
+        // the last emitted token, from the lane that wrote it
+        last = __shfl(last, (c - 1) % kWave);
+        if (lane == 0) {
+            status[s] = 0;
+            accept_len[s] = a < c ? a : c;
+            n_emit[s] = c;
+            next_tok[s] = last;
+            pos_out[s] = p + c;
+            if constexpr (STOP) {
                 bool is_stop = false;
-                for (int q = 0; q < n_stop; ++q) is_stop |= last == stop_ids[q];
-                status[s] = 0;
-                accept_len[s] = a < c ? a : c;
-                n_emit[s] = c;
-                next_tok[s] = last;
-                pos_out[s] = pos_in[s] + c;
+                for (int q = 0; q < n_stop; ++q) is_stop |= last == s_stop[q];
                 done[s] = is_stop || at_lim;
             }
-            continue;
-        }
-        const int bonus = g[off + a];
-        for (int j = lane; j <= kmax; j += kWave) {
-            int val = -1;
-            if (j < a) {
-                const int x = drafts[(size_t)s * kmax + j];
-                val = d2t ? d2t[x] : x;
-            } else if (j == a) {
-                val = bonus;
-            }
-            e[j] = val;
-        }
-        if (lane == 0) {
-            const int p = pos_in[s];
-            status[s] = 0;
-            accept_len[s] = a;
-            n_emit[s] = a + 1;
-            next_tok[s] = bonus;
-            pos_out[s] = p + a + 1;
         }
     }
 }
@@ -283,7 +278,7 @@ int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kma
     if (d2t && n_draft_vocab < 1) return fail(SPEC_EINVAL, "spec_greedy_accept: d2t given with n_draft_vocab=%d", n_draft_vocab);
     if (!argmax || !k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !seq_status || (kmax > 0 && !drafts))
         return fail(SPEC_EINVAL, "spec_greedy_accept: null required pointer");
-    hipLaunchKernelGGL(accept_kernel<false>, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
+    hipLaunchKernelGGL(accept_kernel<false>, dim3(seq_grid(B, kAcceptThreads)), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
                        drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
                        n_emit, emit, next_tok, seq_status, nullptr, 0, nullptr, nullptr);
     SV_LAUNCH_CHECK("spec_greedy_accept");
@@ -306,7 +301,7 @@ int spec_greedy_accept_stop(const int32_t* argmax, const int32_t* drafts, int32_
     if (!argmax || !k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !done || !seq_status ||
         (kmax > 0 && !drafts) || (n_stop > 0 && !stop_ids))
         return fail(SPEC_EINVAL, "spec_greedy_accept_stop: null required pointer");
-    hipLaunchKernelGGL(accept_kernel<true>, dim3(1), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
+    hipLaunchKernelGGL(accept_kernel<true>, dim3(seq_grid(B, kAcceptThreads)), dim3(kAcceptThreads), 0, (hipStream_t)stream, argmax,
                        drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
                        n_emit, emit, next_tok, seq_status, stop_ids, n_stop, remaining, done);
     SV_LAUNCH_CHECK("spec_greedy_accept_stop");

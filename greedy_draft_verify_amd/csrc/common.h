@@ -109,39 +109,60 @@ __device__ __forceinline__ float unpack_value(unsigned long long key) {
 
 // ---- ragged row packing ------------------------------------------------------
 // Exclusive prefix sums of (k_s + 1) over s (the packed row offsets) for B <= the
-// size of s_off, by a block of NT threads (each a contiguous segment of sequences,
-// then a Hillis-Steele scan of the segment sums). Returns whether the packing is
-// defined: every k_s >= 0 and the sum equals R. Every thread must call it.
+// size of s_off, by a block of NT threads: each thread sums a contiguous segment of
+// sequences, a wave scans its segment sums by shuffles, and the wave totals are
+// exchanged once through LDS (s_wsum and s_wbad hold NT / 64 entries). Returns
+// whether the packing is defined: every k_s >= 0 and the sum equals R. Every
+// thread must call it; it has two workgroup barriers.
 template <int NT>
 __device__ __forceinline__ bool block_row_offsets(const int32_t* __restrict__ k, int B, int R,
-                                                  long long* s_scan, int* s_off, int* s_bad) {
-    const int tid = threadIdx.x;
-    if (tid == 0) *s_bad = 0;
-    __syncthreads();
+                                                  long long* s_wsum, int* s_wbad, int* s_off) {
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int per = (B + NT - 1) / NT;
     const int s0 = min(B, tid * per), s1 = min(B, s0 + per);
     long long local = 0;
+    bool bad = false;
     for (int s = s0; s < s1; ++s) {
         const int ks = k[s];
-        if (ks < 0) *s_bad = 1;
+        bad |= ks < 0;
         local += (long long)ks + 1;
     }
-    s_scan[tid] = local;
-    __syncthreads();
-    for (int d = 1; d < NT; d <<= 1) {
-        const long long v = tid >= d ? s_scan[tid - d] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
+    long long incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const long long o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
     }
-    const long long total = s_scan[NT - 1];
-    long long run = tid ? s_scan[tid - 1] : 0;
+    const bool wave_bad = __ballot(bad) != 0;
+    if (lane == kWave - 1) {
+        s_wsum[wave] = incl;
+        s_wbad[wave] = wave_bad;
+    }
+    __syncthreads();
+    long long before = 0, total = 0;
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const long long v = s_wsum[w];
+        total += v;
+        if (w < wave) before += v;
+        any_bad |= s_wbad[w];
+    }
+    long long run = before + incl - local;
     for (int s = s0; s < s1; ++s) {
         s_off[s] = (int)run;
-        run += (long long)k[s] + 1;
+        if (s + 1 < s1) run += (long long)k[s] + 1;
     }
     __syncthreads();
-    return total == (long long)R && !*s_bad;
+    return total == (long long)R && !any_bad;
+}
+
+// Workgroups for a walk kernel with a wave per sequence: one per NT / 64 sequences,
+// at most 64; each computes the row offsets itself (the scan reads only k).
+inline int seq_grid(int B, int NT) {
+    const int per = NT / kWave, n = (B + per - 1) / per;
+    return n < 64 ? n : 64;
 }
 
 // ---- host error reporting ---------------------------------------------------

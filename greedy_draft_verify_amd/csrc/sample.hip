@@ -6,9 +6,9 @@
 // rejection the row's residual draw is emitted; if every draft is kept, the bonus
 // row's draw from p.
 //
-// One workgroup of 1024 threads: the block scan of the greedy call gives the row
-// offsets, then one wave per sequence; lane j tests draft j (64 at a time) and a
-// ballot of the rejections gives the first one.
+// Workgroups of 1024 threads, each computing the row offsets by the block scan of
+// the greedy call, then a wave per sequence (16 sequences per workgroup); lane j
+// tests draft j (64 at a time) and a ballot of the rejections gives the first one.
 #include "common.h"
 
 namespace sv {
@@ -24,15 +24,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_accept_kernel(
     const int32_t* __restrict__ pos_in, int32_t* pos_out, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ n_emit, int32_t* __restrict__ emit, int32_t* __restrict__ next_tok,
     int32_t* __restrict__ status) {
-    __shared__ long long s_scan[kSampleThreads];
+    __shared__ long long s_wsum[kSampleThreads / kWave];
+    __shared__ int s_wbad[kSampleThreads / kWave];
     __shared__ int s_off[kSampleMaxB];
-    __shared__ int s_bad_k;
     const int tid = threadIdx.x;
-    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_scan, s_off, &s_bad_k);
+    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_wsum, s_wbad, s_off);
 
     const int wave = tid / kWave, lane = tid % kWave;
     constexpr int n_waves = kSampleThreads / kWave;
-    for (int s = wave; s < B; s += n_waves) {
+    for (int s = blockIdx.x * n_waves + wave; s < B; s += gridDim.x * n_waves) {
         const int ks = k[s];
         const int off = s_off[s];
         int bits = 0;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_accept_kernel(
 // ---------------------------------------------------------------------------
 // Dense draft distributions (DSSD _sample_verify with the draft head's full q):
 // q [R][V] and z [R][V] (= logit / T, from spec_lm_head_sample_dense). Three launches:
-//   dense_walk_kernel      one workgroup: row offsets, then a wave per sequence tests
+//   dense_walk_kernel      row offsets per workgroup, then a wave per sequence tests
 //                          u < p(x) / q(x) for its drafts (a ballot gives the first
 //                          rejection) and records (offset, accepted count, status);
 //   dense_residual_kernel  (vocabulary chunk, sequence): for a sequence with a
@@ -138,14 +138,14 @@ __global__ __launch_bounds__(kSampleThreads) void dense_walk_kernel(
     int n_draft_vocab, int V, int B, int R, const float* __restrict__ q, const float* __restrict__ z,
     const float* __restrict__ lse, const int32_t* __restrict__ row_ctr, uint32_t key0, uint32_t key1,
     const int32_t* __restrict__ pos_in, DenseRec* __restrict__ rec, unsigned long long* keys) {
-    __shared__ long long s_scan[kSampleThreads];
+    __shared__ long long s_wsum[kSampleThreads / kWave];
+    __shared__ int s_wbad[kSampleThreads / kWave];
     __shared__ int s_off[kSampleMaxB];
-    __shared__ int s_bad_k;
     const int tid = threadIdx.x;
-    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_scan, s_off, &s_bad_k);
+    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_wsum, s_wbad, s_off);
     const int wave = tid / kWave, lane = tid % kWave;
     constexpr int n_waves = kSampleThreads / kWave;
-    for (int s = wave; s < B; s += n_waves) {
+    for (int s = blockIdx.x * n_waves + wave; s < B; s += gridDim.x * n_waves) {
         const int ks = k[s];
         const int off = s_off[s];
         int bits = 0;
@@ -326,7 +326,7 @@ int spec_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, co
     if (!k || !lse || !sample_p || !sample_res || !row_ctr || !pos_in || !pos_out || !accept_len || !n_emit || !emit ||
         !next_tok || !seq_status || (kmax > 0 && (!drafts || (NQ > 0 && (!q_tok || !q_prob || !z_supp)))))
         return fail(SPEC_EINVAL, "spec_sample_accept: null required pointer");
-    hipLaunchKernelGGL(sample_accept_kernel, dim3(1), dim3(kSampleThreads), 0, (hipStream_t)stream, drafts, kmax, k,
+    hipLaunchKernelGGL(sample_accept_kernel, dim3(seq_grid(B, kSampleThreads)), dim3(kSampleThreads), 0, (hipStream_t)stream, drafts, kmax, k,
                        d2t, n_draft_vocab, V, B, R, q_tok, q_prob, NQ, lse, z_supp, sample_p, sample_res, row_ctr,
                        (uint32_t)seed, (uint32_t)(seed >> 32), pos_in, pos_out, accept_len, n_emit, emit, next_tok,
                        seq_status);
@@ -366,7 +366,7 @@ int spec_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32_t*
         reinterpret_cast<unsigned long long*>(ws + (((size_t)B * sizeof(DenseRec) + 255) & ~(size_t)255));
     hipStream_t st = (hipStream_t)stream;
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    hipLaunchKernelGGL(dense_walk_kernel, dim3(1), dim3(kSampleThreads), 0, st, drafts, kmax, k, d2t, n_draft_vocab, V,
+    hipLaunchKernelGGL(dense_walk_kernel, dim3(seq_grid(B, kSampleThreads)), dim3(kSampleThreads), 0, st, drafts, kmax, k, d2t, n_draft_vocab, V,
                        B, R, q, z, lse, row_ctr, k0, k1, pos_in, rec, keys);
     SV_LAUNCH_CHECK("spec_sample_accept_dense(walk)");
     const int n_chunks = (int)(((V + 3) / 4 + kDenseGroupsPerWg - 1) / kDenseGroupsPerWg);

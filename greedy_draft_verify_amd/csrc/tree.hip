@@ -2,8 +2,8 @@
 // path's K/V (DSSD fast.py, _tree_cycle and _star_cycle). Rows are the tree's nodes
 // in creation order; node i >= 1 carries draft i - 1 and sits in KV slot pos + i.
 //
-// spec_tree_accept: one workgroup of 1024 threads. A block scan gives every
-//   sequence its row offset, then each wave walks one sequence at a time. Lane l
+// spec_tree_accept: workgroups of 1024 threads, each computing every sequence's row
+//   offset by a block scan, then walking its 16 sequences, a wave per sequence. Lane l
 //   holds nodes l + 1 and l + 65 (parent, mapped draft token) and the greedy tokens
 //   of the rows they are; a walk step is one ballot per half ("children of the
 //   current node whose token is the current node's greedy token"), the lowest set
@@ -29,15 +29,15 @@ __global__ __launch_bounds__(kTreeAcceptThreads) void tree_accept_kernel(
     int n_draft_vocab, int V, int B, int R, const int32_t* __restrict__ pos_in, int32_t* pos_out,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ n_emit, int32_t* __restrict__ emit,
     int32_t* __restrict__ next_tok, int32_t* __restrict__ path, int32_t* __restrict__ status) {
-    __shared__ long long s_scan[kTreeAcceptThreads];
+    __shared__ long long s_wsum[kTreeAcceptThreads / kWave];
+    __shared__ int s_wbad[kTreeAcceptThreads / kWave];
     __shared__ int s_off[kTreeMaxB];
-    __shared__ int s_bad_k;
     const int tid = threadIdx.x;
-    const bool packing_ok = block_row_offsets<kTreeAcceptThreads>(k, B, R, s_scan, s_off, &s_bad_k);
+    const bool packing_ok = block_row_offsets<kTreeAcceptThreads>(k, B, R, s_wsum, s_wbad, s_off);
 
     const int wave = tid / kWave, lane = tid % kWave;
     constexpr int n_waves = kTreeAcceptThreads / kWave;
-    for (int s = wave; s < B; s += n_waves) {
+    for (int s = blockIdx.x * n_waves + wave; s < B; s += gridDim.x * n_waves) {
         const int ks = k[s];
         const int off = s_off[s];
         int bits = 0;
@@ -254,7 +254,7 @@ int spec_tree_accept(const int32_t* argmax, const int32_t* drafts, int32_t kmax,
     if (!argmax || !k || !parent || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok ||
         !seq_status || (kmax > 0 && (!drafts || !path)))
         return fail(SPEC_EINVAL, "spec_tree_accept: null required pointer");
-    hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(kTreeAcceptThreads), 0, (hipStream_t)stream, argmax,
+    hipLaunchKernelGGL(tree_accept_kernel, dim3(seq_grid(B, kTreeAcceptThreads)), dim3(kTreeAcceptThreads), 0, (hipStream_t)stream, argmax,
                        drafts, kmax, k, parent, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len, n_emit,
                        emit, next_tok, path, seq_status);
     SV_LAUNCH_CHECK("spec_tree_accept");
