@@ -82,7 +82,8 @@ def _check_rows(got, ref, what, min_decided=0.8):
 
 
 @pytest.mark.parametrize("R,V,NQ,T", [(37, 1000, 4, 0.7), (80, 1000, 8, 1.0), (160, 4099, 1, 1.3),
-                                      (300, 2048, 0, 1.0), (5, 130, 8, 0.5)])
+                                      (300, 2048, 0, 1.0), (5, 130, 8, 0.5), (96, 2000, 3, 1.1),
+                                      (128, 1000, 8, 0.9), (256, 1030, 2, 0.8)])
 def test_lm_head_sample_parity(dev, R, V, NQ, T):
     import greedy_draft_verify_amd as gdv
     print(f"lm_head sample R={R} V={V} NQ={NQ} T={T}", flush=True)
