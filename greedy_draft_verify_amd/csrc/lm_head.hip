@@ -246,13 +246,19 @@ __device__ __forceinline__ void write_z(const f32x4 (&acc)[MT][kLmNT], const Sam
     }
 }
 
-// SHARED: other row groups re-read this vocabulary group's W through the XCD's L2,
-// so W is loaded with the default cache policy instead of as a stream.
-template <int MT, bool SHARED, bool SAMPLE = false>
+// NT: 16-entry vocabulary tiles per wave. At NT = 2 a workgroup covers one packed
+// group of 128 entries; at NT = 4 it covers two adjacent groups (wave w takes tiles
+// 2w, 2w + 1 of each), so every hidden fragment read from LDS feeds twice as many
+// MFMAs and the hidden rows are staged once per 256 entries (the packed layout is
+// the same). SHARED: other row groups re-read this vocabulary group's W through the
+// XCD's L2, so W is loaded with the default cache policy instead of as a stream.
+template <int MT, int NT, bool SHARED, bool SAMPLE = false>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, unsigned long long* __restrict__ keys, unsigned int* __restrict__ ticket,
     int32_t* __restrict__ argmax, float* __restrict__ maxval, SampleArgs sa) {
+    static_assert(NT == 2 || (NT == 4 && !SAMPLE), "the sampling epilogue covers one group per workgroup");
+    constexpr int GPW = NT / 2;                                 // packed groups per workgroup
     constexpr int HSTR = kLmKB + 8;                            // LDS row stride (elements)
     constexpr int HCH = 16 * MT * kLmKB / 8 / kLmThreads;     // hidden chunks per thread per K-block
     static_assert(HCH * kLmThreads * 8 == 16 * MT * kLmKB, "hidden staging must tile evenly");
@@ -275,12 +281,22 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const int r0 = rg * 16 * MT;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int l16 = lane % 16, lq = lane / 16;
-    const int tile0 = (vt * 4 + wave) * kLmNT;       // first 16-row W tile of this wave
+    const int tile0 = (vt * 4 + wave) * kLmNT;       // first 16-row W tile of this wave (NT = 2)
     const int nkb = H / kLmKB;
+    const int n_groups = (V + kLmVocabPerWg - 1) / kLmVocabPerWg;
+    // vocabulary entry of this lane's column in tile nt
+    auto vocab = [&](int nt) { return ((vt * GPW + nt / 2) * kLmTiles + wave * 2 + nt % 2) * 16 + l16; };
 
-    const u16* wt = wp + (((size_t)vt * nkb * kLmTiles + wave * kLmNT) * kLmKS * 64 + lane) * 8;
+    // this wave's fragments of group g (clamped: a workgroup's second group may not
+    // exist when the group count is odd; its entries are >= V and never kept)
+    auto group_base = [&](int g) {
+        return wp + (((size_t)min(g, n_groups - 1) * nkb * kLmTiles + wave * 2) * kLmKS * 64 + lane) * 8;
+    };
+    const u16* wt[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) wt[gi] = group_base(vt * GPW + gi);
     const size_t kb_stride = (size_t)kLmTiles * kLmKS * 512;   // elements per K-block of a group
-    uint4 ring[kLmKS][kLmNT], hnext[HCH];
+    uint4 ring[kLmKS][NT], hnext[HCH];
     // Rows past R re-read row R - 1: a row's logits depend on its own hidden row
     // only, and those rows' results are never written.
     auto load_h = [&](int kb) {
@@ -292,17 +308,18 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
         }
     };
     auto load_slot = [&](int kb, int s, uint4* dst) {
-        const u16* p = wt + (size_t)kb * kb_stride + s * 512;
 #pragma unroll
-        for (int nt = 0; nt < kLmNT; ++nt)
-            dst[nt] = SHARED ? ld16(p + nt * kLmKS * 512) : ld16_stream(p + nt * kLmKS * 512);
+        for (int nt = 0; nt < NT; ++nt) {
+            const u16* p = wt[nt / 2] + (size_t)kb * kb_stride + s * 512 + (nt % 2) * kLmKS * 512;
+            dst[nt] = SHARED ? ld16(p) : ld16_stream(p);
+        }
     };
 
-    f32x4 acc[MT][kLmNT];
+    f32x4 acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < kLmNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One K-block: publish its hidden rows in LDS, request the next block's hidden
     // rows, then per k-step: MFMAs, and re-request that ring slot for the next block.
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < kLmNT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
                     acc[mt][nt] = mfma16x16x32(a[mt], as_bf16x8(ring[s][nt]), acc[mt][nt]);
             if constexpr (more) load_slot(kb + 1, s, ring[s]);
         }
@@ -367,7 +384,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
         return;
     }
 
-    // epilogue: C[row = 16 mt + 4 lq + i][vocab = 16 (tile0 + nt) + l16]
+    // epilogue: C[row = 16 mt + 4 lq + i][vocab = vocab(nt)]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -375,8 +392,8 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
             float bv = -INFINITY;
             int bi = 0x7fffffff;
 #pragma unroll
-            for (int nt = 0; nt < kLmNT; ++nt) {
-                const int v = (tile0 + nt) * 16 + l16;
+            for (int nt = 0; nt < NT; ++nt) {
+                const int v = vocab(nt);
                 const float x = acc[mt][nt][i];
                 if (v < V && better(x, v, bv, bi)) {
                     bv = x;
@@ -427,18 +444,35 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 
 static int n_vtiles(int V) { return (V + kLmVocabPerWg - 1) / kLmVocabPerWg; }
 
-template <int MT, bool SAMPLE = false>
-static void launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
+// Four vocabulary tiles per wave (two packed groups per workgroup) for the greedy
+// pass when the rows need more than one row group of kLmMaxMT tiles (R > 128):
+// measured 5-10% faster there (R = 160: 280 vs 296 us, 256: 388 vs 420, 1024: 1287
+// vs 1437 at H = 4096, V = 151936) and slower at one row group (80: 221 vs 201).
+// Such row groups hold at most 7 tiles (8 tiles of 4 vocabulary tiles do not fit
+// the register file). A row's logits are the same MFMA chain either way, so the
+// results do not depend on the choice.
+constexpr int kLmMaxMTWide = 7;
+static bool lm_wide(int mtiles) { return mtiles > kLmMaxMT; }
+
+// n_vt: workgroups along the vocabulary (packed groups / (NT / 2), rounded up).
+// Returns false if no kernel variant fits (MT, n_rg); nothing is launched then.
+template <int MT, int NT, bool SAMPLE = false>
+static bool launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
                          unsigned long long* keys, unsigned int* ticket, int32_t* argmax, float* maxval,
                          hipStream_t st, const SampleArgs& sa = SampleArgs{}) {
     if (n_rg == 1) {
-        hipLaunchKernelGGL((lm_head_tile_kernel<MT, false, SAMPLE>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden, w,
-                           R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
-    } else if constexpr (MT >= 5) {   // several row groups always have >= 5 tiles each
-        const int grid = (n_vt * n_rg + 7) / 8 * 8;
-        hipLaunchKernelGGL((lm_head_tile_kernel<MT, true, SAMPLE>), dim3(grid), dim3(kLmThreads), 0, st, hidden, w,
-                           R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, NT, false, SAMPLE>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden,
+                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
+        return true;
     }
+    // several row groups have >= 5 tiles each (caps of 8), >= 4 (cap of 7)
+    if constexpr (MT >= 4) {
+        const int grid = (n_vt * n_rg + 7) / 8 * 8;
+        hipLaunchKernelGGL((lm_head_tile_kernel<MT, NT, true, SAMPLE>), dim3(grid), dim3(kLmThreads), 0, st, hidden,
+                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
+        return true;
+    }
+    return false;
 }
 
 // One workgroup per row: the row's softmax statistics from the groups' partials (a
@@ -567,16 +601,18 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
     SampleArgs sa{q_tok, row_ctr, part, z_supp, z_out, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
     hipStream_t st = (hipStream_t)stream;
     const spec_bf16* w = w_packed;
+    bool ok = false;
     switch (MT) {
-        case 1: launch_tiles<1, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 2: launch_tiles<2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 3: launch_tiles<3, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 4: launch_tiles<4, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 5: launch_tiles<5, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 6: launch_tiles<6, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        case 7: launch_tiles<7, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
-        default: launch_tiles<8, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 1: ok = launch_tiles<1, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 2: ok = launch_tiles<2, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 3: ok = launch_tiles<3, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 4: ok = launch_tiles<4, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 5: ok = launch_tiles<5, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 6: ok = launch_tiles<6, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        case 7: ok = launch_tiles<7, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
+        default: ok = launch_tiles<8, 2, true>(hidden, w, R, H, V, n_vt, n_rg, keys, nullptr, nullptr, nullptr, st, sa); break;
     }
+    if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
     SV_LAUNCH_CHECK(name);
     hipLaunchKernelGGL(sample_finalize_kernel, dim3(R), dim3(256), 0, st, part, n_vt, V, keys, q_tok, q_prob, NQ, row_ctr,
                        sa.key0, sa.key1, lse, z_supp, sample_p, sample_res);
@@ -637,16 +673,33 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
     const int MT = (mtiles + n_rg - 1) / n_rg;
     if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_argmax: grid too large");
     hipStream_t st = (hipStream_t)stream;
-    switch (MT) {
-        case 1: launch_tiles<1>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 2: launch_tiles<2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 3: launch_tiles<3>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 4: launch_tiles<4>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 5: launch_tiles<5>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 6: launch_tiles<6>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        case 7: launch_tiles<7>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        default: launch_tiles<8>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+    bool ok = false;
+    if (lm_wide(mtiles)) {
+        const int n_wg = (n_vt + 1) / 2;
+        const int n_rg_w = (mtiles + kLmMaxMTWide - 1) / kLmMaxMTWide;
+        const int MT_w = (mtiles + n_rg_w - 1) / n_rg_w;
+        switch (MT_w) {
+            case 1: ok = launch_tiles<1, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 2: ok = launch_tiles<2, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 3: ok = launch_tiles<3, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 4: ok = launch_tiles<4, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 5: ok = launch_tiles<5, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 6: ok = launch_tiles<6, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            default: ok = launch_tiles<7, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+        }
+    } else {
+        switch (MT) {
+            case 1: ok = launch_tiles<1, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 2: ok = launch_tiles<2, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 3: ok = launch_tiles<3, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 4: ok = launch_tiles<4, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 5: ok = launch_tiles<5, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 6: ok = launch_tiles<6, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 7: ok = launch_tiles<7, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            default: ok = launch_tiles<8, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        }
     }
+    if (!ok) return fail(SPEC_EINVAL, "spec_lm_head_argmax: no kernel variant for R=%d", R);
     SV_LAUNCH_CHECK("spec_lm_head_argmax");
     return SPEC_OK;
 }
