@@ -206,7 +206,9 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
 }
 
 // Dense drafts: every entry's z, staged through LDS two 16-row tiles at a time so
-// that each row's 128 entries of this group leave as 16-byte row-contiguous stores.
+// that each row's 128 entries of this group leave as 16-byte row-contiguous stores,
+// non-temporal: z is read back by later kernels, not by this one, and streaming it
+// past the L2 measured 233 vs 247 us for the b16k4 pass (222 with no z at all).
 constexpr int kZStride = kLmVocabPerWg + 4;   // LDS row stride (floats): spreads the 4 row groups over banks
 
 template <int MT>
@@ -237,7 +239,7 @@ __device__ __forceinline__ void write_z(const f32x4 (&acc)[MT][kLmNT], const Sam
             const float4 val = *reinterpret_cast<const float4*>(zbuf + rl * kZStride + q4 * 4);
             float* dst = sa.z_out + (size_t)r * V + v0;
             if (vec && v0 + 3 < V) {
-                *reinterpret_cast<float4*>(dst) = val;
+                __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w}, reinterpret_cast<f32x4*>(dst));
             } else {
                 const float e4[4] = {val.x, val.y, val.z, val.w};
                 for (int e = 0; e < 4 && v0 + e < V; ++e) dst[e] = e4[e];
