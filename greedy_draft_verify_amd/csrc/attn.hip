@@ -57,6 +57,7 @@ constexpr int kKT = 64;            // tokens per LDS tile of attn_split_kernel (
 constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kMaxRowsPerKvHead = 128;
 constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup handles
+constexpr int kStreamSplit = 1024; // splits of at least this many tokens read the pool non-temporally
 constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
 constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -213,8 +214,10 @@ __device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_
 // 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
 // Register budget: three workgroups per CU at D <= 128 (32 KB of LDS each; at four
 // the checks, records and append spilled registers and measured slower), two at
-// D = 256 (64 KB each).
-template <int D, bool TREE>
+// D = 256 (64 KB each). STREAM: the pool's K/V blocks are read with non-temporal
+// loads (chosen from the split size, i.e. from capacity; the cache policy never
+// changes a result).
+template <int D, bool TREE, bool STREAM>
 __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_ker
             const int pg = t0 / kPage + (b & 3);
             const bool real = t0 < c1 && pg <= last_page;
             const u16* base = (b < 4 ? k_pool : v_pool) + (size_t)(page_of(real ? pg : pg0) * Hkv + hk) * BLK;
-            dst[it] = ld16(base + ch * 8);
+            dst[it] = STREAM ? ld16_stream(base + ch * 8) : ld16(base + ch * 8);
         }
     };
     auto store_tile = [&](int t0, const uint4 (&src)[PER_THREAD]) {
@@ -604,14 +607,24 @@ static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* p
     const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
-    if (parent)
-        hipLaunchKernelGGL((attn_split_kernel<D, true>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
-                           pt, max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax,
-                           k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
-    else
-        hipLaunchKernelGGL((attn_split_kernel<D, false>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool,
-                           pt, max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax,
-                           k_new, v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
+    // Non-temporal pool reads for long contexts (splits of >= kStreamSplit tokens,
+    // i.e. page tables of more than 32K tokens): ragged 904 -> 837 us, long 442 ->
+    // 401 us; for short pools they were slower (b16k4 33.4 -> 36.0, b16tree 50.7 ->
+    // 57.1 us), so those keep the default policy.
+    auto go = [&](auto tree_c, auto stream_c) {
+        constexpr bool T = decltype(tree_c)::value, S = decltype(stream_c)::value;
+        hipLaunchKernelGGL((attn_split_kernel<D, T, S>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
+                           max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax, k_new,
+                           v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
+    };
+    const bool stream_kv = split >= kStreamSplit;
+    if (parent) {
+        if (stream_kv) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
+    } else {
+        if (stream_kv) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
+    }
     const long long items = (long long)R * Hq;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st,
                        rows, packing_ok, R, Hq, n_splits, ml, po, out);

@@ -54,14 +54,6 @@ constexpr int kLmKS = kLmKB / 32;         // MFMA k-steps per K-block
 constexpr int kLmMaxMT = 8;               // 16-row tiles per row group
 constexpr int kLmHAlign = 256;            // H must be a multiple of this
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming 16-byte load: W is touched once per call.
-__device__ __forceinline__ uint4 ld16_stream(const u16* p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 // Packed W: fragment f = (((g * H/128 + kb) * 8 + t) * 4 + s) * 64 + lane holds
 // W[128 g + 16 t + lane % 16][128 kb + 32 s + 8 (lane / 16) .. + 8] (zero past V).
 __global__ __launch_bounds__(256) void lm_head_pack_kernel(const u16* __restrict__ w, int V, int H,
