@@ -28,85 +28,129 @@ __global__ __launch_bounds__(kSampleThreads) void sample_accept_kernel(
     __shared__ int s_wbad[kSampleThreads / kWave];
     __shared__ int s_off[kSampleMaxB];
     const int tid = threadIdx.x;
-    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_wsum, s_wbad, s_off);
-
     const int wave = tid / kWave, lane = tid % kWave;
     constexpr int n_waves = kSampleThreads / kWave;
-    for (int s = blockIdx.x * n_waves + wave; s < B; s += gridDim.x * n_waves) {
-        const int ks = k[s];
+    // the first sequence of this wave: requested before the scan
+    const int s_first = blockIdx.x * n_waves + wave;
+    int ks = 0, p = 0, x = 0;
+    if (s_first < B) {
+        ks = k[s_first];
+        p = pos_in[s_first];
+        if (lane < kmax) x = drafts[(size_t)s_first * kmax + lane];
+    }
+    const bool packing_ok = block_row_offsets<kSampleThreads>(k, B, R, s_wsum, s_wbad, s_off);
+
+    for (int s = s_first; s < B; s += gridDim.x * n_waves) {
+        if (s != s_first) {
+            ks = k[s];
+            p = pos_in[s];
+            x = lane < kmax ? drafts[(size_t)s * kmax + lane] : 0;
+        }
         const int off = s_off[s];
         int bits = 0;
         if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
-        if (pos_in[s] < 0) bits |= SPEC_STATUS_BAD_POS;
+        if (p < 0) bits |= SPEC_STATUS_BAD_POS;
         int32_t* e = emit + (size_t)s * (kmax + 1);
-        int a = ks;
-        bool bad_tok = false;
-        if (!bits) {
-            for (int base = 0; base < ks; base += kWave) {
-                const int j = base + lane;
-                bool rej = false;
-                if (j < ks) {
-                    const int x = drafts[(size_t)s * kmax + j];
-                    int t = x;
-                    if (d2t) {
-                        if (x < 0 || x >= n_draft_vocab) {
-                            bad_tok = true;
-                        } else {
-                            t = d2t[x];
-                            if (t < 0 || t >= V) bad_tok = true;
-                        }
-                    } else if (x < 0 || x >= V) {
-                        bad_tok = true;
-                    }
-                    const size_t r = (size_t)off + j;
-                    int q_e = -1;
-                    for (int q = 0; q < NQ && !bad_tok; ++q)
-                        if (q_tok[r * NQ + q] == t && q_prob[r * NQ + q] > 0.f) {
-                            q_e = q;
-                            break;
-                        }
-                    if (q_e < 0) {
-                        bad_tok = true;
-                    } else {
-                        const float px = __expf(z_supp[r * NQ + q_e] - lse[r]);
-                        const uint4 w = philox10(make_uint4(0u, (uint32_t)row_ctr[2 * r], (uint32_t)row_ctr[2 * r + 1], 1u),
-                                                 key0, key1);
-                        rej = !(u01_23(w.x) < px / q_prob[r * NQ + q_e]);
-                    }
-                }
-                const unsigned long long mm = __ballot(rej);
-                if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
-            }
-            if (__ballot(bad_tok)) bits |= SPEC_STATUS_BAD_TOKEN;
-        }
-        if (bits) {
-            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
+        auto flag = [&](int why) {
+            for (int jj = lane; jj <= kmax; jj += kWave) e[jj] = -1;
             if (lane == 0) {
-                status[s] = bits;
+                status[s] = why;
                 accept_len[s] = -1;
                 n_emit[s] = 0;
                 next_tok[s] = -1;
-                pos_out[s] = pos_in[s];
+                pos_out[s] = p;
             }
+        };
+        if (bits) {
+            flag(bits);
             continue;
         }
+        // Rows off .. off + ks are in range (the packing is defined). Draft j (row
+        // off + j) maps to t; it is kept iff u_r < p(t) / q(t), where q(t) is the mass
+        // of the first support entry holding t with a positive mass (none: the draft
+        // is out of its support, BAD_TOKEN). A row's support, masses, z values, lse and
+        // counters are requested together.
+        auto test = [&](int j, int xv, int& t, bool& bad) {
+            t = xv;
+            if (d2t) {
+                if (xv < 0 || xv >= n_draft_vocab) {
+                    bad = true;
+                    return false;
+                }
+                t = d2t[xv];
+                if (t < 0 || t >= V) bad = true;
+            } else if (xv < 0 || xv >= V) {
+                bad = true;
+            }
+            if (bad) return false;
+            const size_t r = (size_t)off + j;
+            int qt[8];
+            float qp[8], zs[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                qt[q] = q < NQ ? q_tok[r * NQ + q] : -1;
+                qp[q] = q < NQ ? q_prob[r * NQ + q] : 0.f;
+                zs[q] = q < NQ ? z_supp[r * NQ + q] : 0.f;
+            }
+            const float lr = lse[r];
+            const uint32_t ca = (uint32_t)row_ctr[2 * r], cb = (uint32_t)row_ctr[2 * r + 1];
+            int q_e = -1;
+#pragma unroll
+            for (int q = 7; q >= 0; --q)   // the first match wins
+                if (q < NQ && qt[q] == t && qp[q] > 0.f) q_e = q;
+            if (q_e < 0) {
+                bad = true;
+                return false;
+            }
+            float zq = 0.f, pq = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (q == q_e) {
+                    zq = zs[q];
+                    pq = qp[q];
+                }
+            const float px = __expf(zq - lr);
+            const uint4 w = philox10(make_uint4(0u, ca, cb, 1u), key0, key1);
+            return !(u01_23(w.x) < px / pq);
+        };
+        int a = ks;
+        bool bad_tok = false;
+        int t0 = 0;   // lane j < 64: draft j mapped
+        for (int base = 0; base < ks; base += kWave) {
+            const int j = base + lane;
+            bool rej = false;
+            int t = 0;
+            if (j < ks) rej = test(j, base == 0 ? x : drafts[(size_t)s * kmax + j], t, bad_tok);
+            if (base == 0) t0 = t;
+            const unsigned long long mm = __ballot(rej);
+            if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
+        }
+        if (__ballot(bad_tok)) {
+            flag(SPEC_STATUS_BAD_TOKEN);
+            continue;
+        }
+        // the residual draw of the first rejected row, or the bonus row's draw from p
         const int tok = a < ks ? sample_res[off + a] : sample_p[off + ks];
-        for (int j = lane; j <= kmax; j += kWave) {
+        for (int jj = lane; jj <= kmax; jj += kWave) {
             int val = -1;
-            if (j < a) {
-                const int x = drafts[(size_t)s * kmax + j];
-                val = d2t ? d2t[x] : x;
-            } else if (j == a) {
+            if (jj < a) {
+                if (jj < kWave) {
+                    val = t0;   // jj == lane
+                } else {
+                    const int xv = drafts[(size_t)s * kmax + jj];
+                    val = d2t ? d2t[xv] : xv;
+                }
+            } else if (jj == a) {
                 val = tok;
             }
-            e[j] = val;
+            e[jj] = val;
         }
         if (lane == 0) {
             status[s] = 0;
             accept_len[s] = a;
             n_emit[s] = a + 1;
             next_tok[s] = tok;
-            pos_out[s] = pos_in[s] + a + 1;
+            pos_out[s] = p + a + 1;
         }
     }
 }
