@@ -44,7 +44,7 @@ ATTN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, 1024])   # 1024: pool read with non-temporal loads
 def test_tiny_workload_attention(dev, split):
     x = synth.make_verify_inputs("tiny", seed=0)
     out, kp, vp, st = gpu_attn(x, dev, kv_split_tokens=split)

@@ -51,7 +51,7 @@ def _tree_case(wl, seed, shape):
 
 @pytest.mark.parametrize("wl", TREE_CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("shape", ["trie", "star", "random"])
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, 1024])   # 1024: pool read with non-temporal loads
 def test_tree_attention_parity(dev, wl, shape, split):
     print(f"tree attention {wl.name} {shape} split={split}", flush=True)
     x, parent = _tree_case(wl, 0, shape)
@@ -76,7 +76,7 @@ def test_b16tree_attention_sampled(dev):
 
 
 @pytest.mark.parametrize("wl", TREE_CASES[:3], ids=lambda w: w.name)
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, 1024])
 def test_chain_tree_gives_chain_bytes(dev, wl, split):
     x = synth.make_verify_inputs(wl, seed=1, with_lm_head=False)
     parent = synth.make_parents(x.k, 1, wl.name, "chain", kmax=wl.kmax)
