@@ -33,29 +33,49 @@ __global__ __launch_bounds__(kTreeAcceptThreads) void tree_accept_kernel(
     __shared__ int s_wbad[kTreeAcceptThreads / kWave];
     __shared__ int s_off[kTreeMaxB];
     const int tid = threadIdx.x;
-    const bool packing_ok = block_row_offsets<kTreeAcceptThreads>(k, B, R, s_wsum, s_wbad, s_off);
-
     const int wave = tid / kWave, lane = tid % kWave;
     constexpr int n_waves = kTreeAcceptThreads / kWave;
-    for (int s = blockIdx.x * n_waves + wave; s < B; s += gridDim.x * n_waves) {
-        const int ks = k[s];
+    // A sequence's scalars, root parent and nodes c = lane + 1, lane + 65 (parent,
+    // draft) up to kmax; for a wave's first sequence they are requested before the
+    // row-offset scan, the greedy tokens right after it.
+    int ks = 0, p = 0, root = -1, par_k[2] = {-2, -2}, x_k[2] = {0, 0};
+    auto fetch = [&](int s) {
+        ks = k[s];
+        p = pos_in[s];
+        root = parent[(size_t)s * (kmax + 1)];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = lane + 1 + 64 * h;
+            par_k[h] = c <= kmax ? parent[(size_t)s * (kmax + 1) + c] : -2;
+            x_k[h] = c <= kmax ? drafts[(size_t)s * kmax + c - 1] : 0;
+        }
+    };
+    const int s_first = blockIdx.x * n_waves + wave;
+    if (s_first < B) fetch(s_first);
+    const bool packing_ok = block_row_offsets<kTreeAcceptThreads>(k, B, R, s_wsum, s_wbad, s_off);
+
+    for (int s = s_first; s < B; s += gridDim.x * n_waves) {
+        if (s != s_first) fetch(s);
         const int off = s_off[s];
         int bits = 0;
         if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
-        if (pos_in[s] < 0) bits |= SPEC_STATUS_BAD_POS;
+        if (p < 0) bits |= SPEC_STATUS_BAD_POS;
         int32_t* e = emit + (size_t)s * (kmax + 1);
         int32_t* ph = path + (size_t)s * kmax;
         // nodes c0 = lane + 1 and c1 = lane + 65: parent, mapped token, greedy token
         int par[2] = {-2, -2}, tok[2] = {-1, -1}, gn[2] = {0, 0};
+        int g_root = 0;
         if (!bits) {
-            if (lane == 0 && parent[(size_t)s * (kmax + 1)] != -1) bits |= SPEC_STATUS_BAD_TREE;
+            // rows off .. off + ks are in range (the packing is defined)
+            g_root = g[off];
+            if (root != -1) bits |= SPEC_STATUS_BAD_TREE;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int c = lane + 1 + 64 * h;
                 if (c > ks) continue;
-                par[h] = parent[(size_t)s * (kmax + 1) + c];
+                par[h] = par_k[h];
                 if (par[h] < 0 || par[h] >= c) bits |= SPEC_STATUS_BAD_TREE;
-                const int x = drafts[(size_t)s * kmax + c - 1];
+                const int x = x_k[h];
                 int mapped = x;
                 if (d2t) {
                     if (x < 0 || x >= n_draft_vocab) {
@@ -81,12 +101,12 @@ __global__ __launch_bounds__(kTreeAcceptThreads) void tree_accept_kernel(
                 accept_len[s] = -1;
                 n_emit[s] = 0;
                 next_tok[s] = -1;
-                pos_out[s] = pos_in[s];
+                pos_out[s] = p;
             }
             continue;
         }
         // the walk: u = current node, gu = its greedy token; lane d % 64 keeps step d
-        int u = 0, gu = g[off], a = 0;
+        int u = 0, gu = g_root, a = 0;
         int path_lo = -1, path_hi = -1, emit_lo = -1, emit_hi = -1;   // steps lane, lane + 64
         for (;;) {
             const unsigned long long lo = __ballot(par[0] == u && tok[0] == gu);
@@ -123,7 +143,7 @@ __global__ __launch_bounds__(kTreeAcceptThreads) void tree_accept_kernel(
             accept_len[s] = a;
             n_emit[s] = a + 1;
             next_tok[s] = gu;
-            pos_out[s] = pos_in[s] + a + 1;
+            pos_out[s] = p + a + 1;
         }
     }
 }
