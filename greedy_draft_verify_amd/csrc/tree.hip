@@ -162,7 +162,7 @@ __device__ __forceinline__ int v_blk_off(int t, int d) {
 
 // grid (B, item blocks): item = one K chunk (kv head, 8 channels) or one V channel
 // (kv head, channel) of the sequence; every workgroup of a sequence checks the path
-// on its own (the same reads, from cache) and gives up on the same verdict.
+// on its own (the same reads, from cache) and gives up on the same outcome.
 // No __restrict__ on the pools: sources and destinations share them.
 __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(
     u16* k_pool, u16* v_pool, int64_t n_pages, const int32_t* __restrict__ page_table, int max_pages,
