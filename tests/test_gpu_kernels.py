@@ -163,7 +163,8 @@ def synth_status(name):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("R,H,V", [(1, 256, 1), (4, 256, 1024), (5, 256, 1000), (17, 768, 4097),
                                    (80, 512, 3000), (96, 256, 129), (130, 256, 777), (300, 256, 2000),
-                                   (129, 256, 129), (200, 256, 100), (256, 512, 4097)])
+                                   (129, 256, 129), (200, 256, 100), (256, 512, 4097),
+                                   (112, 512, 1000), (120, 256, 3000)])
 def test_lm_head_shapes(dev, R, H, V):
     rng = np.random.default_rng(R * 1000 + V)
     h = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(torch.bfloat16)
