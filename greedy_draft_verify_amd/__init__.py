@@ -41,7 +41,7 @@ class _KPolicyStruct(ctypes.Structure):
     _fields_ = [("kmin", ctypes.c_int32), ("kmax", ctypes.c_int32), ("prior_p", ctypes.c_double),
                 ("prior_n", ctypes.c_double), ("draft_us", ctypes.c_double), ("n_points", ctypes.c_int32),
                 ("cost_rows", ctypes.c_double * SPEC_KPOLICY_MAXPTS), ("cost_us", ctypes.c_double * SPEC_KPOLICY_MAXPTS),
-                ("att", ctypes.c_double * SPEC_KPOLICY_MAXK), ("succ", ctypes.c_double * SPEC_KPOLICY_MAXK)]
+                ("tried", ctypes.c_double * SPEC_KPOLICY_MAXK), ("kept", ctypes.c_double * SPEC_KPOLICY_MAXK)]
 
 _lib = None
 

@@ -66,10 +66,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_accept_kernel(
             continue;
         }
         // Rows off .. off + ks are in range (the packing is defined). Draft j (row
-        // off + j) maps to t; it is kept iff u_r < p(t) / q(t), where q(t) is the mass
-        // of the first support entry holding t with a positive mass (none: the draft
-        // is out of its support, BAD_TOKEN). A row's support, masses, z values, lse and
-        // counters are requested together.
+        // off + j) maps to t; it is kept iff u_r < p(t) / q(t), where q(t) is the
+        // summed mass of the support entries holding t, the q of the residual draw
+        // (not positive: the draft is out of its support, BAD_TOKEN); p(t) comes from
+        // the z of the first entry holding t. A row's support, masses, z values, lse
+        // and counters are requested together.
         auto test = [&](int j, int xv, int& t, bool& bad) {
             t = xv;
             if (d2t) {
@@ -94,21 +95,20 @@ __global__ __launch_bounds__(kSampleThreads) void sample_accept_kernel(
             }
             const float lr = lse[r];
             const uint32_t ca = (uint32_t)row_ctr[2 * r], cb = (uint32_t)row_ctr[2 * r + 1];
-            int q_e = -1;
+            // entries in ascending order: the mass summed, the first entry's z kept
+            float zq = 0.f, pq = 0.f;
+            bool found = false;
 #pragma unroll
-            for (int q = 7; q >= 0; --q)   // the first match wins
-                if (q < NQ && qt[q] == t && qp[q] > 0.f) q_e = q;
-            if (q_e < 0) {
+            for (int q = 0; q < 8; ++q)
+                if (q < NQ && qt[q] == t) {
+                    if (!found) zq = zs[q];
+                    found = true;
+                    pq += qp[q];
+                }
+            if (!(pq > 0.f)) {
                 bad = true;
                 return false;
             }
-            float zq = 0.f, pq = 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (q == q_e) {
-                    zq = zs[q];
-                    pq = qp[q];
-                }
             const float px = __expf(zq - lr);
             const uint4 w = philox10(make_uint4(0u, ca, cb, 1u), key0, key1);
             return !(u01_23(w.x) < px / pq);

@@ -31,7 +31,8 @@
  * The method follows the page "span-02 engine/crates/model/src/spec.rs"
  * (module doc: ONE batched verify forward of B(k+1) rows over each branch's own
  * pages, KV appended in place at pos..pos+k, greedy acceptance, rollback by
- * advancing pos only, rejected KV never attended because kv_hi = position;
+ * advancing pos only; rows past the new pos hold stale KV that no later row reads,
+ * since each row's keys stop at its own position;
  * SpecReq: the KV slot of position p lives in page pages[p / 16]).
  *
  * Conventions shared by every entry point
@@ -194,8 +195,8 @@ int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_pac
 /* ---------------------------------------------------------------------------
  * spec_greedy_accept — greedy acceptance and rollback bookkeeping.
  *
- * Defined by: span-02 spec.rs module doc ("a token is emitted only if it equals
- * the target's argmax at the verify row before it"; rollback = pos advances by
+ * Defined by: span-02 spec.rs module doc (a draft survives only while it matches
+ * the target's greedy choice at the row that verifies it; rollback moves pos past
  * the accepted tokens) and step_chunk (next pos = pos + a + 1, next token = last
  * emitted); DSSD fast.py generate_spec (first miss stops; target[len(committed)]
  * appended as correction or bonus); oxinfer qwen_mtp.rs speculative_accept
@@ -441,15 +442,16 @@ int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int3
 
 /* spec_sample_accept — the chain walk. For sequence s (rows off_s .. off_s + k_s,
  * packed as for the greedy call) and j = 0 .. k_s - 1, row r = off_s + j, draft
- * x = map(drafts[s][j]) (d2t as in spec_greedy_accept) whose support entry e has
- * q_tok[r][e] == x and q_prob[r][e] > 0 (the first such entry):
- *   keep x iff u_r < exp(z_supp[r][e] - lse[r]) / q_prob[r][e]
+ * x = map(drafts[s][j]) (d2t as in spec_greedy_accept), q_x = the summed mass of
+ * the row's support entries holding x (the same q_v as the residual draw uses) and
+ * e the first entry holding x:
+ *   keep x iff u_r < exp(z_supp[r][e] - lse[r]) / q_x
  *   else emit sample_res[r] and stop;
  * if every draft is kept, emit sample_p[off_s + k_s]. Outputs as
  * spec_greedy_accept (accept_len, n_emit = accept_len + 1, emit [B][kmax + 1] with
  * -1 after the last token, next_tok = the drawn token, pos_out = pos_in +
- * accept_len + 1). A draft outside its row's support, or outside its vocabulary,
- * sets SPEC_STATUS_BAD_TOKEN; status bits and the outputs of a flagged sequence as
+ * accept_len + 1). A draft outside its row's support (q_x <= 0), or outside its
+ * vocabulary, sets SPEC_STATUS_BAD_TOKEN; status bits and the outputs of a flagged sequence as
  * spec_greedy_accept. lse, z_supp, sample_p and sample_res are the outputs of
  * spec_lm_head_sample for the same rows, row_ctr and seed.
  * Limits: 1 <= B <= 8192, 0 <= kmax <= 1024, R >= 1, V >= 1, 0 <= NQ <= 8. */
@@ -498,18 +500,20 @@ int spec_sample_accept_dense(const int32_t* drafts, int32_t kmax, const int32_t*
 /* ---------------------------------------------------------------------------
  * Adaptive draft depth (host side; no GPU work, no allocation).
  *
- * Defined by: span-02 spec.rs KPolicy (a running estimate of the conditional
- * acceptance of draft position j given that positions < j were kept, with prior
- * pseudo-counts; a piecewise-linear verify cost in the number of rows; k chosen to
- * minimise the expected time per emitted token) and oxinfer DraftCosts (the same
- * trade-off from measured round times and per-position acceptance rates).
- *   p_j       = (succ[j] + prior_p * prior_n) / (att[j] + prior_n)
- *   E(k)      = 1 + sum_{i=1..k} prod_{j<i} p_j        (tokens per sequence per cycle)
- *   verify(r) = the cost table at r rows: linear through the origin below the first
- *               point, linear between points, the last segment extended beyond
- *   choose(B) = argmin over k in kmin .. kmax of (verify(B (k + 1)) + k draft_us) / E(k)
- *               (the smaller k on ties); with row_cap > 0, k <= max(row_cap / B - 1, kmin)
- *   update(k, a): for j < k, att[j] += (j <= a), succ[j] += (j < a)
+ * Defined by: span-02 spec.rs KPolicy (a smoothed estimate of how often draft
+ * position j is kept once every earlier position was, a verify cost that grows
+ * piecewise linearly with the rows, and k picked for the least expected time per
+ * emitted token) and oxinfer DraftCosts (the same trade-off from measured round
+ * times and per-position acceptance rates). For positions j and depths k:
+ *   p_j       = (kept[j] + prior_p * prior_n) / (tried[j] + prior_n)
+ *   E(k)      = sum_{i=0..k} p_0 p_1 ... p_{i-1}   (kept drafts + the bonus; the
+ *               i = 0 term is 1)
+ *   verify(r) = the polyline through (0, 0) and the (cost_rows, cost_us) points,
+ *               its last piece continued past the last point
+ *   choose(B) = the smallest k in kmin .. kmax with the least
+ *               (verify(B (k + 1)) + k draft_us) / E(k); with row_cap > 0 the top
+ *               is lowered to max(row_cap / B - 1, kmin)
+ *   update(k, a): tried[j] += 1 for j < min(k, a + 1); kept[j] += 1 for j < min(k, a)
  * The caller owns the struct (plain data; copy it freely).
  * ------------------------------------------------------------------------- */
 #define SPEC_KPOLICY_MAXK 64
@@ -521,8 +525,8 @@ typedef struct {
     int32_t n_points;                 /* verify cost table: rows (increasing) -> us */
     double cost_rows[SPEC_KPOLICY_MAXPTS];
     double cost_us[SPEC_KPOLICY_MAXPTS];
-    double att[SPEC_KPOLICY_MAXK];    /* attempts of draft position j */
-    double succ[SPEC_KPOLICY_MAXK];   /* ... and how many were kept */
+    double tried[SPEC_KPOLICY_MAXK];  /* rounds that reached draft position j */
+    double kept[SPEC_KPOLICY_MAXK];   /* ... and kept its draft */
 } spec_kpolicy;
 
 /* Sets every field and zeroes the counters. EINVAL unless 0 <= kmin <= kmax < 64,

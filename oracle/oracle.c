@@ -723,13 +723,15 @@ void oracle_sample_rows(const double* logits, int32_t R, int32_t V, double T, co
  * row r = off_s + j, draft x = drafts[s][j] (a target id, or a draft-vocabulary id
  * mapped through d2t), q(x) = the mass of x in the row's q support:
  *   accept x iff u_r < p_r(x) / q(x)   (u_r the row's acceptance uniform; the
- *                                       probability is min(1, p / q))
+ *                                       probability is min(1, p / q); q(x) is
+ *                                       the summed mass of the support entries
+ *                                       holding x, the q the residual uses)
  *   else emit sample_res[r], stop.
  * If every draft is accepted, emit sample_p of the bonus row off_s + k_s.
  *   accept_len = accepted drafts, emit = accepted tokens ++ [the sampled token],
  *   pos_out = pos_in + accept_len + 1, next_tok = the sampled token.
- * Status bits as oracle_greedy_accept; a draft whose (mapped) id is not in its
- * row's q support with a positive mass sets ORC_BAD_TOKEN. */
+ * Status bits as oracle_greedy_accept; a draft whose (mapped) id has no positive
+ * summed mass in its row's q support sets ORC_BAD_TOKEN. */
 void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k, const int32_t* d2t,
                           int32_t n_draft_vocab, int32_t V, int32_t B, int32_t R, const int32_t* q_tok,
                           const float* q_prob, int32_t NQ, const double* lse, const double* z_supp,
@@ -752,6 +754,7 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
         int32_t* e = emit + (int64_t)s * (kmax + 1);
         for (int j = 0; j <= kmax; ++j) e[j] = -1;
         int supp_e[1024];
+        double supp_q[1024];
         if (!bits) {
             for (int j = 0; j < ks; ++j) {
                 const int32_t x = drafts[(int64_t)s * kmax + j];
@@ -768,12 +771,13 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
                 }
                 const int64_t r = off + j;
                 supp_e[j] = -1;
-                for (int q = 0; q < NQ; ++q)
-                    if (q_tok[r * NQ + q] == t && q_prob[r * NQ + q] > 0.f) {
+                supp_q[j] = 0.0;
+                for (int q = NQ - 1; q >= 0; --q)
+                    if (q_tok[r * NQ + q] == t) {
                         supp_e[j] = q;
-                        break;
+                        supp_q[j] += (double)q_prob[r * NQ + q];
                     }
-                if (supp_e[j] < 0) bits |= ORC_BAD_TOKEN;
+                if (supp_e[j] < 0 || !(supp_q[j] > 0.0)) bits |= ORC_BAD_TOKEN;
             }
         }
         if (bits) {
@@ -791,7 +795,7 @@ void oracle_sample_accept(const int32_t* drafts, int32_t kmax, const int32_t* k,
             const int q = supp_e[a];
             const double px = exp(z_supp[r * NQ + q] - lse[r]);
             const double u = oracle_accept_uniform(row_ctr + 2 * r, seed);
-            if (u < px / (double)q_prob[r * NQ + q]) {
+            if (u < px / supp_q[a]) {
                 e[a] = q_tok[r * NQ + q];
                 continue;
             }

@@ -148,6 +148,8 @@ def _accept_case(rng, B, kmax, V, NQ, T=1.0):
             # the support: n of the row's 2n most likely tokens, so that drafts are often kept
             top = np.argsort(logits[r])[::-1][:2 * n]
             toks = rng.choice(top, n, replace=False)
+            if n > 1 and rng.uniform() < 0.3:
+                toks[-1] = toks[0]                  # a token listed twice: its q is the summed mass
             w = rng.uniform(0.05, 1, n)
             q_tok[r, :n] = toks
             q_prob[r, :n] = (w / w.sum()).astype(np.float32)
@@ -181,8 +183,9 @@ def _undecided_seqs(c, seed=5):
     for s in range(c["B"]):
         for j in range(c["k"][s]):
             r = c["off"][s] + j
-            e = int(np.nonzero(c["q_tok"][r] == c["drafts"][s, j])[0][0])
-            ratio = math.exp(c["rows"]["z_supp"][r, e] - c["rows"]["lse"][r]) / float(c["q_prob"][r, e])
+            hold = np.nonzero(c["q_tok"][r] == c["drafts"][s, j])[0]
+            q_x = float(c["q_prob"][r, hold].astype(np.float64).sum())
+            ratio = math.exp(c["rows"]["z_supp"][r, hold[0]] - c["rows"]["lse"][r]) / q_x
             u = oracle.accept_uniform(c["row_ctr"][r], seed)
             if abs(u - ratio) <= 1e-4 * max(ratio, 1e-30):
                 out.add(s)

@@ -21,9 +21,9 @@ def test_acceptance_estimate_is_the_smoothed_rate():
     for a in (0, 1, 3, 3, 3, 4):       # rounds of k = 4 drafts with a kept
         pol.update(4, a)
     # position j is attempted when a >= j and kept when a > j
-    assert pol.att[:4] == [6, 5, 4, 4] and pol.succ[:4] == [5, 4, 4, 1]
+    assert pol.tried[:4] == [6, 5, 4, 4] and pol.kept[:4] == [5, 4, 4, 1]
     assert math.isclose(pol.p(0), (5 + 2) / (6 + 4)) and math.isclose(pol.p(3), (1 + 2) / (4 + 4))
-    assert pol.att[4] == 0
+    assert pol.tried[4] == 0
 
 
 def test_verify_cost_interpolates_the_table():

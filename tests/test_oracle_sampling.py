@@ -71,11 +71,20 @@ def test_gumbel_max_draws_follow_softmax_and_residual():
     assert np.isnan(out["z_supp"][0, 3])
 
 
-def _one_draft_batch(B, p_logits, p2_logits, q, rng, T=1.0):
-    """B sequences, one draft each, drawn from q; returns the emitted tokens."""
+def _one_draft_batch(B, p_logits, p2_logits, q, rng, T=1.0, support=None):
+    """B sequences, one draft each, drawn from q; returns the emitted tokens. The
+    support list is q's nonzero entries, or support = (tokens, masses), whose masses
+    summed per token must give q (a token may appear in several entries)."""
     V = len(p_logits)
     x = rng.choice(V, size=B, p=q)
-    supp = np.nonzero(q)[0]
+    if support is None:
+        supp = np.nonzero(q)[0]
+        masses = q[supp]
+    else:
+        supp, masses = (np.asarray(a) for a in support)
+        summed = np.zeros(V)
+        np.add.at(summed, supp, masses)
+        np.testing.assert_allclose(summed, q)
     NQ = len(supp)
     R = 2 * B
     logits = np.empty((R, V))
@@ -84,7 +93,7 @@ def _one_draft_batch(B, p_logits, p2_logits, q, rng, T=1.0):
     q_tok = np.full((R, NQ), -1, np.int32)
     q_prob = np.zeros((R, NQ), np.float32)
     q_tok[0::2] = supp
-    q_prob[0::2] = q[supp]
+    q_prob[0::2] = masses
     row_ctr = np.stack([np.repeat(np.arange(B), 2) * 0 + np.tile([100, 101], B), np.repeat(np.arange(B), 2)],
                        1).astype(np.int32)
     rows = oracle.sample_rows(logits, T, q_tok, q_prob, row_ctr, seed=99)
@@ -118,6 +127,31 @@ def test_speculative_sampling_emits_the_target_distribution(q):
     assert abs(acc.mean() - rate) < 5 * np.sqrt(rate * (1 - rate) / B)
     assert (res["emit"][acc, 0] == x[acc]).all()
     assert (res["pos_out"] == 100 + res["accept_len"] + 1).all()
+
+
+def test_duplicated_support_entries_still_emit_the_target_distribution():
+    """A token listed in several support entries has q = the entries' summed mass,
+    in the keep test as in the residual; keeping it with probability p / (one
+    entry's mass) instead would raise its acceptance rate and bias the emitted
+    tokens away from p."""
+    rng = np.random.default_rng(6)
+    B = 60000
+    p_logits = np.array([0.3, 1.2, -0.4, 0.8, 0.0])
+    p2_logits = np.array([-1.0, 0.0, 2.0, 0.5, 0.1])
+    q = np.array([0.5, 0.0, 0.3, 0.2, 0.0])
+    support = ([0, 2, 0, 3], [0.25, 0.3, 0.25, 0.2])
+    x, res = _one_draft_batch(B, p_logits, p2_logits, q, rng, support=support)
+    ok, info = _band(np.bincount(res["emit"][:, 0], minlength=5), _softmax(p_logits), B)
+    assert ok, info
+    acc = res["accept_len"] == 1
+    p = _softmax(p_logits)
+    kept0 = acc[x == 0].mean()
+    want0 = min(1.0, p[0] / q[0])
+    assert abs(kept0 - want0) < 5 * np.sqrt(want0 * (1 - want0) / (x == 0).sum())
+    rate = np.minimum(p, q).sum()
+    assert abs(acc.mean() - rate) < 5 * np.sqrt(rate * (1 - rate) / B)
+    ok, info = _band(np.bincount(res["emit"][acc, 1], minlength=5), _softmax(p2_logits), int(acc.sum()))
+    assert ok, info
 
 
 def test_zero_temperature_reduces_to_greedy_acceptance():

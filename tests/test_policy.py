@@ -47,7 +47,7 @@ def test_batch_update_skips_flagged_sequences():
     for kk, aa in zip(k, a):
         if aa >= 0:
             ref.update(int(kk), int(aa))
-    assert list(lib.st.att[:8]) == ref.att[:8] and list(lib.st.succ[:8]) == ref.succ[:8]
+    assert list(lib.st.tried[:8]) == ref.tried[:8] and list(lib.st.kept[:8]) == ref.kept[:8]
 
 
 def test_policy_argument_checks():
