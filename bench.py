@@ -142,6 +142,122 @@ def time_call(f, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / reps / 1e3
 
 
+def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
+    """Times one verify step: an eager loop of the three calls with HIP events on the
+    launch stream around each call, then the same step captured once as a HIP graph
+    and replayed (the launches' host overhead and gaps leave the step). Every replay
+    must reproduce the eager step's bytes."""
+    stream = torch.cuda.current_stream()
+
+    def run_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        step.attn()
+        if ev:
+            ev[1].record(stream)
+        step.lm_head()
+        if ev:
+            ev[2].record(stream)
+        step.accept()
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        run_step()
+    torch.cuda.synchronize()
+    assert (step.attn_status.cpu() == 0).all() and (step.acc_status.cpu() == 0).all()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        run_step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(stop) / steps
+    eager_out = step.outputs()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run_step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run_step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop) / steps
+    for a, b in zip(eager_out, step.outputs()):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "graph replay differs from the eager step"
+    del graph
+    return {"graph_ms": graph_ms, "eager_ms": eager_ms,
+            "attn_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+            "lm_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+            "acc_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))}
+
+
+def step_report(step: VerifyStep, t: dict) -> dict:
+    """Rates and rooflines of a timed verify step."""
+    x, wl = step.x, step.x.wl
+    acc_len = step.acc_len.cpu().numpy()
+    emitted = int((acc_len + 1).sum())
+    lm_b = lm_head_bytes(x.R, wl.H, wl.V)
+    at_b = attn_bytes(x)
+    lm_gbs = lm_b / (t["lm_ms"] / 1e3) / 1e9
+    at_gbs = at_b / (t["attn_ms"] / 1e3) / 1e9
+    lm_tflops = 2.0 * x.R * wl.H * wl.V / (t["lm_ms"] / 1e3) / 1e12
+    return {"rows": x.R, "step_us": t["graph_ms"] * 1e3, "eager_step_us": t["eager_ms"] * 1e3,
+            "rows_per_s": x.R / (t["graph_ms"] / 1e3), "emitted_tokens_per_s": emitted / (t["graph_ms"] / 1e3),
+            "emitted_per_step": emitted,
+            "accept_len_hist": np.bincount(acc_len, minlength=wl.kmax + 1).tolist(),
+            "kernel_us": {"spec_verify_attn": t["attn_ms"] * 1e3, "spec_lm_head_argmax": t["lm_ms"] * 1e3,
+                          "spec_greedy_accept": t["acc_ms"] * 1e3},
+            "attn": {"bound": "hbm", "algorithmic_bytes": at_b, "achieved": at_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS},
+            "lm_head": {"bound": "hbm" if x.R < 312 else "mfma", "algorithmic_bytes": lm_b, "GB/s": lm_gbs,
+                        "hbm_frac": lm_gbs / HBM_PEAK_GBS, "TFLOP/s": lm_tflops,
+                        "mfma_frac": lm_tflops / BF16_PEAK_TFLOPS}}
+
+
+def config_leg(name: str, dev, steps: int, warmup: int, seed: int = 0) -> dict:
+    """The verify step (attention + lm_head + accept) on another workload, timed as the
+    headline step is. Drafts: the greedy tokens of an untimed lm_head pass, corrupted
+    per position (the parity tests use the oracle's greedy tokens; the two agree on
+    every row whose top-2 gap exceeds 5e-2)."""
+    x = synth.make_verify_inputs(name, seed=seed, device=dev)
+    wl = x.wl
+    step = VerifyStep(x, dev)
+    x.w = None
+    torch.cuda.empty_cache()
+    step.lm_head()
+    torch.cuda.synchronize()
+    g0 = step.argmax.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    step.drafts = i32(synth.make_drafts(wl, x.k, [g0[off[s]:off[s] + x.k[s]] for s in range(len(x.pos))],
+                                        seed=seed, d2t=x.d2t), dev)
+    rep = step_report(step, time_verify_step(step, steps, warmup))
+    ctx = f"U{{{wl.ctx_lo}..{wl.ctx_hi}}}" if wl.ctx_lo != wl.ctx_hi else str(wl.ctx_lo)
+    ks = f"k={wl.k}" if wl.k is not None else f"k_s ~ U{{{wl.k_lo}..{wl.k_hi}}}"
+    rep = {"workload": f"{name}: B={len(x.pos)}, {ks}, context {ctx}, {wl.Hq}q/{wl.Hkv}kv heads, head_dim {wl.D}, "
+                       f"hidden {wl.H}, vocab {wl.V}" + (f", d2t {len(x.d2t)} entries" if x.d2t is not None else ""),
+           "kv_split_tokens": gdv.attn_split_tokens(x.page_table.shape[1]), **rep}
+    log(f"[bench] {name}: step {rep['step_us']:.1f} us ({rep['rows_per_s']:.0f} rows/s, "
+        f"{rep['emitted_tokens_per_s']:.0f} tokens/s): attn {rep['kernel_us']['spec_verify_attn']:.1f} us "
+        f"({100 * rep['attn']['frac']:.0f}% HBM), lm_head {rep['kernel_us']['spec_lm_head_argmax']:.1f} us "
+        f"({100 * rep['lm_head']['hbm_frac']:.0f}% HBM, {100 * rep['lm_head']['mfma_frac']:.0f}% MFMA), accept "
+        f"{rep['kernel_us']['spec_greedy_accept']:.1f} us")
+    del step, x
+    torch.cuda.empty_cache()
+    return rep
+
+
 def delta_leg(dev, reps: int):
     """Gated DeltaNet verify with per-token record and fused rollback (mode BOTH) on the
     hybrid workload: B=32, T=5, 32 heads, 128x128 fp32 state. Algorithmic bytes: S_0
@@ -185,7 +301,10 @@ def delta_leg(dev, reps: int):
                             "verify_frac": byts_v / sec_v / 1e9 / HBM_PEAK_GBS,
                             "rescan_us": sec_s * 1e6, "rescan_bytes": byts_s,
                             "rescan_frac": byts_s / sec_s / 1e9 / HBM_PEAK_GBS,
-                            "total_us": (sec_v + sec_s) * 1e6}}
+                            "total_us": (sec_v + sec_s) * 1e6},
+            # one round at this workload's L mix: record every state and restore by the
+            # fused copy, or keep the inputs and re-run the committed prefix
+            "per_round_us": {"record": sec * 1e6, "stash": (sec_v + sec_s) * 1e6}}
 
 
 def tree_leg(dev, w_packed, reps: int, seed: int = 0):
@@ -449,7 +568,7 @@ def lm_head_sweep(x: synth.VerifyInputs, w_packed, dev, reps: int):
     out = []
     g = torch.Generator(device=dev)
     g.manual_seed(1)
-    for R in (80, 160, 288, 512, 1024):
+    for R in (80, 160, 288, 311, 512, 1024):
         h = torch.randn((R, wl.H), generator=g, device=dev).to(torch.bfloat16)
         am = torch.empty(R, dtype=torch.int32, device=dev)
         ws = gdv.workspace(gdv.lm_head_argmax_workspace_bytes(R, wl.H, wl.V), dev, zero=True)
@@ -521,13 +640,14 @@ def cpu_baseline(x_host: synth.VerifyInputs, n_seq: int, min_seconds: float = 10
                 break
     except OSError:
         pass
+    g_all, t1_all, t2_all = oracle.lm_head_argmax(hb, wb, R, wl.H, wl.V)[:3]
     return dict(value=R / secs, unit="rows/s", cores=cores, kind="oracle",
                 sample=f"first {n_seq} of {len(x_host.pos)} sequences ({R} rows), the whole oracle step "
                        f"repeated {reps} times ({t_attn + t_lm + t_acc:.1f} s); per repetition: fp64 "
                        f"attention+append {t_attn / reps:.3f}s, lm_head+argmax {t_lm / reps:.3f}s, accept "
                        f"{t_acc / reps:.5f}s; host: {model}, os.cpu_count() = {os.cpu_count()}",
                 single_core_value=R / secs_1, single_core_seconds=secs_1,
-                seconds=secs)
+                seconds=secs, greedy=(rows, g_all, t1_all - t2_all))
 
 
 def main():
@@ -541,9 +661,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip every leg reported beside the step")
-    ap.add_argument("--extras", default="sweep,delta,tree,sampling,adaptive",
-                    help="comma list of the legs reported beside the step: sweep (lm_head rows), delta "
-                         "(DeltaNet), tree, sampling, adaptive (verify cost by rows + draft-depth policy)")
+    ap.add_argument("--extras", default="configs,sweep,delta,tree,sampling,adaptive",
+                    help="comma list of the legs reported beside the step: configs (the verify step on the "
+                         "tiny, ragged and long workloads), sweep (lm_head rows), delta (DeltaNet), tree, "
+                         "sampling, adaptive (verify cost by rows + draft-depth policy)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed loop, copy this many MiB 3 times (a plain copy kernel of known "
                          "size, used to scale hardware byte counters)")
@@ -554,106 +675,68 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
     t_gen = time.perf_counter()
     x = synth.make_verify_inputs(args.workload, seed=args.seed, device=dev)
     wl = x.wl
     log(f"[bench] {wl.name}: B={len(x.pos)} R={x.R} pos {x.pos.min()}..{x.pos.max()} pool {x.n_pages} pages, "
         f"inputs drawn in {time.perf_counter() - t_gen:.1f}s")
-    # host copies for the CPU baseline (before any append touches the pool)
-    x_host = None
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+
+    # The CPU baseline runs first, on host copies (before any append touches the
+    # pool): the oracle's step on a bounded sample, whose greedy tokens also give the
+    # drafts of the timed step when the sample covers every sequence.
+    cpu, oracle_greedy = None, None
     if not args.no_cpu_baseline:
         x_host = synth.VerifyInputs(wl, x.pos, x.k, x.R, x.page_table, x.n_pages, x.q.cpu(), x.k_new.cpu(),
                                     x.v_new.cpu(), x.k_pool.cpu(), x.v_pool.cpu(), x.hidden.cpu(), x.w.cpu(), x.d2t)
+        n_seq = min(args.cpu_sample_seqs, len(x.pos))
+        log(f"[bench] cpu baseline: oracle on {n_seq} sequences ...")
+        cpu = cpu_baseline(x_host, n_seq)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} rows/s ({cpu['sample']})")
+        cpu.pop("seconds")
+        rows_o, g_o, gap_o = cpu.pop("greedy")
+        if len(rows_o) == x.R:
+            oracle_greedy = (g_o, gap_o)
+        del x_host
 
     step = VerifyStep(x, dev)
     x.w = None                      # the packed copy is the one the step reads
     torch.cuda.empty_cache()
-    # drafts: greedy tokens of an untimed lm_head pass, corrupted per position
+    # an untimed lm_head pass: the GPU's greedy tokens, compared with the oracle's
     step.lm_head()
     torch.cuda.synchronize()
-    g0 = step.argmax.cpu().numpy()
-    off = np.concatenate([[0], np.cumsum(x.k + 1)])
-    true_next = [g0[off[s]:off[s] + x.k[s]] for s in range(len(x.pos))]
+    g_gpu = step.argmax.cpu().numpy()
+    drafts_note = {}
+    if oracle_greedy is not None:
+        g_src = oracle_greedy[0]
+        diff = g_gpu != g_src
+        drafts_note = {"drafts_from": "oracle greedy tokens (fp64), corrupted per position",
+                       "gpu_argmax_rows_differing_from_oracle": int(diff.sum()),
+                       "of_which_oracle_gap_le_5e-2": int((diff & (oracle_greedy[1] <= 5e-2)).sum())}
+    else:
+        g_src = g_gpu
+        drafts_note = {"drafts_from": "GPU greedy tokens of an untimed lm_head pass (no CPU baseline run), "
+                                      "corrupted per position"}
+    true_next = [g_src[off[s]:off[s] + x.k[s]] for s in range(len(x.pos))]
     step.drafts = i32(synth.make_drafts(wl, x.k, true_next, seed=args.seed, d2t=x.d2t), dev)
 
-    def run_step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        step.attn()
-        if ev:
-            ev[1].record(stream)
-        step.lm_head()
-        if ev:
-            ev[2].record(stream)
-        step.accept()
-        if ev:
-            ev[3].record(stream)
-
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-    assert (step.attn_status.cpu() == 0).all() and (step.acc_status.cpu() == 0).all()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        run_step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    eager_ms_step = start.elapsed_time(stop) / args.steps
-    eager_out = step.outputs()
-
-    # The same step captured once as a HIP graph and replayed: the launches' host
-    # overhead and gaps leave the step. Every replay must reproduce the eager bytes.
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        run_step()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        run_step()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    for a, b in zip(eager_out, step.outputs()):
-        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "graph replay differs from the eager step"
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    lm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    acc_len = step.acc_len.cpu().numpy()
-    emitted = int((acc_len + 1).sum())
-    rows_per_s = x.R / (ms_step / 1e3)
-    lm_b = lm_head_bytes(x.R, wl.H, wl.V)
-    at_b = attn_bytes(x)
-    lm_gbs = lm_b / (lm_ms / 1e3) / 1e9
-    at_gbs = at_b / (attn_ms / 1e3) / 1e9
-    lm_tflops = 2.0 * x.R * wl.H * wl.V / (lm_ms / 1e3) / 1e12
-    hist = np.bincount(acc_len, minlength=wl.kmax + 1).tolist()
-    log(f"[bench] step {ms_step * 1e3:.1f} us (graph replay; eager {eager_ms_step * 1e3:.1f} us): attn {attn_ms * 1e3:.1f} us ({at_gbs:.0f} GB/s), lm_head "
-        f"{lm_ms * 1e3:.1f} us ({lm_gbs:.0f} GB/s, {lm_tflops:.1f} TFLOP/s), accept {acc_ms * 1e3:.1f} us; "
-        f"accept-length histogram {hist}")
+    t = time_verify_step(step, args.steps, args.warmup)
+    rep = step_report(step, t)
+    ms_step = t["graph_ms"]
+    lm, at = rep["lm_head"], rep["attn"]
+    log(f"[bench] step {ms_step * 1e3:.1f} us (graph replay; eager {t['eager_ms'] * 1e3:.1f} us): attn "
+        f"{t['attn_ms'] * 1e3:.1f} us ({at['achieved']:.0f} GB/s), lm_head {t['lm_ms'] * 1e3:.1f} us "
+        f"({lm['GB/s']:.0f} GB/s, {lm['TFLOP/s']:.1f} TFLOP/s), accept {t['acc_ms'] * 1e3:.1f} us; "
+        f"accept-length histogram {rep['accept_len_hist']}; {drafts_note}")
 
     extras = {}
     legs = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
-    unknown = legs - {"sweep", "delta", "tree", "sampling", "adaptive"}
+    unknown = legs - {"configs", "sweep", "delta", "tree", "sampling", "adaptive"}
     if unknown:
         raise SystemExit(f"bench.py: unknown --extras legs {sorted(unknown)}")
     if legs:
         if "sweep" in legs:
             extras["lm_head_row_sweep"] = lm_head_sweep(x, step.w_packed, dev, reps=10)
-        if "delta" in legs:
-            extras["delta_roofline"] = delta_leg(dev, reps=20)
         if "tree" in legs and wl.H == 4096 and wl.V == 151936:
             extras["tree_verify"] = tree_leg(dev, step.w_packed, reps=20, seed=args.seed)
         if "sampling" in legs:
@@ -661,19 +744,33 @@ def main():
             extras["sampling_dense_verify"] = sampling_dense_leg(step, dev, reps=20)
         if "adaptive" in legs and wl.name == "b16k4":
             extras["adaptive_k"] = kpolicy_leg(step, dev, reps=10, seed=args.seed)
+        if "configs" in legs or "delta" in legs:
+            # the other workloads of the verify step, each timed like the headline one
+            # (the headline step's buffers are released first)
+            del step
+            torch.cuda.empty_cache()
+            configs = {}
+            if "configs" in legs:
+                for name in ("tiny", "ragged", "long"):
+                    if name != wl.name:
+                        configs[name] = config_leg(name, dev, steps=max(10, args.steps // 5), warmup=args.warmup,
+                                                   seed=args.seed)
+            if "delta" in legs:
+                configs["delta"] = delta_leg(dev, reps=20)
+                dl = configs["delta"]
+                ist = dl["input_stash"]
+                log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
+                    f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
+                    f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
+                    f"{ist['rescan_us']:.1f} us (record+rollback vs stash per round at this L mix: "
+                    f"{dl['per_round_us']['record']:.1f} vs {dl['per_round_us']['stash']:.1f} us)")
+            extras["configs"] = configs
         if "lm_head_row_sweep" in extras:
             sw = ", ".join(f"R={e['rows']}: {e['us']:.0f} us {e['TFLOP/s']:.0f} TF/s" for e in extras["lm_head_row_sweep"])
             log(f"[bench] lm_head sweep: {sw}")
-        if "delta_roofline" in extras:
-            dl = extras["delta_roofline"]
-            ist = dl["input_stash"]
-            log(f"[bench] delta verify+record+rollback {dl['verify_record_rollback_us']:.1f} us "
-                f"({dl['achieved']:.0f} GB/s, {100 * dl['frac']:.0f}% of HBM peak); rollback alone "
-                f"{dl['rollback_only_us']:.1f} us; input stash: verify {ist['verify_us']:.1f} us + re-scan "
-                f"{ist['rescan_us']:.1f} us")
         if "adaptive_k" in extras:
             ak = extras["adaptive_k"]
-            tbl = ", ".join(f"{r}: {t:.0f}" for r, t in ak["verify_us_by_rows"])
+            tbl = ", ".join(f"{r}: {t_:.0f}" for r, t_ in ak["verify_us_by_rows"])
             ch = ", ".join(f"p={c['accept_p']}/d={c['draft_us']:.0f}->k={c['k']}" for c in ak["choices"])
             log(f"[bench] verify us by rows (B=16): {tbl}; policy: {ch}")
         sv_ = extras.get("sampling_verify")
@@ -709,22 +806,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cpu = None
-    if x_host is not None:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_seqs} sequences ...")
-        cpu = cpu_baseline(x_host, args.cpu_sample_seqs)
-        log(f"[bench] cpu baseline {cpu['value']:.3f} rows/s ({cpu['sample']})")
-        cpu.pop("seconds")
-
+    lm_frac = lm["hbm_frac"] if lm["bound"] == "hbm" else lm["mfma_frac"]
     result = {
         "metric": "verify rows/s (B=16, k=4; emitted tokens/s and roofline fractions alongside)",
-        "value": rows_per_s,
+        "value": rep["rows_per_s"],
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "eager_ms_per_step": eager_ms_step,
+        "eager_ms_per_step": t["eager_ms"],
         "step_launch": "HIP graph replay of the three entry points (per-entry times and rooflines from the eager loop)",
         "higher_is_better": True,
         "scaling": "weak",
@@ -735,18 +826,22 @@ def main():
                    "context": f"U{{{wl.ctx_lo}..{wl.ctx_hi}}}", "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "hidden": wl.H, "vocab": wl.V, "page": 16,
                    "kv_split_tokens": gdv.attn_split_tokens(x.page_table.shape[1])},
-        "emitted_tokens_per_s": emitted / (ms_step / 1e3),
-        "emitted_per_step": emitted,
-        "accept_len_hist": hist,
-        "kernel_us": {"spec_verify_attn": attn_ms * 1e3, "spec_lm_head_argmax": lm_ms * 1e3,
-                      "spec_greedy_accept": acc_ms * 1e3},
-        "roofline": {"kernel": "spec_lm_head_argmax", "bound": "hbm", "achieved": lm_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
+        **drafts_note,
+        "emitted_tokens_per_s": rep["emitted_tokens_per_s"],
+        "emitted_per_step": rep["emitted_per_step"],
+        "accept_len_hist": rep["accept_len_hist"],
+        "kernel_us": rep["kernel_us"],
+        "roofline": {"kernel": "spec_lm_head_argmax", "bound": lm["bound"],
+                     "achieved": lm["GB/s"] if lm["bound"] == "hbm" else lm["TFLOP/s"],
+                     "peak": HBM_PEAK_GBS if lm["bound"] == "hbm" else BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if lm["bound"] == "hbm" else "TFLOP/s", "frac": lm_frac,
                      "traffic": measured_traffic("lm_head_tile") if wl.name == "b16k4" else None,
-                     "mfma_frac": lm_tflops / BF16_PEAK_TFLOPS, "algorithmic_bytes": lm_b},
-        "attn_roofline": {"kernel": "spec_verify_attn", "bound": "hbm", "achieved": at_gbs, "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS, "algorithmic_bytes": at_b,
-                          "traffic_split_kernel": measured_traffic("attn_split") if wl.name == "b16k4" else None},
+                     "hbm_frac": lm["hbm_frac"], "mfma_frac": lm["mfma_frac"],
+                     "algorithmic_bytes": lm["algorithmic_bytes"]},
+        "attn_roofline": {"kernel": "spec_verify_attn", "bound": "hbm", "achieved": at["achieved"],
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": at["frac"],
+                          "algorithmic_bytes": at["algorithmic_bytes"],
+                          "traffic": measured_traffic("attn_split") if wl.name == "b16k4" else None},
         "cpu_baseline": cpu,
         **extras,
         "context": "pages' own figure: 6.5 ms per 16-row whole-model verify, RTX 5090 with CUDA graphs "
