@@ -24,7 +24,8 @@ DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH, DELTA_VERIFY, DELTA_RESCAN = 1, 2, 3, 
 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_verify_attn_workspace_bytes", "spec_verify_attn",
-            "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_packed_bytes",
+            "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_argmax_noalloc",
+            "spec_lm_head_packed_bytes",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
             "spec_kv_compact", "spec_lm_head_sample_workspace_bytes", "spec_lm_head_sample",
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.spec_lm_head_argmax_workspace_bytes.argtypes = [i32, i32, i32]
         L.spec_lm_head_argmax_workspace_bytes.restype = sz
         L.spec_lm_head_argmax.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.spec_lm_head_argmax_noalloc.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.spec_lm_head_packed_bytes.argtypes = [i32, i32]
         L.spec_lm_head_packed_bytes.restype = sz
         L.spec_lm_head_pack.argtypes = [vp, i32, i32, vp, vp]
@@ -332,6 +334,30 @@ def spec_lm_head_argmax(hidden, w_packed, V, argmax, maxval=None, workspace_buf=
     rc = lib().spec_lm_head_argmax(_ptr(hidden), _ptr(w_packed), R, H, V, _ptr(argmax), _ptr(maxval),
                                    _ptr(workspace_buf), workspace_buf.numel(), _stream(stream))
     _check(rc, "spec_lm_head_argmax")
+
+
+NOALLOC_MAX_ROWS = 8192
+
+
+def spec_lm_head_argmax_noalloc(hidden, w_packed, V, argmax, maxval=None, stream=None):
+    """spec_lm_head_argmax with no workspace: the library keeps its ticket and keys in
+    a device array of its own (rows R <= NOALLOC_MAX_ROWS; calls on one GPU must not
+    overlap in time)."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
+    _want(argmax, torch.int32, "argmax", 1)
+    if maxval is not None:
+        _want(maxval, torch.float32, "maxval", 1)
+    R, H = hidden.shape
+    if w_packed.numel() * 2 != lm_head_packed_bytes(V, H):
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {lm_head_packed_bytes(V, H)} "
+                        f"for V={V} H={H}")
+    _shape(argmax, (R,), "argmax")
+    if maxval is not None:
+        _shape(maxval, (R,), "maxval")
+    rc = lib().spec_lm_head_argmax_noalloc(_ptr(hidden), _ptr(w_packed), R, H, V, _ptr(argmax), _ptr(maxval),
+                                           _stream(stream))
+    _check(rc, "spec_lm_head_argmax_noalloc")
 
 
 def spec_greedy_accept(argmax, drafts, k, d2t, V, pos_in, pos_out, accept_len, n_emit, emit, next_tok,

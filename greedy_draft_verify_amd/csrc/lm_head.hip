@@ -27,6 +27,7 @@
 // zero. The order is total, so the result does not depend on which workgroup
 // finishes when; each logit is one MFMA chain over K in a fixed order, so a row's
 // result does not depend on R or the row group.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -707,3 +708,79 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// spec_lm_head_argmax_noalloc: the same lm_head with its ticket and keys in a
+// library-owned device array instead of a caller workspace.
+namespace sv {
+
+constexpr size_t kScratchBytes = SPEC_NOALLOC_SCRATCH_BYTES;
+// One copy per GPU the library runs on, held until the process ends. In host code
+// this name is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* __restrict__ p, int n16) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+constexpr int kMaxDevices = 64;
+
+// The current device's copy of the scratch array (looked up once per device).
+static int scratch_for_current_device(void** out) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SPEC_EHIP, "spec_lm_head_argmax_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_ECAPACITY, "spec_lm_head_argmax_noalloc: device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SPEC_EHIP, "spec_lm_head_argmax_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return SPEC_OK;
+}
+
+}  // namespace sv
+
+extern "C" int spec_lm_head_argmax_noalloc(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,
+                                           int32_t V, int32_t* argmax, float* maxval, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    if (R < 1) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: R=%d < 1", R);
+    if (R > SPEC_NOALLOC_MAX_ROWS)
+        return fail(SPEC_ECAPACITY, "spec_lm_head_argmax_noalloc: R=%d exceeds the %d rows its scratch array holds",
+                    R, SPEC_NOALLOC_MAX_ROWS);
+    // the checks of spec_lm_head_argmax, made before anything is launched
+    if (H < kLmHAlign || H % kLmHAlign)
+        return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: H=%d not a positive multiple of %d", H, kLmHAlign);
+    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: V=%d", V);
+    if (!hidden || !w_packed || !argmax) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: null required pointer");
+    if (!aligned16(hidden) || !aligned16(w_packed))
+        return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: hidden and w_packed must be 16-byte aligned");
+    const size_t need = spec_lm_head_argmax_workspace_bytes(R, H, V);
+    if (need == 0 || need > kScratchBytes) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: R=%d V=%d", R, V);
+    void* ws = nullptr;
+    const int rc = scratch_for_current_device(&ws);
+    if (rc != SPEC_OK) return rc;
+    // the ticket and this call's keys start at zero (a fill kernel, so that the call
+    // can be captured into a graph)
+    const int n16 = (int)((need + 15) / 16);
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3((n16 + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<uint4*>(ws), n16);
+    SV_LAUNCH_CHECK("spec_lm_head_argmax_noalloc");
+    const int r2 = spec_lm_head_argmax(hidden, w_packed, R, H, V, argmax, maxval, ws, need, stream);
+    if (r2 != SPEC_OK) {
+        // the message names the shared checks; say which entry point failed
+        const std::string msg = last_error();
+        last_error().clear();
+        return fail(r2, "spec_lm_head_argmax_noalloc: %s", msg.c_str());
+    }
+    return SPEC_OK;
+}

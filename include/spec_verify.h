@@ -180,6 +180,23 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
                         int32_t V, int32_t* argmax, float* maxval, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* spec_lm_head_argmax_noalloc — spec_lm_head_argmax with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). It computes exactly what
+ * spec_lm_head_argmax computes (the same kernels, so the same bytes) and calls no
+ * allocating routine: its ticket and per-row keys live in a library-owned device
+ * array of SPEC_NOALLOC_SCRATCH_BYTES bytes per GPU, which holds them for rows
+ * R <= SPEC_NOALLOC_MAX_ROWS (larger R: SPEC_ECAPACITY, nothing launched). Each call
+ * first clears the part of the array it uses with a small fill kernel on the
+ * caller's stream, then runs the lm_head. The array is shared by every call on one
+ * GPU: calls that may overlap in time on the same GPU race and must be ordered by
+ * the caller (e.g. one stream). Arguments, layouts and the other limits as
+ * spec_lm_head_argmax. */
+#define SPEC_NOALLOC_MAX_ROWS 8192
+#define SPEC_NOALLOC_SCRATCH_BYTES (256 + 8 * SPEC_NOALLOC_MAX_ROWS)
+int spec_lm_head_argmax_noalloc(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,
+                                int32_t V, int32_t* argmax, float* maxval, void* stream);
+
 /* spec_lm_head_pack — one-time re-layout of a row-major lm_head weight w [V][H]
  * (bf16) into the packed form spec_lm_head_argmax reads. Vocabulary rows are
  * taken in groups of 128 and channels in K-blocks of 128; a group stores its
