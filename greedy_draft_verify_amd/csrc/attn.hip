@@ -62,9 +62,13 @@ constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
 constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
 constexpr float kLog2e = 1.4426950408889634f;
 
+// address-space pointer types of global_load_lds (global source, LDS destination)
+typedef const __attribute__((address_space(1))) void* global_cptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 struct RowRec {
     int32_t p;      // position of the row
-    int32_t nc;     // splits the combine merges for it (0: its sequence is skipped)
+    int32_t nc;     // splits the merge kernel combines for it (0: nothing to merge)
 };
 
 // In-block offsets of token t, channel d (see the pool format above).
@@ -76,8 +80,9 @@ __device__ __forceinline__ int v_off(int t, int d) {
 }
 
 // ---------------------------------------------------------------------------
-// Online softmax over one 64-token tile (4 pages) for one 16-row query tile.
-//   src.k(p, ds): K A-fragment of the tile's page p (0..3), k-step ds
+// Online softmax over one tile of NP pages (NP = 4: 64 tokens, NP = 2: 32 tokens)
+// for one 16-row query tile.
+//   src.k(p, ds): K A-fragment of the tile's page p, k-step ds
 //   src.v(p, dt): V fragment (4 tokens of channel 16 dt + l16) of page p
 //   lane l holds query row m = l % 16 of the tile; after the S^T MFMAs it holds
 //   the scores of tokens t0 + 16 p + 4 (l / 16) + i, i = 0..3.
@@ -96,13 +101,15 @@ struct TileMath {
     static constexpr int NDT = D / 16;
 
     // win (tree rows only): bit o set iff the row keeps key slot t0 + o
-    template <bool TREE, class Src>
+    template <bool TREE, int NP, class Src>
     __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int t0, int p_m,
                                                uint64_t win, bool full, int lq, float scale_log2,
                                                float& m_run, float& l_lane, f32x4 (&o)[NDT]) {
-        float sc[16];
+        static_assert(NP == 2 || NP == 4, "tiles of 32 or 64 tokens");
+        constexpr int NS = 4 * NP;   // scores per lane
+        float sc[NS];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < NP; ++p) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) acc = mfma16x16x32(as_bf16x8(src.k(p, ds)), qf[ds], acc);
@@ -115,7 +122,7 @@ struct TileMath {
             const uint64_t wl = TREE ? win >> (4 * lq) : 0ull;
             const uint32_t w_lo = (uint32_t)wl, w_hi = (uint32_t)(wl >> 32);
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
+            for (int jj = 0; jj < NS; ++jj) {
                 const int o_t = 16 * (jj >> 2) + 4 * lq + (jj & 3);
                 const uint32_t half = (jj >> 3) ? w_hi : w_lo;
                 const bool keep = TREE ? ((half >> (16 * ((jj >> 2) & 1) + (jj & 3))) & 1u) : (t0 + o_t <= p_m);
@@ -124,7 +131,7 @@ struct TileMath {
         }
         float tmax = sc[0];
 #pragma unroll
-        for (int jj = 1; jj < 16; ++jj) tmax = fmaxf(tmax, sc[jj]);
+        for (int jj = 1; jj < NS; ++jj) tmax = fmaxf(tmax, sc[jj]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const bool raise = tmax > m_run + kRescaleLog2;       // also true on a row's first tile
@@ -139,18 +146,20 @@ struct TileMath {
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
+        for (int jj = 0; jj < NS; ++jj) {
             sc[jj] = fast_exp2(sc[jj] - m_use);
             psum += sc[jj];
         }
         l_lane += psum;
-        // 32-token halves h: k-slot 8 lq + jj <-> token 32 h + 16 (jj/4) + 4 lq + jj%4
-        const bf16x8 pf0 = pack8(sc), pf1 = pack8(sc + 8);
+        // 32-token halves hh: k-slot 8 lq + jj <-> token 32 hh + 16 (jj/4) + 4 lq + jj%4
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint2 a0 = src.v(0, dt), b0 = src.v(1, dt), a1 = src.v(2, dt), b1 = src.v(3, dt);
-            f32x4 acc = mfma16x16x32(as_bf16x8(make_uint4(a0.x, a0.y, b0.x, b0.y)), pf0, o[dt]);
-            o[dt] = mfma16x16x32(as_bf16x8(make_uint4(a1.x, a1.y, b1.x, b1.y)), pf1, acc);
+        for (int hh = 0; hh < NP / 2; ++hh) {
+            const bf16x8 pf = pack8(sc + 8 * hh);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const uint2 a = src.v(2 * hh, dt), b = src.v(2 * hh + 1, dt);
+                o[dt] = mfma16x16x32(as_bf16x8(make_uint4(a.x, a.y, b.x, b.y)), pf, o[dt]);
+            }
         }
     }
 };
@@ -195,76 +204,85 @@ __device__ __forceinline__ uint64_t tree_window(uint4 mk, int sh) {
     return funnel64(e2, 0ull, sh - 128);
 }
 
-// Writes one query tile's split partial (unnormalised O, running max, sum).
+// Writes a 16-row query tile's normalised output: lane l holds row l % 16, channels
+// 16 dt + 4 (l / 16) + i.
 template <int D>
-__device__ __forceinline__ void store_partial(const f32x4 (&o)[D / 16], float m_run, float l_lane, bool m_ok,
-                                              int p_m, int c0, size_t idx, int lq, float2* part_ml,
-                                              float* part_o) {
-    float l_tot = l_lane + __shfl_xor(l_lane, 16);
-    l_tot = l_tot + __shfl_xor(l_tot, 32);
-    if (!m_ok || p_m < c0) return;
-    if (lq == 0) part_ml[idx] = make_float2(m_run, l_tot);
-    float* po = part_o + idx * D + lq * 4;
+__device__ __forceinline__ void store_out(const f32x4 (&o)[D / 16], float inv, u16* dst) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const uint32_t a = (uint32_t)f2bf(o[dt][0] * inv) | ((uint32_t)f2bf(o[dt][1] * inv) << 16);
+        const uint32_t b = (uint32_t)f2bf(o[dt][2] * inv) | ((uint32_t)f2bf(o[dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(a, b);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// attn_split_kernel: one workgroup per (sequence, kv head, split, 64-row group);
-// 64-token tiles (4 K blocks + 4 V blocks, copied linearly) staged in LDS.
-// Register budget: three workgroups per CU at D <= 128 (32 KB of LDS each; at four
-// the checks, records and append spilled registers and measured slower), two at
-// D = 256 (64 KB each). STREAM: the pool's K/V blocks are read with non-temporal
-// loads (chosen from the split size, i.e. from capacity; the cache policy never
-// changes a result).
+// attn_kernel: one workgroup per (sequence, kv head, split, 64-row group), kv head
+// fastest. A split's K/V blocks go from HBM straight into LDS (global_load_lds: no
+// staging registers), one tile of KT tokens at a time; the register file left free
+// lets more workgroups share a CU, so their tiles are in flight while one computes.
+// Splits past the sequence's last position leave before any tile work. The rows of a
+// sequence that fits one split are final here; otherwise each split writes its
+// partial (unnormalised O, running max, sum) for attn_combine_kernel.
+// STREAM: pool blocks are read non-temporally (chosen from the split size, i.e. from
+// capacity; the cache policy never changes a result).
+template <int D>
+struct AttnCfg {
+    static constexpr int KT = 64;                              // tokens per tile
+    static constexpr int NP = KT / kPage;                      // pages per tile
+    static constexpr int BLK = kPage * D;                      // elements per block
+    static constexpr int CPB = BLK * 2 / 1024;                 // 1 KB chunks per block (>= 2)
+    static constexpr int NCH = 2 * NP * (CPB > 0 ? CPB : 1);   // chunks per tile
+    static constexpr int WAVE_CH = NCH / 4;                    // chunks per wave
+    // workgroups per CU (LDS: one tile, 16 / 32 / 64 KB; at D = 256 32-token tiles at
+    // three per CU measured slower, long 441 vs 423 us)
+    static constexpr int MINB = D <= 64 ? 5 : D <= 128 ? 4 : 2;
+};
+
 template <int D, bool TREE, bool STREAM>
-__global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_kernel(
+__global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, int Hq, int Hkv, float scale_log2, int split, int n_splits,
-    float2* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ parent, int kmax,
-    const u16* __restrict__ k_new, const u16* __restrict__ v_new, int64_t n_pages, int B, int R,
-    int32_t* __restrict__ status, RowRec* __restrict__ rows, int32_t* __restrict__ packing_ok,
-    u16* k_pool_w, u16* v_pool_w) {
+    RowRec* __restrict__ rows, int32_t* __restrict__ packing_ok, float2* __restrict__ part_ml, float* __restrict__ part_o,
+    const int32_t* __restrict__ parent, int kmax, const u16* __restrict__ k_new, const u16* __restrict__ v_new,
+    int64_t n_pages, int B, int R, int32_t* __restrict__ status, u16* __restrict__ out, u16* k_pool_w,
+    u16* v_pool_w) {
     using TM = TileMath<D>;
-    constexpr int NDS = TM::NDS, NDT = TM::NDT;
-    constexpr int BLK = kPage * D;               // elements per block
-    constexpr int BLK_CH = BLK / 8;              // 16-byte chunks per block
-    constexpr int PER_THREAD = 8 * BLK_CH / kAttnThreads;
-    __shared__ __attribute__((aligned(16))) u16 smem[8 * BLK];   // K0..K3, V0..V3
-    __shared__ int s_anc[TREE ? kMaxTreeNodes : 1];               // tree rows: ancestor links
-    __shared__ uint4 s_mask[TREE ? kMaxTreeNodes : 1];            // tree rows: ancestor masks
+    using C = AttnCfg<D>;
+    constexpr int KT = C::KT, NP = C::NP, BLK = C::BLK, NDS = TM::NDS, NDT = TM::NDT;
+    static_assert(C::NCH % 4 == 0 && C::CPB >= 2, "a tile must split into whole 1 KB chunks per wave");
+    __shared__ __attribute__((aligned(16))) u16 smem[2 * NP * BLK];   // K blocks, then V blocks
+    __shared__ int s_anc[TREE ? kMaxTreeNodes : 1];                    // tree rows: ancestor links
+    __shared__ uint4 s_mask[TREE ? kMaxTreeNodes : 1];                 // tree rows: ancestor masks
 
-    // kv head fastest: the workgroups of one (sequence, split) start together and
-    // fetch the Hkv blocks of each page (adjacent in the pool) at about the same time
     const int hk = blockIdx.x % Hkv;
     const int c = (blockIdx.x / Hkv) % n_splits;
     const int mgroup = blockIdx.x / Hkv / n_splits;
     const int s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int c0 = c * split;
-    // Page ids of this split (lane i holds page c0/16 + i + 64 r), requested together
-    // with the sequence's metadata: the index depends on the launch coordinates only
-    // (clamped to the page-table row; entries past the sequence's last page are never
-    // used), so the first tile waits on one round trip, not two.
     const int pg0 = c0 / kPage;
+    // the split's page ids (lane i holds page pg0 + i + 64 r) and the tree parents are
+    // requested with the sequence's metadata: the indexes depend on the launch only
     int pid[(kMaxSplit / kPage + kWave - 1) / kWave];
 #pragma unroll
     for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
         pid[r] = page_table[(size_t)s * max_pages + min(pg0 + r * kWave + lane, max_pages - 1)];
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int G = Hq / Hkv;
-    const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
-    // tree rows: thread i's node parent (clamped to the table), requested with the metadata
     int par_i = 0;
     if (TREE) par_i = parent[(size_t)s * (kmax + 1) + min(tid, kmax)];
     const int ks = k[s], P0 = pos[s];
-    // The sequence's checks and records, with no kernel of their own: every wave forms
-    // the row packing on its own (each k is read by every wave, from cache), and the
-    // workgroup checks its positions, the parent list (tree rows) and its own page ids
-    // before any of its tiles is read. The whole page list is checked at the end by the
-    // workgroups that write the sequence's records or append its rows, the only writes
-    // a flagged sequence must not make.
+    const int G = Hq / Hkv;
+    const int last = P0 + ks;                     // the sequence's last position
+    const int T = ks + 1, M = G * T;
+    // Splits past the sequence's last position (and row groups past its rows) have no
+    // work: they leave now, unless they write the sequence's status.
+    const bool lead = hk == 0 && c == 0 && mgroup == 0;
+    const bool has_work = ks >= 0 && P0 >= 0 && c0 <= last && mgroup * kRowsPerGroup < M;
+    if (!has_work && !lead) return;
+
+    // Row packing: every wave forms it on its own (each k is read by every wave, from cache).
     long long before = 0, total = 0;
     int rowbad = 0;
     for (int i = lane; i < B; i += kWave) {
@@ -279,189 +297,200 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_ker
         total += __shfl_xor(total, d);
         rowbad |= __shfl_xor(rowbad, d);
     }
-    // wave-uniform: kept in scalar registers
     const bool packed = __builtin_amdgcn_readfirstlane(!rowbad && total == (long long)R);
-    const int off = __builtin_amdgcn_readfirstlane((int)before);    // the sequence's first packed row
+    const int off = __builtin_amdgcn_readfirstlane((int)before);
     const bool pos_ok = P0 >= 0 && (ks < 0 || ((long long)P0 + ks) / kPage < max_pages);
-    int basic = 0;     // packing and position flags
+    int basic = 0;
     if (!packed || ks > kmax) basic |= SPEC_STATUS_BAD_ROWS;
     if (!pos_ok) basic |= SPEC_STATUS_BAD_POS;
-    // tree rows: node i's parent must come before it (the root's is -1)
     bool tree_bad = false;
     if constexpr (TREE) {
         bool bad = false;
         if (ks >= 0 && ks <= kmax && tid <= ks) bad = tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid);
         tree_bad = __syncthreads_or(bad) != 0;
     }
+    // this split's own page ids (the whole list is checked by the workgroups that write
+    // the status or append rows)
     bool own_bad = false;
     if (!basic) {
-        const int hi = min((P0 + ks) / kPage, pg0 + split / kPage - 1);
+        const int hi = min(last / kPage, pg0 + split / kPage - 1);
 #pragma unroll
         for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r) {
-            const int p = pg0 + r * kWave + lane;
-            if (p <= hi && (pid[r] < 0 || (int64_t)pid[r] >= n_pages)) own_bad = true;
+            const int pg = pg0 + r * kWave + lane;
+            if (pg <= hi && (pid[r] < 0 || (int64_t)pid[r] >= n_pages)) own_bad = true;
         }
     }
-    // this workgroup may read its pages and write partials (the same for every wave)
-    const bool ok = __builtin_amdgcn_readfirstlane(!basic && !tree_bad && __ballot(own_bad) == 0ull);
-    const int T = ks + 1, M = G * T, last = P0 + T - 1;
-    if (ok && c0 <= last && mgroup * kRowsPerGroup < M) {
-    const int c1 = min(c0 + split, last + 1);
+    const bool seq_ok = !basic && !tree_bad;      // the same for every workgroup of the sequence
+    const bool ok = __builtin_amdgcn_readfirstlane(seq_ok && __ballot(own_bad) == 0ull);
+    const bool work = has_work && seq_ok;
+    const int nc = last / split + 1;              // splits of the sequence with keys
 
+    const int m_tile0 = mgroup * kRowsPerGroup + wave * 16;
     const bool active = m_tile0 < M;
     const int m = m_tile0 + l16;
     const bool m_ok = m < M;
     const int jrow = m_ok ? m / G : 0;
     const int h = hk * G + (m_ok ? m % G : 0);
     const int p_m = m_ok ? P0 + jrow : -1;
-    bf16x8 qf[NDS];
-    if (active) {
-        const size_t qoff = ((size_t)(off + jrow) * Hq + h) * D;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds)
-            qf[ds] = as_bf16x8(m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0));
-    }
     f32x4 o[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_lane = 0.f;
-    const int last_page = last / kPage;
-    auto page_of = [&](int pg) -> int64_t {   // pg: absolute page index, wave-uniform
-        const int i = pg - pg0;
-        int id = 0;
-#pragma unroll
-        for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
-            if ((i >> 6) == r) id = __builtin_amdgcn_readlane(pid[r], i & 63);
-        return id;
-    };
 
-    // A tile's 16-byte chunks: chunk it of this thread lies in block b (0..3 K, 4..7 V of
-    // the tile's four pages; the same for the whole wave) at offset ch. The loads carry
-    // no data-dependent work, so all of a tile's loads are in flight together; pages past
-    // the sequence read a valid chunk of the split's first page instead, and their data
-    // is zeroed when the tile is written to LDS, where the V slots past the last written
-    // position are cleared too (a zero softmax weight must not meet what they hold).
-    auto chunk_blk = [&](int it) {
-        return __builtin_amdgcn_readfirstlane((it * kAttnThreads + wave * kWave) / BLK_CH);
-    };
-    auto load_tile = [&](int t0, uint4 (&dst)[PER_THREAD]) {
+    if (work && ok) {
+        const int c1 = min(c0 + split, last + 1);
+        const int last_page = last / kPage;
+        auto page_of = [&](int pg) -> int64_t {   // pg: absolute page index, wave-uniform
+            const int i = pg - pg0;
+            int id = 0;
 #pragma unroll
-        for (int it = 0; it < PER_THREAD; ++it) {
-            const int b = chunk_blk(it), ch = (it * kAttnThreads + tid) % BLK_CH;
-            const int pg = t0 / kPage + (b & 3);
-            const bool real = t0 < c1 && pg <= last_page;
-            const u16* base = (b < 4 ? k_pool : v_pool) + (size_t)(page_of(real ? pg : pg0) * Hkv + hk) * BLK;
-            dst[it] = STREAM ? ld16_stream(base + ch * 8) : ld16(base + ch * 8);
-        }
-    };
-    auto store_tile = [&](int t0, const uint4 (&src)[PER_THREAD]) {
+            for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
+                if ((i >> 6) == r) id = __builtin_amdgcn_readlane(pid[r], i & 63);
+            return id;
+        };
+        // A tile: chunk qc = it * 4 + wave (1 KB each) of block qc / CPB (K blocks of
+        // the tile's pages, then their V blocks) goes to LDS chunk qc. Pages past the
+        // sequence read the split's first page instead; their V is zeroed below.
+        auto load_tile = [&](int t0) {
+            // the tile's page ids first: a read of pid[] waits on the load counter, which
+            // must not happen between two of the tile's LDS loads
+            int64_t page[NP];
 #pragma unroll
-        for (int it = 0; it < PER_THREAD; ++it) {
-            const int b = chunk_blk(it), ch = (it * kAttnThreads + tid) % BLK_CH;
-            const int pg = t0 / kPage + (b & 3);
-            uint4 v = src[it];
-            if (pg > last_page) v = make_uint4(0, 0, 0, 0);
-            if (b >= 4) {
-                // chunk = 8 consecutive V elements: tokens 4 g .. 4 g + 3 of two channels
-                const int tok0 = pg * kPage + 4 * ((ch * 8 % 256) / 64);
-                const uint2 lo = mask_v(make_uint2(v.x, v.y), tok0, last);
-                const uint2 hi = mask_v(make_uint2(v.z, v.w), tok0, last);
-                v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            for (int p = 0; p < NP; ++p) {
+                const int pg = t0 / kPage + p;
+                page[p] = page_of(pg <= last_page ? pg : pg0);
             }
-            st16(smem + (it * kAttnThreads + tid) * 8, v);
-        }
-    };
-    // Chain rows: in a tile that reaches the new rows, those rows' K and V are taken
-    // from k_new / v_new (the bytes the append writes to the pool, which this kernel
-    // itself may be writing), over the staged pool bytes; one item per (row, 8
-    // channels): a 16-byte K chunk and 8 V elements (each in its token's slot of a
-    // 4-token group).
-    auto new_rows_tile = [&](int t0) {
-        const int r_lo = max(t0, P0), r_hi = min(t0 + kKT - 1, last);
-        constexpr int dch = D / 8;
-        const int n_it = (r_hi - r_lo + 1) * dch;
-        for (int i = tid; i < n_it; i += kAttnThreads) {
-            const int tp = r_lo + i / dch, dc = i % dch;
-            const size_t src = ((size_t)(off + tp - P0) * Hkv + hk) * D + dc * 8;
-            const uint4 kv = ld16(k_new + src), vv = ld16(v_new + src);
-            const int p = (tp - t0) / kPage, t = tp % kPage;
-            st16(smem + p * BLK + k_off(t, dc * 8), kv);
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                smem[(4 + p) * BLK + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
-        }
-    };
-    auto use_tile = [&](int t0, const uint4 (&stg)[PER_THREAD], auto refill) {
-        __syncthreads();  // previous tile's LDS reads are done
-        store_tile(t0, stg);
-        if (t0 + kKT > P0) {
-            __syncthreads();   // the staged pool bytes are in place
-            new_rows_tile(t0);
-        }
-        __syncthreads();
-        refill();
-        if (!active) return;
-        // full: every row keeps every key of the tile (chain: the tile ends at or before
-        // the first row's position; tree: at or before the root)
-        const bool full = t0 + kKT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
-        const uint64_t win = (TREE && !full) ? tree_window(s_mask[jrow], t0 - P0 + 64) : 0ull;
-        const LdsTile<D> src{smem + lane * 8, smem + 4 * BLK + lane * 4};
-        TM::template run<TREE>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
-    };
-    // The next tile is requested into registers while the current one is used from LDS.
-    uint4 stage[PER_THREAD];
-    load_tile(c0, stage);
-    if constexpr (TREE) {
-        // Ancestor masks, built while the first tile's loads are in flight (nodes past
-        // k_s are never read). Invariant: mask(j) holds the nodes from j up to, not
-        // including, anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)),
-        // doubling the covered distance. The root is its own ancestor (mask {0}), and
-        // depth <= ks, so ceil(log2(ks + 1)) rounds reach it from every node.
-        uint4 mk = make_uint4(0, 0, 0, 0);
-        if (tid <= ks) {
-            mk.x = tid < 32 ? 1u << tid : 0u;
-            mk.y = tid >= 32 && tid < 64 ? 1u << (tid - 32) : 0u;
-            mk.z = tid >= 64 && tid < 96 ? 1u << (tid - 64) : 0u;
-            mk.w = tid >= 96 ? 1u << (tid - 96) : 0u;
-            s_anc[tid] = tid == 0 ? 0 : par_i;
-            s_mask[tid] = mk;
-        }
-        __syncthreads();
-        for (int reach = 1; reach <= ks; reach *= 2) {
-            int a2 = 0;
-            uint4 m2 = make_uint4(0, 0, 0, 0);
-            if (tid <= ks) {
-                const int an = s_anc[tid];
-                a2 = s_anc[an];
-                m2 = s_mask[an];
+            for (int it = 0; it < C::WAVE_CH; ++it) {
+                const int qc = it * 4 + wave;
+                const int b = qc / C::CPB, part = qc % C::CPB;
+                int64_t pgid = page[0];
+#pragma unroll
+                for (int p = 1; p < NP; ++p)
+                    if ((b % NP) == p) pgid = page[p];
+                const u16* src = (b < NP ? k_pool : v_pool) + (size_t)(pgid * Hkv + hk) * BLK + part * 512 + lane * 8;
+                __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(smem + qc * 512), 16, 0,
+                                                 STREAM ? 2 : 0);   // 2: non-temporal
             }
-            __syncthreads();
+        };
+        // Tiles that reach the new rows: V slots past the last position are zeroed (a
+        // zero softmax weight must not meet what they hold) and the new rows' K and V
+        // are taken from k_new / v_new (the bytes the append writes, which this kernel
+        // itself may be writing to the pool).
+        auto fix_tile = [&](int t0) {
+            constexpr int VW = BLK / 4;    // 8-byte V words per block
+            for (int i = tid; i < NP * VW; i += kAttnThreads) {
+                const int p = i / VW, wi = i % VW;
+                const int pg = t0 / kPage + p;
+                if (pg * kPage + kPage - 1 <= last) continue;
+                const int tok0 = pg * kPage + 4 * ((wi * 4 % 256) / 64);
+                uint2* w = reinterpret_cast<uint2*>(smem + (NP + p) * BLK) + wi;
+                *w = mask_v(*w, tok0, last);
+            }
+            const int r_lo = max(t0, P0), r_hi = min(t0 + KT - 1, last);
+            constexpr int dch = D / 8;
+            const int n_it = (r_hi - r_lo + 1) * dch;
+            for (int i = tid; i < n_it; i += kAttnThreads) {
+                const int tp = r_lo + i / dch, dc = i % dch;
+                const size_t src = ((size_t)(off + tp - P0) * Hkv + hk) * D + dc * 8;
+                const uint4 kv = ld16(k_new + src), vv = ld16(v_new + src);
+                const int p = (tp - t0) / kPage, t = tp % kPage;
+                st16(smem + p * BLK + k_off(t, dc * 8), kv);
+                const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    smem[(NP + p) * BLK + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+            }
+        };
+        load_tile(c0);
+        bf16x8 qf[NDS];
+        if (active) {
+            const size_t qoff = ((size_t)(off + jrow) * Hq + h) * D;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds)
+                qf[ds] = as_bf16x8(m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0));
+        }
+        if constexpr (TREE) {
+            // Ancestor masks, built while the first tile's loads are in flight (nodes past
+            // k_s are never read). Invariant: mask(j) holds the nodes from j up to, not
+            // including, anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)),
+            // doubling the covered distance. The root is its own ancestor (mask {0}), and
+            // depth <= ks, so ceil(log2(ks + 1)) rounds reach it from every node.
+            uint4 mk = make_uint4(0, 0, 0, 0);
             if (tid <= ks) {
-                mk.x |= m2.x;
-                mk.y |= m2.y;
-                mk.z |= m2.z;
-                mk.w |= m2.w;
-                s_anc[tid] = a2;
+                mk.x = tid < 32 ? 1u << tid : 0u;
+                mk.y = tid >= 32 && tid < 64 ? 1u << (tid - 32) : 0u;
+                mk.z = tid >= 64 && tid < 96 ? 1u << (tid - 64) : 0u;
+                mk.w = tid >= 96 ? 1u << (tid - 96) : 0u;
+                s_anc[tid] = tid == 0 ? 0 : par_i;
                 s_mask[tid] = mk;
             }
             __syncthreads();
+            for (int reach = 1; reach <= ks; reach *= 2) {
+                int a2 = 0;
+                uint4 m2 = make_uint4(0, 0, 0, 0);
+                if (tid <= ks) {
+                    const int an = s_anc[tid];
+                    a2 = s_anc[an];
+                    m2 = s_mask[an];
+                }
+                __syncthreads();
+                if (tid <= ks) {
+                    mk.x |= m2.x;
+                    mk.y |= m2.y;
+                    mk.z |= m2.z;
+                    mk.w |= m2.w;
+                    s_anc[tid] = a2;
+                    s_mask[tid] = mk;
+                }
+                __syncthreads();
+            }
+        }
+        for (int t0 = c0; t0 < c1; t0 += KT) {
+            // this wave's LDS loads of the tile have landed; after the barrier, every wave's
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (t0 + KT > P0) {
+                fix_tile(t0);
+                __syncthreads();
+            }
+            if (active) {
+                // full: every row keeps every key of the tile (chain: the tile ends at or
+                // before the first row's position; tree: at or before the root)
+                const bool full = t0 + KT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
+                const uint64_t win = (TREE && !full) ? tree_window(s_mask[jrow], t0 - P0 + 64) : 0ull;
+                const LdsTile<D> src{smem + lane * 8, smem + NP * BLK + lane * 4};
+                TM::template run<TREE, NP>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
+            }
+            if (t0 + KT < c1) {
+                __syncthreads();              // every wave is done reading the tile
+                load_tile(t0 + KT);
+            }
         }
     }
-    for (int t0 = c0; t0 < c1; t0 += kKT)
-        use_tile(t0, stage, [&] {
-            if (t0 + kKT < c1) load_tile(t0 + kKT, stage);
-        });
-    if (active) {
-        const size_t idx = ((size_t)(off + jrow) * Hq + h) * n_splits + c;
-        store_partial<D>(o, m_run, l_lane, m_ok, p_m, c0, idx, lq, part_ml, part_o);
+
+    // ---- rows of a single-split sequence are final; otherwise the split partial ----
+    if (work && ok && active && m_ok) {
+        float l_tot = l_lane + __shfl_xor(l_lane, 16);
+        l_tot = l_tot + __shfl_xor(l_tot, 32);
+        if (nc == 1) {
+            // the merge of one split is the same arithmetic (weight exp2(0) = 1, sum l)
+            store_out<D>(o, 1.f / l_tot, out + ((size_t)(off + jrow) * Hq + h) * D + lq * 4);
+        } else if (p_m >= c0) {
+            // rows whose keys all lie before this split need no partial (the merge reads
+            // splits 0 .. p / split of a row at position p)
+            const size_t idx = ((size_t)(off + jrow) * Hq + h) * n_splits + c;
+            if (lq == 0) part_ml[idx] = make_float2(m_run, l_tot);
+            float* po = part_o + idx * D + lq * 4;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+        }
     }
-    }   // this workgroup's tiles
+
+    // ---- the sequence's status (one workgroup) and the append of this kv head's
+    // new rows that fall in this split (the row-group-0 workgroups) ---------------
     {
-        // the sequence's records (one workgroup per sequence) and the append of this kv
-        // head's new rows that fall in this split (the workgroups of row group 0)
-        const bool lead = hk == 0 && c == 0 && mgroup == 0;
-        const bool writer = mgroup == 0 && !basic && !tree_bad && c0 <= last && c0 + split > P0;
+        const bool writer = mgroup == 0 && seq_ok && has_work && c0 + split > P0;
         if (!lead && !writer) return;
         int flags = basic | (tree_bad ? SPEC_STATUS_BAD_TREE : 0);
         if (pos_ok && ks >= 0) {
@@ -478,10 +507,10 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_ker
                         flags |= SPEC_STATUS_BAD_PAGE;
             }
         }
+        // bitwise OR over the workgroup: across each wave, then across the 4 waves
 #pragma unroll
         for (int d = 32; d > 0; d >>= 1) flags |= __shfl_xor(flags, d);
-        int* s_fl = reinterpret_cast<int*>(smem);
-        __syncthreads();   // the tiles' LDS reads are done
+        __shared__ int s_fl[4];
         if (lane == 0) s_fl[wave] = flags;
         __syncthreads();
         const int bits = s_fl[0] | s_fl[1] | s_fl[2] | s_fl[3];
@@ -490,10 +519,12 @@ __global__ __launch_bounds__(kAttnThreads, D <= 128 ? 3 : 2) void attn_split_ker
                 status[s] = bits;
                 if (s == 0) *packing_ok = packed;
             }
-            // per-row record for the combine (only when the packing is defined; otherwise
-            // the combine writes nothing)
+            // per-row records for the merge kernel (only when the packing is defined;
+            // otherwise it writes nothing): the splits to merge, 0 when the sequence is
+            // skipped or its rows were written here
             if (packed)
-                for (int j = tid; j <= ks; j += kAttnThreads) rows[off + j] = RowRec{P0 + j, bits ? 0 : (P0 + j) / split + 1};
+                for (int j = tid; j <= ks; j += kAttnThreads)
+                    rows[off + j] = RowRec{P0 + j, (bits || nc == 1) ? 0 : (P0 + j) / split + 1};
         }
         if (!writer || bits) return;
         // 8 channels (one 16-byte chunk of a row) per item
@@ -599,23 +630,21 @@ static AttnWs attn_ws_layout(int32_t R, int32_t Hq, int32_t D, int64_t n_splits)
 }
 
 template <int D>
-static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* pt,
-                        int max_pages, const int32_t* pos, const int32_t* k, int kmax,
-                        RowRec* rows, int32_t* packing_ok, int B, int R, int Hq, int Hkv, float scale,
-                        int split, int n_splits, float2* ml, float* po, u16* out, const int32_t* parent,
-                        const u16* k_new, const u16* v_new, int64_t n_pages, int32_t* status, hipStream_t st) {
+static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* pt, int max_pages,
+                        const int32_t* pos, const int32_t* k, int kmax, RowRec* rows, int32_t* packing_ok, int B,
+                        int R, int Hq, int Hkv, float scale, int split, int n_splits, float2* ml, float* po, u16* out,
+                        const int32_t* parent, const u16* k_new, const u16* v_new, int64_t n_pages,
+                        int32_t* status, hipStream_t st) {
     const int kv_rows = (Hq / Hkv) * (kmax + 1);   // most query rows of one kv head
     const int mgroups = (kv_rows + kRowsPerGroup - 1) / kRowsPerGroup;
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
     // Non-temporal pool reads for long contexts (splits of >= kStreamSplit tokens,
-    // i.e. page tables of more than 32K tokens): ragged 904 -> 837 us, long 442 ->
-    // 401 us; for short pools they were slower (b16k4 33.4 -> 36.0, b16tree 50.7 ->
-    // 57.1 us), so those keep the default policy.
+    // i.e. page tables of more than 32K tokens).
     auto go = [&](auto tree_c, auto stream_c) {
         constexpr bool T = decltype(tree_c)::value, S = decltype(stream_c)::value;
-        hipLaunchKernelGGL((attn_split_kernel<D, T, S>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt,
-                           max_pages, pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, ml, po, parent, kmax, k_new,
-                           v_new, n_pages, B, R, status, rows, packing_ok, k_pool, v_pool);
+        hipLaunchKernelGGL((attn_kernel<D, T, S>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt, max_pages,
+                           pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, rows, packing_ok, ml, po, parent, kmax,
+                           k_new, v_new, n_pages, B, R, status, out, k_pool, v_pool);
     };
     const bool stream_kv = split >= kStreamSplit;
     if (parent) {
