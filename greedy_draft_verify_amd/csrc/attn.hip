@@ -60,6 +60,7 @@ constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup
 constexpr int kStreamSplit = 1024; // splits of at least this many tokens read the pool non-temporally
 constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
 constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
+constexpr int kRemapMaxB = 256;    // batches up to this size dispatch the workgroups with work first
 constexpr float kLog2e = 1.4426950408889634f;
 
 // address-space pointer types of global_load_lds (global source, LDS destination)
@@ -256,16 +257,76 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     __shared__ int s_anc[TREE ? kMaxTreeNodes : 1];                    // tree rows: ancestor links
     __shared__ uint4 s_mask[TREE ? kMaxTreeNodes : 1];                 // tree rows: ancestor masks
 
-    const int hk = blockIdx.x % Hkv;
-    const int c = (blockIdx.x / Hkv) % n_splits;
-    const int mgroup = blockIdx.x / Hkv / n_splits;
-    const int s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int G = Hq / Hkv;
+    // Row packing (every wave forms it on its own; each k is read by every wave, from
+    // cache) and, for batches of at most kRemapMaxB sequences, the work list: the
+    // launch's workgroups are numbered in dispatch order and mapped onto the (sequence,
+    // row group, split, kv head) items that have work, so that every such workgroup is
+    // dispatched before any without (a sequence whose k or pos is invalid counts one
+    // item, its status). Larger batches use the launch coordinates directly.
+    int hk, c, mgroup, s;
+    long long before = 0, total = 0;
+    int rowbad = 0;
+    if (B <= kRemapMaxB) {
+        const long long wid = (long long)blockIdx.x + (long long)gridDim.x * blockIdx.z;
+        long long run = 0;            // items before the current chunk of 64 sequences
+        int found = -1, f_ks = 0, f_pos = 0;
+        long long f_local = 0;
+#pragma unroll
+        for (int i0 = 0; i0 < kRemapMaxB; i0 += kWave) {
+            if (i0 >= B) break;
+            const int i = i0 + lane;
+            int ki = 0, pi = 0;
+            long long ni = 0, nr = 0;
+            if (i < B) {
+                ki = k[i];
+                pi = pos[i];
+                const bool valid = ki >= 0 && ki <= kmax && pi >= 0 && ((long long)pi + ki) / kPage < max_pages;
+                ni = valid ? (long long)((pi + ki) / split + 1) * Hkv * ((G * (ki + 1) + kRowsPerGroup - 1) / kRowsPerGroup)
+                           : 1;
+                nr = (long long)ki + 1;
+                rowbad |= ki < 0;
+            }
+            long long incl = ni, rincl = nr;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const long long o = __shfl_up(incl, d), ro = __shfl_up(rincl, d);
+                if (lane >= d) {
+                    incl += o;
+                    rincl += ro;
+                }
+            }
+            const unsigned long long hit = __ballot(i < B && wid >= run + incl - ni && wid < run + incl);
+            if (found < 0 && hit) {
+                const int hl = __ffsll((long long)hit) - 1;
+                found = i0 + hl;
+                f_local = wid - (run + __shfl(incl - ni, hl));
+                f_ks = __shfl(ki, hl);
+                f_pos = __shfl(pi, hl);
+                before = total + __shfl(rincl - nr, hl);
+            }
+            run += __shfl(incl, kWave - 1);
+            total += __shfl(rincl, kWave - 1);
+        }
+        rowbad = __ballot(rowbad) != 0ull;
+        if (found < 0) return;        // past the last item
+        s = found;
+        const bool valid = f_ks >= 0 && f_ks <= kmax && f_pos >= 0 && ((long long)f_pos + f_ks) / kPage < max_pages;
+        const int nsp = valid ? (f_pos + f_ks) / split + 1 : 1;
+        hk = (int)(f_local % Hkv);
+        c = (int)((f_local / Hkv) % nsp);
+        mgroup = (int)(f_local / Hkv / nsp);
+    } else {
+        hk = blockIdx.x % Hkv;
+        c = (blockIdx.x / Hkv) % n_splits;
+        mgroup = blockIdx.x / Hkv / n_splits;
+        s = blockIdx.z;
+    }
     const int c0 = c * split;
     const int pg0 = c0 / kPage;
-    // the split's page ids (lane i holds page pg0 + i + 64 r) and the tree parents are
-    // requested with the sequence's metadata: the indexes depend on the launch only
+    // the split's page ids (lane i holds page pg0 + i + 64 r) and the tree parents
     int pid[(kMaxSplit / kPage + kWave - 1) / kWave];
 #pragma unroll
     for (int r = 0; r < (int)(sizeof(pid) / sizeof(int)); ++r)
@@ -273,7 +334,6 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     int par_i = 0;
     if (TREE) par_i = parent[(size_t)s * (kmax + 1) + min(tid, kmax)];
     const int ks = k[s], P0 = pos[s];
-    const int G = Hq / Hkv;
     const int last = P0 + ks;                     // the sequence's last position
     const int T = ks + 1, M = G * T;
     // Splits past the sequence's last position (and row groups past its rows) have no
@@ -282,20 +342,19 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     const bool has_work = ks >= 0 && P0 >= 0 && c0 <= last && mgroup * kRowsPerGroup < M;
     if (!has_work && !lead) return;
 
-    // Row packing: every wave forms it on its own (each k is read by every wave, from cache).
-    long long before = 0, total = 0;
-    int rowbad = 0;
-    for (int i = lane; i < B; i += kWave) {
-        const long long kk = k[i];
-        total += kk + 1;
-        if (i < s) before += kk + 1;
-        rowbad |= kk < 0;
-    }
+    if (B > kRemapMaxB) {
+        for (int i = lane; i < B; i += kWave) {
+            const long long kk = k[i];
+            total += kk + 1;
+            if (i < s) before += kk + 1;
+            rowbad |= kk < 0;
+        }
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        before += __shfl_xor(before, d);
-        total += __shfl_xor(total, d);
-        rowbad |= __shfl_xor(rowbad, d);
+        for (int d = 32; d > 0; d >>= 1) {
+            before += __shfl_xor(before, d);
+            total += __shfl_xor(total, d);
+            rowbad |= __shfl_xor(rowbad, d);
+        }
     }
     const bool packed = __builtin_amdgcn_readfirstlane(!rowbad && total == (long long)R);
     const int off = __builtin_amdgcn_readfirstlane((int)before);
