@@ -841,7 +841,10 @@ def main():
         "attn_roofline": {"kernel": "spec_verify_attn", "bound": "hbm", "achieved": at["achieved"],
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": at["frac"],
                           "algorithmic_bytes": at["algorithmic_bytes"],
-                          "traffic": measured_traffic("attn_split") if wl.name == "b16k4" else None},
+                          # the call's two kernels: the split kernel and the combine
+                          "traffic": (None if wl.name != "b16k4" or measured_traffic("attn_kernel") is None
+                                      or measured_traffic("attn_combine") is None
+                                      else measured_traffic("attn_kernel") + measured_traffic("attn_combine"))},
         "cpu_baseline": cpu,
         **extras,
         "context": "pages' own figure: 6.5 ms per 16-row whole-model verify, RTX 5090 with CUDA graphs "
