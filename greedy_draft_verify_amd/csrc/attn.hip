@@ -32,16 +32,16 @@
 //   2. attn_combine_kernel one wave per (row, q head): merges the row's splits in
 //      ascending order (log-sum-exp weights) and writes bf16.
 //
-// Tree rows (spec_verify_attn_tree; DSSD fast.py, _set_rows and _tree_cycle): the
-// k+1 rows of a sequence are the nodes of a draft tree in creation order; node j
-// still writes slot pos + j, but attends to slots 0..pos and to the slots pos + u of
-// the nodes u on its own path. Each split workgroup checks the parent list and turns
-// it into one 128-bit ancestor mask per node (pointer jumping over the parent links in
-// LDS while its first tile's loads are in flight: after r rounds a node's mask covers
-// its 2^r nearest ancestors). It keeps key slot t for a row iff t <= pos, or bit t - pos of the row's
-// mask is set: for a tile that reaches past pos it shifts the mask into a 64-bit
-// window aligned with the tile. A chain (parent j - 1) keeps exactly the keys
-// t <= pos + j, so it gives the bytes of spec_verify_attn.
+// Tree rows (spec_verify_attn_tree; DSSD fast.py, _set_rows, _tree_cycle and
+// _attention): the k+1 rows of a sequence are the nodes of a draft tree in creation
+// order; node j still writes slot pos + j, but attends to slots 0..pos and then to the
+// nodes of its own path in depth order, exactly as its one-row decode does once the
+// accepted path is compacted into slots pos + 1.. (see "Tree rows as chain rows"
+// below). Each split workgroup checks the parent list and turns it into one 128-bit
+// ancestor mask per node (pointer jumping over the parent links in LDS while its first
+// tile's loads are in flight: after r rounds a node's mask covers its 2^r nearest
+// ancestors); a node's depth is the mask's population count minus one. A chain (parent
+// j - 1) is its own compacted path, so it gives the bytes of spec_verify_attn.
 //
 // Row invariance: splits sit at absolute multiples of kv_split_tokens and steps at
 // absolute multiples of 32; every row's operations run in the same order whichever
@@ -63,9 +63,32 @@ constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit 
 constexpr int kRemapMaxB = 256;    // batches up to this size dispatch the workgroups with work first
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The tree call's LDS beyond the tile, in u16 units from its start: the K rows and the V
+// rows of nodes 1..kmax (row u - 1: D channels), then per node its ancestor mask (16
+// bytes) and ancestor link (4 bytes), then per wave one depth-ordered path (kmax + 1
+// bytes, rounded to 16).
+struct TreeLds {
+    int nv, mask, anc, path, path_stride, end;
+    __host__ __device__ TreeLds(int kmax, int D) {
+        nv = kmax * D;
+        mask = 2 * kmax * D;
+        anc = mask + 8 * (kmax + 1);
+        path_stride = (kmax + 1 + 15) / 16 * 16;
+        path = anc + ((2 * (kmax + 1) + 7) / 8) * 8;
+        end = path + 2 * path_stride;
+    }
+    __host__ __device__ size_t bytes() const { return (size_t)end * 2; }
+};
+
 // address-space pointer types of global_load_lds (global source, LDS destination)
 typedef const __attribute__((address_space(1))) void* global_cptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8;
+typedef __attribute__((address_space(3))) const u32x4* lds_cu4;
+__device__ __forceinline__ uint4 lds_ld16(lds_cu4 p) {
+    const u32x4 v = *p;
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 struct RowRec {
     int32_t p;      // position of the row
@@ -101,11 +124,13 @@ struct TileMath {
     static constexpr int NDS = D / 32;
     static constexpr int NDT = D / 16;
 
-    // win (tree rows only): bit o set iff the row keeps key slot t0 + o
-    template <bool TREE, int NP, class Src>
-    __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int t0, int p_m,
-                                               uint64_t win, bool full, int lq, float scale_log2,
-                                               float& m_run, float& l_lane, f32x4 (&o)[NDT]) {
+    // p_m: the row's position (it keeps the tile's keys t <= p_m; full: every row keeps
+    // every key). A row with p_m < t0 gets only -inf scores, and such a tile leaves its
+    // state exactly as it was: no raise, zero weights, zero sum, and zero P in P V.
+    template <int NP, class Src>
+    __device__ __forceinline__ static void run(const bf16x8 (&qf)[NDS], const Src& src, int t0, int p_m, bool full,
+                                               int lq, float scale_log2, float& m_run, float& l_lane,
+                                               f32x4 (&o)[NDT]) {
         static_assert(NP == 2 || NP == 4, "tiles of 32 or 64 tokens");
         constexpr int NS = 4 * NP;   // scores per lane
         float sc[NS];
@@ -118,16 +143,10 @@ struct TileMath {
             for (int i = 0; i < 4; ++i) sc[4 * p + i] = acc[i] * scale_log2;
         }
         if (!full) {   // some token of the tile lies past some row's position
-            // tree: this lane's tokens are 16 (jj / 4) + 4 lq + jj % 4, so after one
-            // shift by 4 lq every bit sits at a constant offset of a 32-bit half
-            const uint64_t wl = TREE ? win >> (4 * lq) : 0ull;
-            const uint32_t w_lo = (uint32_t)wl, w_hi = (uint32_t)(wl >> 32);
 #pragma unroll
             for (int jj = 0; jj < NS; ++jj) {
                 const int o_t = 16 * (jj >> 2) + 4 * lq + (jj & 3);
-                const uint32_t half = (jj >> 3) ? w_hi : w_lo;
-                const bool keep = TREE ? ((half >> (16 * ((jj >> 2) & 1) + (jj & 3))) & 1u) : (t0 + o_t <= p_m);
-                if (!keep) sc[jj] = -INFINITY;
+                if (t0 + o_t > p_m) sc[jj] = -INFINITY;
             }
         }
         float tmax = sc[0];
@@ -165,6 +184,7 @@ struct TileMath {
     }
 };
 
+
 // Fragments of a 64-token tile read from LDS (4 K blocks, then 4 V blocks).
 template <int D>
 struct LdsTile {
@@ -185,24 +205,39 @@ __device__ __forceinline__ uint2 mask_v(uint2 v, int tok0, int last) {
     return make_uint2(v.x & m0, v.y & m1);
 }
 
-// Bits n .. n + 63 of the 128-bit value hi:lo (0 <= n < 64).
-__device__ __forceinline__ uint64_t funnel64(uint64_t lo, uint64_t hi, int n) {
-    return n == 0 ? lo : (lo >> n) | (hi << (64 - n));
+// Tree rows as chain rows. Node u at depth d_u attends to slots 0..pos and then to the
+// nodes of its path in depth order: the keys of a chain row at position pos + d_u
+// whose slots pos + i hold the path's node at depth i (its one-row decode once the
+// accepted path is compacted). So node u's rows run as that chain row: position
+// pos + d_u, the same tiles, splits and merge. Their keys differ from the tile's slots
+// only at pos + 1 .. pos + d_u and only when the path is not the nodes 1 .. d_u
+// (d_u < u). A tile holding such slots is run once for the other rows; then, per root
+// path through such nodes, the workgroup rewrites the tile's slots pos + i with the
+// path's node at depth i (the others get node i back) and the waves holding those
+// nodes' rows run the tile again. In each run the rows it does not serve get position
+// -1: -inf scores only, which leave a row's state as it was. So each row's arithmetic is the
+// arithmetic of its chain row (an MFMA column's result depends only on that column's
+// operands).
+
+__device__ __forceinline__ int tree_depth(uint4 mk) {   // mk: a node's ancestors and itself
+    return __popc(mk.x) + __popc(mk.y) + __popc(mk.z) + __popc(mk.w) - 1;
 }
 
-// Keep-window of a tree row for the tile starting at key slot t0: bit o says whether
-// slot t0 + o is kept. With u = slot - pos, slots u <= 0 (the committed keys and the
-// root) are always kept and 1 <= u <= 127 follow the ancestor mask; over the 192-bit
-// value [64 ones | mask bits 0..127] (the root's bit forced on) the window is the 64
-// bits from sh = t0 - pos + 64, which a tile that reaches past pos has in 1..191.
-// sh is the same for the whole wave.
-__device__ __forceinline__ uint64_t tree_window(uint4 mk, int sh) {
-    const uint64_t e0 = ~0ull;
-    const uint64_t e1 = ((uint64_t)mk.y << 32 | mk.x) | 1ull;
-    const uint64_t e2 = (uint64_t)mk.w << 32 | mk.z;
-    if (sh < 64) return funnel64(e0, e1, sh);
-    if (sh < 128) return funnel64(e1, e2, sh - 64);
-    return funnel64(e2, 0ull, sh - 128);
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// path[i] = the node at depth i on the way to the node whose ancestor set is mk (a
+// parent has a smaller index than its child, so depth order is index order).
+__device__ __forceinline__ void build_path(uint4 mk, lds_u8 path, int lane) {
+    const uint64_t lo = (uint64_t)mk.y << 32 | mk.x, hi = (uint64_t)mk.w << 32 | mk.z;
+    const uint64_t below = (1ull << lane) - 1ull;
+    wave_sync();
+    if ((lo >> lane) & 1ull) path[__popcll(lo & below)] = (uint8_t)lane;
+    if ((hi >> lane) & 1ull) path[__popcll(lo) + __popcll(hi & below)] = (uint8_t)(64 + lane);
+    wave_sync();
 }
 
 // Writes a 16-row query tile's normalised output: lane l holds row l % 16, channels
@@ -238,10 +273,12 @@ struct AttnCfg {
     // workgroups per CU (LDS: one tile, 16 / 32 / 64 KB; at D = 256 32-token tiles at
     // three per CU measured slower, long 441 vs 423 us)
     static constexpr int MINB = D <= 64 ? 5 : D <= 128 ? 4 : 2;
+    // tree rows (the node runs' bookkeeping): at D = 64, five per CU spill inside the tile loop
+    static constexpr int MINB_TREE = D <= 128 ? 4 : 2;
 };
 
 template <int D, bool TREE, bool STREAM>
-__global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, TREE ? AttnCfg<D>::MINB_TREE : AttnCfg<D>::MINB) void attn_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k_pool, const u16* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ k, int Hq, int Hkv, float scale_log2, int split, int n_splits,
@@ -254,8 +291,15 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     constexpr int KT = C::KT, NP = C::NP, BLK = C::BLK, NDS = TM::NDS, NDT = TM::NDT;
     static_assert(C::NCH % 4 == 0 && C::CPB >= 2, "a tile must split into whole 1 KB chunks per wave");
     __shared__ __attribute__((aligned(16))) u16 smem[2 * NP * BLK];   // K blocks, then V blocks
-    __shared__ int s_anc[TREE ? kMaxTreeNodes : 1];                    // tree rows: ancestor links
-    __shared__ uint4 s_mask[TREE ? kMaxTreeNodes : 1];                 // tree rows: ancestor masks
+    // tree rows, sized at launch from kmax (TreeLds): the new rows 1..k (K, then V), the
+    // ancestor masks and links, and a path per wave
+    extern __shared__ __attribute__((aligned(16))) u16 s_dyn[];
+    const TreeLds tl(kmax, D);
+    u16* const s_nk = s_dyn;
+    u16* const s_nv = s_dyn + tl.nv;
+    uint4* const s_mask = reinterpret_cast<uint4*>(s_dyn + tl.mask);
+    int* const s_anc = reinterpret_cast<int*>(s_dyn + tl.anc);
+    uint8_t* const s_path = reinterpret_cast<uint8_t*>(s_dyn + tl.path);
 
     const int tid = threadIdx.x, lane = tid % kWave, l16 = lane % 16, lq = lane / 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -316,7 +360,9 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
         const bool valid = f_ks >= 0 && f_ks <= kmax && f_pos >= 0 && ((long long)f_pos + f_ks) / kPage < max_pages;
         const int nsp = valid ? (f_pos + f_ks) / split + 1 : 1;
         hk = (int)(f_local % Hkv);
+        // tree rows: a sequence's last splits first (they hold the node runs, the longest work)
         c = (int)((f_local / Hkv) % nsp);
+        if (TREE) c = nsp - 1 - c;
         mgroup = (int)(f_local / Hkv / nsp);
     } else {
         hk = blockIdx.x % Hkv;
@@ -366,7 +412,12 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     if constexpr (TREE) {
         bool bad = false;
         if (ks >= 0 && ks <= kmax && tid <= ks) bad = tid == 0 ? par_i != -1 : (par_i < 0 || par_i >= tid);
-        tree_bad = __syncthreads_or(bad) != 0;
+        // workgroup OR through 4 words of LDS (__syncthreads_or would take 256 bytes)
+        __shared__ int s_tb[4];
+        const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0ull;
+        if (lane == 0) s_tb[wave] = wave_bad;
+        __syncthreads();
+        tree_bad = (s_tb[0] | s_tb[1] | s_tb[2] | s_tb[3]) != 0;
     }
     // this split's own page ids (the whole list is checked by the workgroups that write
     // the status or append rows)
@@ -390,7 +441,7 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
     const bool m_ok = m < M;
     const int jrow = m_ok ? m / G : 0;
     const int h = hk * G + (m_ok ? m % G : 0);
-    const int p_m = m_ok ? P0 + jrow : -1;
+    int p_m = m_ok ? P0 + jrow : -1;              // tree rows: P0 + depth, set below
     f32x4 o[NDT];
 #pragma unroll
     for (int i = 0; i < NDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -427,7 +478,11 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
 #pragma unroll
                 for (int p = 1; p < NP; ++p)
                     if ((b % NP) == p) pgid = page[p];
-                const u16* src = (b < NP ? k_pool : v_pool) + (size_t)(pgid * Hkv + hk) * BLK + part * 512 + lane * 8;
+                // the block's address is the same for the whole wave: kept in scalar registers
+                const uint64_t blk = (uint64_t)((b < NP ? k_pool : v_pool) + (size_t)(pgid * Hkv + hk) * BLK + part * 512);
+                const uint64_t blk_s = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(blk >> 32)) << 32 |
+                                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)blk);
+                const u16* src = reinterpret_cast<const u16*>(blk_s) + lane * 8;
                 __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(smem + qc * 512), 16, 0,
                                                  STREAM ? 2 : 0);   // 2: non-temporal
             }
@@ -470,6 +525,17 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
                 qf[ds] = as_bf16x8(m_ok ? ld16(q + qoff + ds * 32 + lq * 8) : make_uint4(0, 0, 0, 0));
         }
         if constexpr (TREE) {
+            // The new rows' LDS copy (read on tiles past the root), when this split has
+            // such tiles.
+            if (c1 > P0 + 1) {
+                constexpr int dch = D / 8;
+                for (int i = tid; i < ks * dch; i += kAttnThreads) {
+                    const int u = 1 + i / dch, dc = i % dch;
+                    const size_t src = ((size_t)(off + u) * Hkv + hk) * D + dc * 8;
+                    st16(s_nk + (u - 1) * D + dc * 8, ld16(k_new + src));
+                    st16(s_nv + (u - 1) * D + dc * 8, ld16(v_new + src));
+                }
+            }
             // Ancestor masks, built while the first tile's loads are in flight (nodes past
             // k_s are never read). Invariant: mask(j) holds the nodes from j up to, not
             // including, anc(j); a round adds mask(anc(j)) and moves anc(j) to anc(anc(j)),
@@ -504,6 +570,7 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
                 }
                 __syncthreads();
             }
+            if (m_ok) p_m = P0 + tree_depth(s_mask[jrow]);
         }
         for (int t0 = c0; t0 < c1; t0 += KT) {
             // this wave's LDS loads of the tile have landed; after the barrier, every wave's
@@ -513,13 +580,69 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
                 fix_tile(t0);
                 __syncthreads();
             }
-            if (active) {
-                // full: every row keeps every key of the tile (chain: the tile ends at or
-                // before the first row's position; tree: at or before the root)
-                const bool full = t0 + KT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
-                const uint64_t win = (TREE && !full) ? tree_window(s_mask[jrow], t0 - P0 + 64) : 0ull;
-                const LdsTile<D> src{smem + lane * 8, smem + NP * BLK + lane * 4};
-                TM::template run<TREE, NP>(qf, src, t0, p_m, win, full, lq, scale_log2, m_run, l_lane, o);
+            // full: every row keeps every key of the tile (chain: the tile ends at or before
+            // the first row's position; tree: at or before the root)
+            const bool full = t0 + KT - 1 <= P0 + (TREE ? 0 : m_tile0 / G);
+            const LdsTile<D> src{smem + lane * 8, smem + NP * BLK + lane * 4};
+            // Tree rows: run 0 serves the rows whose keys here are the tile's slots. The
+            // nodes of the row group whose paths have slots here are then served in runs of
+            // one root path each: the tile's new-row slots are rewritten with the path of the
+            // remaining such node of highest index n (no remaining node lies below it), and
+            // the run serves n and the remaining such nodes above it, whose paths are
+            // prefixes of n's (a row masks the slots past its own depth). One instance of the
+            // tile code serves every run.
+            const int dep = p_m - P0;
+            const bool own = TREE && !full && m_ok && dep < jrow && P0 + dep >= t0 && P0 + 1 <= t0 + KT - 1;
+            const int i_lo = max(1, t0 - P0), i_hi = min(ks, t0 + KT - 1 - P0);   // new-row slots pos + i here
+            uint32_t rem[4] = {0u, 0u, 0u, 0u};   // nodes still to serve, one bit each
+            if (TREE && !full && i_lo <= i_hi) {
+                const int g_hi = min((mgroup * kRowsPerGroup + kRowsPerGroup - 1) / G, ks);
+#pragma unroll 1
+                for (int n = max(mgroup * kRowsPerGroup / G, 1); n <= g_hi; ++n) {
+                    const int d = __builtin_amdgcn_readfirstlane(tree_depth(lds_ld16((lds_cu4)s_mask + n)));
+                    if (d < n && P0 + d >= t0) rem[n >> 5] |= 1u << (n & 31);
+                }
+            }
+            const lds_u8 path = (lds_u8)(s_path + wave * tl.path_stride);
+            bool pending = own;                   // this lane's row still waits for its run
+            int p_run = own ? -1 : p_m;           // run 0
+            bool first = true;
+#pragma unroll 1
+            for (;;) {
+                if (active && (first || __builtin_amdgcn_ballot_w64(p_run >= 0)))
+                    TM::template run<NP>(qf, src, t0, p_run, full && first, lq, scale_log2, m_run, l_lane, o);
+                if (!TREE || !(rem[0] | rem[1] | rem[2] | rem[3])) break;
+                first = false;
+                const int w = rem[3] ? 3 : rem[2] ? 2 : rem[1] ? 1 : 0;
+                const int n = 32 * w + 31 - __clz(rem[w]);
+                const uint4 mk = lds_ld16((lds_cu4)s_mask + n);
+                const int d = __builtin_amdgcn_readfirstlane(tree_depth(mk));
+                const uint32_t mw[4] = {(uint32_t)__builtin_amdgcn_readfirstlane(mk.x),
+                                        (uint32_t)__builtin_amdgcn_readfirstlane(mk.y),
+                                        (uint32_t)__builtin_amdgcn_readfirstlane(mk.z),
+                                        (uint32_t)__builtin_amdgcn_readfirstlane(mk.w)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rem[q] &= ~mw[q];
+                // this run serves the rows of n and of the waiting nodes above it
+                const uint32_t jw = jrow < 32 ? mw[0] : jrow < 64 ? mw[1] : jrow < 96 ? mw[2] : mw[3];
+                const bool served = pending && ((jw >> (jrow & 31)) & 1u);
+                pending = pending && !served;
+                p_run = served ? p_m : -1;
+                build_path(mk, path, lane);
+                __syncthreads();              // the tile's previous run is done
+                constexpr int dch = D / 8;
+                for (int it = tid; it < (i_hi - i_lo + 1) * dch; it += kAttnThreads) {
+                    const int i = i_lo + it / dch, dc = it % dch;
+                    const int u = i <= d ? (int)path[i] : i;
+                    const int tp = P0 + i, pp = (tp - t0) / kPage, t = tp % kPage;
+                    st16(smem + pp * BLK + k_off(t, dc * 8), ld16(s_nk + (u - 1) * D + dc * 8));
+                    const uint4 vv = ld16(s_nv + (u - 1) * D + dc * 8);
+                    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        smem[(NP + pp) * BLK + v_off(t, dc * 8 + e)] = (u16)((e & 1) ? (vw[e / 2] >> 16) : (vw[e / 2] & 0xffffu));
+                }
+                __syncthreads();
             }
             if (t0 + KT < c1) {
                 __syncthreads();              // every wave is done reading the tile
@@ -582,8 +705,11 @@ __global__ __launch_bounds__(kAttnThreads, AttnCfg<D>::MINB) void attn_kernel(
             // otherwise it writes nothing): the splits to merge, 0 when the sequence is
             // skipped or its rows were written here
             if (packed)
-                for (int j = tid; j <= ks; j += kAttnThreads)
-                    rows[off + j] = RowRec{P0 + j, (bits || nc == 1) ? 0 : (P0 + j) / split + 1};
+                for (int j = tid; j <= ks; j += kAttnThreads) {
+                    // tree rows: the position of the row's chain row (the masks exist when bits == 0)
+                    const int pj = P0 + ((TREE && !bits) ? tree_depth(s_mask[j]) : j);
+                    rows[off + j] = RowRec{pj, (bits || nc == 1) ? 0 : pj / split + 1};
+                }
         }
         if (!writer || bits) return;
         // 8 channels (one 16-byte chunk of a row) per item
@@ -669,6 +795,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// A tree workgroup's whole LDS: the tile (4 K and 4 V blocks), two 4-word flag
+// arrays and TreeLds. gfx950 gives a workgroup 160 KB.
+static size_t tree_lds_bytes(int D, int kmax) {
+    return (size_t)2 * kKT * D * sizeof(u16) + 32 + TreeLds(kmax, D).bytes();
+}
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+
 static int64_t split_count(int32_t max_pages, int32_t split) {
     return ((int64_t)max_pages * kPage + split - 1) / split;
 }
@@ -699,9 +832,10 @@ static void launch_attn(const u16* q, u16* k_pool, u16* v_pool, const int32_t* p
     dim3 grid(mgroups * n_splits * Hkv, 1, B);
     // Non-temporal pool reads for long contexts (splits of >= kStreamSplit tokens,
     // i.e. page tables of more than 32K tokens).
+    const size_t node_lds = parent ? TreeLds(kmax, D).bytes() : 0;
     auto go = [&](auto tree_c, auto stream_c) {
         constexpr bool T = decltype(tree_c)::value, S = decltype(stream_c)::value;
-        hipLaunchKernelGGL((attn_kernel<D, T, S>), grid, dim3(kAttnThreads), 0, st, q, k_pool, v_pool, pt, max_pages,
+        hipLaunchKernelGGL((attn_kernel<D, T, S>), grid, dim3(kAttnThreads), node_lds, st, q, k_pool, v_pool, pt, max_pages,
                            pos, k, Hq, Hkv, scale * kLog2e, split, n_splits, rows, packing_ok, ml, po, parent, kmax,
                            k_new, v_new, n_pages, B, R, status, out, k_pool, v_pool);
     };
@@ -767,6 +901,9 @@ static int verify_attn_impl(const char* name, const spec_bf16* q, const spec_bf1
     if (kmax < 0 || (long long)(Hq / Hkv) * (kmax + 1) > kMaxRowsPerKvHead)
         return fail(SPEC_EINVAL, "%s: kmax=%d (need 0 <= (Hq/Hkv)*(kmax+1) <= %d)", name, kmax, kMaxRowsPerKvHead);
     if (max_pages < 1 || n_pages < 1) return fail(SPEC_EINVAL, "%s: max_pages=%d n_pages=%lld", name, max_pages, (long long)n_pages);
+    if (parent && tree_lds_bytes(D, kmax) > kLdsPerWorkgroup)
+        return fail(SPEC_EINVAL, "%s: kmax=%d at D=%d needs %zu bytes of LDS per workgroup (> %zu)", name, kmax, D,
+                    tree_lds_bytes(D, kmax), kLdsPerWorkgroup);
     if (!(scale > 0.f)) return fail(SPEC_EINVAL, "%s: scale must be > 0", name);
     if (kv_split_tokens < 0 || kv_split_tokens % kKT || kv_split_tokens > kMaxSplit)
         return fail(SPEC_EINVAL, "%s: kv_split_tokens=%d not a multiple of 64 in 0..%d", name, kv_split_tokens, kMaxSplit);

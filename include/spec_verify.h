@@ -362,7 +362,15 @@ int spec_delta_verify_rollback(int32_t mode, const spec_bf16* q, const spec_bf16
  *   t in {0, ..., pos[s]}  followed by  {pos[s] + u : u in path(j)}
  * (ascending slot order, which is the path's root-to-leaf order), i.e.
  *   out[r, h, :] = sum_t softmax_t(scale * q[r,h,:] . K_t[hk,:]) V_t[hk,:].
- * Extra limit: kmax <= 127. workspace: spec_verify_attn_tree_workspace_bytes. */
+ * Bytes: row j's output is bit-identical to spec_verify_attn's one-row decode of
+ * the same query at position pos[s] + depth(j) (same kv_split_tokens) over a pool
+ * whose slots pos[s] + 1 .. pos[s] + depth(j) hold path(j)'s K/V in order, i.e. to
+ * its decode after the accepted path is compacted (DSSD fast.py _attention: one
+ * query per row over its exact path). Inputs are finite.
+ * Extra limits: kmax <= 127, and the workgroup's LDS (the 64-token tile, K and V
+ * of kmax new rows, 20 bytes per node and 4 paths) must fit gfx950's 160 KB: at
+ * D = 256 that means kmax <= 93 (SPEC_EINVAL otherwise).
+ * workspace: spec_verify_attn_tree_workspace_bytes. */
 size_t spec_verify_attn_tree_workspace_bytes(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
                                              int32_t max_pages, int32_t kv_split_tokens, int32_t kmax);
 int spec_verify_attn_tree(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16* v_new,

@@ -97,6 +97,10 @@ def test_host_argument_checks():
     assert tree(None, 3, 1 << 30) == -1 and b"parent" in L.spec_last_error()
     assert tree(p, 128, 1 << 30) == -1 and b"kmax" in L.spec_last_error()
     assert tree(p, 3, need - 1) == -4
+    # the LDS limit: at D = 256 a tree call holds K and V of kmax new rows beside the tile
+    tree256 = lambda kmax: L.spec_verify_attn_tree(p, p, p, p, p, 10, p, 4, p, p, p, kmax, 2, 8, 1, 1, 256, 0.1, 0,
+                                                   p, p, 1 << 30, p, None)
+    assert tree256(94) == -1 and b"LDS" in L.spec_last_error()
     acc = lambda kmax, parent, path: L.spec_tree_accept(p, p, kmax, p, parent, None, 0, 100, 2, 8, p, p, p, p, p,
                                                         p, path, p, None)
     assert acc(128, p, p) == -1 and b"kmax" in L.spec_last_error()

@@ -6,9 +6,9 @@ plus the slots of its own path; the acceptance walk follows the child whose toke
 the current node's greedy token; the accepted path's K/V moves to slots pos + 1...
 
 Bars: tree attention within |err| <= 2e-2 + 1e-2 |ref| of the oracle, the K/V append
-and the compaction bit-exact, the acceptance walk bit-exact; a chain-shaped tree
-gives the chain entry point's bytes, and a row's bytes do not depend on the nodes
-outside its path.
+and the compaction bit-exact, the acceptance walk bit-exact; every tree row gives the
+bytes of its one-row decode after compaction (so a chain-shaped tree gives the chain
+entry point's bytes, and a row's bytes do not depend on the nodes outside its path).
 """
 import math
 
@@ -86,6 +86,99 @@ def test_chain_tree_gives_chain_bytes(dev, wl, split):
     assert torch.equal(out_t.view(torch.int16), out_c.view(torch.int16))
     assert torch.equal(kp_t.view(torch.int16), kp_c.view(torch.int16))
     assert torch.equal(vp_t.view(torch.int16), vp_c.view(torch.int16))
+
+
+def _paths(parent, ks):
+    """Each node's path from the root, in depth order."""
+    paths = []
+    for j in range(ks + 1):
+        p, u = [], j
+        while u != -1:
+            p.append(u)
+            u = int(parent[u])
+        paths.append(p[::-1])
+    return paths
+
+
+def _assert_rows_equal(out, ref, x, parent, what):
+    """Bytes equal; otherwise names the first differing rows (sequence, node, depth)."""
+    a, b = out.view(torch.int16).cpu().numpy(), ref.view(torch.int16).cpu().numpy()
+    bad = np.nonzero((a != b).reshape(a.shape[0], -1).any(axis=1))[0]
+    if len(bad):
+        off = np.concatenate([[0], np.cumsum(x.k + 1)])
+        desc = []
+        for r in bad[:8]:
+            s = int(np.searchsorted(off, r, side="right") - 1)
+            j = int(r - off[s])
+            d = len(_paths(parent[s], int(x.k[s]))[j]) - 1
+            desc.append(f"seq {s} node {j} depth {d} pos {int(x.pos[s])}")
+        raise AssertionError(f"{what}: {len(bad)} of {a.shape[0]} rows differ: " + "; ".join(desc))
+
+
+def _one_row_decodes(x, parent, dev, split):
+    """Every tree row as its one-row decode once its path is compacted: for node j of
+    sequence s at depth d, a one-row sequence whose slots pos..pos + d - 1 hold the
+    path's nodes 0 = a_0, .., a_{d-1} (appended by a chain call) and whose row is node
+    j's query at position pos + d with node j's K/V as its new row. Each such sequence
+    gets its own copies of the pages from pos on. Returns the rows' bytes [R, Hq, D]."""
+    B = len(x.pos)
+    off = np.concatenate([[0], np.cumsum(x.k + 1)])
+    n0 = x.k_pool.shape[0]
+    src_pages, tables, ent = [], [], []
+    for s in range(B):
+        P0 = int(x.pos[s])
+        for j, path in enumerate(_paths(parent[s], int(x.k[s]))):
+            d = len(path) - 1
+            row = x.page_table[s].copy()
+            for pg in range(P0 // 16, (P0 + d) // 16 + 1):
+                src_pages.append(int(row[pg]))
+                row[pg] = n0 + len(src_pages) - 1
+            tables.append(row)
+            ent.append((s, P0, d, [int(off[s] + a) for a in path]))
+    src = torch.tensor(src_pages, dtype=torch.long)
+    kp = torch.cat([x.k_pool, x.k_pool[src]]).to(dev)
+    vp = torch.cat([x.v_pool, x.v_pool[src]]).to(dev)
+    tables = np.stack(tables).astype(np.int32)
+    # the path's nodes above the row go to slots pos .. pos + d - 1
+    pre = [i for i, e in enumerate(ent) if e[2] >= 1]
+    if pre:
+        kk = np.array([ent[i][2] - 1 for i in pre], np.int32)
+        rows = torch.tensor([r for i in pre for r in ent[i][3][:-1]], dtype=torch.long)
+        q0 = torch.zeros((len(rows), x.wl.Hq, x.wl.D), dtype=torch.bfloat16)
+        _, kp, vp, st = gpu_attn(x, dev, kv_split_tokens=split, pos=np.array([ent[i][1] for i in pre], np.int32),
+                                 k=kk, page_table=tables[pre], k_pool=kp, v_pool=vp, q=q0, k_new=x.k_new[rows],
+                                 v_new=x.v_new[rows], kmax=int(kk.max()))
+        assert (st == 0).all()
+    last = torch.tensor([e[3][-1] for e in ent], dtype=torch.long)
+    out, _, _, st = gpu_attn(x, dev, kv_split_tokens=split, pos=np.array([e[1] + e[2] for e in ent], np.int32),
+                             k=np.zeros(len(ent), np.int32), page_table=tables, k_pool=kp, v_pool=vp, q=x.q[last],
+                             k_new=x.k_new[last], v_new=x.v_new[last], kmax=0)
+    assert (st == 0).all()
+    return out
+
+
+@pytest.mark.parametrize("wl", TREE_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("shape", ["trie", "star", "random"])
+@pytest.mark.parametrize("split", [0, 64])
+def test_tree_row_is_its_one_row_decode(dev, wl, shape, split):
+    """DSSD fast.py _attention: a tree row attends to its exact path, so its bytes are
+    those of the one-row decode at pos + depth after the path is compacted."""
+    print(f"tree row = one-row decode {wl.name} {shape} split={split}", flush=True)
+    x, parent = _tree_case(wl, 5, shape)
+    out, _, _, st = gpu_attn_tree(x, parent, dev, kv_split_tokens=split)
+    assert (st == 0).all()
+    ref = _one_row_decodes(x, parent, dev, split)
+    _assert_rows_equal(out, ref, x, parent, f"{wl.name} {shape}")
+
+
+def test_b16tree_rows_are_their_one_row_decodes(dev):
+    """The 16-node tree workload at full size, every row of every sequence."""
+    x = synth.make_verify_inputs("b16tree", seed=0, with_lm_head=False)
+    parent = synth.make_parents(x.k, 0, "b16tree", "trie")
+    out, _, _, st = gpu_attn_tree(x, parent, dev)
+    assert (st == 0).all()
+    ref = _one_row_decodes(x, parent, dev, 0)
+    _assert_rows_equal(out, ref, x, parent, "b16tree")
 
 
 @pytest.mark.parametrize("wl", [TREE_CASES[1], TREE_CASES[3]], ids=lambda w: w.name)
@@ -327,3 +420,36 @@ def test_attention_status_combinations_match_the_oracle(dev, tree):
         else:
             assert np.isnan(out.float().cpu().numpy()).all()
             assert np.array_equal(bits(kp), bits(x.k_pool)) and np.array_equal(bits(vp), bits(x.v_pool))
+
+
+@pytest.mark.parametrize("tree", [False, True])
+def test_attention_ignores_workspace_contents(dev, tree):
+    """The merge reads only partials this call wrote: a workspace full of 0xFF bytes (NaN
+    partials) gives the bytes of a zeroed one, at the full b16 sizes."""
+    import greedy_draft_verify_amd as gdv
+    x = synth.make_verify_inputs("b16tree" if tree else "b16k4", seed=0, device=dev, with_lm_head=False)
+    wl = x.wl
+    B = len(x.pos)
+    pt, pos, k = (torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev) for a in (x.page_table, x.pos, x.k))
+    parent = torch.from_numpy(synth.make_parents(x.k, 0, "b16tree", "trie")).to(dev) if tree else None
+    if tree:
+        nbytes = gdv.verify_attn_tree_workspace_bytes(B, x.R, wl.Hq, wl.Hkv, wl.D, x.page_table.shape[1], wl.kmax)
+    else:
+        nbytes = gdv.verify_attn_workspace_bytes(B, x.R, wl.Hq, wl.Hkv, wl.D, x.page_table.shape[1])
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=dev)
+        kp, vp = x.k_pool.clone(), x.v_pool.clone()
+        out = torch.full((x.R, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device=dev)
+        st = torch.full((B,), -7, dtype=torch.int32, device=dev)
+        if tree:
+            gdv.spec_verify_attn_tree(x.q, x.k_new, x.v_new, kp, vp, pt, pos, k, parent, x.scale, out, st,
+                                      workspace_buf=ws)
+        else:
+            gdv.spec_verify_attn(x.q, x.k_new, x.v_new, kp, vp, pt, pos, k, wl.kmax, x.scale, out, st,
+                                 workspace_buf=ws)
+        torch.cuda.synchronize()
+        assert (st == 0).all()
+        assert not torch.isnan(out.float()).any()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
