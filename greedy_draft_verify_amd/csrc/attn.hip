@@ -55,11 +55,10 @@ namespace sv {
 
 constexpr int kKT = 64;            // tokens per LDS tile of attn_split_kernel (4 pages)
 constexpr int kAttnThreads = 256;  // 4 waves
-constexpr int kMaxRowsPerKvHead = 128;
+constexpr int kMaxK = 127;         // drafts per sequence (the acceptance calls' limit; 128-bit tree masks)
 constexpr int kRowsPerGroup = 64;  // query rows one attn_split_kernel workgroup handles
 constexpr int kStreamSplit = 1024; // splits of at least this many tokens read the pool non-temporally
 constexpr int kMaxSplit = 2048;    // largest kv_split_tokens
-constexpr int kMaxTreeNodes = 128; // rows per sequence of a tree call (128-bit ancestor masks)
 constexpr int kRemapMaxB = 256;    // batches up to this size dispatch the workgroups with work first
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -692,7 +691,10 @@ __global__ __launch_bounds__(kAttnThreads, TREE ? AttnCfg<D>::MINB_TREE : AttnCf
         // bitwise OR over the workgroup: across each wave, then across the 4 waves
 #pragma unroll
         for (int d = 32; d > 0; d >>= 1) flags |= __shfl_xor(flags, d);
-        __shared__ int s_fl[4];
+        // the 4 words live in the tile's LDS (so that a chain workgroup's LDS is the tile
+        // alone): every wave must be done reading its last tile first
+        int* const s_fl = reinterpret_cast<int*>(smem);
+        __syncthreads();
         if (lane == 0) s_fl[wave] = flags;
         __syncthreads();
         const int bits = s_fl[0] | s_fl[1] | s_fl[2] | s_fl[3];
@@ -795,10 +797,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// A tree workgroup's whole LDS: the tile (4 K and 4 V blocks), two 4-word flag
-// arrays and TreeLds. gfx950 gives a workgroup 160 KB.
+// A tree workgroup's whole LDS: the tile (4 K and 4 V blocks), the parent check's
+// 4-word flag array and TreeLds. gfx950 gives a workgroup 160 KB.
 static size_t tree_lds_bytes(int D, int kmax) {
-    return (size_t)2 * kKT * D * sizeof(u16) + 32 + TreeLds(kmax, D).bytes();
+    return (size_t)2 * kKT * D * sizeof(u16) + 16 + TreeLds(kmax, D).bytes();
 }
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 
@@ -898,8 +900,7 @@ static int verify_attn_impl(const char* name, const spec_bf16* q, const spec_bf1
     if (Hq / Hkv > 16) return fail(SPEC_EINVAL, "%s: Hq/Hkv=%d > 16", name, Hq / Hkv);
     if (B < 1 || B > 4096) return fail(SPEC_EINVAL, "%s: B=%d outside 1..4096", name, B);
     if (R < 1) return fail(SPEC_EINVAL, "%s: R=%d < 1", name, R);
-    if (kmax < 0 || (long long)(Hq / Hkv) * (kmax + 1) > kMaxRowsPerKvHead)
-        return fail(SPEC_EINVAL, "%s: kmax=%d (need 0 <= (Hq/Hkv)*(kmax+1) <= %d)", name, kmax, kMaxRowsPerKvHead);
+    if (kmax < 0 || kmax > kMaxK) return fail(SPEC_EINVAL, "%s: kmax=%d outside 0..%d", name, kmax, kMaxK);
     if (max_pages < 1 || n_pages < 1) return fail(SPEC_EINVAL, "%s: max_pages=%d n_pages=%lld", name, max_pages, (long long)n_pages);
     if (parent && tree_lds_bytes(D, kmax) > kLdsPerWorkgroup)
         return fail(SPEC_EINVAL, "%s: kmax=%d at D=%d needs %zu bytes of LDS per workgroup (> %zu)", name, kmax, D,

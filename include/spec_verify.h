@@ -133,7 +133,8 @@ const char* spec_last_error(void);
  * calls that must agree use the same value.
  *
  * Limits: D in {64, 128, 256}; 1 <= Hkv <= Hq, Hq % Hkv == 0, Hq / Hkv <= 16;
- * 1 <= B <= 4096; R >= 1; scale > 0; (Hq / Hkv) * (kmax + 1) <= 128; 16-byte
+ * 1 <= B <= 4096; R >= 1; scale > 0; 0 <= kmax <= 127 (so a kv head serves up to
+ * (Hq / Hkv) * 128 = 2048 query rows of a sequence, 64 per workgroup); 16-byte
  * aligned q, k_new, v_new, k_pool, v_pool, out, workspace.
  * A flagged sequence writes nothing to the pool or to its out rows.
  * workspace: at least spec_verify_attn_workspace_bytes(...) bytes; no state is

@@ -62,8 +62,8 @@ def test_host_argument_checks():
     # misaligned pointer
     rc = L.spec_verify_attn(_vp(0x1002), p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
     assert rc == -1 and b"aligned" in L.spec_last_error()
-    # kmax too large for the query-row limit
-    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 40, 1, 4, 16, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
+    # kmax past the draft limit (127)
+    rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 128, 1, 4, 16, 1, 64, 0.1, 0, p, p, 1 << 30, p, None)
     assert rc == -1 and b"kmax" in L.spec_last_error()
     # workspace too small
     rc = L.spec_verify_attn(p, p, p, p, p, 10, p, 4, p, p, 3, 1, 4, 4, 1, 64, 0.1, 0, p, p, 16, p, None)

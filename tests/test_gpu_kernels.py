@@ -41,6 +41,7 @@ ATTN_CASES = [
     _wl("agqa", 4, 3, 4, 50, 600, 32, 8, 128, 48),
     _wl("awide", 2, 6, 6, 100, 300, 16, 2, 256, 32),     # G*T = 56 rows per kv head
     _wl("atall", 2, 7, 7, 100, 300, 64, 4, 64, 32),      # G*T = 128 rows: both row groups
+    _wl("adeep", 2, 30, 40, 100, 600, 32, 4, 128, 48),   # G*T up to 328 rows: six row groups
 ]
 
 
@@ -88,13 +89,15 @@ def test_attention_rows_equal_one_row_decode(dev):
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_attention_kmax_does_not_change_results(dev, D):
-    """kmax only sizes the launch (one or two 64-row groups): results are byte-identical."""
+    """kmax only sizes the launch (one to eight 64-row groups): results are byte-identical."""
     wl = _wl(f"both{D}", 4, 0, 3, 10, 1500, 4, 1, D, 128)
     x = synth.make_verify_inputs(wl, seed=9, with_lm_head=False)
     small, _, _, st1 = gpu_attn(x, dev, kmax=3)       # 16 rows per kv head: one row group
     large, _, _, st2 = gpu_attn(x, dev, kmax=31)      # 128 rows: two row groups
-    assert (st1 == 0).all() and (st2 == 0).all()
+    huge, _, _, st3 = gpu_attn(x, dev, kmax=127)      # 512 rows: eight row groups
+    assert (st1 == 0).all() and (st2 == 0).all() and (st3 == 0).all()
     assert torch.equal(small.view(torch.int16), large.view(torch.int16))
+    assert torch.equal(small.view(torch.int16), huge.view(torch.int16))
     _, ref, *_ = oracle_attn(x)
     assert_close(small.float().cpu().numpy(), ref, "both kernels")
 
@@ -150,7 +153,7 @@ def test_attention_rows_beyond_kmax(dev):
     for s in np.nonzero(over)[0]:
         assert np.isnan(o[off[s]:off[s + 1]]).all()
     with pytest.raises(gdv.SpecError):
-        gpu_attn(x, dev, kmax=8)      # 16 * 9 = 144 query rows > 128
+        gpu_attn(x, dev, kmax=128)    # past the 127-draft limit
 
 
 def synth_status(name):

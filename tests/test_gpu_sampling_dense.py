@@ -133,9 +133,12 @@ def test_dense_walk_error_paths(dev):
 @pytest.mark.parametrize("T", [1.0, 0.6])
 def test_dense_end_to_end_from_the_lm_head(dev, T):
     """lm_head pass with z kept, then the walk, against the oracle's fp64 logits; the
-    pass's lse and draw from p equal the support-list pass with no support."""
+    pass's lse and draw from p equal the support-list pass with no support. Sequences
+    the fp64 logits leave undecided (within the logits' tolerance) are compared with the
+    oracle's walk over the GPU's own z, decided beyond fp32 rounding, so that nearly
+    every sequence is compared one way or the other."""
     import greedy_draft_verify_amd as gdv
-    B, kmax, V, H = 12, 4, 4096, 256
+    B, kmax, V, H = 32, 4, 4096, 256
     rng = np.random.default_rng(17)
     k = rng.integers(0, kmax + 1, B).astype(np.int32)
     R = int((k + 1).sum())
@@ -184,6 +187,15 @@ def test_dense_end_to_end_from_the_lm_head(dev, T):
     assert decided.mean() > 0.5, decided.mean()
     for key in KEYS:
         assert np.array_equal(got[key][decided], ref[key][decided]), key
+    # the same walk over the GPU's z (as fp64 logits): decided beyond fp32 rounding
+    ref_g = oracle.sample_accept_dense(drafts, kmax, k, None, 0, V, B, R, zg * T, T, q, row_ctr, seed, pos, rel=1e-5)
+    tight = (ref_g["margin"] > 1e-4) & (ref_g["gap"] > 1e-4)
+    for key in KEYS:
+        assert np.array_equal(got[key][tight], ref_g[key][tight]), key
+    covered = decided | tight
+    print(f"T={T}: {int(decided.sum())} of {B} sequences decided on fp64 logits, {int(tight.sum())} on the GPU's z, "
+          f"{int(covered.sum())} compared")
+    assert tight.mean() > 0.9 and covered.mean() >= 0.9, (tight.mean(), covered.mean())
 
 
 def test_dense_pass_b16k4_rows(dev):

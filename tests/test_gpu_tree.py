@@ -40,6 +40,7 @@ TREE_CASES = [
     _wl("t128", 4, 5, 15, 200, 1100, 32, 8, 128, 80),      # G * (kmax + 1) = 64
     _wl("t256", 2, 6, 12, 500, 900, 16, 2, 256, 64),       # G * (kmax + 1) = 104
     _wl("tbig", 2, 100, 127, 30, 300, 1, 1, 64, 32),       # 128 nodes: every mask word, two row groups
+    _wl("tdeep", 2, 40, 63, 300, 900, 32, 8, 128, 64),     # G * (kmax + 1) = 256: four row groups
 ]
 
 
