@@ -172,6 +172,23 @@ def test_tree_row_is_its_one_row_decode(dev, wl, shape, split):
     _assert_rows_equal(out, ref, x, parent, f"{wl.name} {shape}")
 
 
+def test_tree_rows_at_the_lds_limit(dev):
+    """D = 256 with kmax = 93: the tile, K and V of 93 new rows and the node tables take
+    163,056 of the workgroup's 163,840 bytes of LDS; every row is still its one-row
+    decode, and one more draft is refused before launch."""
+    import greedy_draft_verify_amd as gdv
+    wl = _wl("tlds", 2, 80, 93, 100, 400, 2, 2, 256, 40)
+    x, parent = _tree_case(wl, 6, "random")
+    assert parent.shape[1] == 94
+    out, _, _, st = gpu_attn_tree(x, parent, dev)
+    assert (st == 0).all()
+    ref = _one_row_decodes(x, parent, dev, 0)
+    _assert_rows_equal(out, ref, x, parent, "tlds")
+    wide = np.concatenate([parent, np.full((len(x.k), 1), -1, np.int32)], 1)   # kmax = 94
+    with pytest.raises(gdv.SpecError, match="LDS"):
+        gpu_attn_tree(x, wide, dev)
+
+
 def test_b16tree_rows_are_their_one_row_decodes(dev):
     """The 16-node tree workload at full size, every row of every sequence."""
     x = synth.make_verify_inputs("b16tree", seed=0, with_lm_head=False)
