@@ -128,10 +128,31 @@ def measured_traffic(kernel_key: str):
     return float(kv["traffic_bytes_per_launch"])
 
 
+SETTLE_S = 0.04
+
+
+def settle(fn, seconds: float = SETTLE_S) -> int:
+    """Untimed calls of fn, back to back, for at least `seconds`, made right before a
+    timed region. After an idle spell of a few ms (a graph capture, a host-side check)
+    the MI355X needs ~25 ms of load to return to its steady clocks: 20-step windows of
+    the b16k4 step opened 5 steps after such a spell measure 243-253 us, the same
+    windows after 100 steps 235 us. Returns the number of calls."""
+    t0, n, batch = time.perf_counter(), 0, 4
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        n += batch
+        batch = min(2 * batch, 64)
+    return n
+
+
 def time_call(f, reps: int, warmup: int = 3) -> float:
-    """Mean seconds per call of f over reps back-to-back calls (HIP events on the current stream)."""
+    """Mean seconds per call of f over reps back-to-back calls (HIP events on the current
+    stream), after the warmup calls and the settle phase."""
     for _ in range(warmup):
         f()
+    settle(f)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -145,8 +166,9 @@ def time_call(f, reps: int, warmup: int = 3) -> float:
 def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
     """Times one verify step: an eager loop of the three calls with HIP events on the
     launch stream around each call, then the same step captured once as a HIP graph
-    and replayed (the launches' host overhead and gaps leave the step). Every replay
-    must reproduce the eager step's bytes."""
+    and replayed (the launches' host overhead and gaps leave the step). Each timed
+    region follows the warmup steps and the settle phase. Every replay must reproduce
+    the eager step's bytes."""
     stream = torch.cuda.current_stream()
 
     def run_step(ev=None):
@@ -168,6 +190,7 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
     assert (step.attn_status.cpu() == 0).all() and (step.acc_status.cpu() == 0).all()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle_eager = settle(run_step)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
@@ -187,6 +210,7 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
         run_step()
     for _ in range(warmup):
         graph.replay()
+    settle_graph = settle(graph.replay)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(steps):
@@ -197,7 +221,7 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
     for a, b in zip(eager_out, step.outputs()):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "graph replay differs from the eager step"
     del graph
-    return {"graph_ms": graph_ms, "eager_ms": eager_ms,
+    return {"graph_ms": graph_ms, "eager_ms": eager_ms, "settle_steps": [settle_eager, settle_graph],
             "attn_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
             "lm_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
             "acc_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))}
@@ -356,6 +380,7 @@ def tree_leg(dev, w_packed, reps: int, seed: int = 0):
     torch.cuda.synchronize()
     assert (ast.cpu() == 0).all() and (cst.cpu() == 0).all()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    settle(lambda: [f() for f in fns])
     for ev in evs:
         ev[0].record(stream)
         for i, f in enumerate(fns):
@@ -431,6 +456,7 @@ def sampling_leg(step: "VerifyStep", dev, reps: int, temperature: float = 0.1):
     torch.cuda.synchronize()
     assert (st.cpu() == 0).all()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    settle(lambda: [f() for f in fns])
     for ev in evs:
         ev[0].record(stream)
         for i, f in enumerate(fns):
@@ -493,6 +519,7 @@ def sampling_dense_leg(step: "VerifyStep", dev, reps: int, temperature: float = 
     torch.cuda.synchronize()
     assert (st.cpu() == 0).all()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    settle(lambda: [f() for f in fns])
     for ev in evs:
         ev[0].record(stream)
         for i, f in enumerate(fns):
@@ -539,6 +566,7 @@ def kpolicy_leg(step: "VerifyStep", dev, reps: int, seed: int = 0):
         for _ in range(3):
             for f in fns:
                 f()
+        settle(lambda: [f() for f in fns])
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -817,6 +845,9 @@ def main():
         "ms_per_step": ms_step,
         "eager_ms_per_step": t["eager_ms"],
         "step_launch": "HIP graph replay of the three entry points (per-entry times and rooflines from the eager loop)",
+        "settle": {"seconds": SETTLE_S, "steps": t["settle_steps"],
+                   "note": "untimed steps right before each timed region, after the warmup steps: the GPU "
+                           "returns to its steady clocks ~25 ms into a load after idling"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
