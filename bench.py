@@ -224,7 +224,9 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
     return {"graph_ms": graph_ms, "eager_ms": eager_ms, "settle_steps": [settle_eager, settle_graph],
             "attn_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
             "lm_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
-            "acc_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))}
+            "acc_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
+            "median_us": {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+                          for i, name in enumerate(("spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept"))}}
 
 
 def step_report(step: VerifyStep, t: dict) -> dict:
@@ -243,6 +245,7 @@ def step_report(step: VerifyStep, t: dict) -> dict:
             "accept_len_hist": np.bincount(acc_len, minlength=wl.kmax + 1).tolist(),
             "kernel_us": {"spec_verify_attn": t["attn_ms"] * 1e3, "spec_lm_head_argmax": t["lm_ms"] * 1e3,
                           "spec_greedy_accept": t["acc_ms"] * 1e3},
+            "kernel_us_median": t["median_us"],
             "attn": {"bound": "hbm", "algorithmic_bytes": at_b, "achieved": at_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS},
             "lm_head": {"bound": "hbm" if x.R < 312 else "mfma", "algorithmic_bytes": lm_b, "GB/s": lm_gbs,
@@ -862,6 +865,7 @@ def main():
         "emitted_per_step": rep["emitted_per_step"],
         "accept_len_hist": rep["accept_len_hist"],
         "kernel_us": rep["kernel_us"],
+        "kernel_us_median": rep["kernel_us_median"],
         "roofline": {"kernel": "spec_lm_head_argmax", "bound": lm["bound"],
                      "achieved": lm["GB/s"] if lm["bound"] == "hbm" else lm["TFLOP/s"],
                      "peak": HBM_PEAK_GBS if lm["bound"] == "hbm" else BF16_PEAK_TFLOPS,
