@@ -1,8 +1,11 @@
 """Seeded random shapes against the oracle, beside the hand-picked cases: head dims,
 query/kv head ratios, batch sizes, ragged k, positions from 0 up, split sizes and kmax
 above the largest k for the chain and tree attention (tree shapes trie, star, random
-and chain), and row / vocabulary / hidden sizes for the lm_head. Each case prints its
-parameters first; the same tolerance as the other parity tests."""
+and chain), row / vocabulary / hidden sizes for the lm_head and its sampling form
+(support sizes and temperatures too), and batch, draft length, head count and accepted
+lengths (0 up to past the draft) for the DeltaNet record / rollback and input-stash
+modes. Each case prints its parameters first; the same tolerance as the other parity
+tests."""
 import math
 
 import numpy as np
@@ -86,3 +89,67 @@ def test_lm_head_random_shapes(dev, seed):
     g_ref, t1, t2, _ = oracle.lm_head_argmax(bits(h), bits(w), R, H, V)
     n_undecided = check_argmax(g, mv, g_ref, t1, t2, f"random lm_head seed {seed}")
     assert n_undecided <= max(2, R // 3)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lm_head_sample_random_shapes(dev, seed):
+    import greedy_draft_verify_amd as gdv
+    from tests.test_gpu_sampling import _check_rows, _support, gpu_sample_rows
+    rng = np.random.default_rng(8500 + seed)
+    R = int(rng.integers(1, 300))
+    H = int(rng.choice([256, 512]))
+    V = int(rng.integers(100, 5000))
+    NQ = int(rng.integers(0, 9))
+    T = float(rng.uniform(0.4, 1.6))
+    print(f"[rand sample] seed {seed}: R={R} H={H} V={V} NQ={NQ} T={T:.3f}", flush=True)
+    g = torch.Generator().manual_seed(8500 + seed)
+    hidden = torch.randn((R, H), generator=g).to(torch.bfloat16)
+    w = (torch.randn((V, H), generator=g) / math.sqrt(H / 4)).to(torch.bfloat16)
+    q_tok, q_prob = _support(rng, R, V, NQ)
+    row_ctr = np.stack([rng.integers(0, 1 << 20, R), rng.integers(0, 1 << 30, R)], 1).astype(np.int32)
+    key = int(rng.integers(0, 1 << 62))
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    got = gpu_sample_rows(hidden.to(dev), wp, V, T, q_tok, q_prob, row_ctr, key, dev)
+    logits = oracle.lm_head_logits(bits(hidden), bits(w), R, H, V)
+    ref = oracle.sample_rows(logits, T, q_tok, q_prob, row_ctr, key)
+    _check_rows(got, ref, f"random sampling seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_delta_random_shapes(dev, seed):
+    """Record + fused rollback (mode 3) on random (B, T, heads) with L from 0 past T."""
+    import greedy_draft_verify_amd as gdv
+    rng = np.random.default_rng(8800 + seed)
+    B, T, Hd = int(rng.integers(1, 5)), int(rng.integers(1, 40)), int(rng.integers(1, 4))
+    L = rng.integers(0, T + 3, B).astype(np.int32)
+    print(f"[rand delta] seed {seed}: B={B} T={T} Hd={Hd} L={L.tolist()}", flush=True)
+    d = synth.make_delta_inputs(seed=8800 + seed, B=B, T=T, Hd=Hd)
+    st = d.state.to(dev).clone()
+    rec = torch.full((B, T, Hd, 128, 128), float("nan"), dtype=torch.float32, device=dev)
+    o = torch.full((B, T, Hd, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    to = lambda t: t.to(dev)
+    gdv.spec_delta_verify_rollback(gdv.DELTA_BOTH, to(d.q), to(d.k), to(d.v), to(d.a), to(d.b), 1.0, st, rec,
+                                   torch.from_numpy(L).to(dev), o)
+    torch.cuda.synchronize()
+    rec_ref, o_ref = oracle.delta_verify(bits(d.q), bits(d.k), bits(d.v), d.a.numpy(), d.b.numpy(), 1.0,
+                                         d.state.numpy(), B, T, Hd, 128, 128)
+    assert_close(rec.cpu().numpy(), rec_ref, f"random delta record seed {seed}")
+    assert_close(o.float().cpu().numpy(), o_ref, f"random delta output seed {seed}")
+    for s in range(B):
+        Ls = min(int(L[s]), T)
+        # the restored state is the recorded S_L itself (the same bytes), or S_0 for L = 0
+        want = d.state[s] if Ls == 0 else rec[s, Ls - 1].cpu()
+        assert torch.equal(st[s].cpu(), want), f"sequence {s}, L {int(L[s])}"
+    # the input-stash pair: VERIFY gives the same outputs and leaves S_0, RESCAN of the
+    # committed prefix leaves exactly the restored bytes
+    s4 = d.state.to(dev).clone()
+    o4 = torch.full_like(o, float("nan"))
+    gdv.spec_delta_verify_rollback(gdv.DELTA_VERIFY, to(d.q), to(d.k), to(d.v), to(d.a), to(d.b), 1.0, s4, None,
+                                   None, o4)
+    s5 = d.state.to(dev).clone()
+    gdv.spec_delta_verify_rollback(gdv.DELTA_RESCAN, to(d.q), to(d.k), to(d.v), to(d.a), to(d.b), 1.0, s5, None,
+                                   torch.from_numpy(L).to(dev), None)
+    torch.cuda.synchronize()
+    assert torch.equal(o4.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(s4.cpu(), d.state), "VERIFY must not modify the state"
+    assert torch.equal(s5, st), "RESCAN must give the restored record's bytes"
