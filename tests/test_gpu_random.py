@@ -7,6 +7,7 @@ lengths (0 up to past the draft) for the DeltaNet record / rollback and input-st
 modes. Each case prints its parameters first; the same tolerance as the other parity
 tests."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -22,6 +23,12 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 SPLITS = [0, 64, 128, 192, 256, 320, 512, 1024, 2048]
+# GDV_RANDOM_SCALE multiplies the number of seeds of every test here (a longer sweep)
+_SCALE = max(1, int(os.environ.get("GDV_RANDOM_SCALE", "1")))
+
+
+def _seeds(n):
+    return range(n * _SCALE)
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +55,7 @@ def _random_workload(seed, k_cap):
     return wl, split, kmax, rng
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", _seeds(16))
 def test_attention_random_shapes(dev, seed):
     wl, split, kmax, _ = _random_workload(seed, 12)
     x = synth.make_verify_inputs(wl, seed=seed, with_lm_head=False)
@@ -61,7 +68,7 @@ def test_attention_random_shapes(dev, seed):
     assert_close(out.float().cpu().numpy(), ref, f"random attention seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", _seeds(8))
 def test_tree_attention_random_shapes(dev, seed):
     wl, split, _, rng = _random_workload(100 + seed, 20)
     shape = ["trie", "star", "random", "chain"][seed % 4]
@@ -76,7 +83,7 @@ def test_tree_attention_random_shapes(dev, seed):
     assert_close(out.float().cpu().numpy(), ref, f"random tree attention seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", _seeds(8))
 def test_lm_head_random_shapes(dev, seed):
     rng = np.random.default_rng(8000 + seed)
     R = int(rng.integers(1, 400))
@@ -91,7 +98,7 @@ def test_lm_head_random_shapes(dev, seed):
     assert n_undecided <= max(2, R // 3)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", _seeds(6))
 def test_lm_head_sample_random_shapes(dev, seed):
     import greedy_draft_verify_amd as gdv
     from tests.test_gpu_sampling import _check_rows, _support, gpu_sample_rows
@@ -112,10 +119,11 @@ def test_lm_head_sample_random_shapes(dev, seed):
     got = gpu_sample_rows(hidden.to(dev), wp, V, T, q_tok, q_prob, row_ctr, key, dev)
     logits = oracle.lm_head_logits(bits(hidden), bits(w), R, H, V)
     ref = oracle.sample_rows(logits, T, q_tok, q_prob, row_ctr, key)
-    _check_rows(got, ref, f"random sampling seed {seed}")
+    # every decided row must match; at a few rows one near-tie is a large share
+    _check_rows(got, ref, f"random sampling seed {seed}", min_decided=0.5)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", _seeds(6))
 def test_delta_random_shapes(dev, seed):
     """Record + fused rollback (mode 3) on random (B, T, heads) with L from 0 past T."""
     import greedy_draft_verify_amd as gdv
