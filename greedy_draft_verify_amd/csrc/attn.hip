@@ -500,6 +500,11 @@ __global__ __launch_bounds__(kAttnThreads, TREE ? AttnCfg<D>::MINB_TREE : AttnCf
                 uint2* w = reinterpret_cast<uint2*>(smem + (NP + p) * BLK) + wi;
                 *w = mask_v(*w, tok0, last);
             }
+            // The masking above rewrites whole 8-byte V words, which also hold tokens
+            // <= last of the last page (new rows among them): every wave must be done
+            // with it before any new row is written below, or a word written back by
+            // one wave can undo another wave's new-row value.
+            __syncthreads();
             const int r_lo = max(t0, P0), r_hi = min(t0 + KT - 1, last);
             constexpr int dch = D / 8;
             const int n_it = (r_hi - r_lo + 1) * dch;

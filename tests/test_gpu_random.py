@@ -161,3 +161,53 @@ def test_delta_random_shapes(dev, seed):
     assert torch.equal(o4.view(torch.int16), o.view(torch.int16))
     assert torch.equal(s4.cpu(), d.state), "VERIFY must not modify the state"
     assert torch.equal(s5, st), "RESCAN must give the restored record's bytes"
+
+
+# --------------------------------------------------------------------------- integer walks
+def _walk_case(seed):
+    rng = np.random.default_rng(9100 + seed)
+    B = int(rng.choice([1, 2, 3, 16, 63, 64, 65, 200, 1500]))
+    kmax = int(rng.choice([0, 1, 3, 7, 15, 31, 63, 64, 65, 127]))
+    V = int(rng.integers(2, 3000))
+    n_d2t = int(rng.choice([0, 0, V + int(rng.integers(0, 500))]))
+    return rng, B, kmax, V, n_d2t
+
+
+@pytest.mark.parametrize("seed", _seeds(10))
+def test_greedy_accept_random_shapes(dev, seed):
+    """Bit-exact acceptance (with and without a draft map, stop tokens and limits)
+    on random batch, draft length and vocabulary sizes."""
+    from tests.helpers import assert_accept_equal, gpu_accept
+    from tests.test_gpu_stop import _case, gpu_accept_stop
+    rng, B, kmax, V, n_d2t = _walk_case(seed)
+    print(f"[rand accept] seed {seed}: B={B} kmax={kmax} V={V} d2t={n_d2t}", flush=True)
+    g, drafts, k, d2t, R, pos, rng2 = _case(9100 + seed, B, kmax, V, p_match=float(rng.uniform(0.3, 0.95)),
+                                            n_d2t=n_d2t)
+    nd = 0 if d2t is None else len(d2t)
+    got = gpu_accept(g, drafts, k, d2t, V, pos, dev, kmax=kmax)
+    ref = oracle.greedy_accept(g, drafts, kmax, k, d2t, nd, V, B, R, pos)
+    assert_accept_equal(got, ref, f"random accept seed {seed}")
+    n_stop = int(rng.integers(0, 17))
+    stops = [int(t) for t in rng2.choice(g, n_stop)] if n_stop else []
+    remaining = rng2.integers(1, kmax + 3, B).astype(np.int32) if rng.uniform() < 0.5 else None
+    got_s = gpu_accept_stop(g, drafts, k, d2t, V, stops, remaining, pos, dev)
+    ref_s = oracle.greedy_accept_stop(g, drafts, kmax, k, d2t, nd, V, B, R, stops, remaining, pos)
+    for key in ("status", "accept_len", "n_emit", "pos_out", "next_tok", "emit", "done"):
+        assert np.array_equal(got_s[key], ref_s[key]), (key, seed)
+
+
+@pytest.mark.parametrize("seed", _seeds(10))
+def test_tree_accept_random_shapes(dev, seed):
+    """Bit-exact tree walks on random batch and tree sizes, shapes and draft maps."""
+    from tests.helpers import gpu_tree_accept
+    from tests.test_gpu_tree import _accept_inputs, _assert_tree_accept_equal, _oracle_accept
+    rng = np.random.default_rng(9300 + seed)
+    B = int(rng.choice([1, 5, 16, 64, 65, 300]))
+    kmax = int(rng.choice([1, 2, 4, 15, 31, 63, 64, 100, 127]))   # the helpers size drafts for kmax >= 1
+    shape = str(rng.choice(["trie", "star", "random", "chain"]))
+    n_d2t = int(rng.choice([0, 0, 700]))
+    print(f"[rand tree accept] seed {seed}: B={B} kmax={kmax} {shape} d2t={n_d2t}", flush=True)
+    args = _accept_inputs(9300 + seed, B, kmax, shape, n_d2t=n_d2t, p_corrupt=float(rng.uniform(0.1, 0.6)))
+    ref = _oracle_accept(*args)
+    got = gpu_tree_accept(*args[:-1], dev)
+    _assert_tree_accept_equal(got, ref, f"random tree accept seed {seed}")

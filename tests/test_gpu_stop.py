@@ -49,7 +49,7 @@ def _case(seed, B, kmax, V, p_match=0.8, n_d2t=0):
         inv = {}
         for i, t in enumerate(d2t):
             inv.setdefault(int(t), i)
-        drafts = np.where(drafts >= 0, np.vectorize(lambda t: inv[int(t)])(np.maximum(drafts, 0)), -1).astype(np.int32)
+        drafts = np.where(drafts >= 0, np.vectorize(lambda t: inv[int(t)], otypes=[np.int32])(np.maximum(drafts, 0)), -1).astype(np.int32)
     pos = rng.integers(0, 10000, B).astype(np.int32)
     return g, drafts, k, d2t, R, pos, rng
 

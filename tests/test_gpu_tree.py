@@ -269,7 +269,7 @@ def _accept_inputs(seed, B, kmax, shape, V=500, n_d2t=0, k_fixed=False, p_corrup
         inv = {}
         for i, t in enumerate(d2t):
             inv.setdefault(int(t), i)
-        mapped = np.vectorize(lambda t: inv[int(t)])(np.maximum(drafts, 0))
+        mapped = np.vectorize(lambda t: inv[int(t)], otypes=[np.int32])(np.maximum(drafts, 0))
         drafts = np.where(drafts >= 0, mapped, -1).astype(np.int32)
     pos = rng.integers(0, 100000, B).astype(np.int32)
     return g, drafts, k, parent, d2t, V, pos, R
@@ -471,3 +471,59 @@ def test_attention_ignores_workspace_contents(dev, tree):
         assert not torch.isnan(out.float()).any()
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+# --------------------------------------------------------------------------- new-row slots
+POISON_CASES = [_wl("pchain", 24, 3, 6, 200, 700, 8, 2, 128, 48), _wl("ptree", 16, 15, 15, 200, 700, 8, 2, 128, 48),
+                _wl("pd64", 12, 5, 9, 100, 500, 4, 1, 64, 40), _wl("pd256", 8, 7, 13, 100, 400, 8, 2, 256, 32),
+                "b16k4", "b16tree"]
+
+
+def _poison_new_row_slots(x):
+    """Sets the pool's K and V at positions pos .. pos + k of every sequence (the slots
+    the call appends to) to 4096."""
+    from tests.pool_layout import k_offsets, v_offsets
+    kb, vb = bits(x.k_pool).copy(), bits(x.v_pool).copy()
+    big = np.uint16(0x4580)     # 4096.0 in bf16
+    ko, vo = k_offsets(x.wl.D), v_offsets(x.wl.D)
+    for s in range(len(x.pos)):
+        for p in range(int(x.pos[s]), int(x.pos[s]) + int(x.k[s]) + 1):
+            page, t = int(x.page_table[s, p // 16]), p % 16
+            kb[page, :, ko[t]] = big
+            vb[page, :, vo[t]] = big
+    x.k_pool = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16)
+    x.v_pool = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("wl", POISON_CASES, ids=lambda w: w if isinstance(w, str) else w.name)
+def test_new_row_slots_never_keep_old_pool_values(dev, wl):
+    """The pool's slots at positions pos .. pos + k (the rows being verified) hold 4096
+    before the call; the kernel must read the new rows there (the oracle appends them
+    first), so a new-row value lost in the tile's LDS copy shows as an error of
+    hundreds. Repeated calls must give identical bytes (at the b16 sizes the oracle
+    checks four sequences, over 30 calls: such a loss depends on the waves' timing)."""
+    full = isinstance(wl, str)
+    x = synth.make_verify_inputs(wl, seed=5 if not full else 0, device="cpu", with_lm_head=False)
+    tree = (wl if full else wl.name) in ("ptree", "b16tree")
+    _poison_new_row_slots(x)
+    parent = synth.make_parents(x.k, 0 if full else 5, "b16tree", "trie") if tree else None
+    seqs = [0, 5, 11, 15] if full else None
+    reps = 30 if full else 6
+    print(f"[poison] {x.wl.name}: B={len(x.pos)} D={x.wl.D} tree={tree}", flush=True)
+    if tree:
+        rows, ref, _, _, st = oracle_attn_tree(x, parent, seqs=seqs)
+    else:
+        rows, ref, _, _, st = oracle_attn(x, seqs=seqs)
+    assert (st == 0).all()
+    # device-resident inputs: the calls run back to back, as in a decode loop
+    for name in ("q", "k_new", "v_new", "k_pool", "v_pool"):
+        setattr(x, name, getattr(x, name).to(dev))
+    first = None
+    for rep in range(reps):
+        out, _, _, status = gpu_attn_tree(x, parent, dev) if tree else gpu_attn(x, dev)
+        assert (status == 0).all()
+        assert_close(out.float().cpu().numpy()[rows], ref, f"{x.wl.name} call {rep}")
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out.view(torch.int16), first.view(torch.int16)), f"{x.wl.name}: call {rep} differs"
