@@ -1,7 +1,7 @@
 """Seeded random shapes against the oracle, beside the hand-picked cases: head dims,
 query/kv head ratios, batch sizes, ragged k, positions from 0 up, split sizes and kmax
 above the largest k for the chain and tree attention (tree shapes trie, star, random
-and chain), row / vocabulary / hidden sizes for the lm_head and its sampling form
+and chain; every other seed with the new-row slots of the pool set to 4096 beforehand), row / vocabulary / hidden sizes for the lm_head and its sampling form
 (support sizes and temperatures too), and batch, draft length, head count and accepted
 lengths (0 up to past the draft) for the DeltaNet record / rollback and input-stash
 modes. Each case prints its parameters first; the same tolerance as the other parity
@@ -18,6 +18,7 @@ from greedy_draft_verify_amd import synth
 from tests.conftest import gpu_available
 from tests.helpers import (assert_close, bits, check_argmax, gpu_attn, gpu_attn_tree, gpu_lm_head, oracle_attn,
                            oracle_attn_tree)
+from tests.test_gpu_tree import _poison_new_row_slots
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -59,6 +60,8 @@ def _random_workload(seed, k_cap):
 def test_attention_random_shapes(dev, seed):
     wl, split, kmax, _ = _random_workload(seed, 12)
     x = synth.make_verify_inputs(wl, seed=seed, with_lm_head=False)
+    if seed % 2:
+        _poison_new_row_slots(x)    # a new-row value lost on the way to the tile shows as a large error
     print(f"[rand attn] seed {seed}: D={wl.D} Hq={wl.Hq} Hkv={wl.Hkv} B={len(x.pos)} pos {x.pos.tolist()} "
           f"k {x.k.tolist()} kmax {kmax} split {split}", flush=True)
     out, kp, vp, st = gpu_attn(x, dev, kv_split_tokens=split, kmax=kmax)
@@ -73,6 +76,8 @@ def test_tree_attention_random_shapes(dev, seed):
     wl, split, _, rng = _random_workload(100 + seed, 20)
     shape = ["trie", "star", "random", "chain"][seed % 4]
     x = synth.make_verify_inputs(wl, seed=seed, with_lm_head=False)
+    if seed % 2:
+        _poison_new_row_slots(x)
     parent = synth.make_parents(x.k, seed, wl.name, shape, kmax=wl.kmax)
     print(f"[rand tree] seed {seed}: D={wl.D} Hq={wl.Hq} Hkv={wl.Hkv} B={len(x.pos)} pos {x.pos.tolist()} "
           f"k {x.k.tolist()} shape {shape} split {split}", flush=True)
