@@ -251,7 +251,8 @@ template <int MT, int NT, bool SHARED, bool SAMPLE = false>
 __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
     const u16* __restrict__ hidden, const u16* __restrict__ wp, int R, int H, int V, int n_vt,
     int n_rg, unsigned long long* __restrict__ keys, unsigned int* __restrict__ ticket,
-    int32_t* __restrict__ argmax, float* __restrict__ maxval, SampleArgs sa) {
+    int32_t* __restrict__ argmax, float* __restrict__ maxval, SampleArgs sa,
+    unsigned long long* __restrict__ key_rows) {
     static_assert(NT == 2 || (NT == 4 && !SAMPLE), "the sampling epilogue covers one group per workgroup");
     constexpr int GPW = NT / 2;                                 // packed groups per workgroup
     // LDS row stride (elements): 144 measured 1-2% faster than 136 at 80 rows, and
@@ -425,10 +426,16 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
             const Best o = wbest[wv][tid];
             if (better(o.v, o.i, b.v, b.i)) b = o;
         }
-        // the returned value is consumed, so the wave waits until the update is performed
-        const unsigned long long prev = atomicMax(keys + r0 + tid, pack_best(b));
-        asm volatile("" : : "v"(prev));
+        if (key_rows) {
+            // few rows: this workgroup's row of keys, merged by lm_head_rows_finalize_kernel
+            key_rows[(size_t)vt * R + r0 + tid] = pack_best(b);
+        } else {
+            // the returned value is consumed, so the wave waits until the update is performed
+            const unsigned long long prev = atomicMax(keys + r0 + tid, pack_best(b));
+            asm volatile("" : : "v"(prev));
+        }
     }
+    if (key_rows) return;
     // The last workgroup to finish turns the keys into the outputs and leaves the
     // workspace zero for the next call. Keys and ticket are only touched by atomics,
     // which are ordered where they are performed, so no cache flush is needed: every
@@ -445,6 +452,61 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
         if (maxval) maxval[r] = unpack_value(key);
     }
     if (tid == 0) atomicExch(ticket, 0u);
+}
+
+// Few rows (at most kLmKeyRowsMaxR): each workgroup stores its per-row keys as one
+// row of a [workgroups][R] array with plain stores, and this kernel merges them, 8
+// rows per workgroup, each thread reading every 32nd workgroup's keys of its row. At
+// these row counts the workgroups end close together, and the atomic maxima and
+// ticket of the general path then queue at the end of the kernel. Measured at
+// H = 4096, V = 151936 (outputs identical): 1 row 203 -> 183 us, 16: 194 -> 183,
+// 32: 195 -> 185, 48: 196 -> 188, 56: 197 -> 193, 64: 197 -> 195; 72 equal and 80-96
+// rows 1-2 us slower, so the general path is kept there. The maximum of the keys is
+// the same whichever path takes it.
+constexpr int kLmKeyRowsMaxR = 64;
+static_assert(kLmKeyRowsMaxR <= 4 * 16, "the dispatch passes the key rows to the tile kernels of up to 4 row tiles");
+
+__global__ __launch_bounds__(256) void lm_head_rows_finalize_kernel(unsigned long long* __restrict__ key_rows,
+                                                                    int n_wg, int R, int32_t* __restrict__ argmax,
+                                                                    float* __restrict__ maxval) {
+    const int r = blockIdx.x * 8 + threadIdx.x % 8;
+    const int j0 = threadIdx.x / 8;
+    unsigned long long best = 0ull;
+    // every key is read by one thread, which leaves it zero (the workspace is zero
+    // after every call, whichever path the call took)
+    if (r < R) {
+        int i = j0;
+        for (; i + 7 * 32 < n_wg; i += 8 * 32) {
+            unsigned long long k[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) k[u] = key_rows[(size_t)(i + u * 32) * R + r];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                best = k[u] > best ? k[u] : best;
+                key_rows[(size_t)(i + u * 32) * R + r] = 0ull;
+            }
+        }
+        for (; i < n_wg; i += 32) {
+            const unsigned long long x = key_rows[(size_t)i * R + r];
+            best = x > best ? x : best;
+            key_rows[(size_t)i * R + r] = 0ull;
+        }
+    }
+    // lanes 8 apart hold the same row
+#pragma unroll
+    for (int d = 8; d < kWave; d <<= 1) {
+        const unsigned long long o = __shfl_xor(best, d);
+        best = o > best ? o : best;
+    }
+    __shared__ unsigned long long s_b[4][8];
+    if (threadIdx.x % kWave < 8) s_b[threadIdx.x / kWave][threadIdx.x % 8] = best;
+    __syncthreads();
+    if (threadIdx.x < 8 && r < R) {
+#pragma unroll
+        for (int w = 1; w < 4; ++w) best = s_b[w][threadIdx.x] > best ? s_b[w][threadIdx.x] : best;
+        argmax[r] = (int32_t)~(uint32_t)best;
+        if (maxval) maxval[r] = unpack_value(best);
+    }
 }
 
 static int n_vtiles(int V) { return (V + kLmVocabPerWg - 1) / kLmVocabPerWg; }
@@ -464,17 +526,18 @@ static bool lm_wide(int mtiles) { return mtiles > kLmMaxMT; }
 template <int MT, int NT, bool SAMPLE = false>
 static bool launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, int n_vt, int n_rg,
                          unsigned long long* keys, unsigned int* ticket, int32_t* argmax, float* maxval,
-                         hipStream_t st, const SampleArgs& sa = SampleArgs{}) {
+                         hipStream_t st, const SampleArgs& sa = SampleArgs{},
+                         unsigned long long* key_rows = nullptr) {
     if (n_rg == 1) {
         hipLaunchKernelGGL((lm_head_tile_kernel<MT, NT, false, SAMPLE>), dim3(n_vt), dim3(kLmThreads), 0, st, hidden,
-                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
+                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa, key_rows);
         return true;
     }
     // several row groups have >= 5 tiles each (caps of 8), >= 4 (cap of 7)
     if constexpr (MT >= 4) {
         const int grid = (n_vt * n_rg + 7) / 8 * 8;
         hipLaunchKernelGGL((lm_head_tile_kernel<MT, NT, true, SAMPLE>), dim3(grid), dim3(kLmThreads), 0, st, hidden,
-                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa);
+                           w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, sa, key_rows);
         return true;
     }
     return false;
@@ -627,6 +690,75 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
 
 }  // namespace sv
 
+namespace sv {
+
+// The greedy lm_head call: argument checks, then the tile kernel for the row count;
+// allow_rows lets few rows take the key-rows path (whose part of the workspace the
+// no-allocation entry point does not have).
+static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R,
+                              int32_t H, int32_t V, int32_t* argmax, float* maxval, void* workspace,
+                              size_t workspace_bytes, bool allow_rows, hipStream_t st) {
+    if (R < 1) return fail(SPEC_EINVAL, "%s: R=%d < 1", name, R);
+    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "%s: H=%d not a positive multiple of %d", name, H, kLmHAlign);
+    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "%s: V=%d", name, V);
+    if (!hidden || !w_packed || !argmax) return fail(SPEC_EINVAL, "%s: null required pointer", name);
+    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "%s: hidden and w_packed must be 16-byte aligned", name);
+    const spec_bf16* w = w_packed;
+    const int n_vt = n_vtiles(V);
+    const size_t keys_bytes = 256 + (size_t)R * sizeof(unsigned long long);
+    if (!workspace || workspace_bytes < keys_bytes || !aligned16(workspace))
+        return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes,
+                    keys_bytes);
+    // the key-rows path when the workspace holds its keys too (a workspace sized for
+    // more rows may not: then the general path, with the same result)
+    const bool rows_path = allow_rows && R <= kLmKeyRowsMaxR &&
+                           workspace_bytes >= keys_bytes + (size_t)n_vt * R * sizeof(unsigned long long);
+    unsigned int* ticket = static_cast<unsigned int*>(workspace);
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
+    unsigned long long* key_rows =
+        rows_path ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + keys_bytes) : nullptr;
+    // row groups of at most kLmMaxMT 16-row tiles, balanced (160 rows: 2 x 80)
+    const int mtiles = (R + 15) / 16;
+    const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
+    const int MT = (mtiles + n_rg - 1) / n_rg;
+    if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "%s: grid too large", name);
+    bool ok = false;
+    const SampleArgs no_sa{};
+    if (lm_wide(mtiles)) {
+        const int n_wg = (n_vt + 1) / 2;
+        const int n_rg_w = (mtiles + kLmMaxMTWide - 1) / kLmMaxMTWide;
+        const int MT_w = (mtiles + n_rg_w - 1) / n_rg_w;
+        switch (MT_w) {
+            case 1: ok = launch_tiles<1, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 2: ok = launch_tiles<2, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 3: ok = launch_tiles<3, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 4: ok = launch_tiles<4, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 5: ok = launch_tiles<5, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            case 6: ok = launch_tiles<6, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+            default: ok = launch_tiles<7, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
+        }
+    } else {
+        switch (MT) {
+            case 1: ok = launch_tiles<1, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
+            case 2: ok = launch_tiles<2, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
+            case 3: ok = launch_tiles<3, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
+            case 4: ok = launch_tiles<4, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
+            case 5: ok = launch_tiles<5, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 6: ok = launch_tiles<6, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 7: ok = launch_tiles<7, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            default: ok = launch_tiles<8, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+        }
+    }
+    if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
+    if (rows_path)
+        hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8), dim3(256), 0, st, key_rows, n_vt, R, argmax,
+                           maxval);
+    SV_LAUNCH_CHECK(name);
+    return SPEC_OK;
+}
+
+}  // namespace sv
+
 extern "C" {
 
 int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
@@ -652,61 +784,18 @@ int spec_lm_head_sample_dense(const spec_bf16* hidden, const spec_bf16* w_packed
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
     if (R < 1 || V < 1) return 0;
-    return 256 + (size_t)R * sizeof(unsigned long long);   // ticket (padded), one key per row
+    // ticket (padded), one key per row; at few rows also the [workgroups][R] key rows
+    size_t n = 256 + (size_t)R * sizeof(unsigned long long);
+    if (R <= sv::kLmKeyRowsMaxR) n += (size_t)sv::n_vtiles(V) * R * sizeof(unsigned long long);
+    return n;
 }
 
 int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
                         int32_t* argmax, float* maxval, void* workspace, size_t workspace_bytes,
                         void* stream) {
-    using namespace sv;
-    last_error().clear();
-    if (R < 1) return fail(SPEC_EINVAL, "spec_lm_head_argmax: R=%d < 1", R);
-    if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "spec_lm_head_argmax: H=%d not a positive multiple of %d", H, kLmHAlign);
-    if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "spec_lm_head_argmax: V=%d", V);
-    if (!hidden || !w_packed || !argmax) return fail(SPEC_EINVAL, "spec_lm_head_argmax: null required pointer");
-    if (!aligned16(hidden) || !aligned16(w_packed)) return fail(SPEC_EINVAL, "spec_lm_head_argmax: hidden and w_packed must be 16-byte aligned");
-    const spec_bf16* w = w_packed;
-    const size_t need = spec_lm_head_argmax_workspace_bytes(R, H, V);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(SPEC_EWORKSPACE, "spec_lm_head_argmax: workspace %zu bytes < %zu required (or null/misaligned)", workspace_bytes, need);
-    const int n_vt = n_vtiles(V);
-    unsigned int* ticket = static_cast<unsigned int*>(workspace);
-    unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
-    // row groups of at most kLmMaxMT 16-row tiles, balanced (160 rows: 2 x 80)
-    const int mtiles = (R + 15) / 16;
-    const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
-    const int MT = (mtiles + n_rg - 1) / n_rg;
-    if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "spec_lm_head_argmax: grid too large");
-    hipStream_t st = (hipStream_t)stream;
-    bool ok = false;
-    if (lm_wide(mtiles)) {
-        const int n_wg = (n_vt + 1) / 2;
-        const int n_rg_w = (mtiles + kLmMaxMTWide - 1) / kLmMaxMTWide;
-        const int MT_w = (mtiles + n_rg_w - 1) / n_rg_w;
-        switch (MT_w) {
-            case 1: ok = launch_tiles<1, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            case 2: ok = launch_tiles<2, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            case 3: ok = launch_tiles<3, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            case 4: ok = launch_tiles<4, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            case 5: ok = launch_tiles<5, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            case 6: ok = launch_tiles<6, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-            default: ok = launch_tiles<7, 4>(hidden, w, R, H, V, n_wg, n_rg_w, keys, ticket, argmax, maxval, st); break;
-        }
-    } else {
-        switch (MT) {
-            case 1: ok = launch_tiles<1, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 2: ok = launch_tiles<2, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 3: ok = launch_tiles<3, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 4: ok = launch_tiles<4, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 5: ok = launch_tiles<5, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 6: ok = launch_tiles<6, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 7: ok = launch_tiles<7, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            default: ok = launch_tiles<8, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-        }
-    }
-    if (!ok) return fail(SPEC_EINVAL, "spec_lm_head_argmax: no kernel variant for R=%d", R);
-    SV_LAUNCH_CHECK("spec_lm_head_argmax");
-    return SPEC_OK;
+    sv::last_error().clear();
+    return sv::lm_head_argmax_run("spec_lm_head_argmax", hidden, w_packed, R, H, V, argmax, maxval, workspace,
+                                  workspace_bytes, true, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -766,8 +855,9 @@ extern "C" int spec_lm_head_argmax_noalloc(const spec_bf16* hidden, const spec_b
     if (!hidden || !w_packed || !argmax) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: null required pointer");
     if (!aligned16(hidden) || !aligned16(w_packed))
         return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: hidden and w_packed must be 16-byte aligned");
-    const size_t need = spec_lm_head_argmax_workspace_bytes(R, H, V);
-    if (need == 0 || need > kScratchBytes) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: R=%d V=%d", R, V);
+    // the ticket and one key per row (the key-rows path of few rows is not used here)
+    const size_t need = 256 + (size_t)R * sizeof(unsigned long long);
+    if (need > kScratchBytes) return fail(SPEC_EINVAL, "spec_lm_head_argmax_noalloc: R=%d V=%d", R, V);
     void* ws = nullptr;
     const int rc = scratch_for_current_device(&ws);
     if (rc != SPEC_OK) return rc;
@@ -777,12 +867,6 @@ extern "C" int spec_lm_head_argmax_noalloc(const spec_bf16* hidden, const spec_b
     hipLaunchKernelGGL(scratch_clear_kernel, dim3((n16 + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                        static_cast<uint4*>(ws), n16);
     SV_LAUNCH_CHECK("spec_lm_head_argmax_noalloc");
-    const int r2 = spec_lm_head_argmax(hidden, w_packed, R, H, V, argmax, maxval, ws, need, stream);
-    if (r2 != SPEC_OK) {
-        // the message names the shared checks; say which entry point failed
-        const std::string msg = last_error();
-        last_error().clear();
-        return fail(r2, "spec_lm_head_argmax_noalloc: %s", msg.c_str());
-    }
-    return SPEC_OK;
+    return lm_head_argmax_run("spec_lm_head_argmax_noalloc", hidden, w_packed, R, H, V, argmax, maxval, ws, need,
+                              false, (hipStream_t)stream);
 }

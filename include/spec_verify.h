@@ -170,11 +170,15 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
  * argmax [R] int32, maxval [R] fp32.
  * Limits: R >= 1, H % 256 == 0, 1 <= V < 2^31 - 1; 16-byte aligned hidden,
  * w_packed, workspace. NaN logits never win. workspace: at least
- * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes (a ticket counter and one
- * 64-bit key per row, through which the workgroups merge their per-row maxima). It
- * must be all zero the first time it is used; every call leaves it zero again, so a
- * workspace is zero-filled once and then reused (also across HIP graph replays).
- * Calls that may overlap in time must not share a workspace.
+ * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes: a ticket counter and one
+ * 64-bit key per row, through which the workgroups merge their per-row maxima, and
+ * for R <= 64 after them one 64-bit key per (vocabulary workgroup, row), through
+ * which a second small kernel merges them instead (a workspace of at least the ticket
+ * and per-row keys but too small for these makes the call take the first way: the
+ * same result; smaller than that: SPEC_EWORKSPACE). The workspace must be all zero
+ * the first time it is used; every call leaves it zero again, so a workspace is
+ * zero-filled once and then reused, also for other row counts and across HIP graph
+ * replays. Calls that may overlap in time must not share a workspace.
  * ------------------------------------------------------------------------- */
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V);
 int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,
@@ -184,7 +188,8 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
 /* spec_lm_head_argmax_noalloc — spec_lm_head_argmax with no workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc). It computes exactly what
- * spec_lm_head_argmax computes (the same kernels, so the same bytes) and calls no
+ * spec_lm_head_argmax computes (the same tile kernel, so the same bytes; at R <= 64
+ * it merges the per-row maxima through the per-row keys, as at larger R) and calls no
  * allocating routine: its ticket and per-row keys live in a library-owned device
  * array of SPEC_NOALLOC_SCRATCH_BYTES bytes per GPU, which holds them for rows
  * R <= SPEC_NOALLOC_MAX_ROWS (larger R: SPEC_ECAPACITY, nothing launched). Each call

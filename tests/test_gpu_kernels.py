@@ -223,6 +223,34 @@ def test_lm_head_workspace_reuse(dev):
         assert int(ws.count_nonzero()) == 0, f"workspace not left zero after R={R}"
 
 
+@pytest.mark.parametrize("R", [1, 5, 16, 33, 48, 64])
+def test_lm_head_key_rows_path_equals_the_atomic_path(dev, R):
+    """At R <= 64 the per-row maxima are merged by a second kernel from per-workgroup
+    key rows; a workspace holding only the ticket and per-row keys makes the call merge
+    them through the atomic keys instead. Both give the same bytes, and both leave the
+    workspace zero."""
+    import greedy_draft_verify_amd as gdv
+    rng = np.random.default_rng(60 + R)
+    H, V = 512, 20000
+    w = torch.from_numpy((rng.standard_normal((V, H)) / math.sqrt(H)).astype(np.float32)).to(torch.bfloat16)
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    h = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(torch.bfloat16).to(dev)
+    full = gdv.lm_head_argmax_workspace_bytes(R, H, V)
+    small = 256 + 8 * R
+    assert full > small
+    outs = []
+    for nbytes in (full, small):
+        ws = gdv.workspace(nbytes, dev, zero=True)
+        am, mv = torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.float32, device=dev)
+        gdv.spec_lm_head_argmax(h, wp, V, am, mv, workspace_buf=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, nbytes
+        outs.append((am.cpu(), mv.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+    g_ref, t1, t2, _ = oracle.lm_head_argmax(bits(h), bits(w), R, H, V)
+    check_argmax(outs[0][0].numpy(), outs[0][1].numpy(), g_ref, t1, t2, f"key rows R={R}")
+
+
 def test_lm_head_tiny_workload(dev):
     x = synth.make_verify_inputs("tiny", seed=0)
     g, mv = gpu_lm_head(x.hidden, x.w, dev)
