@@ -393,7 +393,7 @@ def spec_lm_head_sample(hidden, w_packed, V, temperature, q_tok, q_prob, row_ctr
                         sample_res, workspace_buf=None, stream=None):
     """hidden [R,H] bf16, w_packed from spec_lm_head_pack; q_tok [R,NQ] int32 / q_prob [R,NQ] fp32
     (NQ may be 0: pass tensors of shape [R,0]); row_ctr [R,2] int32; outputs lse [R] fp32,
-    z_supp [R,NQ] fp32, sample_p/sample_res [R] int32. A workspace_buf must be zero on first use."""
+    z_supp [R,NQ] fp32, sample_p/sample_res [R] int32. A workspace_buf may hold anything."""
     _want(hidden, torch.bfloat16, "hidden", 2)
     _want(w_packed, torch.bfloat16, "w_packed", 1)
     R, H = hidden.shape
@@ -459,7 +459,7 @@ def spec_lm_head_sample_dense(hidden, w_packed, V, temperature, row_ctr, seed, l
                               stream=None):
     """The sampling pass for dense draft distributions: lse [R] fp32, sample_p [R] int32 (a
     draw from p of every row) and z [R,V] fp32 (logit / temperature of every entry). A
-    workspace_buf must be zero on first use (spec_lm_head_sample's size)."""
+    workspace_buf (spec_lm_head_sample's size) may hold anything."""
     _want(hidden, torch.bfloat16, "hidden", 2)
     _want(w_packed, torch.bfloat16, "w_packed", 1)
     R, H = hidden.shape

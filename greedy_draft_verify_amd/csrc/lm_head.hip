@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void lm_head_pack_kernel(const u16* __restrict
 struct SampleArgs {
     const int32_t* q_tok;     // [R][NQ] draft support per row (-1: unused)
     const int32_t* row_ctr;   // [R][2] Philox counter words of the row
-    float2* part;             // [R][n_vt] (max, sum of exp) per vocabulary group
+    float2* part;             // [R][n_vt] (max, sum of exp) per vocabulary group; best keys by atomics
+    float4* part4;            // or, at few rows: [R][n_vt] (max, sum of exp, best key's low and high words)
     float* z_supp;            // [R][NQ]
     float* z_out;             // [R][V] z of every entry, or null
     float inv_t;
@@ -193,8 +194,16 @@ __device__ __forceinline__ void sample_epilogue(const f32x4 (&acc)[MT][kLmNT], c
             const Best o = wbest[wv][tid];
             if (better(o.v, o.i, bb.v, bb.i)) bb = o;
         }
-        sa.part[(size_t)r * n_vt + vt] = make_float2(m, sm);
-        if (bb.i != 0x7fffffff) atomicMax(keys + r, pack_best(bb));
+        if (sa.part4) {
+            // few rows: one 16-byte record per (row, group), merged by the finalize (the
+            // atomics would queue at the end of the kernel, as in the greedy pass)
+            const unsigned long long key = bb.i != 0x7fffffff ? pack_best(bb) : 0ull;
+            sa.part4[(size_t)r * n_vt + vt] =
+                make_float4(m, sm, __uint_as_float((uint32_t)key), __uint_as_float((uint32_t)(key >> 32)));
+        } else {
+            sa.part[(size_t)r * n_vt + vt] = make_float2(m, sm);
+            if (bb.i != 0x7fffffff) atomicMax(keys + r, pack_best(bb));
+        }
     }
 }
 
@@ -552,31 +561,52 @@ static bool launch_tiles(const u16* hidden, const u16* w, int R, int H, int V, i
 //                                   z_v - lse + G_v outside the support
 // with ties to the smaller index. The row's key is reset to zero.
 __global__ __launch_bounds__(256) void sample_finalize_kernel(
-    const float2* __restrict__ part, int n_vt, int V, unsigned long long* __restrict__ keys,
+    const float2* __restrict__ part, const float4* __restrict__ part4, int n_vt, int V,
+    unsigned long long* __restrict__ keys,
     const int32_t* __restrict__ q_tok, const float* __restrict__ q_prob, int NQ, const int32_t* __restrict__ row_ctr,
     uint32_t key0, uint32_t key1, float* __restrict__ lse_out, float* __restrict__ z_supp,
     int32_t* __restrict__ sample_p, int32_t* __restrict__ sample_res) {
     __shared__ float2 s_w[4];
+    __shared__ unsigned long long s_k[4];
     const int r = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     float m = -INFINITY, sm = 0.f;
-    for (int c = tid; c < n_vt; c += 256) {
-        const float2 pm = part[(size_t)r * n_vt + c];
-        ms_merge(m, sm, pm.x, pm.y);
+    unsigned long long key = 0ull;
+    if (part4) {
+        for (int c = tid; c < n_vt; c += 256) {
+            const float4 pm = part4[(size_t)r * n_vt + c];
+            ms_merge(m, sm, pm.x, pm.y);
+            const unsigned long long k = (unsigned long long)__float_as_uint(pm.w) << 32 | __float_as_uint(pm.z);
+            key = k > key ? k : key;
+        }
+    } else {
+        for (int c = tid; c < n_vt; c += 256) {
+            const float2 pm = part[(size_t)r * n_vt + c];
+            ms_merge(m, sm, pm.x, pm.y);
+        }
     }
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) {
         const float om = __shfl_xor(m, d), os = __shfl_xor(sm, d);
         ms_merge(m, sm, om, os);
+        const unsigned long long ok = __shfl_xor(key, d);
+        key = ok > key ? ok : key;
     }
-    if (lane == 0) s_w[wave] = make_float2(m, sm);
+    if (lane == 0) {
+        s_w[wave] = make_float2(m, sm);
+        s_k[wave] = key;
+    }
     __syncthreads();
     if (tid != 0) return;
     float M = s_w[0].x, S = s_w[0].y;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) ms_merge(M, S, s_w[w].x, s_w[w].y);
+    for (int w = 1; w < 4; ++w) {
+        ms_merge(M, S, s_w[w].x, s_w[w].y);
+        key = s_k[w] > key ? s_k[w] : key;
+    }
+    key = s_k[0] > key ? s_k[0] : key;
+    if (!part4) key = atomicExch(keys + r, 0ull);   // the atomic maxima; left zero
     const float lse = M + __logf(S);
     lse_out[r] = lse;
-    const unsigned long long key = atomicExch(keys + r, 0ull);
     Best bp{-INFINITY, 0x7fffffff}, br{-INFINITY, 0x7fffffff};
     if (key != 0ull) {
         const float zg = unpack_value(key);
@@ -633,8 +663,10 @@ int spec_lm_head_pack(const spec_bf16* w, int32_t V, int32_t H, spec_bf16* w_pac
 size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
     if (R < 1 || V < 1) return 0;
-    // one key per row, then (max, sum of exp) per (row, vocabulary group)
-    return 256 + (size_t)R * sizeof(unsigned long long) + (size_t)R * sv::n_vtiles(V) * sizeof(float2);
+    // a header and one key per row, then per (row, vocabulary group) (max, sum of exp)
+    // or, up to 64 rows, (max, sum of exp, best key)
+    return 256 + ((size_t)R * sizeof(unsigned long long) + 15) / 16 * 16 +
+           (size_t)R * sv::n_vtiles(V) * (R <= sv::kLmKeyRowsMaxR ? sizeof(float4) : sizeof(float2));
 }
 
 }  // extern "C"
@@ -661,12 +693,16 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
         return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes, need);
     const int n_vt = n_vtiles(V);
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
-    float2* part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + 256 + (size_t)R * sizeof(unsigned long long));
+    // the per-(row, group) records, 16-byte aligned after the per-row keys
+    char* rec = static_cast<char*>(workspace) + 256 + ((size_t)R * sizeof(unsigned long long) + 15) / 16 * 16;
+    const bool records = R <= kLmKeyRowsMaxR;
+    float2* part = records ? nullptr : reinterpret_cast<float2*>(rec);
+    float4* part4 = records ? reinterpret_cast<float4*>(rec) : nullptr;
     const int mtiles = (R + 15) / 16;
     const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
     const int MT = (mtiles + n_rg - 1) / n_rg;
     if ((long long)n_vt * n_rg + 8 > 0x7fffffffLL) return fail(SPEC_ECAPACITY, "%s: grid too large", name);
-    SampleArgs sa{q_tok, row_ctr, part, z_supp, z_out, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
+    SampleArgs sa{q_tok, row_ctr, part, part4, z_supp, z_out, 1.f / temperature, NQ, (uint32_t)seed, (uint32_t)(seed >> 32)};
     hipStream_t st = (hipStream_t)stream;
     const spec_bf16* w = w_packed;
     bool ok = false;
@@ -682,7 +718,8 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
     }
     if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
     SV_LAUNCH_CHECK(name);
-    hipLaunchKernelGGL(sample_finalize_kernel, dim3(R), dim3(256), 0, st, part, n_vt, V, keys, q_tok, q_prob, NQ, row_ctr,
+    hipLaunchKernelGGL(sample_finalize_kernel, dim3(R), dim3(256), 0, st, part, part4, n_vt, V, keys, q_tok, q_prob, NQ,
+                       row_ctr,
                        sa.key0, sa.key1, lse, z_supp, sample_p, sample_res);
     SV_LAUNCH_CHECK(name);
     return SPEC_OK;

@@ -459,12 +459,12 @@ int spec_kv_compact(spec_bf16* k_pool, spec_bf16* v_pool, int64_t n_pages, const
  *   sample_res[r] = argmax_{v : p_v > q_v} ln(p_v - q_v) + G_v  (a draw from
  *                   norm(max(p - q, 0)); sample_p[r] if that set is empty)
  * with q_v the summed mass of v in the row's support. Logits never reach memory:
- * the tile kernel leaves per-(row, vocabulary group) softmax partials, the support
- * z's and the best z + G outside the support (a packed 64-bit key per row); a
- * per-row kernel reduces the partials in a fixed order and forms the draws.
- * workspace: spec_lm_head_sample_workspace_bytes(R, H, V) bytes, zero on first use;
- * every call leaves it zero (calls sharing one must not overlap). Limits as
- * spec_lm_head_argmax; 0 <= NQ <= 8; temperature finite and > 0. */
+ * the tile kernel leaves one record per (row, vocabulary group) (softmax partials
+ * and the best z + G outside the support as a packed 64-bit key) and the support
+ * z's; a per-row kernel reduces the records in a fixed order and forms the draws.
+ * workspace: spec_lm_head_sample_workspace_bytes(R, H, V) bytes, any contents
+ * (every call writes the records it reads; calls sharing one must not overlap).
+ * Limits as spec_lm_head_argmax; 0 <= NQ <= 8; temperature finite and > 0. */
 size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V);
 int spec_lm_head_sample(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
                         float temperature, const int32_t* q_tok, const float* q_prob, int32_t NQ,
