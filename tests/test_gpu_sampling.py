@@ -101,7 +101,7 @@ def test_lm_head_sample_parity(dev, R, V, NQ, T):
     logits = oracle.lm_head_logits(bits(hidden), bits(w), R, H, V)
     ref = oracle.sample_rows(logits, T, q_tok, q_prob, row_ctr, seed)
     _check_rows(got, ref, f"R={R} V={V}")
-    # the workspace is left zero: a second call with it gives the same bytes
+    # a second call with the same workspace gives the same bytes
     again = gpu_sample_rows(hidden.to(dev), wp, V, T, q_tok, q_prob, row_ctr, seed, dev, ws=ws)
     for key in ("lse", "sample_p", "sample_res"):
         assert np.array_equal(again[key], got[key]), key
