@@ -54,6 +54,11 @@ constexpr int kLmKB = 128;                // channels per K-block
 constexpr int kLmKS = kLmKB / 32;         // MFMA k-steps per K-block
 constexpr int kLmMaxMT = 8;               // 16-row tiles per row group
 constexpr int kLmHAlign = 256;            // H must be a multiple of this
+// Few-row paths. Greedy: one key per (vocabulary workgroup, row) in rows of this
+// stride (R rounded up to 8 keys, so a row starts on a 64-byte boundary). Sampling,
+// up to kLmSampleRecordsMaxR rows: one 16-byte record per (row, vocabulary group).
+__host__ __device__ constexpr int key_rows_stride(int R) { return (R + 7) / 8 * 8; }
+constexpr int kLmSampleRecordsMaxR = 64;
 
 // Packed W: fragment f = (((g * H/128 + kb) * 8 + t) * 4 + s) * 64 + lane holds
 // W[128 g + 16 t + lane % 16][128 kb + 32 s + 8 (lane / 16) .. + 8] (zero past V).
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
         }
         if (key_rows) {
             // few rows: this workgroup's row of keys, merged by lm_head_rows_finalize_kernel
-            key_rows[(size_t)vt * R + r0 + tid] = pack_best(b);
+            key_rows[(size_t)vt * key_rows_stride(R) + r0 + tid] = pack_best(b);
         } else {
             // the returned value is consumed, so the wave waits until the update is performed
             const unsigned long long prev = atomicMax(keys + r0 + tid, pack_best(b));
@@ -464,55 +469,74 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 }
 
 // Few rows (at most kLmKeyRowsMaxR): each workgroup stores its per-row keys as one
-// row of a [workgroups][R] array with plain stores, and this kernel merges them, 8
-// rows per workgroup, each thread reading every 32nd workgroup's keys of its row. At
-// these row counts the workgroups end close together, and the atomic maxima and
-// ticket of the general path then queue at the end of the kernel. Measured at
-// H = 4096, V = 151936 (outputs identical): 1 row 203 -> 183 us, 16: 194 -> 183,
-// 32: 195 -> 185, 48: 196 -> 188, 56: 197 -> 193, 64: 197 -> 195; 72 equal and 80-96
-// rows 1-2 us slower, so the general path is kept there. The maximum of the keys is
-// the same whichever path takes it.
+// row of a [workgroups][key_rows_stride(R)] array with plain stores, and
+// lm_head_rows_finalize_kernel merges them. At these row counts the workgroups end
+// close together, and the atomic maxima and ticket of the general path then queue at
+// the end of the kernel. Measured at H = 4096, V = 151936 (outputs identical): 1 row
+// 203 -> 183 us, 16: 194 -> 183, 32: 195 -> 185, 48: 196 -> 188, 64: 197 -> 195. At 72
+// and 80 rows the tile kernel is 6 us faster this way (193 vs 199 us at 80) but the
+// finalize launch costs as much, and at 96 rows 1 us more; the general path is kept
+// there. The maximum of the keys is the same whichever path takes it.
 constexpr int kLmKeyRowsMaxR = 64;
 static_assert(kLmKeyRowsMaxR <= 4 * 16, "the dispatch passes the key rows to the tile kernels of up to 4 row tiles");
 
-__global__ __launch_bounds__(256) void lm_head_rows_finalize_kernel(unsigned long long* __restrict__ key_rows,
-                                                                    int n_wg, int R, int32_t* __restrict__ argmax,
-                                                                    float* __restrict__ maxval) {
-    const int r = blockIdx.x * 8 + threadIdx.x % 8;
-    const int j0 = threadIdx.x / 8;
-    unsigned long long best = 0ull;
-    // every key is read by one thread, which leaves it zero (the workspace is zero
-    // after every call, whichever path the call took)
-    if (r < R) {
-        int i = j0;
-        for (; i + 7 * 32 < n_wg; i += 8 * 32) {
-            unsigned long long k[8];
+// Finalize: 8 rows per workgroup of 1024 threads. Thread t reads the keys of rows
+// 2(t%4), 2(t%4)+1 of the block (one 16-byte load: the stride is a multiple of 8
+// keys) from every 256th vocabulary workgroup, starting at t/4, all of them requested
+// before any is used (one round trip up to 2048 vocabulary workgroups); lanes 4 apart
+// then merge, then the 16 waves through LDS. Every key read is written back as zero,
+// so the workspace is zero after every call, whichever path the call took. (At
+// V = 151936: 4.9-5.4 us for 16-64 rows, against 5.8-6.4 for 256 threads reading one
+// key at a time in dependent batches.)
+constexpr int kLmFinThreads = 1024;
+constexpr int kLmFinBatch = 8;
+
+__global__ __launch_bounds__(kLmFinThreads) void lm_head_rows_finalize_kernel(unsigned long long* __restrict__ key_rows,
+                                                                              int n_wg, int R, int32_t* __restrict__ argmax,
+                                                                              float* __restrict__ maxval) {
+    constexpr int kStep = kLmFinThreads / 4;
+    const int q = threadIdx.x % 4, j0 = threadIdx.x / 4;
+    const int r0 = blockIdx.x * 8 + 2 * q;
+    const size_t stride = (size_t)key_rows_stride(R);
+    uint4* base = reinterpret_cast<uint4*>(key_rows + r0);
+    unsigned long long b0 = 0ull, b1 = 0ull;
+    for (int i0 = j0; i0 < n_wg; i0 += kLmFinBatch * kStep) {
+        uint4 k[kLmFinBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) k[u] = key_rows[(size_t)(i + u * 32) * R + r];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                best = k[u] > best ? k[u] : best;
-                key_rows[(size_t)(i + u * 32) * R + r] = 0ull;
-            }
+        for (int u = 0; u < kLmFinBatch; ++u) {
+            const int i = i0 + u * kStep;
+            k[u] = i < n_wg ? base[(size_t)i * stride / 2] : make_uint4(0, 0, 0, 0);
         }
-        for (; i < n_wg; i += 32) {
-            const unsigned long long x = key_rows[(size_t)i * R + r];
-            best = x > best ? x : best;
-            key_rows[(size_t)i * R + r] = 0ull;
+#pragma unroll
+        for (int u = 0; u < kLmFinBatch; ++u) {
+            const int i = i0 + u * kStep;
+            const unsigned long long x0 = ((unsigned long long)k[u].y << 32) | k[u].x;
+            const unsigned long long x1 = ((unsigned long long)k[u].w << 32) | k[u].z;
+            b0 = x0 > b0 ? x0 : b0;
+            b1 = x1 > b1 ? x1 : b1;
+            if (i < n_wg) base[(size_t)i * stride / 2] = make_uint4(0, 0, 0, 0);
         }
     }
-    // lanes 8 apart hold the same row
+    // lanes 4 apart hold the same two rows
 #pragma unroll
-    for (int d = 8; d < kWave; d <<= 1) {
-        const unsigned long long o = __shfl_xor(best, d);
-        best = o > best ? o : best;
+    for (int d = 4; d < kWave; d <<= 1) {
+        const unsigned long long o0 = __shfl_xor(b0, d), o1 = __shfl_xor(b1, d);
+        b0 = o0 > b0 ? o0 : b0;
+        b1 = o1 > b1 ? o1 : b1;
     }
-    __shared__ unsigned long long s_b[4][8];
-    if (threadIdx.x % kWave < 8) s_b[threadIdx.x / kWave][threadIdx.x % 8] = best;
+    constexpr int NW = kLmFinThreads / kWave;
+    __shared__ unsigned long long s_b[NW][8];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane < 4) {
+        s_b[wave][2 * lane] = b0;
+        s_b[wave][2 * lane + 1] = b1;
+    }
     __syncthreads();
+    const int r = blockIdx.x * 8 + threadIdx.x;
     if (threadIdx.x < 8 && r < R) {
+        unsigned long long best = s_b[0][threadIdx.x];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) best = s_b[w][threadIdx.x] > best ? s_b[w][threadIdx.x] : best;
+        for (int w = 1; w < NW; ++w) best = s_b[w][threadIdx.x] > best ? s_b[w][threadIdx.x] : best;
         argmax[r] = (int32_t)~(uint32_t)best;
         if (maxval) maxval[r] = unpack_value(best);
     }
@@ -666,7 +690,7 @@ size_t spec_lm_head_sample_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     // a header and one key per row, then per (row, vocabulary group) (max, sum of exp)
     // or, up to 64 rows, (max, sum of exp, best key)
     return 256 + ((size_t)R * sizeof(unsigned long long) + 15) / 16 * 16 +
-           (size_t)R * sv::n_vtiles(V) * (R <= sv::kLmKeyRowsMaxR ? sizeof(float4) : sizeof(float2));
+           (size_t)R * sv::n_vtiles(V) * (R <= sv::kLmSampleRecordsMaxR ? sizeof(float4) : sizeof(float2));
 }
 
 }  // extern "C"
@@ -695,7 +719,7 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
     // the per-(row, group) records, 16-byte aligned after the per-row keys
     char* rec = static_cast<char*>(workspace) + 256 + ((size_t)R * sizeof(unsigned long long) + 15) / 16 * 16;
-    const bool records = R <= kLmKeyRowsMaxR;
+    const bool records = R <= kLmSampleRecordsMaxR;
     float2* part = records ? nullptr : reinterpret_cast<float2*>(rec);
     float4* part4 = records ? reinterpret_cast<float4*>(rec) : nullptr;
     const int mtiles = (R + 15) / 16;
@@ -746,14 +770,16 @@ static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const s
     if (!workspace || workspace_bytes < keys_bytes || !aligned16(workspace))
         return fail(SPEC_EWORKSPACE, "%s: workspace %zu bytes < %zu required (or null/misaligned)", name, workspace_bytes,
                     keys_bytes);
-    // the key-rows path when the workspace holds its keys too (a workspace sized for
-    // more rows may not: then the general path, with the same result)
+    // the key-rows path when the workspace holds its key rows too (a workspace sized
+    // for more rows may not: then the general path, with the same result); they start
+    // 64-byte aligned after the keys (the finalize reads them 16 bytes at a time)
+    const size_t rows_at = 256 + (size_t)key_rows_stride(R) * sizeof(unsigned long long);
     const bool rows_path = allow_rows && R <= kLmKeyRowsMaxR &&
-                           workspace_bytes >= keys_bytes + (size_t)n_vt * R * sizeof(unsigned long long);
+                           workspace_bytes >= rows_at + (size_t)n_vt * key_rows_stride(R) * sizeof(unsigned long long);
     unsigned int* ticket = static_cast<unsigned int*>(workspace);
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
     unsigned long long* key_rows =
-        rows_path ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + keys_bytes) : nullptr;
+        rows_path ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + rows_at) : nullptr;
     // row groups of at most kLmMaxMT 16-row tiles, balanced (160 rows: 2 x 80)
     const int mtiles = (R + 15) / 16;
     const int n_rg = (mtiles + kLmMaxMT - 1) / kLmMaxMT;
@@ -788,7 +814,7 @@ static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const s
     }
     if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
     if (rows_path)
-        hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8), dim3(256), 0, st, key_rows, n_vt, R, argmax,
+        hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8), dim3(kLmFinThreads), 0, st, key_rows, n_vt, R, argmax,
                            maxval);
     SV_LAUNCH_CHECK(name);
     return SPEC_OK;
@@ -821,9 +847,11 @@ int spec_lm_head_sample_dense(const spec_bf16* hidden, const spec_bf16* w_packed
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
     if (R < 1 || V < 1) return 0;
-    // ticket (padded), one key per row; at few rows also the [workgroups][R] key rows
+    // ticket (padded), one key per row; at few rows the keys padded to
+    // key_rows_stride(R) and then the [workgroups][key_rows_stride(R)] key rows
     size_t n = 256 + (size_t)R * sizeof(unsigned long long);
-    if (R <= sv::kLmKeyRowsMaxR) n += (size_t)sv::n_vtiles(V) * R * sizeof(unsigned long long);
+    if (R <= sv::kLmKeyRowsMaxR)
+        n = 256 + (size_t)(sv::n_vtiles(V) + 1) * sv::key_rows_stride(R) * sizeof(unsigned long long);
     return n;
 }
 

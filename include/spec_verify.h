@@ -172,8 +172,9 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
  * w_packed, workspace. NaN logits never win. workspace: at least
  * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes: a ticket counter and one
  * 64-bit key per row, through which the workgroups merge their per-row maxima, and
- * for R <= 64 after them one 64-bit key per (vocabulary workgroup, row), through
- * which a second small kernel merges them instead (a workspace of at least the ticket
+ * for R <= 64, after the per-row keys padded to a multiple of 8, one 64-bit key per
+ * (vocabulary workgroup, row) in rows of that padded length, through which a second
+ * small kernel merges them instead (a workspace of at least the ticket
  * and per-row keys but too small for these makes the call take the first way: the
  * same result; smaller than that: SPEC_EWORKSPACE). The workspace must be all zero
  * the first time it is used; every call leaves it zero again, so a workspace is
