@@ -480,11 +480,12 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 constexpr int kLmKeyRowsMaxR = 64;
 static_assert(kLmKeyRowsMaxR <= 4 * 16, "the dispatch passes the key rows to the tile kernels of up to 4 row tiles");
 
-// Finalize: 8 rows per workgroup of 1024 threads. Thread t reads the keys of rows
-// 2(t%4), 2(t%4)+1 of the block (one 16-byte load: the stride is a multiple of 8
-// keys) from every 256th vocabulary workgroup, starting at t/4, all of them requested
-// before any is used (one round trip up to 2048 vocabulary workgroups); lanes 4 apart
-// then merge, then the 16 waves through LDS. Every key read is written back as zero,
+// Finalize: 8 rows per workgroup of up to 1024 threads (4 per vocabulary workgroup,
+// rounded up to whole waves). Thread t reads the keys of rows 2(t%4), 2(t%4)+1 of the
+// block (one 16-byte load: the stride is a multiple of 8 keys) from every
+// (threads/4)-th vocabulary workgroup, starting at t/4, all of them requested before
+// any is used (one round trip up to 2048 vocabulary workgroups); lanes 4 apart then
+// merge, then the waves through LDS. Every key read is written back as zero,
 // so the workspace is zero after every call, whichever path the call took. (At
 // V = 151936: 4.9-5.4 us for 16-64 rows, against 5.8-6.4 for 256 threads reading one
 // key at a time in dependent batches.)
@@ -494,7 +495,7 @@ constexpr int kLmFinBatch = 8;
 __global__ __launch_bounds__(kLmFinThreads) void lm_head_rows_finalize_kernel(unsigned long long* __restrict__ key_rows,
                                                                               int n_wg, int R, int32_t* __restrict__ argmax,
                                                                               float* __restrict__ maxval) {
-    constexpr int kStep = kLmFinThreads / 4;
+    const int kStep = (int)blockDim.x / 4;
     const int q = threadIdx.x % 4, j0 = threadIdx.x / 4;
     const int r0 = blockIdx.x * 8 + 2 * q;
     const size_t stride = (size_t)key_rows_stride(R);
@@ -524,8 +525,8 @@ __global__ __launch_bounds__(kLmFinThreads) void lm_head_rows_finalize_kernel(un
         b0 = o0 > b0 ? o0 : b0;
         b1 = o1 > b1 ? o1 : b1;
     }
-    constexpr int NW = kLmFinThreads / kWave;
-    __shared__ unsigned long long s_b[NW][8];
+    const int NW = (int)blockDim.x / kWave;
+    __shared__ unsigned long long s_b[kLmFinThreads / kWave][8];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if (lane < 4) {
         s_b[wave][2 * lane] = b0;
@@ -535,7 +536,6 @@ __global__ __launch_bounds__(kLmFinThreads) void lm_head_rows_finalize_kernel(un
     const int r = blockIdx.x * 8 + threadIdx.x;
     if (threadIdx.x < 8 && r < R) {
         unsigned long long best = s_b[0][threadIdx.x];
-#pragma unroll
         for (int w = 1; w < NW; ++w) best = s_b[w][threadIdx.x] > best ? s_b[w][threadIdx.x] : best;
         argmax[r] = (int32_t)~(uint32_t)best;
         if (maxval) maxval[r] = unpack_value(best);
@@ -814,7 +814,8 @@ static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const s
     }
     if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
     if (rows_path)
-        hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8), dim3(kLmFinThreads), 0, st, key_rows, n_vt, R, argmax,
+        hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8),
+                           dim3(std::min(kLmFinThreads, (4 * n_vt + kWave - 1) / kWave * kWave)), 0, st, key_rows, n_vt, R, argmax,
                            maxval);
     SV_LAUNCH_CHECK(name);
     return SPEC_OK;
