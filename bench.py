@@ -73,6 +73,9 @@ class VerifyStep:
         self.pos_out, self.acc_len, self.n_emit, self.next_tok, self.acc_status = e(), e(), e(), e(), e()
         self.emit = torch.empty((self.B, wl.kmax + 1), dtype=torch.int32, device=dev)
         self.drafts = None
+        # the timed step takes the lm_head and the acceptance as one call
+        # (spec_lm_head_argmax_accept: the same bytes as the two calls in turn)
+        self.fused = True
 
     def attn(self):
         gdv.spec_verify_attn(self.q, self.k_new, self.v_new, self.k_pool, self.v_pool, self.page_table,
@@ -82,6 +85,16 @@ class VerifyStep:
     def lm_head(self):
         gdv.spec_lm_head_argmax(self.hidden, self.w_packed, self.x.wl.V, self.argmax, self.maxval,
                                 workspace_buf=self.lm_ws)
+
+    def lm_head_accept(self):
+        gdv.spec_lm_head_argmax_accept(self.hidden, self.w_packed, self.x.wl.V, self.argmax, self.maxval,
+                                       self.drafts, self.k, self.d2t, self.pos, self.pos_out, self.acc_len,
+                                       self.n_emit, self.emit, self.next_tok, self.acc_status,
+                                       workspace_buf=self.lm_ws)
+
+    def lm_ops(self):
+        """Names of the timed step's second and third calls (the third absent when fused)."""
+        return ("spec_lm_head_argmax_accept", None) if self.fused else ("spec_lm_head_argmax", "spec_greedy_accept")
 
     def accept(self):
         gdv.spec_greedy_accept(self.argmax, self.drafts, self.k, self.d2t, self.x.wl.V, self.pos, self.pos_out,
@@ -177,10 +190,14 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
         step.attn()
         if ev:
             ev[1].record(stream)
-        step.lm_head()
+        if step.fused:
+            step.lm_head_accept()
+        else:
+            step.lm_head()
         if ev:
             ev[2].record(stream)
-        step.accept()
+        if not step.fused:
+            step.accept()
         if ev:
             ev[3].record(stream)
 
@@ -226,7 +243,7 @@ def time_verify_step(step: VerifyStep, steps: int, warmup: int) -> dict:
             "lm_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
             "acc_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
             "median_us": {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
-                          for i, name in enumerate(("spec_verify_attn", "spec_lm_head_argmax", "spec_greedy_accept"))}}
+                          for i, name in enumerate(("spec_verify_attn",) + step.lm_ops()) if name}}
 
 
 def step_report(step: VerifyStep, t: dict) -> dict:
@@ -240,11 +257,13 @@ def step_report(step: VerifyStep, t: dict) -> dict:
     at_gbs = at_b / (t["attn_ms"] / 1e3) / 1e9
     lm_tflops = 2.0 * x.R * wl.H * wl.V / (t["lm_ms"] / 1e3) / 1e12
     return {"rows": x.R, "step_us": t["graph_ms"] * 1e3, "eager_step_us": t["eager_ms"] * 1e3,
+            "lm_us": (t["lm_ms"] + (0.0 if step.fused else t["acc_ms"])) * 1e3,
             "rows_per_s": x.R / (t["graph_ms"] / 1e3), "emitted_tokens_per_s": emitted / (t["graph_ms"] / 1e3),
             "emitted_per_step": emitted,
             "accept_len_hist": np.bincount(acc_len, minlength=wl.kmax + 1).tolist(),
-            "kernel_us": {"spec_verify_attn": t["attn_ms"] * 1e3, "spec_lm_head_argmax": t["lm_ms"] * 1e3,
-                          "spec_greedy_accept": t["acc_ms"] * 1e3},
+            "kernel_us": {name: v for name, v in zip(("spec_verify_attn",) + step.lm_ops(),
+                                                     (t["attn_ms"] * 1e3, t["lm_ms"] * 1e3, t["acc_ms"] * 1e3))
+                          if name},
             "kernel_us_median": t["median_us"],
             "attn": {"bound": "hbm", "algorithmic_bytes": at_b, "achieved": at_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": at_gbs / HBM_PEAK_GBS},
@@ -277,9 +296,8 @@ def config_leg(name: str, dev, steps: int, warmup: int, seed: int = 0) -> dict:
            "kv_split_tokens": gdv.attn_split_tokens(x.page_table.shape[1]), **rep}
     log(f"[bench] {name}: step {rep['step_us']:.1f} us ({rep['rows_per_s']:.0f} rows/s, "
         f"{rep['emitted_tokens_per_s']:.0f} tokens/s): attn {rep['kernel_us']['spec_verify_attn']:.1f} us "
-        f"({100 * rep['attn']['frac']:.0f}% HBM), lm_head {rep['kernel_us']['spec_lm_head_argmax']:.1f} us "
-        f"({100 * rep['lm_head']['hbm_frac']:.0f}% HBM, {100 * rep['lm_head']['mfma_frac']:.0f}% MFMA), accept "
-        f"{rep['kernel_us']['spec_greedy_accept']:.1f} us")
+        f"({100 * rep['attn']['frac']:.0f}% HBM), lm_head+accept {rep['lm_us']:.1f} us "
+        f"({100 * rep['lm_head']['hbm_frac']:.0f}% HBM, {100 * rep['lm_head']['mfma_frac']:.0f}% MFMA)")
     del step, x
     torch.cuda.empty_cache()
     return rep
@@ -753,11 +771,12 @@ def main():
 
     t = time_verify_step(step, args.steps, args.warmup)
     rep = step_report(step, t)
+    lm_call = step.lm_ops()[0]
     ms_step = t["graph_ms"]
     lm, at = rep["lm_head"], rep["attn"]
     log(f"[bench] step {ms_step * 1e3:.1f} us (graph replay; eager {t['eager_ms'] * 1e3:.1f} us): attn "
-        f"{t['attn_ms'] * 1e3:.1f} us ({at['achieved']:.0f} GB/s), lm_head {t['lm_ms'] * 1e3:.1f} us "
-        f"({lm['GB/s']:.0f} GB/s, {lm['TFLOP/s']:.1f} TFLOP/s), accept {t['acc_ms'] * 1e3:.1f} us; "
+        f"{t['attn_ms'] * 1e3:.1f} us ({at['achieved']:.0f} GB/s), lm_head+accept {rep['lm_us']:.1f} us "
+        f"({lm['GB/s']:.0f} GB/s, {lm['TFLOP/s']:.1f} TFLOP/s); "
         f"accept-length histogram {rep['accept_len_hist']}; {drafts_note}")
 
     extras = {}
@@ -866,7 +885,7 @@ def main():
         "accept_len_hist": rep["accept_len_hist"],
         "kernel_us": rep["kernel_us"],
         "kernel_us_median": rep["kernel_us_median"],
-        "roofline": {"kernel": "spec_lm_head_argmax", "bound": lm["bound"],
+        "roofline": {"kernel": lm_call, "bound": lm["bound"],
                      "achieved": lm["GB/s"] if lm["bound"] == "hbm" else lm["TFLOP/s"],
                      "peak": HBM_PEAK_GBS if lm["bound"] == "hbm" else BF16_PEAK_TFLOPS,
                      "unit": "GB/s" if lm["bound"] == "hbm" else "TFLOP/s", "frac": lm_frac,

@@ -25,6 +25,7 @@ DELTA_RECORD, DELTA_ROLLBACK, DELTA_BOTH, DELTA_VERIFY, DELTA_RESCAN = 1, 2, 3, 
 EXPORTED = ["spec_version", "spec_last_error", "spec_attn_split_tokens",
             "spec_verify_attn_workspace_bytes", "spec_verify_attn",
             "spec_lm_head_argmax_workspace_bytes", "spec_lm_head_argmax", "spec_lm_head_argmax_noalloc",
+            "spec_lm_head_argmax_accept",
             "spec_lm_head_packed_bytes",
             "spec_lm_head_pack", "spec_greedy_accept", "spec_delta_verify_rollback",
             "spec_verify_attn_tree_workspace_bytes", "spec_verify_attn_tree", "spec_tree_accept",
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.spec_lm_head_argmax_workspace_bytes.restype = sz
         L.spec_lm_head_argmax.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.spec_lm_head_argmax_noalloc.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.spec_lm_head_argmax_accept.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, i32, vp, vp,
+                                                 vp, vp, vp, vp, vp, vp, sz, vp]
         L.spec_lm_head_packed_bytes.argtypes = [i32, i32]
         L.spec_lm_head_packed_bytes.restype = sz
         L.spec_lm_head_pack.argtypes = [vp, i32, i32, vp, vp]
@@ -383,6 +386,43 @@ def spec_greedy_accept(argmax, drafts, k, d2t, V, pos_in, pos_out, accept_len, n
                                   _ptr(accept_len), _ptr(n_emit), _ptr(emit), _ptr(next_tok),
                                   _ptr(seq_status), _stream(stream))
     _check(rc, "spec_greedy_accept")
+
+
+def spec_lm_head_argmax_accept(hidden, w_packed, V, argmax, maxval, drafts, k, d2t, pos_in, pos_out, accept_len,
+                               n_emit, emit, next_tok, seq_status, workspace_buf=None, stream=None):
+    """spec_lm_head_argmax then spec_greedy_accept on its argmax, in one call (same arguments
+    and outputs as the two; the workspace as spec_lm_head_argmax's)."""
+    _want(hidden, torch.bfloat16, "hidden", 2)
+    _want(w_packed, torch.bfloat16, "w_packed", 1)
+    _want(argmax, torch.int32, "argmax", 1)
+    if maxval is not None:
+        _want(maxval, torch.float32, "maxval", 1)
+    for t, n in ((drafts, "drafts"), (k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (emit, "emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _want(t, torch.int32, n)
+    if d2t is not None:
+        _want(d2t, torch.int32, "d2t", 1)
+    _want(drafts, torch.int32, "drafts", 2)
+    R, H = hidden.shape
+    B, kmax = drafts.shape
+    if w_packed.numel() * 2 != lm_head_packed_bytes(V, H):
+        raise SpecError(f"w_packed: {w_packed.numel() * 2} bytes, expected {lm_head_packed_bytes(V, H)} "
+                        f"for V={V} H={H}")
+    _shape(argmax, (R,), "argmax")
+    if maxval is not None:
+        _shape(maxval, (R,), "maxval")
+    _shape(emit, (B, kmax + 1), "emit")
+    for t, n in ((k, "k"), (pos_in, "pos_in"), (pos_out, "pos_out"), (accept_len, "accept_len"),
+                 (n_emit, "n_emit"), (next_tok, "next_tok"), (seq_status, "seq_status")):
+        _shape(t, (B,), n)
+    if workspace_buf is None:
+        workspace_buf = workspace(lm_head_argmax_workspace_bytes(R, H, V), hidden.device, zero=True)
+    rc = lib().spec_lm_head_argmax_accept(_ptr(hidden), _ptr(w_packed), R, H, V, _ptr(argmax), _ptr(maxval),
+                                          _ptr(drafts), kmax, _ptr(k), _ptr(d2t), 0 if d2t is None else d2t.shape[0],
+                                          B, _ptr(pos_in), _ptr(pos_out), _ptr(accept_len), _ptr(n_emit), _ptr(emit),
+                                          _ptr(next_tok), _ptr(seq_status), _ptr(workspace_buf),
+                                          workspace_buf.numel(), _stream(stream))
+    _check(rc, "spec_lm_head_argmax_accept")
 
 
 def lm_head_sample_workspace_bytes(R, H, V) -> int:

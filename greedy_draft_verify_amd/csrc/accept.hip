@@ -26,7 +26,6 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int kAcceptThreads = 1024;
-constexpr int kAcceptMaxB = 8192;
 constexpr int kMaxStop = 16;
 
 // STOP: the emitted tokens end after the first stop token and after remaining[s]
@@ -38,6 +37,116 @@ constexpr int kMaxStop = 16;
 // its greedy tokens right after it; the bonus token and the emitted tokens are then
 // taken from registers (draft j and row j live in lane j), so a sequence with
 // k < 64 costs two dependent global round trips.
+// One sequence's acceptance, by one wave. gs[j] is the greedy token of the sequence's
+// row j (j <= ks), in global memory or LDS; ks, p, lim and x (lane j's draft j) are
+// loaded and bits holds the flags of the sequence found by the caller.
+template <bool STOP>
+__device__ __forceinline__ void accept_one(
+    int s, int lane, const int32_t* gs, int bits, int ks, int p, int lim, int x, const int32_t* __restrict__ drafts,
+    int kmax, const int32_t* __restrict__ d2t, int n_draft_vocab, int V, int32_t* pos_out,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ n_emit, int32_t* __restrict__ emit,
+    int32_t* __restrict__ next_tok, int32_t* __restrict__ status, const int* s_stop, int n_stop,
+    int32_t* __restrict__ done) {
+    int32_t* e = emit + (size_t)s * (kmax + 1);
+    auto flag = [&](int why) {
+        for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
+        if (lane == 0) {
+            status[s] = why;
+            accept_len[s] = -1;
+            n_emit[s] = 0;
+            next_tok[s] = -1;
+            pos_out[s] = p;
+            if constexpr (STOP) done[s] = 0;
+        }
+    };
+    if (bits) {
+        flag(bits);
+        return;
+    }
+    // rows off .. off + ks are in range (the packing is defined); lane j < 64 holds
+    // draft j mapped (x0) and the greedy token of row j (g0)
+    const int g0 = lane <= ks ? gs[lane] : 0;
+    bool bad_tok = false;
+    auto map_draft = [&](int xv, bool& bad) {
+        if (d2t) {
+            if (xv < 0 || xv >= n_draft_vocab) {
+                bad = true;
+                return 0;
+            }
+            const int m = d2t[xv];
+            if (m < 0 || m >= V) bad = true;
+            return m;
+        }
+        if (xv < 0 || xv >= V) bad = true;
+        return xv;
+    };
+    const int x0 = lane < ks ? map_draft(x, bad_tok) : 0;
+    // first mismatch; token range checks over every used draft
+    int a = ks;
+    {
+        const unsigned long long mm = __ballot(lane < ks && (bad_tok || x0 != g0));
+        if (mm) a = (int)__builtin_ctzll(mm);
+    }
+    for (int base = kWave; base < ks; base += kWave) {
+        const int j = base + lane;
+        bool miss = false;
+        if (j < ks) {
+            const int mj = map_draft(drafts[(size_t)s * kmax + j], bad_tok);
+            miss = bad_tok || mj != gs[j];
+        }
+        const unsigned long long mm = __ballot(miss);
+        if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
+    }
+    if (__ballot(bad_tok)) {
+        flag(SPEC_STATUS_BAD_TOKEN);
+        return;
+    }
+    // token j of the output: mapped draft j for j < a, the greedy token of row a at a
+    const int g_a = a < kWave ? __shfl(g0, a) : gs[a];
+    auto token = [&](int j) {
+        if (j == a) return g_a;
+        if (j < kWave) return x0;   // j == lane
+        const int xv = drafts[(size_t)s * kmax + j];
+        return d2t ? d2t[xv] : xv;
+    };
+    int c = a + 1;   // tokens emitted
+    if constexpr (STOP) {
+        // up to and including the first stop token, then at most lim tokens
+        for (int base = 0; base <= a; base += kWave) {
+            const int j = base + lane;
+            bool is_stop = false;
+            if (j <= a) {
+                const int t = token(j);
+                for (int q = 0; q < n_stop; ++q) is_stop |= t == s_stop[q];
+            }
+            const unsigned long long mm = __ballot(is_stop);
+            if (mm && c == a + 1) c = base + (int)__builtin_ctzll(mm) + 1;
+        }
+    }
+    const bool at_lim = c >= lim;
+    if (at_lim) c = lim;
+    int last = -1;
+    for (int j = lane; j <= kmax; j += kWave) {
+        const int val = j < c ? token(j) : -1;
+        e[j] = val;
+        if (j == c - 1) last = val;
+    }
+    // the last emitted token, from the lane that wrote it
+    last = __shfl(last, (c - 1) % kWave);
+    if (lane == 0) {
+        status[s] = 0;
+        accept_len[s] = a < c ? a : c;
+        n_emit[s] = c;
+        next_tok[s] = last;
+        pos_out[s] = p + c;
+        if constexpr (STOP) {
+            bool is_stop = false;
+            for (int q = 0; q < n_stop; ++q) is_stop |= last == s_stop[q];
+            done[s] = is_stop || at_lim;
+        }
+    }
+}
+
 template <bool STOP>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const int32_t* __restrict__ g, const int32_t* __restrict__ drafts, int kmax,
@@ -77,105 +186,104 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
         if (p < 0) bits |= SPEC_STATUS_BAD_POS;
         if (STOP && remaining && !bits && lim < 1) bits = SPEC_STATUS_BAD_LIMIT;
-        int32_t* e = emit + (size_t)s * (kmax + 1);
-        auto flag = [&](int why) {
-            for (int j = lane; j <= kmax; j += kWave) e[j] = -1;
-            if (lane == 0) {
-                status[s] = why;
-                accept_len[s] = -1;
-                n_emit[s] = 0;
-                next_tok[s] = -1;
-                pos_out[s] = p;
-                if constexpr (STOP) done[s] = 0;
-            }
-        };
-        if (bits) {
-            flag(bits);
-            continue;
-        }
-        // rows off .. off + ks are in range (the packing is defined); lane j < 64 holds
-        // draft j mapped (x0) and the greedy token of row j (g0)
-        const int g0 = lane <= ks ? g[off + lane] : 0;
-        bool bad_tok = false;
-        auto map_draft = [&](int xv, bool& bad) {
-            if (d2t) {
-                if (xv < 0 || xv >= n_draft_vocab) {
-                    bad = true;
-                    return 0;
+        accept_one<STOP>(s, lane, g + off, bits, ks, p, lim, x, drafts, kmax, d2t, n_draft_vocab, V, pos_out,
+                         accept_len, n_emit, emit, next_tok, status, s_stop, n_stop, done);
+    }
+}
+
+// The greedy step's argmax finalize fused with the acceptance (the lm_head's few-row
+// path stores one key per (vocabulary workgroup, row); this kernel stands in for its
+// finalize and for accept_kernel). One workgroup per sequence: it merges the keys of
+// the sequence's own rows into their greedy tokens (the maximum key, as the finalize
+// takes it), writes argmax (and maxval) for those rows, writes back as zero every key
+// it read, and one wave then takes the sequence's acceptance with the tokens in LDS.
+// With an undefined packing (every sequence flagged) workgroup s takes the rows
+// s*R/B .. (s+1)*R/B - 1 instead, so argmax is still written and the keys cleared.
+__global__ __launch_bounds__(kAcceptThreads) void argmax_accept_kernel(
+    unsigned long long* __restrict__ key_rows, int n_vt, int stride, int R, int32_t* __restrict__ argmax,
+    float* __restrict__ maxval, const int32_t* __restrict__ drafts, int kmax, const int32_t* __restrict__ k,
+    const int32_t* __restrict__ d2t, int n_draft_vocab, int V, int B, const int32_t* __restrict__ pos_in,
+    int32_t* pos_out, int32_t* __restrict__ accept_len, int32_t* __restrict__ n_emit,
+    int32_t* __restrict__ emit, int32_t* __restrict__ next_tok, int32_t* __restrict__ status) {
+    constexpr int NW = kAcceptThreads / kWave;
+    __shared__ long long s_wsum[NW];
+    __shared__ int s_wbad[NW];
+    __shared__ int s_off[kAcceptMaxB];
+    __shared__ unsigned long long s_best[kArgmaxAcceptMaxRows];
+    __shared__ int s_g[kArgmaxAcceptMaxRows];
+    const int tid = threadIdx.x, lane = tid % kWave, s = blockIdx.x;
+    // the sequence's scalars and drafts (wave 0 takes the acceptance), requested
+    // before the scan
+    const int ks = k[s];
+    int p = 0, x = 0;
+    if (tid < kWave) {
+        p = pos_in[s];
+        if (lane < kmax) x = drafts[(size_t)s * kmax + lane];
+    }
+    if (tid < kArgmaxAcceptMaxRows) s_best[tid] = 0ull;   // visible after the scan's barriers
+    const bool packing_ok = block_row_offsets<kAcceptThreads>(k, B, R, s_wsum, s_wbad, s_off);
+    int r_lo, n_rows;
+    if (packing_ok) {
+        r_lo = s_off[s];
+        n_rows = ks + 1;   // rows r_lo .. r_lo + ks < R
+    } else {
+        r_lo = (int)((long long)s * R / B);
+        n_rows = (int)((long long)(s + 1) * R / B) - r_lo;
+    }
+    // thread t: row t % n_rows, every (per)-th vocabulary workgroup from t / n_rows, a
+    // batch of 8 keys requested before any is used (neighbouring threads read
+    // neighbouring keys of one vocabulary workgroup's row block); the maxima meet in
+    // LDS. (Whole waves or lane groups per row, merged by shuffles, measured slower:
+    // each lane then reads its own row block, 14.5 vs 9.4 us at 16 sequences of 5 rows.)
+    if (n_rows > 0) {
+        const int per = kAcceptThreads / n_rows;
+        const int j = tid % n_rows, v0 = tid / n_rows;
+        if (v0 < per) {
+            unsigned long long* col = key_rows + r_lo + j;
+            unsigned long long best = 0ull;
+            for (int i0 = v0; i0 < n_vt; i0 += 8 * per) {
+                unsigned long long kk[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * per;
+                    kk[u] = i < n_vt ? col[(size_t)i * stride] : 0ull;
                 }
-                const int m = d2t[xv];
-                if (m < 0 || m >= V) bad = true;
-                return m;
-            }
-            if (xv < 0 || xv >= V) bad = true;
-            return xv;
-        };
-        const int x0 = lane < ks ? map_draft(x, bad_tok) : 0;
-        // first mismatch; token range checks over every used draft
-        int a = ks;
-        {
-            const unsigned long long mm = __ballot(lane < ks && (bad_tok || x0 != g0));
-            if (mm) a = (int)__builtin_ctzll(mm);
-        }
-        for (int base = kWave; base < ks; base += kWave) {
-            const int j = base + lane;
-            bool miss = false;
-            if (j < ks) {
-                const int mj = map_draft(drafts[(size_t)s * kmax + j], bad_tok);
-                miss = bad_tok || mj != g[off + j];
-            }
-            const unsigned long long mm = __ballot(miss);
-            if (mm && a == ks) a = base + (int)__builtin_ctzll(mm);
-        }
-        if (__ballot(bad_tok)) {
-            flag(SPEC_STATUS_BAD_TOKEN);
-            continue;
-        }
-        // token j of the output: mapped draft j for j < a, the greedy token of row a at a
-        const int g_a = a < kWave ? __shfl(g0, a) : g[off + a];
-        auto token = [&](int j) {
-            if (j == a) return g_a;
-            if (j < kWave) return x0;   // j == lane
-            const int xv = drafts[(size_t)s * kmax + j];
-            return d2t ? d2t[xv] : xv;
-        };
-        int c = a + 1;   // tokens emitted
-        if constexpr (STOP) {
-            // up to and including the first stop token, then at most lim tokens
-            for (int base = 0; base <= a; base += kWave) {
-                const int j = base + lane;
-                bool is_stop = false;
-                if (j <= a) {
-                    const int t = token(j);
-                    for (int q = 0; q < n_stop; ++q) is_stop |= t == s_stop[q];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * per;
+                    best = kk[u] > best ? kk[u] : best;
+                    if (i < n_vt) col[(size_t)i * stride] = 0ull;
                 }
-                const unsigned long long mm = __ballot(is_stop);
-                if (mm && c == a + 1) c = base + (int)__builtin_ctzll(mm) + 1;
             }
-        }
-        const bool at_lim = c >= lim;
-        if (at_lim) c = lim;
-        int last = -1;
-        for (int j = lane; j <= kmax; j += kWave) {
-            const int val = j < c ? token(j) : -1;
-            e[j] = val;
-            if (j == c - 1) last = val;
-        }
-        // the last emitted token, from the lane that wrote it
-        last = __shfl(last, (c - 1) % kWave);
-        if (lane == 0) {
-            status[s] = 0;
-            accept_len[s] = a < c ? a : c;
-            n_emit[s] = c;
-            next_tok[s] = last;
-            pos_out[s] = p + c;
-            if constexpr (STOP) {
-                bool is_stop = false;
-                for (int q = 0; q < n_stop; ++q) is_stop |= last == s_stop[q];
-                done[s] = is_stop || at_lim;
-            }
+            atomicMax(&s_best[j], best);
         }
     }
+    __syncthreads();
+    if (tid < n_rows) {
+        const unsigned long long key = s_best[tid];
+        const int gv = (int32_t)~(uint32_t)key;
+        s_g[tid] = gv;
+        argmax[r_lo + tid] = gv;
+        if (maxval) maxval[r_lo + tid] = unpack_value(key);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        int bits = 0;
+        if (!packing_ok || ks > kmax) bits |= SPEC_STATUS_BAD_ROWS;
+        if (p < 0) bits |= SPEC_STATUS_BAD_POS;
+        accept_one<false>(s, lane, s_g, bits, ks, p, 0x7fffffff, x, drafts, kmax, d2t, n_draft_vocab, V, pos_out,
+                          accept_len, n_emit, emit, next_tok, status, nullptr, 0, nullptr);
+    }
+}
+
+int launch_argmax_accept(unsigned long long* key_rows, int n_vt, int stride, int R, int32_t* argmax, float* maxval,
+                         const int32_t* drafts, int kmax, const int32_t* k, const int32_t* d2t, int n_draft_vocab,
+                         int V, int B, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                         int32_t* emit, int32_t* next_tok, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(argmax_accept_kernel, dim3(B), dim3(kAcceptThreads), 0, st, key_rows, n_vt, stride, R, argmax,
+                       maxval, drafts, kmax, k, d2t, n_draft_vocab, V, B, pos_in, pos_out, accept_len, n_emit, emit,
+                       next_tok, status);
+    return SPEC_OK;
 }
 
 // The stop rule on its own, applied in place to the outputs of any acceptance walk

@@ -175,6 +175,16 @@ inline int seq_grid(int B, int NT) {
 std::string& last_error();
 int fail(int code, const char* fmt, ...);
 
+// Acceptance limits, and the greedy step's fused argmax finalize + acceptance
+// (accept.hip), launched by spec_lm_head_argmax_accept after the lm_head's pass that
+// stores one key per (vocabulary workgroup, row) in rows of `stride` keys.
+constexpr int kAcceptMaxB = 8192;
+constexpr int kArgmaxAcceptMaxRows = 96;
+int launch_argmax_accept(unsigned long long* key_rows, int n_vt, int stride, int R, int32_t* argmax, float* maxval,
+                         const int32_t* drafts, int kmax, const int32_t* k, const int32_t* d2t, int n_draft_vocab,
+                         int V, int B, const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                         int32_t* emit, int32_t* next_tok, int32_t* status, hipStream_t st);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 #define SV_LAUNCH_CHECK(what)                                                              \

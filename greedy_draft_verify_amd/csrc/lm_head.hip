@@ -478,7 +478,8 @@ __global__ __launch_bounds__(kLmThreads, 2) void lm_head_tile_kernel(
 // finalize launch costs as much, and at 96 rows 1 us more; the general path is kept
 // there. The maximum of the keys is the same whichever path takes it.
 constexpr int kLmKeyRowsMaxR = 64;
-static_assert(kLmKeyRowsMaxR <= 4 * 16, "the dispatch passes the key rows to the tile kernels of up to 4 row tiles");
+static_assert(kLmKeyRowsMaxR <= 6 * 16 && kArgmaxAcceptMaxRows <= 6 * 16,
+              "the dispatch passes the key rows to the tile kernels of up to 6 row tiles");
 
 // Finalize: 8 rows per workgroup of up to 1024 threads (4 per vocabulary workgroup,
 // rounded up to whole waves). Thread t reads the keys of rows 2(t%4), 2(t%4)+1 of the
@@ -753,12 +754,15 @@ static int lm_head_sample_impl(const char* name, const spec_bf16* hidden, const 
 
 namespace sv {
 
-// The greedy lm_head call: argument checks, then the tile kernel for the row count;
-// allow_rows lets few rows take the key-rows path (whose part of the workspace the
-// no-allocation entry point does not have).
+// The greedy lm_head call: argument checks, then the tile kernel for the row count.
+// Up to rows_max rows the key-rows path is taken when the workspace holds it (the
+// no-allocation entry point passes 0). With rows_out the call stops after the tile
+// kernel and hands over the key rows (null after the general path), which the
+// caller's own kernel then merges; otherwise the finalize kernel merges them.
 static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R,
                               int32_t H, int32_t V, int32_t* argmax, float* maxval, void* workspace,
-                              size_t workspace_bytes, bool allow_rows, hipStream_t st) {
+                              size_t workspace_bytes, int rows_max, hipStream_t st,
+                              unsigned long long** rows_out = nullptr) {
     if (R < 1) return fail(SPEC_EINVAL, "%s: R=%d < 1", name, R);
     if (H < kLmHAlign || H % kLmHAlign) return fail(SPEC_EINVAL, "%s: H=%d not a positive multiple of %d", name, H, kLmHAlign);
     if (V < 1 || V == 0x7fffffff) return fail(SPEC_EINVAL, "%s: V=%d", name, V);
@@ -774,7 +778,7 @@ static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const s
     // for more rows may not: then the general path, with the same result); they start
     // 64-byte aligned after the keys (the finalize reads them 16 bytes at a time)
     const size_t rows_at = 256 + (size_t)key_rows_stride(R) * sizeof(unsigned long long);
-    const bool rows_path = allow_rows && R <= kLmKeyRowsMaxR &&
+    const bool rows_path = R <= rows_max &&
                            workspace_bytes >= rows_at + (size_t)n_vt * key_rows_stride(R) * sizeof(unsigned long long);
     unsigned int* ticket = static_cast<unsigned int*>(workspace);
     unsigned long long* keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
@@ -806,14 +810,16 @@ static int lm_head_argmax_run(const char* name, const spec_bf16* hidden, const s
             case 2: ok = launch_tiles<2, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
             case 3: ok = launch_tiles<3, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
             case 4: ok = launch_tiles<4, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
-            case 5: ok = launch_tiles<5, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
-            case 6: ok = launch_tiles<6, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
+            case 5: ok = launch_tiles<5, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
+            case 6: ok = launch_tiles<6, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st, no_sa, key_rows); break;
             case 7: ok = launch_tiles<7, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
             default: ok = launch_tiles<8, 2>(hidden, w, R, H, V, n_vt, n_rg, keys, ticket, argmax, maxval, st); break;
         }
     }
     if (!ok) return fail(SPEC_EINVAL, "%s: no kernel variant for R=%d", name, R);
-    if (rows_path)
+    if (rows_out)
+        *rows_out = key_rows;
+    else if (rows_path)
         hipLaunchKernelGGL(lm_head_rows_finalize_kernel, dim3((R + 7) / 8),
                            dim3(std::min(kLmFinThreads, (4 * n_vt + kWave - 1) / kWave * kWave)), 0, st, key_rows, n_vt, R, argmax,
                            maxval);
@@ -848,10 +854,11 @@ int spec_lm_head_sample_dense(const spec_bf16* hidden, const spec_bf16* w_packed
 size_t spec_lm_head_argmax_workspace_bytes(int32_t R, int32_t H, int32_t V) {
     (void)H;
     if (R < 1 || V < 1) return 0;
-    // ticket (padded), one key per row; at few rows the keys padded to
-    // key_rows_stride(R) and then the [workgroups][key_rows_stride(R)] key rows
+    // ticket (padded), one key per row; at few rows (the key-rows paths of this call
+    // and of spec_lm_head_argmax_accept) the keys padded to key_rows_stride(R) and
+    // then the [workgroups][key_rows_stride(R)] key rows
     size_t n = 256 + (size_t)R * sizeof(unsigned long long);
-    if (R <= sv::kLmKeyRowsMaxR)
+    if (R <= std::max(sv::kLmKeyRowsMaxR, sv::kArgmaxAcceptMaxRows))
         n = 256 + (size_t)(sv::n_vtiles(V) + 1) * sv::key_rows_stride(R) * sizeof(unsigned long long);
     return n;
 }
@@ -861,7 +868,37 @@ int spec_lm_head_argmax(const spec_bf16* hidden, const spec_bf16* w_packed, int3
                         void* stream) {
     sv::last_error().clear();
     return sv::lm_head_argmax_run("spec_lm_head_argmax", hidden, w_packed, R, H, V, argmax, maxval, workspace,
-                                  workspace_bytes, true, (hipStream_t)stream);
+                                  workspace_bytes, sv::kLmKeyRowsMaxR, (hipStream_t)stream);
+}
+
+int spec_lm_head_argmax_accept(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H, int32_t V,
+                               int32_t* argmax, float* maxval, const int32_t* drafts, int32_t kmax, const int32_t* k,
+                               const int32_t* d2t, int32_t n_draft_vocab, int32_t B, const int32_t* pos_in,
+                               int32_t* pos_out, int32_t* accept_len, int32_t* n_emit, int32_t* emit, int32_t* next_tok,
+                               int32_t* seq_status, void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace sv;
+    last_error().clear();
+    const char* name = "spec_lm_head_argmax_accept";
+    // the acceptance's checks first, so that a refused call launches nothing
+    if (B < 1 || B > kAcceptMaxB) return fail(SPEC_EINVAL, "%s: B=%d outside 1..%d", name, B, kAcceptMaxB);
+    if (kmax < 0 || kmax > 1024) return fail(SPEC_EINVAL, "%s: kmax=%d outside 0..1024", name, kmax);
+    if (d2t && n_draft_vocab < 1) return fail(SPEC_EINVAL, "%s: d2t given with n_draft_vocab=%d", name, n_draft_vocab);
+    if (!k || !pos_in || !pos_out || !accept_len || !n_emit || !emit || !next_tok || !seq_status || (kmax > 0 && !drafts))
+        return fail(SPEC_EINVAL, "%s: null required pointer", name);
+    hipStream_t st = (hipStream_t)stream;
+    unsigned long long* key_rows = nullptr;
+    const int rc = lm_head_argmax_run(name, hidden, w_packed, R, H, V, argmax, maxval, workspace, workspace_bytes,
+                                      kArgmaxAcceptMaxRows, st, &key_rows);
+    if (rc != SPEC_OK) return rc;
+    if (key_rows) {
+        launch_argmax_accept(key_rows, n_vtiles(V), key_rows_stride(R), R, argmax, maxval, drafts, kmax, k, d2t,
+                             n_draft_vocab, V, B, pos_in, pos_out, accept_len, n_emit, emit, next_tok, seq_status, st);
+        SV_LAUNCH_CHECK(name);
+        return SPEC_OK;
+    }
+    // the general path: the argmax is complete, the acceptance runs on its own
+    return spec_greedy_accept(argmax, drafts, kmax, k, d2t, n_draft_vocab, V, B, R, pos_in, pos_out, accept_len,
+                              n_emit, emit, next_tok, seq_status, stream);
 }
 
 }  // extern "C"
@@ -934,5 +971,5 @@ extern "C" int spec_lm_head_argmax_noalloc(const spec_bf16* hidden, const spec_b
                        static_cast<uint4*>(ws), n16);
     SV_LAUNCH_CHECK("spec_lm_head_argmax_noalloc");
     return lm_head_argmax_run("spec_lm_head_argmax_noalloc", hidden, w_packed, R, H, V, argmax, maxval, ws, need,
-                              false, (hipStream_t)stream);
+                              0, (hipStream_t)stream);
 }

@@ -9,6 +9,7 @@
  *   spec_verify_attn           KV append in place + paged causal attention
  *   spec_lm_head_argmax        lm_head contraction with the greedy argmax fused in
  *   spec_greedy_accept         greedy acceptance and position rollback
+ *   spec_lm_head_argmax_accept the lm_head argmax and the greedy acceptance in one call
  *   spec_delta_verify_rollback Gated DeltaNet per-token state record and restore
  *
  * and, for drafts shaped as a tree (trie or star) instead of a chain:
@@ -172,9 +173,10 @@ int spec_verify_attn(const spec_bf16* q, const spec_bf16* k_new, const spec_bf16
  * w_packed, workspace. NaN logits never win. workspace: at least
  * spec_lm_head_argmax_workspace_bytes(R, H, V) bytes: a ticket counter and one
  * 64-bit key per row, through which the workgroups merge their per-row maxima, and
- * for R <= 64, after the per-row keys padded to a multiple of 8, one 64-bit key per
+ * for R <= 96, after the per-row keys padded to a multiple of 8, one 64-bit key per
  * (vocabulary workgroup, row) in rows of that padded length, through which a second
- * small kernel merges them instead (a workspace of at least the ticket
+ * small kernel merges them instead (this call up to R = 64, spec_lm_head_argmax_accept
+ * up to 96) (a workspace of at least the ticket
  * and per-row keys but too small for these makes the call take the first way: the
  * same result; smaller than that: SPEC_EWORKSPACE). The workspace must be all zero
  * the first time it is used; every call leaves it zero again, so a workspace is
@@ -246,6 +248,26 @@ int spec_greedy_accept(const int32_t* argmax, const int32_t* drafts, int32_t kma
                        int32_t B, int32_t R, const int32_t* pos_in, int32_t* pos_out,
                        int32_t* accept_len, int32_t* n_emit, int32_t* emit, int32_t* next_tok,
                        int32_t* seq_status, void* stream);
+
+/* spec_lm_head_argmax_accept — spec_lm_head_argmax followed by spec_greedy_accept
+ * on its argmax, as one call: the same outputs, bit for bit (argmax, maxval when
+ * non-NULL, and every acceptance output and status), with the arguments of the two
+ * calls (R, the packing of k and the workspace as there; the workspace is sized by
+ * spec_lm_head_argmax_workspace_bytes(R, H, V), must be zero the first time it is
+ * used and is left zero). Defined by the two passages cited for those calls; the
+ * fusion is this library's: for R <= 96 with the full workspace the per-row maxima
+ * over vocabulary groups are taken by the acceptance kernel itself (one workgroup
+ * per sequence merges its own rows' keys, then one wave walks its drafts), which
+ * saves the separate finalize of the few-row path and one launch. Otherwise it runs
+ * the two calls' kernels in turn. Returns the first error of either call's checks
+ * before launching anything that call would launch.
+ * ------------------------------------------------------------------------- */
+int spec_lm_head_argmax_accept(const spec_bf16* hidden, const spec_bf16* w_packed, int32_t R, int32_t H,
+                               int32_t V, int32_t* argmax, float* maxval, const int32_t* drafts, int32_t kmax,
+                               const int32_t* k, const int32_t* d2t, int32_t n_draft_vocab, int32_t B,
+                               const int32_t* pos_in, int32_t* pos_out, int32_t* accept_len, int32_t* n_emit,
+                               int32_t* emit, int32_t* next_tok, int32_t* seq_status, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* spec_greedy_accept_stop — spec_greedy_accept with stop tokens and a generation
  * limit (oxinfer step: an accepted stop token ends the round, the committed tokens

@@ -140,3 +140,21 @@ def test_product_path_does_not_touch_the_oracle():
                 assert not re.search(r"^\s*(import|from)\s+oracle\b|oracle\.(so|h|c)\b", src, re.M), f
     out = subprocess.run(["ldd", gdv.LIB_PATH], capture_output=True, text=True).stdout
     assert "oracle" not in out
+
+
+def test_fused_argmax_accept_checks_before_launching():
+    """spec_lm_head_argmax_accept refuses bad acceptance or lm_head arguments with the
+    codes of the two calls it stands for (host checks only: fake pointers never reach
+    a kernel)."""
+    L = gdv.lib()
+    p = _vp()
+    args = lambda B, kmax, H, ws: (p, p, 4, H, 1000, p, None, p, kmax, p, None, 0, B, p, p, p, p, p, p, p, p, ws,
+                                   None)
+    assert L.spec_lm_head_argmax_accept(*args(0, 3, 256, 1 << 30)) == -1          # B < 1
+    assert b"B=0" in L.spec_last_error()
+    assert L.spec_lm_head_argmax_accept(*args(1, 1025, 256, 1 << 30)) == -1       # kmax > 1024
+    assert L.spec_lm_head_argmax_accept(*args(1, 3, 100, 1 << 30)) == -1         # H not a multiple of 256
+    assert L.spec_lm_head_argmax_accept(*args(1, 3, 256, 8)) == -4                # workspace too small
+    # a null required pointer of the acceptance
+    assert L.spec_lm_head_argmax_accept(p, p, 4, 256, 1000, p, None, p, 3, None, None, 0, 1, p, p, p, p, p, p, p,
+                                        p, 1 << 30, None) == -1
