@@ -216,3 +216,50 @@ def test_tree_accept_random_shapes(dev, seed):
     ref = _oracle_accept(*args)
     got = gpu_tree_accept(*args[:-1], dev)
     _assert_tree_accept_equal(got, ref, f"random tree accept seed {seed}")
+
+
+@pytest.mark.parametrize("seed", _seeds(10))
+def test_lm_head_argmax_accept_random_shapes(dev, seed):
+    """spec_lm_head_argmax_accept gives the bytes of spec_lm_head_argmax followed by
+    spec_greedy_accept on random batch, ragged k, draft map, hidden and vocabulary sizes
+    (fused up to 96 rows, the two calls' kernels above), and its walk is the oracle's on
+    its greedy tokens."""
+    import greedy_draft_verify_amd as gdv
+    from tests.test_gpu_fused import _run, _same
+    rng = np.random.default_rng(9700 + seed)
+    kmax = int(rng.choice([0, 1, 3, 7, 15, 31, 63, 95]))
+    B = int(rng.integers(1, 41))
+    k = rng.integers(0, kmax + 1, B).astype(np.int32)
+    R = int((k + 1).sum())
+    H = int(rng.choice([256, 512]))
+    V = int(rng.integers(1, 6000))
+    print(f"[rand argmax+accept] seed {seed}: B={B} kmax={kmax} R={R} H={H} V={V}", flush=True)
+    w = torch.from_numpy((rng.standard_normal((V, H)) / math.sqrt(H)).astype(np.float32)).to(torch.bfloat16)
+    wp = gdv.spec_lm_head_pack(w.to(dev))
+    h = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(torch.bfloat16).to(dev)
+    g = torch.empty(R, dtype=torch.int32, device=dev)
+    gdv.spec_lm_head_argmax(h, wp, V, g)
+    g = g.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(k + 1)])
+    p_match = float(rng.uniform(0.3, 0.95))
+    drafts = np.zeros((B, kmax), np.int32)
+    for s in range(B):
+        for j in range(int(k[s])):
+            drafts[s, j] = g[off[s] + j] if rng.random() < p_match else int(rng.integers(0, V))
+    d2t_np = None
+    if V > 1 and rng.random() < 0.4:
+        # drafts in a draft vocabulary: id i stands for target d2t[i]
+        d2t_np = rng.permutation(V).astype(np.int32)
+        inv = np.argsort(d2t_np).astype(np.int32)
+        drafts = inv[drafts]
+    pos = rng.integers(0, 100000, B).astype(np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    d2t = None if d2t_np is None else t(d2t_np)
+    a = _run(gdv, True, h, wp, V, t(drafts), t(k), d2t, t(pos))
+    b = _run(gdv, False, h, wp, V, t(drafts), t(k), d2t, t(pos))
+    _same(a, b, f"random argmax+accept seed {seed}")
+    ref = oracle.greedy_accept(a["argmax"].numpy(), drafts, kmax, k, d2t_np, 0 if d2t_np is None else V, V, B, R,
+                               pos)
+    for n, m in (("pos_out", "pos_out"), ("accept_len", "accept_len"), ("n_emit", "n_emit"), ("emit", "emit"),
+                 ("next_tok", "next_tok"), ("seq_status", "status")):
+        assert np.array_equal(a[n].numpy(), ref[m]), (n, seed)
