@@ -1,7 +1,8 @@
 """The verify step captured as a HIP graph and replayed gives the eager step's bytes.
 
-The benchmark times graph replays of spec_verify_attn -> spec_lm_head_argmax ->
-spec_greedy_accept. This test captures that step for the b16k4 workload (the
+The benchmark times graph replays of spec_verify_attn -> spec_lm_head_argmax_accept
+(the lm_head and the acceptance as one call; the two calls in turn give the same
+bytes). This test captures that step, and the one with the two calls, for the b16k4 workload (the
 benchmark's configuration) and for a ragged batch, replays it several times with
 eager work and host synchronisations between the replays, and checks every output
 of every replay against the eager step byte for byte (the step appends the same
@@ -17,8 +18,9 @@ from tests.conftest import gpu_available
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two_calls"])
 @pytest.mark.parametrize("name", ["b16k4", "ragged"])
-def test_graph_replay_matches_eager(name):
+def test_graph_replay_matches_eager(name, fused):
     import bench
     dev = torch.device("cuda:0")
     x = synth.make_verify_inputs(name, seed=3, device=dev)
@@ -33,8 +35,11 @@ def test_graph_replay_matches_eager(name):
 
     def run():
         step.attn()
-        step.lm_head()
-        step.accept()
+        if fused:
+            step.lm_head_accept()
+        else:
+            step.lm_head()
+            step.accept()
 
     run()
     torch.cuda.synchronize()
